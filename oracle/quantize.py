@@ -1,0 +1,97 @@
+"""Per-group and per-block FP8 quantization with FP32 scales.
+
+Test infrastructure (see the package docstring): not part of the product path.
+
+The recipe ("DeepSeek recipe: per-(1x128) activation scales x per-(128x128)
+weight scales", deepgemm-rust README, "What's implemented" table, fp8_gemm_nt
+row): each 128 inputs of a row get an FP8 rounding with a scale of their own
+(Linnet "Backend plugins" page, module docstring of the DeepGEMM plugin
+source), and the weight has one scale per 128x128 block.  Scales are FP32, not
+powers of two: the Hopper kernels take f32 scales and the plugin asks for no
+UE8M0 cast (Linnet page, DeepGemm.probe comment and the fp8_gemm_nt call with
+disable_ue8m0_cast=True).
+
+Readings where the pages are silent (each listed in the design notes):
+* scale s = fl32(amax / 448) with amax the exact float32 maximum magnitude;
+* an all-zero group gets s = 1;
+* the element is y = fl32(x / s), a correctly rounded float32 division (not a
+  multiplication by a reciprocal), then rounded to E4M3 (``e4m3_encode``);
+* activation scales are stored "column by column" with the rows padded to a
+  multiple of four (Linnet page, module docstring and the `padded` row count
+  in _BlockProduct.execute): SA is float32 [K/128][sa_ld], sa_ld = roundup(M, 4),
+  entry [g][m] the scale of row m's group g; entries of rows >= M unspecified
+  (this oracle fills them with NaN);
+* weight scales are row-major float32 [ceil(N/128)][K/128] (deepgemm-rust
+  README, "Quick start", the sfb shape); a partial last block of rows uses the
+  rows present.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .e4m3 import E4M3_MAX, e4m3_encode
+
+GROUP = 128
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float32."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _scale_of(amax: np.ndarray) -> np.ndarray:
+    """FP32 scale for a set of float32 amax values: fl32(amax / 448), 1 if amax == 0."""
+    amax = np.asarray(amax, dtype=np.float32)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)  # IEEE float32 division
+    return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize_groups(x_bf16: np.ndarray, sa_ld: int | None = None):
+    """Activation quantization, one scale per (row, 128-column group).
+
+    x_bf16: uint16 [M][K] bfloat16 bit patterns, K a multiple of 128.
+    Returns (q uint8 [M][K] E4M3 codes, sa float32 [K/128][sa_ld]).
+    """
+    x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
+    m, k = x_bf16.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    if sa_ld is None:
+        sa_ld = -(-m // 4) * 4
+    if sa_ld < m:
+        raise ValueError("sa_ld must be at least M")
+    x = bf16_bits_to_f32(x_bf16).reshape(m, k // GROUP, GROUP)
+    amax = np.max(np.abs(x), axis=2) if m else np.zeros((0, k // GROUP), np.float32)
+    s = _scale_of(amax)  # [M][K/128]
+    y = (x / s[:, :, None]).astype(np.float32)  # IEEE float32 division
+    q = e4m3_encode(y).reshape(m, k)
+    sa = np.full((k // GROUP, sa_ld), np.nan, dtype=np.float32)
+    sa[:, :m] = s.T
+    return q, sa
+
+
+def quantize_blocks(w_bf16: np.ndarray):
+    """Weight quantization, one scale per 128x128 block.
+
+    w_bf16: uint16 [N][K] bfloat16 bit patterns, K a multiple of 128.
+    Returns (q uint8 [N][K], sb float32 [ceil(N/128)][K/128]).
+    """
+    w_bf16 = np.asarray(w_bf16, dtype=np.uint16)
+    n, k = w_bf16.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    w = bf16_bits_to_f32(w_bf16)
+    nb, kb = -(-n // GROUP), k // GROUP
+    q = np.empty((n, k), dtype=np.uint8)
+    sb = np.empty((nb, kb), dtype=np.float32)
+    for i in range(nb):
+        rows = slice(i * GROUP, min(n, (i + 1) * GROUP))
+        for j in range(kb):
+            cols = slice(j * GROUP, (j + 1) * GROUP)
+            block = w[rows, cols]
+            s = _scale_of(np.max(np.abs(block)))
+            sb[i, j] = s
+            q[rows, cols] = e4m3_encode((block / s).astype(np.float32))
+    return q, sb

@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for the block-scaled FP8 linear, shared by the
+tests, the benchmark and the oracle's callers.
+
+This module holds input generation only: Gaussian draws, outlier planting,
+top-k expert routing and the 128-row-aligned grouped layout.  It contains none
+of the method's arithmetic (no quantization, scaling or products) and imports
+neither the oracle nor the HIP library, so both sides can consume its arrays.
+
+Every value is drawn in float32 from numpy's PCG64 and rounded to the nearest
+bfloat16 (ties to even); the bfloat16 bit patterns (uint16) are what both
+sides receive.  Workload shapes are the ones the pages' model uses (Qwen3-8B
+linears, Linnet "Backend plugins" page, DeepGEMM section; the M=1, N=12288,
+K=4096 decode linear of the AReno FP8 decode pull request, "Testing" section)
+and a 32-expert MoE layer with K=7168, N=4096 per expert.  No trained weights
+or real prompts are involved.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ALIGN = 128  # grouped layout: every group starts at a multiple of 128 rows
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), as uint16 bits.
+    Inputs here are finite Gaussian draws; NaN/inf are not produced."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _rngs(seed: int, n: int) -> list[np.random.Generator]:
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def gaussian_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return f32_to_bf16_bits(x)
+
+
+def activation_bf16(rng: np.random.Generator, m: int, k: int, outliers: bool, outlier_rng=None) -> np.ndarray:
+    """A ~ N(0, 1) in float32; with ``outliers``, exactly round(0.001*M*K)
+    distinct uniformly chosen positions are multiplied by 20 before the
+    bfloat16 rounding."""
+    x = rng.standard_normal(size=(m, k), dtype=np.float32)
+    if outliers:
+        n_out = int(round(0.001 * m * k))
+        if n_out:
+            orng = outlier_rng if outlier_rng is not None else rng
+            pos = orng.choice(m * k, size=n_out, replace=False)
+            x.reshape(-1)[pos] *= np.float32(20.0)
+    return f32_to_bf16_bits(x)
+
+
+# --------------------------------------------------------------------- dense
+@dataclass
+class Linear:
+    name: str
+    m: int
+    n: int
+    k: int
+    a: np.ndarray  # uint16 [M][K] bf16 bits
+    b: np.ndarray  # uint16 [N][K] bf16 bits
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+
+def single_linear(seed: int = 1) -> Linear:
+    """Single linear: A 128x512 ~ N(0,1), B 256x512 ~ N(0,0.02)."""
+    ra, rb = _rngs(seed, 2)
+    return Linear("single_128x256x512", 128, 256, 512, gaussian_bf16(ra, (128, 512), 1.0), gaussian_bf16(rb, (256, 512), 0.02))
+
+
+PREFILL_SHAPES = (("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 24576, 4096), ("down", 4096, 12288))
+
+
+def prefill_linears(seed: int = 2, m: int = 2048, names=None) -> list[Linear]:
+    """Qwen3-8B-shaped prefill linears at M tokens: activations N(0,1) with
+    0.1% outliers x20, weights N(0,0.02)."""
+    rngs = _rngs(seed, 3 * len(PREFILL_SHAPES))
+    out = []
+    for i, (name, n, k) in enumerate(PREFILL_SHAPES):
+        if names is not None and name not in names:
+            continue
+        ra, rb, ro = rngs[3 * i : 3 * i + 3]
+        a = activation_bf16(ra, m, k, outliers=True, outlier_rng=ro)
+        b = gaussian_bf16(rb, (n, k), 0.02)
+        out.append(Linear(f"prefill_{name}_{m}x{n}x{k}", m, n, k, a, b))
+    return out
+
+
+DECODE_SHAPES = ((12288, 4096), (4096, 12288))
+
+
+def decode_linear(m: int, n: int, k: int, seed: int = 3) -> Linear:
+    """Decode-shaped linear (M in {1,4,16}); same distributions as prefill."""
+    sub = {(12288, 4096): 0, (4096, 12288): 1}.get((n, k), 2)
+    ra, rb, ro = _rngs(seed * 1000 + sub * 100 + m, 3)
+    a = activation_bf16(ra, m, k, outliers=True, outlier_rng=ro)
+    b = gaussian_bf16(rb, (n, k), 0.02)
+    return Linear(f"decode_{m}x{n}x{k}", m, n, k, a, b)
+
+
+def square_linear(m: int, n: int, k: int, seed: int = 5) -> Linear:
+    ra, rb = _rngs(seed * 1000 + (m >> 10), 2)
+    return Linear(f"square_{m}x{n}x{k}", m, n, k, gaussian_bf16(ra, (m, k), 1.0), gaussian_bf16(rb, (n, k), 0.02))
+
+
+def random_linear(m: int, n: int, k: int, seed: int, a_std: float = 1.0, b_std: float = 0.02) -> Linear:
+    ra, rb = _rngs(seed, 2)
+    return Linear(f"rand_{m}x{n}x{k}", m, n, k, gaussian_bf16(ra, (m, k), a_std), gaussian_bf16(rb, (n, k), b_std))
+
+
+# ------------------------------------------------------------------- grouped
+def zipf_topk_routing(rng: np.random.Generator, tokens: int, experts: int, topk: int, alpha: float) -> np.ndarray:
+    """Each token picks ``topk`` distinct experts, drawn one after another
+    without replacement with probability proportional to rank^-alpha
+    (rank r = 1..experts is expert r-1).  Returns int64 [tokens][topk]."""
+    p = np.arange(1, experts + 1, dtype=np.float64) ** -alpha
+    p /= p.sum()
+    return np.stack([rng.choice(experts, size=topk, replace=False, p=p) for _ in range(tokens)])
+
+
+def grouped_layout(group_sizes, align: int = ALIGN):
+    """128-row-aligned contiguous layout: group g occupies rows
+    [start[g], start[g] + size[g]) and is zero-padded to a multiple of
+    ``align``; m_indices[r] = g for a real row of group g and -1 for padding.
+    Returns (starts int64[G], padded_sizes int64[G], m_indices int32[M_pad])."""
+    sizes = np.asarray(group_sizes, dtype=np.int64)
+    padded = -(-sizes // align) * align
+    starts = np.concatenate([[0], np.cumsum(padded)[:-1]]).astype(np.int64)
+    m_indices = np.full(int(padded.sum()), -1, dtype=np.int32)
+    for g, (s, n) in enumerate(zip(starts, sizes)):
+        m_indices[s : s + n] = g
+    return starts, padded, m_indices
+
+
+@dataclass
+class Grouped:
+    name: str
+    num_groups: int
+    n: int
+    k: int
+    sizes: np.ndarray  # real rows per group
+    starts: np.ndarray
+    m_indices: np.ndarray  # int32 [M_pad]
+    a: np.ndarray  # uint16 [M_pad][K]; padding rows are +0
+    b: np.ndarray  # uint16 [G][N][K]
+    token_of_row: np.ndarray = field(default=None)  # int64 [M_pad], -1 on padding
+
+    @property
+    def m(self) -> int:
+        return int(self.m_indices.shape[0])
+
+    @property
+    def useful_flops(self) -> int:
+        return 2 * int(self.sizes.sum()) * self.n * self.k
+
+
+def moe_grouped(
+    seed: int = 4,
+    experts: int = 32,
+    tokens: int = 8192,
+    topk: int = 4,
+    alpha: float = 1.1,
+    n: int = 4096,
+    k: int = 7168,
+    with_weights: bool = True,
+) -> Grouped:
+    """MoE grouped workload: tokens x_t ~ N(0,1), routed top-k by a seeded
+    Zipf(alpha) expert choice; rows grouped by expert in ascending token order
+    and zero-padded to 128-row multiples; expert weights [G][N][K] ~ N(0,0.02)."""
+    r_route, r_x, r_w = _rngs(seed, 3)
+    choice = zipf_topk_routing(r_route, tokens, experts, topk, alpha)
+    sizes = np.array([(choice == g).any(axis=1).sum() for g in range(experts)], dtype=np.int64)
+    starts, _padded, m_indices = grouped_layout(sizes)
+    x = gaussian_bf16(r_x, (tokens, k), 1.0)
+    a = np.zeros((m_indices.shape[0], k), dtype=np.uint16)
+    token_of_row = np.full(m_indices.shape[0], -1, dtype=np.int64)
+    for g in range(experts):
+        toks = np.nonzero((choice == g).any(axis=1))[0]  # ascending token order
+        a[starts[g] : starts[g] + toks.size] = x[toks]
+        token_of_row[starts[g] : starts[g] + toks.size] = toks
+    if with_weights:
+        b = np.empty((experts, n, k), dtype=np.uint16)
+        for g in range(experts):
+            b[g] = gaussian_bf16(r_w, (n, k), 0.02)
+    else:
+        b = None
+    return Grouped(f"moe_{experts}x{n}x{k}_zipf{alpha}_top{topk}", experts, n, k, sizes, starts, m_indices, a, b, token_of_row)
+
+
+def small_grouped(sizes, n: int, k: int, seed: int) -> Grouped:
+    """A small grouped case with given real group sizes (zeros allowed)."""
+    r_x, r_w = _rngs(seed, 2)
+    sizes = np.asarray(sizes, dtype=np.int64)
+    starts, _padded, m_indices = grouped_layout(sizes)
+    a = np.zeros((m_indices.shape[0], k), dtype=np.uint16)
+    for g, (s, c) in enumerate(zip(starts, sizes)):
+        a[s : s + c] = gaussian_bf16(r_x, (int(c), k), 1.0)
+    b = gaussian_bf16(r_w, (len(sizes), n, k), 0.02)
+    token_of_row = np.where(m_indices >= 0, np.arange(m_indices.shape[0]), -1)
+    return Grouped(f"grouped_{len(sizes)}x{n}x{k}", len(sizes), n, k, sizes, starts, m_indices, a, b, token_of_row)
