@@ -1,0 +1,221 @@
+"""Fine-grained block-scaled FP8 linear for AMD MI355X (gfx950).
+
+A thin Python binding over libfgfp8.so, the C-ABI library declared in
+include/fgfp8.h.  Every step of the path runs in the library's HIP kernels;
+this module only checks tensor dtypes/shapes, passes device pointers and the
+current torch stream, and turns error codes into exceptions.  torch provides
+device memory and streams and nothing else.  Importing the package fails
+loudly if the library has not been built (there is no fallback path).
+
+Calls (names as on the deepgemm-rust README, "What's implemented", and the
+Linnet DeepGEMM plugin source):
+
+    q, sa = quantize_fp8_groups(x)                   # x: bf16 [M, K]
+    qb, sb = quantize_fp8_blocks(w)                  # w: bf16 [N, K]
+    fp8_gemm_nt((q, sa), (qb, sb), d)                # d: bf16 [M, N], in place
+    m_grouped_fp8_gemm_nt_contiguous((q, sa), (qb, sb), d, m_indices)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libfgfp8.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fgfp8.h")
+
+FGFP8_OK, FGFP8_EINVAL, FGFP8_ENODEV, FGFP8_ELAUNCH = 0, 1, 2, 3
+GROUP = 128
+
+if not os.path.exists(LIBRARY_PATH):
+    raise ImportError(
+        f"{LIBRARY_PATH} is missing: build it with `python fine_grained_block_fp8_amd/build.py` "
+        "(the FP8 linear has no path other than its HIP kernels)"
+    )
+
+_lib = ctypes.CDLL(LIBRARY_PATH)
+_i64, _vp, _fp, _i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32
+_lib.quantize_fp8_groups.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
+_lib.quantize_fp8_blocks.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
+_lib.fp8_gemm_nt.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
+_lib.m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _vp, _i64, _i64, _i64, _vp]
+_lib.fgfp8_last_error.argtypes = []
+_lib.fgfp8_last_error.restype = ctypes.c_char_p
+_lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
+for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
+              "fgfp8_describe_gemm"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+
+class Fgfp8Error(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[fgfp8 error {code}] {message}")
+        self.code = code
+
+
+def last_error() -> str:
+    return (_lib.fgfp8_last_error() or b"").decode()
+
+
+def _check(rc: int) -> None:
+    if rc != FGFP8_OK:
+        raise Fgfp8Error(rc, last_error())
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/fgfp8.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype in {dtypes} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def padded_rows(m: int) -> int:
+    """Scale leading dimension: rows padded to a multiple of four."""
+    return -(-m // 4) * 4
+
+
+def quantize_fp8_groups(x: torch.Tensor, sa_ld: int | None = None, out=None):
+    """Per-(1x128) activation quantization.  x: bf16 [M, K].  Returns
+    (q float8_e4m3fn [M, K], sa float32 [K/128, sa_ld]), sa MN-major."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    m, k = x.shape
+    sa_ld = padded_rows(m) if sa_ld is None else int(sa_ld)
+    if out is None:
+        q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device=x.device)
+        sa = torch.empty((k // GROUP if k % GROUP == 0 else 0, sa_ld), dtype=torch.float32, device=x.device)
+    else:
+        q, sa = out
+        _need(q, "q", _FP8, 2)
+        _need(sa, "sa", (torch.float32,), 2)
+        if tuple(q.shape) != (m, k) or tuple(sa.shape) != (k // GROUP, sa_ld):
+            raise ValueError("output shapes must be q [M, K] and sa [K/128, sa_ld]")
+    _check(_lib.quantize_fp8_groups(_ptr(x), m, k, _ptr(q), _ptr(sa), sa_ld, _stream(x)))
+    return q, sa
+
+
+def quantize_fp8_blocks(w: torch.Tensor, out=None):
+    """Per-(128x128) weight quantization.  w: bf16 [N, K].  Returns
+    (q float8_e4m3fn [N, K], sb float32 [ceil(N/128), K/128])."""
+    _need(w, "w", (torch.bfloat16,), 2)
+    n, k = w.shape
+    if out is None:
+        q = torch.empty((n, k), dtype=torch.float8_e4m3fn, device=w.device)
+        sb = torch.empty((-(-n // GROUP), k // GROUP if k % GROUP == 0 else 0), dtype=torch.float32, device=w.device)
+    else:
+        q, sb = out
+    _check(_lib.quantize_fp8_blocks(_ptr(w), n, k, _ptr(q), _ptr(sb), _stream(w)))
+    return q, sb
+
+
+def fp8_gemm_nt(a, b, d: torch.Tensor) -> torch.Tensor:
+    """d[M, N] (bf16, written in place) = A . B^T with A = (q [M, K], sa
+    [K/128, sa_ld]) and B = (q [N, K], sb [ceil(N/128), K/128])."""
+    (qa, sa), (qb, sb) = a, b
+    _need(qa, "a", _FP8, 2)
+    _need(qb, "b", _FP8, 2)
+    _need(sa, "sa", (torch.float32,), 2)
+    _need(sb, "sb", (torch.float32,), 2)
+    _need(d, "d", (torch.bfloat16,), 2)
+    m, k = qa.shape
+    n = qb.shape[0]
+    if qb.shape[1] != k:
+        raise ValueError("a and b must share K")
+    if tuple(d.shape) != (m, n):
+        raise ValueError(f"d must be [{m}, {n}]")
+    if k % GROUP == 0 and (sa.shape[0] != k // GROUP or tuple(sb.shape) != (-(-n // GROUP), k // GROUP)):
+        raise ValueError("scale shapes must be sa [K/128, sa_ld] and sb [ceil(N/128), K/128]")
+    _check(_lib.fp8_gemm_nt(_ptr(qa), _ptr(sa), sa.shape[1], _ptr(qb), _ptr(sb), _ptr(d), m, n, k, _stream(d)))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Tensor) -> torch.Tensor:
+    """Grouped product: A = (q [M, K], sa), B = (q [G, N, K], sb [G, ceil(N/128), K/128]),
+    m_indices int32 [M] (group of each row, -1 for padding), d bf16 [M, N]."""
+    (qa, sa), (qb, sb) = a, b
+    _need(qa, "a", _FP8, 2)
+    _need(qb, "b", _FP8, 3)
+    _need(sa, "sa", (torch.float32,), 2)
+    _need(sb, "sb", (torch.float32,), 3)
+    _need(d, "d", (torch.bfloat16,), 2)
+    _need(m_indices, "m_indices", (torch.int32,), 1)
+    m, k = qa.shape
+    g, n, k2 = qb.shape
+    if k2 != k or tuple(d.shape) != (m, n) or m_indices.shape[0] != m:
+        raise ValueError("shape mismatch among a [M, K], b [G, N, K], d [M, N], m_indices [M]")
+    if k % GROUP == 0 and tuple(sb.shape) != (g, -(-n // GROUP), k // GROUP):
+        raise ValueError("sb must be [G, ceil(N/128), K/128]")
+    _check(
+        _lib.m_grouped_fp8_gemm_nt_contiguous(
+            _ptr(qa), _ptr(sa), sa.shape[1], _ptr(m_indices), _ptr(qb), _ptr(sb), g, _ptr(d), m, n, k, _stream(d)
+        )
+    )
+    return d
+
+
+def fp8_linear(x: torch.Tensor, weight) -> torch.Tensor:
+    """The pages' linear (Linnet DeepGEMM plugin, _BlockProduct.execute): round
+    the bf16 input per 1x128 group, then the block-scaled product with the
+    pre-quantized weight (q [N, K], sb).  x: bf16 [..., K]; returns bf16 [..., N]."""
+    qb, sb = weight
+    flat = x.reshape(-1, x.shape[-1])
+    q, sa = quantize_fp8_groups(flat)
+    d = torch.empty((flat.shape[0], qb.shape[0]), dtype=torch.bfloat16, device=x.device)
+    fp8_gemm_nt((q, sa), (qb, sb), d)
+    return d.reshape(*x.shape[:-1], qb.shape[0])
+
+
+def describe_gemm(m: int, n: int, k: int) -> str:
+    buf = ctypes.create_string_buffer(128)
+    _check(_lib.fgfp8_describe_gemm(m, n, k, buf, 128))
+    return buf.value.decode()
+
+
+__all__ = [
+    "FGFP8_EINVAL",
+    "FGFP8_ELAUNCH",
+    "FGFP8_ENODEV",
+    "FGFP8_OK",
+    "Fgfp8Error",
+    "declared_functions",
+    "describe_gemm",
+    "fp8_gemm_nt",
+    "fp8_linear",
+    "last_error",
+    "m_grouped_fp8_gemm_nt_contiguous",
+    "padded_rows",
+    "quantize_fp8_blocks",
+    "quantize_fp8_groups",
+]

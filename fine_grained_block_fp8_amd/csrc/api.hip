@@ -1,0 +1,175 @@
+// The C ABI of libfgfp8 (declared in include/fgfp8.h): argument validation,
+// device check, kernel plan choice, launch on the caller's stream.  No call
+// allocates, frees, synchronizes or reads device memory on the host.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/fgfp8.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device verdict: 0 unknown, 1 gfx950, 2 other.  Device ids beyond the
+// table are checked on every call.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];
+
+int check_device(const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(FGFP8_ENODEV, "%s: no HIP device (%s)", who, hipGetErrorString(e));
+  }
+  int known = dev < kMaxDevices ? g_device_ok[dev].load(std::memory_order_relaxed) : 0;
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(FGFP8_ENODEV, "%s: cannot query device %d (%s)", who, dev, hipGetErrorString(e));
+    }
+    known = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (dev < kMaxDevices) g_device_ok[dev].store(known, std::memory_order_relaxed);
+    if (known == 2) return fail(FGFP8_ENODEV, "%s: device %d is %s, not gfx950", who, dev, prop.gcnArchName);
+  }
+  if (known != 1) return fail(FGFP8_ENODEV, "%s: device %d is not gfx950", who, dev);
+  return FGFP8_OK;
+}
+
+int launched(hipError_t e, const char* who) {
+  if (e != hipSuccess) return fail(FGFP8_ELAUNCH, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+  return FGFP8_OK;
+}
+
+// K is at most 2^24 so that tile offsets (<= 256 rows * K) fit the 32-bit
+// buffer offsets the kernels use.
+constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kMaxRows = int64_t(1) << 31;
+
+int check_k(const char* who, int64_t k) {
+  if (k <= 0 || k % 128 != 0) return fail(FGFP8_EINVAL, "%s: k=%lld must be a positive multiple of 128", who, (long long)k);
+  if (k > kMaxK) return fail(FGFP8_EINVAL, "%s: k=%lld exceeds %lld", who, (long long)k, (long long)kMaxK);
+  return FGFP8_OK;
+}
+
+int check_sa(const char* who, int64_t m, int64_t k, int64_t sa_ld) {
+  if (sa_ld < m || sa_ld % 4 != 0 || sa_ld <= 0)
+    return fail(FGFP8_EINVAL, "%s: sa_ld=%lld must be a positive multiple of 4 and >= m=%lld", who,
+                (long long)sa_ld, (long long)m);
+  if ((k / 128) * sa_ld * 4 >= (int64_t(1) << 31))
+    return fail(FGFP8_EINVAL, "%s: activation scale array (k/128 * sa_ld floats) exceeds 2 GiB", who);
+  return FGFP8_OK;
+}
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && *v && strcmp(v, "0") != 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fgfp8_last_error(void) { return g_last_error.c_str(); }
+
+int quantize_fp8_groups(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, float* sa, int64_t sa_ld,
+                        void* stream) {
+  const char* who = "quantize_fp8_groups";
+  if (m < 0 || m >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m=%lld out of range", who, (long long)m);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (!x_bf16 || !q_e4m3 || !sa) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(sa))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (m == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_quantize_groups(x_bf16, m, k, q_e4m3, sa, sa_ld, (hipStream_t)stream), who);
+}
+
+int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, float* sb, void* stream) {
+  const char* who = "quantize_fp8_blocks";
+  if (n < 0 || (n + 127) / 128 > 65535) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);
+  if (int rc = check_k(who, k)) return rc;
+  if (!w_bf16 || !q_e4m3 || !sb) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(w_bf16) || !aligned16(q_e4m3) || !aligned16(sb))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (n == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_quantize_blocks(w_bf16, n, k, q_e4m3, sb, (hipStream_t)stream), who);
+}
+
+int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
+  const char* who = "fp8_gemm_nt";
+  if (m < 0 || m >= kMaxRows || n < 0 || n >= kMaxRows)
+    return fail(FGFP8_EINVAL, "%s: m=%lld n=%lld out of range", who, (long long)m, (long long)n);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (!a_e4m3 || !sa || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(d_bf16))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (m == 0 || n == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
+  if (env_flag("FGFP8_PRINT_CONFIG"))
+    fprintf(stderr, "[fgfp8] fp8_gemm_nt m=%lld n=%lld k=%lld: %s split=%d\n", (long long)m, (long long)n,
+            (long long)k, fgfp8::gemm_kind_name(plan.kind), plan.split);
+  return launched(fgfp8::launch_gemm(plan, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, (hipStream_t)stream),
+                  who);
+}
+
+int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                                     const void* b_e4m3, const float* sb, int32_t num_groups, void* d_bf16,
+                                     int64_t m, int64_t n, int64_t k, void* stream) {
+  const char* who = "m_grouped_fp8_gemm_nt_contiguous";
+  if (m < 0 || m >= kMaxRows || m % 128 != 0)
+    return fail(FGFP8_EINVAL, "%s: m=%lld must be a non-negative multiple of 128", who, (long long)m);
+  if (n < 0 || n >= kMaxRows) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);
+  if (num_groups < 1) return fail(FGFP8_EINVAL, "%s: num_groups=%d must be >= 1", who, (int)num_groups);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (!a_e4m3 || !sa || !m_indices || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(m_indices) || !aligned16(b_e4m3) || !aligned16(sb) ||
+      !aligned16(d_bf16))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (m == 0 || n == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  if (env_flag("FGFP8_PRINT_CONFIG"))
+    fprintf(stderr, "[fgfp8] m_grouped_fp8_gemm_nt_contiguous m=%lld n=%lld k=%lld groups=%d: tile128x256_w2x2\n",
+            (long long)m, (long long)n, (long long)k, (int)num_groups);
+  return launched(fgfp8::launch_grouped_gemm(a_e4m3, sa, sa_ld, m_indices, b_e4m3, sb, num_groups, d_bf16, m, n, k,
+                                             (hipStream_t)stream),
+                  who);
+}
+
+int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len) {
+  if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: null or empty buffer");
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: bad shape");
+  const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
+  snprintf(buf, (size_t)len, "%s split=%d", fgfp8::gemm_kind_name(plan.kind), plan.split);
+  return FGFP8_OK;
+}
+
+}  // extern "C"

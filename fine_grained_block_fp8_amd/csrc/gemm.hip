@@ -1,0 +1,416 @@
+// Block-scaled FP8 products for gfx950: the dense fp8_gemm_nt, its M-grouped
+// contiguous variant, and a streaming form for decode-shaped M <= 16.
+//
+// Definition (deepgemm-rust README, "What's implemented" table, fp8_gemm_nt
+// row and the kernel notes on per-128-block scale promotion):
+//   D[m][n] = sum_kb sa[kb][m] * sb[n/128][kb] * P(m, n, kb),
+//   P(m, n, kb) = sum_{k in chunk kb} a[m][k] * b[n][k]   (FP8 x FP8, FP32 sum)
+// P of a 16x16 output tile and one 128-wide chunk is exactly one
+// v_mfma_f32_16x16x128_f8f6f4 with a zero accumulator; the scale product is
+// then applied in FP32 registers, acc = fma(P, sa*sb, acc) ("promotion").
+//
+// Operand roles: the MFMA's first operand is a 16-row slice of B and its
+// second a 16-row slice of A, so lane l of the 4-register result holds one
+// row of A (l % 16) and four columns of B.  That makes the promotion scale
+// sa[row] * sb[block] a single per-lane value for the whole 16x16 tile.
+// Within a wave tile of NT 16-column MFMA tiles, MFMA tile t's column c is
+// mapped to wave column NT*c + t, so each lane ends up owning 4*NT
+// consecutive output columns of its row (a 64- or 32-byte contiguous store).
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fgfp8 {
+
+// ------------------------------------------------------------ tile configs
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TM = BM / WAVES_M;  // wave tile rows
+  static constexpr int TN = BN / WAVES_N;  // wave tile columns (inside one 128-column scale block)
+  static constexpr int MT = TM / 16;
+  static constexpr int NT = TN / 16;
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = BM * 128;
+  static constexpr int S_OFF = B_OFF + BN * 128;
+  static constexpr int S_BYTES = BM * 4 < 1024 ? 1024 : BM * 4;
+  static constexpr int STAGE = S_OFF + S_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+  static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
+  static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
+  static_assert(BM * 4 <= 1024, "one wave loads a stage's activation scales");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+using Tile256x256 = Tile<256, 256, 4, 2>;
+using Tile128x256 = Tile<128, 256, 2, 2>;
+using Tile256x128 = Tile<256, 128, 4, 1>;
+using Tile128x128 = Tile<128, 128, 2, 2>;
+
+// LDS layout of a K chunk: row r of a tile is 128 bytes (8 slots of 16 bytes);
+// logical slot c of row r is stored at slot c ^ swz(r).  The XOR with both
+// r's low bits and its next three makes the 16-byte fragment reads
+// conflict-free both for 8 consecutive rows (A fragments) and for rows
+// NT apart (B fragments of the column-interleaved mapping).
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// All waves cooperatively copy chunk kb of the A tile, the B tile and the
+// tile's activation scales into one LDS stage, with direct global->LDS
+// buffer loads (1 KB = 8 tile rows per wave instruction; rows past the
+// matrix edge read as zero).
+template <class C>
+__device__ __forceinline__ void load_stage(uint8_t* st, rsrc_t ra, rsrc_t rb, rsrc_t rs, uint32_t K, int kb,
+                                           uint32_t sa_ld_bytes, int wave, int lane) {
+  constexpr int AS = C::BM / 8, BS = C::BN / 8, SEGS = AS + BS + 1;
+  const int r8 = lane >> 3, cs = lane & 7;
+#pragma unroll
+  for (int s0 = 0; s0 < SEGS; s0 += C::WAVES) {
+    const int s = s0 + wave;
+    if (s < AS) {
+      const int r = s * 8 + r8;
+      load_lds16(ra, st + C::A_OFF + s * 1024, (uint32_t)r * K + kb * 128 + ((cs ^ swz(r)) << 4));
+    } else if (s < AS + BS) {
+      const int r = (s - AS) * 8 + r8;
+      load_lds16(rb, st + C::B_OFF + (s - AS) * 1024, (uint32_t)r * K + kb * 128 + ((cs ^ swz(r)) << 4));
+    } else if (s == AS + BS) {
+      load_lds16(rs, st + C::S_OFF, (uint32_t)kb * sa_ld_bytes + lane * 16);
+    }
+  }
+}
+
+// The 32 bytes lane (row r, k-group lg) contributes to a 16x16x128 MFMA.
+__device__ __forceinline__ v8i_t read_frag(const uint8_t* base, int r, int lg) {
+  const uint8_t* row = base + r * 128;
+  const int sw = swz(r);
+  const uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * lg) ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * lg + 1) ^ sw) << 4));
+  v8i_t f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+__device__ __forceinline__ v4f_t mfma_fp8(const v8i_t& x, const v8i_t& y) {
+  const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// acc += p * s, one FMA per element (single rounding).
+__device__ __forceinline__ void promote(v4f_t& acc, const v4f_t& p, float s) {
+  acc[0] = __builtin_fmaf(p[0], s, acc[0]);
+  acc[1] = __builtin_fmaf(p[1], s, acc[1]);
+  acc[2] = __builtin_fmaf(p[2], s, acc[2]);
+  acc[3] = __builtin_fmaf(p[3], s, acc[3]);
+}
+
+template <class C>
+__device__ __forceinline__ void compute_stage(const uint8_t* st, float sbv, int wm, int wn, int lane,
+                                              v4f_t (&acc)[C::MT][C::NT]) {
+  const int li = lane & 15, lg = lane >> 4;
+  const float* sas = reinterpret_cast<const float*>(st + C::S_OFF);
+  v8i_t af[C::MT];
+  float sc[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; mt++) {
+    const int r = wm * C::TM + 16 * mt + li;
+    af[mt] = read_frag(st + C::A_OFF, r, lg);
+    sc[mt] = sas[r] * sbv;
+  }
+#pragma unroll
+  for (int t = 0; t < C::NT; t++) {
+    const v8i_t bfr = read_frag(st + C::B_OFF, wn * C::TN + C::NT * li + t, lg);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; mt++) promote(acc[mt][t], mfma_fp8(bfr, af[mt]), sc[mt]);
+  }
+}
+
+// Main loop + epilogue for one (m0, n0) output tile.  a / b point at the
+// tile's first row of A / B; sb_base at the first scale row of B's matrix.
+template <class C>
+__device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
+                                          const float* sb_base, uint16_t* __restrict__ d, int64_t M, int64_t N,
+                                          int K, int64_t sa_ld, int64_t m0, int64_t n0) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
+  const int KB = K / kGroup;
+  const uint32_t a_rows = (uint32_t)(M - m0 < C::BM ? M - m0 : C::BM);
+  const uint32_t b_rows = (uint32_t)(N - n0 < C::BN ? N - n0 : C::BN);
+  const rsrc_t ra = make_rsrc(a, a_rows * (uint32_t)K);
+  const rsrc_t rb = make_rsrc(b, b_rows * (uint32_t)K);
+  const rsrc_t rs = make_rsrc(sa + m0, (uint32_t)(((int64_t)KB * sa_ld - m0) * 4));
+  const int64_t nblocks = (N + kGroup - 1) / kGroup;
+  int64_t nb = (n0 + wn * C::TN) / kGroup;
+  if (nb >= nblocks) nb = nblocks - 1;  // a wave entirely past N: its results are never stored
+  const float* sbw = sb_base + nb * KB;
+
+  v4f_t acc[C::MT][C::NT];
+#pragma unroll
+  for (int i = 0; i < C::MT; i++)
+#pragma unroll
+    for (int j = 0; j < C::NT; j++) acc[i][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+
+  load_stage<C>(lds, ra, rb, rs, (uint32_t)K, 0, (uint32_t)(sa_ld * 4), wave, lane);
+  for (int kb = 0; kb < KB; kb++) {
+    const float sbv = sbw[kb];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies into the stage have landed
+    __syncthreads();                     // ... and every other wave's; stage kb-1 is free again
+    if (kb + 1 < KB)
+      load_stage<C>(lds + ((kb + 1) & 1) * C::STAGE, ra, rb, rs, (uint32_t)K, kb + 1, (uint32_t)(sa_ld * 4), wave,
+                    lane);
+    compute_stage<C>(lds + (kb & 1) * C::STAGE, sbv, wm, wn, lane, acc);
+  }
+
+  // Epilogue: lane (li, lg) owns row m0 + wm*TM + 16*mt + li, columns
+  // c0 .. c0 + 4*NT - 1; acc[mt][t][r] is column c0 + NT*r + t.
+  const int li = lane & 15, lg = lane >> 4;
+  const bool vec = (N % 8) == 0;
+#pragma unroll
+  for (int mt = 0; mt < C::MT; mt++) {
+    const int64_t row = m0 + wm * C::TM + 16 * mt + li;
+    if (row >= M) continue;
+    const int64_t c0 = n0 + wn * C::TN + 4 * C::NT * lg;
+    uint16_t* drow = d + row * N;
+    if (vec && c0 + 4 * C::NT <= N) {
+#pragma unroll
+      for (int s = 0; s < C::NT / 2; s++) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int j0 = 8 * s + 2 * e, j1 = j0 + 1;
+          w[e] = pack_bf16x2(acc[mt][j0 % C::NT][j0 / C::NT], acc[mt][j1 % C::NT][j1 / C::NT]);
+        }
+        *reinterpret_cast<uint4*>(drow + c0 + 8 * s) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4 * C::NT; j++)
+        if (c0 + j < N) drow[c0 + j] = (uint16_t)bf16_rne(acc[mt][j % C::NT][j / C::NT]);
+    }
+  }
+}
+
+// Block -> tile order.  Consecutive workgroup ids are dispatched round-robin
+// over the 8 XCDs; remapping gives each XCD a contiguous run of tiles, and the
+// run is walked in bands of 8 tile rows so that the tiles an XCD has in
+// flight share A and B panels in its L2.
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  int v = bid;
+  if ((nblocks & 7) == 0) v = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+  constexpr int kBand = 8;
+  const int per_band = kBand * tiles_n;
+  const int band = v / per_band;
+  const int first = band * kBand;
+  const int rows = tiles_m - first < kBand ? tiles_m - first : kBand;
+  const int r = v - band * per_band;
+  tm = first + r % rows;
+  tn = r / rows;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __restrict__ A, const float* __restrict__ SA,
+                                                             const uint8_t* __restrict__ B,
+                                                             const float* __restrict__ SB, uint16_t* __restrict__ D,
+                                                             int64_t M, int64_t N, int K, int64_t sa_ld, int tiles_m,
+                                                             int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+  gemm_tile<C>(lds, A + m0 * K, B + n0 * K, SA, SB, D, M, N, K, sa_ld, m0, n0);
+}
+
+// Grouped: every BM-row block lies inside one group (groups start at
+// multiples of 128 rows and BM = 128); its group is m_indices of its first
+// row, and a block of padding (-1) is skipped.
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ SA, const int32_t* __restrict__ m_indices,
+    const uint8_t* __restrict__ B, const float* __restrict__ SB, uint16_t* __restrict__ D, int64_t M, int64_t N,
+    int K, int64_t sa_ld, int num_groups, int tiles_m, int tiles_n) {
+  static_assert(C::BM == 128, "grouped blocks are the 128-row alignment unit");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+  const int g = __builtin_amdgcn_readfirstlane(m_indices[m0]);
+  if (g < 0 || g >= num_groups) return;  // padding; uniform across the workgroup, before any barrier
+  const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
+  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, D, M, N, K, sa_ld,
+               m0, n0);
+}
+
+// ------------------------------------------------------------ decode (M <= 16)
+// The product is a stream over B (N*K bytes) with A's <= 16 rows re-read from
+// L2.  A workgroup owns 16 output columns; its SPLIT waves take interleaved K
+// chunks, each lane loading its own 32-byte MFMA fragments straight from
+// global memory, kU chunks per batch so that several loads are in flight per
+// lane.  The waves' FP32 tiles are then summed through LDS.
+constexpr int kDecodeU = 4;
+
+template <int SPLIT>
+__global__ __launch_bounds__(SPLIT * 64) void gemm_decode_kernel(const uint8_t* __restrict__ A,
+                                                                  const float* __restrict__ SA,
+                                                                  const uint8_t* __restrict__ B,
+                                                                  const float* __restrict__ SB,
+                                                                  uint16_t* __restrict__ D, int M, int64_t N, int K,
+                                                                  int64_t sa_ld) {
+  __shared__ v4f_t red[SPLIT][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int KB = K / kGroup;
+  const uint32_t b_rows = (uint32_t)(N - n0 < 16 ? N - n0 : 16);
+  const rsrc_t rb = make_rsrc(B + n0 * K, b_rows * (uint32_t)K);
+  const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K);
+  const uint32_t off = (uint32_t)li * K + lg * 32;
+  const float* sbw = SB + (n0 / kGroup) * KB;
+  const bool row_ok = li < M;
+  v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kb0 = wave; kb0 < KB; kb0 += SPLIT * kDecodeU) {
+    uint4 b0[kDecodeU], b1[kDecodeU], a0[kDecodeU], a1[kDecodeU];
+    float sv[kDecodeU];
+#pragma unroll
+    for (int u = 0; u < kDecodeU; u++) {
+      const int kb = kb0 + u * SPLIT;
+      if (kb < KB) {
+        b0[u] = load_rsrc16(rb, off + kb * 128);
+        b1[u] = load_rsrc16(rb, off + kb * 128 + 16);
+        a0[u] = load_rsrc16(ra, off + kb * 128);
+        a1[u] = load_rsrc16(ra, off + kb * 128 + 16);
+        sv[u] = (row_ok ? SA[(int64_t)kb * sa_ld + li] : 0.0f) * sbw[kb];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecodeU; u++) {
+      const int kb = kb0 + u * SPLIT;
+      if (kb < KB) {
+        v8i_t bf, af;
+        bf[0] = b0[u].x; bf[1] = b0[u].y; bf[2] = b0[u].z; bf[3] = b0[u].w;
+        bf[4] = b1[u].x; bf[5] = b1[u].y; bf[6] = b1[u].z; bf[7] = b1[u].w;
+        af[0] = a0[u].x; af[1] = a0[u].y; af[2] = a0[u].z; af[3] = a0[u].w;
+        af[4] = a1[u].x; af[5] = a1[u].y; af[6] = a1[u].z; af[7] = a1[u].w;
+        promote(acc, mfma_fp8(bf, af), sv[u]);
+      }
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    v4f_t s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < SPLIT; w++) {
+      const v4f_t o = red[w][lane];
+      s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
+    }
+    // lane (li, lg): row li, columns n0 + 4*lg .. n0 + 4*lg + 3
+    if (row_ok) {
+      const int64_t c0 = n0 + 4 * lg;
+      uint16_t* drow = D + (int64_t)li * N;
+      if ((N % 4) == 0 && c0 + 4 <= N) {
+        *reinterpret_cast<uint2*>(drow + c0) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          if (c0 + r < N) drow[c0 + r] = (uint16_t)bf16_rne(s[r]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ host side
+namespace {
+struct Candidate {
+  GemmKind kind;
+  int bm, bn;
+  double eff;  // relative per-tile efficiency (larger tiles reuse more)
+};
+constexpr Candidate kCandidates[] = {
+    {kGemmTile256x256, 256, 256, 1.00},
+    {kGemmTile256x128, 256, 128, 0.90},
+    {kGemmTile128x256, 128, 256, 0.90},
+    {kGemmTile128x128, 128, 128, 0.75},
+};
+constexpr int kCUs = 256;
+}  // namespace
+
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
+  if (m <= 16) {
+    const int64_t slabs = (n + 15) / 16;
+    const int64_t kb = k / kGroup;
+    int split = 4;
+    if (slabs < 512 && kb >= 32) split = 8;
+    return {kGemmDecode, split};
+  }
+  GemmPlan best{kGemmTile256x256, 0};
+  double best_cost = 1e300;
+  for (const Candidate& c : kCandidates) {
+    const int64_t tiles = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
+    const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+    const double cost = (double)rounds * c.bm * c.bn / c.eff;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = {c.kind, 0};
+    }
+  }
+  return best;
+}
+
+const char* gemm_kind_name(GemmKind kind) {
+  switch (kind) {
+    case kGemmTile256x256: return "tile256x256_w4x2";
+    case kGemmTile128x256: return "tile128x256_w2x2";
+    case kGemmTile256x128: return "tile256x128_w4x1";
+    case kGemmTile128x128: return "tile128x128_w2x2";
+    case kGemmDecode: return "decode_slab16";
+  }
+  return "?";
+}
+
+template <class C>
+static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb, void* d,
+                              int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  const int tiles_m = (int)((m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL(gemm_nt_kernel<C>, dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb,
+                     static_cast<uint16_t*>(d), m, n, (int)k, sa_ld, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int SPLIT>
+static hipError_t launch_decode(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
+                                void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_decode_kernel<SPLIT>, dim3((uint32_t)((n + 15) / 16)), dim3(SPLIT * 64), 0, stream,
+                     static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb,
+                     static_cast<uint16_t*>(d), (int)m, n, (int)k, sa_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
+                       const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  switch (plan.kind) {
+    case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmDecode:
+      return plan.split == 8 ? launch_decode<8>(a, sa, sa_ld, b, sb, d, m, n, k, stream)
+                             : launch_decode<4>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                               const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
+                               int64_t k, hipStream_t stream) {
+  using C = Tile128x256;
+  const int tiles_m = (int)(m / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL(grouped_gemm_nt_kernel<C>, dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(a), sa, m_indices, static_cast<const uint8_t*>(b), sb,
+                     static_cast<uint16_t*>(d), m, n, (int)k, sa_ld, (int)num_groups, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace fgfp8

@@ -1,0 +1,38 @@
+// Host-side launchers of the gfx950 kernels (no validation here: the C ABI
+// layer checks every argument before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgfp8 {
+
+hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, float* sa, int64_t sa_ld,
+                                  hipStream_t stream);
+hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream);
+
+// Kernel configurations of the dense product.
+enum GemmKind : int {
+  kGemmTile256x256 = 0,  // 256x256 workgroup tile, 8 waves of 64x128
+  kGemmTile128x256 = 1,  // 128x256, 4 waves of 64x128
+  kGemmTile256x128 = 2,  // 256x128, 4 waves of 64x128
+  kGemmTile128x128 = 3,  // 128x128, 4 waves of 64x64
+  kGemmDecode = 4,       // M <= 16: 16-column slabs, K split across waves
+};
+
+struct GemmPlan {
+  GemmKind kind;
+  int split;  // decode: waves per 16-column slab (K split)
+};
+
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k);
+const char* gemm_kind_name(GemmKind kind);
+
+hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
+                       const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                               const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
+                               int64_t k, hipStream_t stream);
+
+}  // namespace fgfp8

@@ -1,0 +1,103 @@
+// Activation (1x128 group) and weight (128x128 block) quantization to E4M3
+// with FP32 scales, for gfx950.
+//
+// Recipe: per-(1x128) activation scales and per-(128x128) weight scales
+// (deepgemm-rust README, "What's implemented" table, fp8_gemm_nt row); each
+// 128 inputs of a row rounded to FP8 with a scale of their own, the scales
+// stored column by column with rows padded to a multiple of four (Linnet
+// "Backend plugins" page, plugin module docstring).  Scale s = fl32(amax/448),
+// 1 for an all-zero group; element code = E4M3_RNE(fl32(x / s)).
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fgfp8 {
+
+// ---------------------------------------------------------------- groups
+// One wave quantizes four (row, group) slots: the 16 lanes of DPP row j hold
+// row 4q+j of group g, 8 bf16 (16 bytes) per lane, so the group's amax is a
+// 16-lane DPP reduction.  Slot quads are numbered group-major, so a wave's
+// four scales are four consecutive floats of one MN-major scale column.  The
+// kernel is bound by HBM: 2 bytes in and 1 byte out per element.
+constexpr int kQgWaves = 4;
+
+__global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const uint16_t* __restrict__ x,
+                                                                         uint8_t* __restrict__ q,
+                                                                         float* __restrict__ sa, int64_t m, int64_t k,
+                                                                         int64_t sa_ld, int64_t quads_per_group,
+                                                                         int64_t total_quads) {
+  const int lane = threadIdx.x & 63;
+  const int64_t quad = (int64_t)blockIdx.x * kQgWaves + (threadIdx.x >> 6);
+  if (quad >= total_quads) return;  // wave-uniform
+  const int64_t g = quad / quads_per_group;
+  const int64_t row = (quad - g * quads_per_group) * 4 + (lane >> 4);
+  const bool valid = row < m;
+  const int64_t off = row * k + g * kGroup + (lane & 15) * 8;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (valid) v = *reinterpret_cast<const uint4*>(x + off);
+  const uint32_t amax_bits = row16_max_u32(absmax8_bits(v));
+  const float s = group_scale(__uint_as_float(amax_bits));
+  const double r = 1.0 / (double)s;
+  const uint2 o = quantize8(v, r);
+  if (valid) {
+    *reinterpret_cast<uint2*>(q + off) = o;
+    if ((lane & 15) == 0) sa[g * sa_ld + row] = s;
+  }
+}
+
+hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, float* sa, int64_t sa_ld,
+                                  hipStream_t stream) {
+  const int64_t mpad = (m + 3) / 4 * 4;
+  const int64_t quads_per_group = mpad / 4;
+  const int64_t total = quads_per_group * (k / kGroup);
+  const int64_t blocks = (total + kQgWaves - 1) / kQgWaves;
+  hipLaunchKernelGGL(quantize_groups_kernel, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, quads_per_group,
+                     total);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- blocks
+// One workgroup per 128x128 block: thread t owns 64 elements of row t/2; the
+// block amax is a wave shuffle reduction followed by an LDS combine across the
+// four waves.  Offline (weights are quantized once), so simplicity wins.
+__global__ __launch_bounds__(256) void quantize_blocks_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ q,
+                                                              float* __restrict__ sb, int64_t n, int64_t k) {
+  __shared__ uint32_t red[4];
+  const int t = threadIdx.x;
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const int64_t row = nb * kGroup + (t >> 1);
+  const int64_t col = kb * kGroup + (t & 1) * 64;
+  const bool valid = row < n;
+  uint4 v[8];
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    v[i] = valid ? *reinterpret_cast<const uint4*>(w + row * k + col + 8 * i) : make_uint4(0, 0, 0, 0);
+    am = max(am, absmax8_bits(v[i]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
+  if ((t & 63) == 0) red[t >> 6] = am;
+  __syncthreads();
+  am = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = group_scale(__uint_as_float(am));
+  const double r = 1.0 / (double)s;
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const uint2 a = quantize8(v[i], r), b = quantize8(v[i + 1], r);
+      *reinterpret_cast<uint4*>(q + row * k + col + 8 * i) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  }
+  if (t == 0) sb[nb * (k / kGroup) + kb] = s;
+}
+
+hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream) {
+  const int64_t nbk = k / kGroup, nbn = (n + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(quantize_blocks_kernel, dim3((uint32_t)nbk, (uint32_t)nbn), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(w), static_cast<uint8_t*>(q), sb, n, k);
+  return hipGetLastError();
+}
+
+}  // namespace fgfp8

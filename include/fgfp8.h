@@ -1,0 +1,148 @@
+/*
+ * fgfp8.h -- C ABI of libfgfp8, the fine-grained block-scaled FP8 linear for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (deepgemm-rust README, "What's implemented" table, rows
+ * fp8_gemm_nt and m_grouped_fp8_gemm_nt_contiguous): D = A . B^T where A (the
+ * activation, M x K) carries one FP32 scale per 1x128 group of each row and
+ * B (the weight, N x K) one FP32 scale per 128x128 block; both operands are
+ * FP8 E4M3 (OCP "FN": bias 7, largest finite 448, no infinities); the product
+ * is accumulated in FP32, with both scales applied once per 128-wide K chunk,
+ * and written as bfloat16.  The activation is rounded to FP8 per 128 inputs
+ * of a row with a scale of its own, and the activation scales are stored
+ * column by column with the row count padded to a multiple of four (Linnet
+ * "Backend plugins" page, module docstring of the DeepGEMM plugin source and
+ * _BlockProduct.execute).
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a DEVICE pointer (memory of the current HIP
+ *    device), owned by the caller.  The library never allocates, frees or
+ *    synchronizes, never reads device data on the host, and keeps no state
+ *    between calls; every call is legal under HIP graph capture.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    legacy default stream) and runs asynchronously: a return of FGFP8_OK
+ *    means the work was enqueued, not that it finished.
+ *  - Every array is dense row-major with the leading dimension stated.  Base
+ *    pointers must be 16-byte aligned.
+ *  - E4M3 arrays hold one byte per element; bf16 arrays two bytes.
+ *  - Return value: FGFP8_OK (0) or an error code below; on error nothing was
+ *    enqueued and fgfp8_last_error() describes the cause.  No C++ exception
+ *    crosses this interface.
+ *  - Empty problems (m == 0 or n == 0) enqueue nothing and return FGFP8_OK.
+ *  - Calls on one stream are ordered; calls on different streams that write
+ *    the same output race.
+ */
+#ifndef FGFP8_H_
+#define FGFP8_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FGFP8_OK = 0,
+  FGFP8_EINVAL = 1,  /* bad shape, null pointer, misaligned base, bad leading dimension */
+  FGFP8_ENODEV = 2,  /* no HIP device, or the current device is not gfx950 */
+  FGFP8_ELAUNCH = 3, /* the HIP runtime refused a kernel launch */
+};
+
+/* Activation quantization, one scale per 1x128 group of each row.
+ *
+ * Defined by the per-(1x128) activation scales of the recipe (deepgemm-rust
+ * README, "What's implemented", fp8_gemm_nt row) and the Linnet plugin's
+ * rounding of "each 128 inputs of a row to FP8 with a scale of their own"
+ * (Linnet "Backend plugins" page, plugin module docstring).  For row m and
+ * group g (columns 128g .. 128g+127):
+ *     amax = max |x[m][k]|                       (exact, over the group)
+ *     s    = fl32(amax / 448), or 1 when amax == 0
+ *     q    = E4M3(fl32(x[m][k] / s))             (round to nearest even;
+ *                                                 |.| >= 464 saturates to 448;
+ *                                                 the sign of zero is kept)
+ *
+ * x_bf16  [m][k] bfloat16, input.
+ * q_e4m3  [m][k] E4M3 bytes, output.
+ * sa      [k/128][sa_ld] float32, output, MN-major: sa[g*sa_ld + m] is the
+ *         scale of row m, group g.  Entries for m <= row < sa_ld are left
+ *         untouched.
+ * Requirements: k > 0 and k % 128 == 0; sa_ld % 4 == 0 and sa_ld >= m.
+ * Non-finite inputs are outside the contract (results unspecified). */
+int quantize_fp8_groups(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, float* sa, int64_t sa_ld,
+                        void* stream);
+
+/* Weight quantization, one scale per 128x128 block (the per-(128x128) weight
+ * scales of the recipe; deepgemm-rust README, "What's implemented" and
+ * "Quick start", where sfb has shape (n/128, k/128)).  Same rule as
+ * quantize_fp8_groups over each block; the last block row of a matrix whose n
+ * is not a multiple of 128 uses the rows present.  An offline step: weights
+ * are quantized once and kept (Linnet plugin: weight and scale are persistent
+ * parameters).
+ *
+ * w_bf16  [n][k] bfloat16, input.
+ * q_e4m3  [n][k] E4M3 bytes, output.
+ * sb      [ceil(n/128)][k/128] float32, output, row-major.
+ * Requirements: k > 0 and k % 128 == 0. */
+int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, float* sb, void* stream);
+
+/* Block-scaled FP8 product, NT layout (both operands K-contiguous):
+ *     D[m][n] = sum_kb  sa[kb][m] * sb[n/128][kb] * P(m, n, kb),
+ *     P(m, n, kb) = sum over the 128 k of chunk kb of a[m][k] * b[n][k],
+ * with P formed in FP32 by the matrix cores for each 128-wide chunk, then
+ * scaled and accumulated in FP32 registers ("per-128-block scale promotion in
+ * registers", deepgemm-rust README, kernel notes under "What's implemented"),
+ * and rounded once to bfloat16 (round to nearest even).  The summation order
+ * inside a chunk is the hardware's; results agree with any other order to
+ * FP32 rounding ("the two products differ only in the order they sum",
+ * Linnet "Backend plugins" page).
+ *
+ * a_e4m3  [m][k] E4M3, the quantized activation.
+ * sa      [k/128][sa_ld] float32, MN-major activation scales (as written by
+ *         quantize_fp8_groups).
+ * b_e4m3  [n][k] E4M3, the quantized weight.
+ * sb      [ceil(n/128)][k/128] float32, row-major weight scales.
+ * d_bf16  [m][n] bfloat16, output (exactly m x n; no padded rows written).
+ * Requirements: m >= 0, n >= 0, k > 0 and k % 128 == 0, sa_ld % 4 == 0,
+ * sa_ld >= m. */
+int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream);
+
+/* M-grouped contiguous variant for mixture-of-experts layers (deepgemm-rust
+ * README, "What's implemented", m_grouped_fp8_gemm_nt_contiguous row: the
+ * tokens of all experts concatenated, 128-row group alignment; "Quick start",
+ * grouped example for the shapes of b and sfb).
+ *
+ * a_e4m3     [m][k] E4M3: the rows of all groups, each group starting at a
+ *            multiple of 128 rows and padded to a multiple of 128.
+ * sa         [k/128][sa_ld] float32 MN-major scales of a.
+ * m_indices  [m] int32: the group of each row, or -1 for a padding row.  Each
+ *            128-row block is computed with the group of its first row and
+ *            skipped when that is negative or >= num_groups.  The contents
+ *            are device data and never read on the host.
+ * b_e4m3     [num_groups][n][k] E4M3 (equivalently (num_groups*n) x k).
+ * sb         [num_groups][ceil(n/128)][k/128] float32.
+ * d_bf16     [m][n] bfloat16 output; rows whose m_indices entry is -1 are
+ *            unspecified.
+ * Requirements: m % 128 == 0, num_groups >= 1, n >= 0, k > 0 and
+ * k % 128 == 0, sa_ld % 4 == 0, sa_ld >= m. */
+int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                                     const void* b_e4m3, const float* sb, int32_t num_groups, void* d_bf16,
+                                     int64_t m, int64_t n, int64_t k, void* stream);
+
+/* Message for the most recent non-zero status returned on the calling thread
+ * (thread-local; the pointer stays valid until the next failing call on that
+ * thread).  Returns "" if no call has failed. */
+const char* fgfp8_last_error(void);
+
+/* Writes a NUL-terminated description of the kernel configuration that
+ * fp8_gemm_nt would use for (m, n, k) into buf (at most len bytes, truncated)
+ * and returns FGFP8_OK; host-only, enqueues nothing, touches no device.
+ * Mirrors the pages' habit of printing every tile decision next to the
+ * number it produced (deepgemm-rust README, "Benchmark"). */
+int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGFP8_H_ */

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls).
+
+* the library loads and exports every function include/fgfp8.h declares;
+* the header is valid C and C++;
+* argument validation returns FGFP8_EINVAL with a message, before any device
+  is touched;
+* without a usable GPU, well-formed calls return FGFP8_ENODEV instead of
+  crashing (skipped where a GPU is present);
+* the kernel plan chooser is a pure host function and is deterministic.
+"""
+
+import ctypes
+import os
+import shutil
+import subprocess
+
+import pytest
+import torch
+
+import fine_grained_block_fp8_amd as fg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fgfp8.h")
+P = 0x10000  # a 16-byte aligned, never dereferenced pointer value
+
+
+def test_library_exports_every_declared_function():
+    names = fg.declared_functions()
+    assert set(names) == {
+        "quantize_fp8_groups",
+        "quantize_fp8_blocks",
+        "fp8_gemm_nt",
+        "m_grouped_fp8_gemm_nt_contiguous",
+        "fgfp8_last_error",
+        "fgfp8_describe_gemm",
+    }
+    lib = fg.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", fg.LIBRARY_PATH], capture_output=True, text=True).stdout
+        exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+        assert set(names) <= exported
+
+
+@pytest.mark.parametrize("compiler,lang", [("gcc", "c"), ("g++", "c++")])
+def test_header_compiles(compiler, lang, tmp_path):
+    cc = shutil.which(compiler)
+    if cc is None:
+        pytest.skip(f"{compiler} not available")
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text('#include "fgfp8.h"\nint main(void) { return fgfp8_last_error() == 0; }\n')
+    r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-x", lang, "-I", os.path.dirname(HEADER), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _lib():
+    return fg.library()
+
+
+@pytest.mark.parametrize(
+    "args,needle",
+    [
+        ((P, 4, 100, P, P, 4, None), "multiple of 128"),
+        ((P, 4, 0, P, P, 4, None), "multiple of 128"),
+        ((P, 5, 128, P, P, 5, None), "sa_ld"),
+        ((P, 5, 128, P, P, 4, None), "sa_ld"),
+        ((None, 4, 128, P, P, 4, None), "null"),
+        ((P + 8, 4, 128, P, P, 4, None), "aligned"),
+        ((P, -1, 128, P, P, 4, None), "out of range"),
+    ],
+)
+def test_quantize_groups_rejects(args, needle):
+    rc = _lib().quantize_fp8_groups(*args)
+    assert rc == fg.FGFP8_EINVAL
+    assert needle in fg.last_error()
+
+
+def test_quantize_blocks_rejects():
+    lib = _lib()
+    assert lib.quantize_fp8_blocks(P, 10, 130, P, P, None) == fg.FGFP8_EINVAL
+    assert lib.quantize_fp8_blocks(P, 10, 128, None, P, None) == fg.FGFP8_EINVAL
+    assert lib.quantize_fp8_blocks(P, 10, 128, P, P + 4, None) == fg.FGFP8_EINVAL
+
+
+def test_gemm_rejects():
+    lib = _lib()
+    ok = dict(a=P, sa=P, sa_ld=8, b=P, sb=P, d=P, m=8, n=16, k=256)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.fp8_gemm_nt(a["a"], a["sa"], a["sa_ld"], a["b"], a["sb"], a["d"], a["m"], a["n"], a["k"], None)
+
+    assert call(k=200) == fg.FGFP8_EINVAL
+    assert call(sa_ld=6) == fg.FGFP8_EINVAL
+    assert call(sa_ld=4) == fg.FGFP8_EINVAL
+    assert call(d=None) == fg.FGFP8_EINVAL
+    assert call(b=P + 2) == fg.FGFP8_EINVAL
+    assert call(n=-3) == fg.FGFP8_EINVAL
+    assert call(k=1 << 25) == fg.FGFP8_EINVAL
+    # empty problems are a valid no-op, even without a device
+    assert call(m=0) == fg.FGFP8_OK
+    assert call(n=0) == fg.FGFP8_OK
+
+
+def test_grouped_rejects():
+    lib = _lib()
+
+    def call(m=256, g=4, n=128, k=256, sa_ld=256, idx=P):
+        return lib.m_grouped_fp8_gemm_nt_contiguous(P, P, sa_ld, idx, P, P, g, P, m, n, k, None)
+
+    assert call(m=200, sa_ld=200) == fg.FGFP8_EINVAL
+    assert "multiple of 128" in fg.last_error()
+    assert call(g=0) == fg.FGFP8_EINVAL
+    assert call(idx=None) == fg.FGFP8_EINVAL
+    assert call(k=64) == fg.FGFP8_EINVAL
+    assert call(m=0, sa_ld=4) == fg.FGFP8_OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fg.quantize_fp8_groups(x)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="a GPU is present")
+def test_no_device_is_reported_not_crashed():
+    lib = _lib()
+    assert lib.quantize_fp8_groups(P, 4, 128, P, P, 4, None) == fg.FGFP8_ENODEV
+    assert "device" in fg.last_error()
+    assert lib.fp8_gemm_nt(P, P, 8, P, P, P, 8, 16, 256, None) == fg.FGFP8_ENODEV
+    assert lib.quantize_fp8_blocks(P, 16, 256, P, P, None) == fg.FGFP8_ENODEV
+    assert lib.m_grouped_fp8_gemm_nt_contiguous(P, P, 128, P, P, P, 2, P, 128, 64, 128, None) == fg.FGFP8_ENODEV
+
+
+def test_describe_gemm_plans():
+    assert fg.describe_gemm(1, 12288, 4096).startswith("decode")
+    assert fg.describe_gemm(16, 4096, 12288).startswith("decode")
+    assert fg.describe_gemm(8192, 8192, 8192).startswith("tile256x256")
+    assert fg.describe_gemm(2048, 4096, 4096) == fg.describe_gemm(2048, 4096, 4096)
+    buf = ctypes.create_string_buffer(4)
+    assert _lib().fgfp8_describe_gemm(8192, 8192, 8192, buf, 4) == fg.FGFP8_OK
+    assert len(buf.value) == 3  # truncated, NUL-terminated
+    assert _lib().fgfp8_describe_gemm(8, 8, 100, buf, 4) == fg.FGFP8_EINVAL

@@ -1,0 +1,152 @@
+"""GPU parity of fp8_gemm_nt against the oracle run on the same quantized
+inputs (the quantized bytes are first checked bit-exact).  Criteria: the
+normwise relative error <= 2e-3 and the elementwise FP32-order bound
+(tests/parity.py); determinism; NaN-poisoned outputs and guard bands."""
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_fp8_amd as fg
+import oracle
+import workloads
+from tests.parity import (
+    check_gemm,
+    check_sampled,
+    codes,
+    d_to_f64,
+    gpu_hot_path,
+    magnitude_sum,
+    sample_col_blocks,
+    sample_rows,
+    to_dev_u8_fp8,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+def full_check(lin, label):
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    rows = np.arange(lin.m)
+    cblocks = np.arange(-(-lin.n // 128))
+    return check_sampled(lin, q, sa, qb, sb, d, rows, cblocks, label)
+
+
+def test_single_linear_128x256x512():
+    r = full_check(workloads.single_linear(), "128x256x512")
+    assert r["frac_not_bf16_rne"] < 0.05
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_single_linear_other_seeds(seed):
+    full_check(workloads.single_linear(seed), f"single seed {seed}")
+
+
+@pytest.mark.parametrize(
+    "m,n,k",
+    [
+        (1, 128, 128),
+        (3, 200, 768),
+        (5, 16, 256),
+        (16, 1, 128),
+        (17, 136, 128),
+        (127, 264, 384),
+        (129, 520, 768),
+        (256, 512, 768),
+        (300, 384, 1024),
+        (520, 1000, 512),
+    ],
+)
+def test_odd_shapes(m, n, k):
+    full_check(workloads.random_linear(m, n, k, seed=m * 7 + n + k), f"{m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
+def test_prefill_linears_sampled(name):
+    (lin,) = workloads.prefill_linears(names=[name])
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    assert torch.isfinite(d.float()).all(), "unwritten or non-finite outputs"
+    rng = np.random.default_rng(1)
+    check_sampled(lin, q, sa, qb, sb, d, sample_rows(lin.m, 48, rng), sample_col_blocks(lin.n, 12, rng), lin.name)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("n,k", workloads.DECODE_SHAPES)
+def test_decode_linears_full(m, n, k):
+    lin = workloads.decode_linear(m, n, k)
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    rng = np.random.default_rng(2)
+    check_sampled(lin, q, sa, qb, sb, d, np.arange(m), sample_col_blocks(n, 40, rng), lin.name)
+
+
+@pytest.mark.parametrize("m,n,k", [(8192, 8192, 8192), (16384, 16384, 8192)])
+def test_square_sampled(m, n, k):
+    lin = workloads.square_linear(m, n, k)
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    assert torch.isfinite(d.float()).all(), "unwritten or non-finite outputs"
+    rng = np.random.default_rng(3)
+    check_sampled(lin, q, sa, qb, sb, d, sample_rows(m, 24, rng), sample_col_blocks(n, 6, rng), lin.name)
+
+
+def test_constant_scales_closed_form():
+    """Hand-set scales (0.01 / 0.02, deepgemm-rust quick start) on random codes:
+    exercises the GEMM alone with scales the quantizer did not produce."""
+    rng = np.random.default_rng(17)
+    m, n, k = 96, 272, 640
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    qa = rng.choice(finite, size=(m, k)).astype(np.uint8)
+    qb = rng.choice(finite, size=(n, k)).astype(np.uint8)
+    sa = np.full((k // 128, m), 0.01, np.float32)
+    sb = np.full((-(-n // 128), k // 128), 0.02, np.float32)
+    d = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.fp8_gemm_nt((to_dev_u8_fp8(qa), torch.from_numpy(sa).cuda()), (to_dev_u8_fp8(qb), torch.from_numpy(sb).cuda()), d)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    check_gemm(d_to_f64(d), ref, magnitude_sum(qa, sa, qb, sb), k, "constant scales")
+
+
+def test_distinct_scales_per_row_chunk_and_block():
+    """Random scales spanning 2^-12..2^4, different for every (chunk, row) and
+    (column block, chunk): a transposed or shifted scale index fails."""
+    rng = np.random.default_rng(23)
+    m, n, k = 200, 392, 1024
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    qa = rng.choice(finite, size=(m, k)).astype(np.uint8)
+    qb = rng.choice(finite, size=(n, k)).astype(np.uint8)
+    sa = (rng.random((k // 128, 200)) * 2.0 ** rng.integers(-12, 4, size=(k // 128, 200))).astype(np.float32)
+    sb = (rng.random((4, k // 128)) * 2.0 ** rng.integers(-12, 4, size=(4, k // 128))).astype(np.float32)
+    d = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.fp8_gemm_nt((to_dev_u8_fp8(qa), torch.from_numpy(sa).cuda()), (to_dev_u8_fp8(qb), torch.from_numpy(sb).cuda()), d)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    check_gemm(d_to_f64(d), ref, magnitude_sum(qa, sa, qb, sb), k, "distinct scales")
+
+
+def test_deterministic_and_guarded():
+    lin = workloads.random_linear(300, 520, 768, seed=99)
+    q, sa, qb, sb, d1 = gpu_hot_path(lin)
+    guard = 8192
+    buf = torch.full((lin.m * lin.n + guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d2 = buf[: lin.m * lin.n].view(lin.m, lin.n)
+    fg.fp8_gemm_nt((q, sa), (qb, sb), d2)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[lin.m * lin.n :].float()).all(), "write past the end of d"
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16)), "two runs differ"
+
+
+def test_linear_helper_matches_two_calls():
+    lin = workloads.random_linear(33, 256, 512, seed=5)
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    x = torch.from_numpy(lin.a.view(np.int16)).view(torch.bfloat16).cuda()
+    y = fg.fp8_linear(x.view(3, 11, 512), (qb, sb))
+    torch.cuda.synchronize()
+    assert torch.equal(y.reshape(33, 256).view(torch.int16), d.view(torch.int16))
+
+
+def test_runs_on_a_side_stream():
+    lin = workloads.random_linear(64, 256, 256, seed=6)
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    s = torch.cuda.Stream()
+    d2 = torch.empty_like(d)
+    with torch.cuda.stream(s):
+        fg.fp8_gemm_nt((q, sa), (qb, sb), d2)
+    s.synchronize()
+    assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
