@@ -1,0 +1,409 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 linear on one MI355X.
+
+Default workload: the Qwen3-8B-shaped prefill linears at M = 2048 tokens
+(qkv 6144x4096, o 4096x4096, gate_up 24576x4096, down 4096x12288).  One step
+is the whole hot path for all four: the activation is quantized per 1x128
+group (quantize_fp8_groups) and multiplied with the pre-quantized weight
+(fp8_gemm_nt, bf16 out).  Weights are quantized once before timing (an
+offline step, as the pages' plugin keeps weights and scales as persistent
+parameters).  Inputs are seeded synthetic data resident in HBM before the
+timed region.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill]
+
+Prints ONE JSON line: value = TFLOP/s over the step (2*M*N*K summed over the
+four linears, divided by the time of quantize + product), plus
+* roofline: the dominant kernel's algorithmic TFLOP/s from HIP events on the
+  launch stream, against the 5.0 PFLOP/s dense FP8 peak;
+* decode: M=1 linears (act-quant included per call) in GB/s against 8 TB/s,
+  timed by graph replay over 8 rotating weight sets so that the weights stream
+  from HBM rather than the 256 MB last-level cache;
+* cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+Other --workload values (decode, moe, square8k, square16k) time one shape
+for profiling.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 (E4M3) MFMA peak
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "moe", "square8k", "square16k"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    return p.parse_args()
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------- setup
+def dev_bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class PreparedLinear:
+    """Device buffers for one linear: bf16 activation, pre-quantized weight,
+    and preallocated outputs (nothing is allocated inside the timed region)."""
+
+    def __init__(self, lin, fg, torch):
+        self.lin = lin
+        self.x = dev_bf16(lin.a, torch)
+        w = dev_bf16(lin.b, torch)
+        self.qb, self.sb = fg.quantize_fp8_blocks(w)
+        del w
+        m, k = lin.m, lin.k
+        self.q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device="cuda")
+        self.sa = torch.empty((k // 128, fg.padded_rows(m)), dtype=torch.float32, device="cuda")
+        self.d = torch.empty((m, lin.n), dtype=torch.bfloat16, device="cuda")
+        self.plan = fg.describe_gemm(m, lin.n, k)
+        self.kernel = self.plan.split()[0]
+
+    def run(self, fg, ev=None):
+        if ev is not None:
+            ev[0].record()
+        fg.quantize_fp8_groups(self.x, out=(self.q, self.sa))
+        if ev is not None:
+            ev[1].record()
+        fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d)
+        if ev is not None:
+            ev[2].record()
+
+
+def quant_bytes(m, k):
+    return 3 * m * k + 4 * (-(-m // 4) * 4) * (k // 128)
+
+
+def gemm_bytes(m, n, k):
+    return m * k + 4 * (-(-m // 4) * 4) * (k // 128) + n * k + 4 * (-(-n // 128)) * (k // 128) + 2 * m * n
+
+
+# --------------------------------------------------------------- prefill step
+def bench_linears(linears, steps, warmup, fg, torch):
+    preps = [PreparedLinear(l, fg, torch) for l in linears]
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        for p in preps:
+            p.run(fg)
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in preps] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for p, ev in zip(preps, events[s]):
+            p.run(fg, ev)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = []
+    for i, p in enumerate(preps):
+        qt = np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(steps)]) * 1e-3
+        gt = np.mean([events[s][i][1].elapsed_time(events[s][i][2]) for s in range(steps)]) * 1e-3
+        lin = p.lin
+        per.append(
+            {
+                "name": lin.name,
+                "m": lin.m,
+                "n": lin.n,
+                "k": lin.k,
+                "kernel": p.plan,
+                "quant_us": qt * 1e6,
+                "quant_gbs": quant_bytes(lin.m, lin.k) / qt / 1e9,
+                "gemm_us": gt * 1e6,
+                "gemm_tflops": lin.flops / gt / 1e12,
+                "_kernel": p.kernel,
+                "_flops": lin.flops,
+                "_gemm_s": gt,
+            }
+        )
+    return preps, elapsed, per
+
+
+def roofline_of(per):
+    """Dominant kernel (largest total time among the GEMM kernels): its
+    algorithmic FLOPs per launch over its mean launch duration."""
+    by = {}
+    for r in per:
+        e = by.setdefault(r["_kernel"], {"flops": 0, "s": 0.0, "n": 0})
+        e["flops"] += r["_flops"]
+        e["s"] += r["_gemm_s"]
+        e["n"] += 1
+    name, e = max(by.items(), key=lambda kv: kv[1]["s"])
+    flops_per_launch = e["flops"] / e["n"]
+    mean_s = e["s"] / e["n"]
+    achieved = flops_per_launch / mean_s / 1e12
+    return {
+        "bound": "mfma",
+        "kernel": f"gemm_nt_kernel<{name}>",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_FP8_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+        "traffic": None,
+        "launches_per_step": e["n"],
+        "mean_launch_us": round(mean_s * 1e6, 2),
+        "algorithmic_gflop_per_launch": round(flops_per_launch / 1e9, 3),
+    }
+
+
+# ------------------------------------------------------------------- decode
+def bench_decode(fg, torch, m=1, shapes=((12288, 4096), (4096, 12288)), sets=8, reps=50):
+    """Act-quant + product per call, M=1; 8 rotating weight sets (8 x 50 MB >
+    256 MB last-level cache) replayed from a HIP graph, and eagerly."""
+    import workloads
+
+    out = []
+    for n, k in shapes:
+        lin = workloads.decode_linear(m, n, k)
+        x = dev_bf16(lin.a, torch)
+        w = dev_bf16(lin.b, torch)
+        qb0, sb0 = fg.quantize_fp8_blocks(w)
+        del w
+        weights = [(qb0, sb0)] + [(qb0.clone(), sb0.clone()) for _ in range(sets - 1)]
+        q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device="cuda")
+        sa = torch.empty((k // 128, fg.padded_rows(m)), dtype=torch.float32, device="cuda")
+        d = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+        def one_round():
+            for qb, sb in weights:
+                fg.quantize_fp8_groups(x, out=(q, sa))
+                fg.fp8_gemm_nt((q, sa), (qb, sb), d)
+
+        for _ in range(3):
+            one_round()
+        torch.cuda.synchronize()
+        # eager, back-to-back
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            one_round()
+        e1.record()
+        torch.cuda.synchronize()
+        eager_s = e0.elapsed_time(e1) * 1e-3 / (reps * sets)
+        # graph replay
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            one_round()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                one_round()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_s = e0.elapsed_time(e1) * 1e-3 / (reps * sets)
+        nbytes = quant_bytes(m, k) + gemm_bytes(m, n, k)
+        out.append(
+            {
+                "m": m,
+                "n": n,
+                "k": k,
+                "kernel": fg.describe_gemm(m, n, k),
+                "bytes_per_call": nbytes,
+                "graph_us": round(graph_s * 1e6, 3),
+                "graph_gbs": round(nbytes / graph_s / 1e9, 1),
+                "graph_frac_hbm": round(nbytes / graph_s / 1e9 / PEAK_HBM_GBS, 4),
+                "eager_us": round(eager_s * 1e6, 3),
+                "eager_gbs": round(nbytes / eager_s / 1e9, 1),
+                "weight_sets": sets,
+            }
+        )
+        del weights, qb0, sb0, g
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(linears, rows=None, cols=2048):
+    """The oracle (unchanged) on a bounded sample: every row of each linear's
+    activation, the first `cols` output columns (16 weight blocks) of each
+    linear; timed = activation quantization + block-scaled product."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    prepared = []
+    for lin in linears:
+        nc = min(cols, lin.n)
+        qb, sb = oracle.quantize_blocks(lin.b[:nc])  # offline, untimed (as on the GPU side)
+        a = lin.a if rows is None else lin.a[:rows]
+        prepared.append((a, qb, sb))
+    flops = 0
+    t0 = time.perf_counter()
+    for a, qb, sb in prepared:
+        q, sa = oracle.quantize_groups(a)
+        oracle.gemm_nt(q, sa, qb, sb)
+        flops += 2 * a.shape[0] * qb.shape[0] * a.shape[1]
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    m = prepared[0][0].shape[0]
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{m} rows x first {cols} output columns of each of the {len(linears)} linears "
+        f"(quantize_groups + gemm_nt, FP64, numpy+BLAS); {flops / 1e9:.1f} GFLOP in {dt:.1f} s",
+        "seconds": round(dt, 2),
+    }
+
+
+# --------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(
+            json.dumps(
+                {"error": "this build measures one GPU: the block-scaled FP8 linear runs on a single MI355X; "
+                 "multi-GPU sharding is described, not run", "n_gpus": args.gpus}
+            )
+        )
+        sys.exit(2)
+    import torch
+
+    import fine_grained_block_fp8_amd as fg
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')}")
+
+    if args.workload == "prefill":
+        linears = workloads.prefill_linears()
+        workload = "qwen3_8b_prefill_linears_m2048"
+    elif args.workload == "decode":
+        linears = [workloads.decode_linear(1, 12288, 4096), workloads.decode_linear(1, 4096, 12288)]
+        workload = "decode_m1_linears"
+    elif args.workload == "square8k":
+        linears = [workloads.square_linear(8192, 8192, 8192)]
+        workload = "square_8192x8192x8192"
+    elif args.workload == "square16k":
+        linears = [workloads.square_linear(16384, 16384, 8192)]
+        workload = "square_16384x16384x8192"
+    else:
+        linears = None
+        workload = "moe_32experts_zipf1.1_top4_k7168_n4096"
+
+    if linears is not None:
+        log(f"workload {workload}: " + ", ".join(f"{l.name} [{fg.describe_gemm(l.m, l.n, l.k)}]" for l in linears))
+        preps, elapsed, per = bench_linears(linears, args.steps, args.warmup, fg, torch)
+        total_flops = sum(l.flops for l in linears)
+        ms_per_step = elapsed / args.steps * 1e3
+        value = total_flops * args.steps / elapsed / 1e12
+        gemm_s = sum(r["_gemm_s"] for r in per)
+        roof = roofline_of(per)
+        del preps
+    else:
+        value, ms_per_step, per, roof, gemm_s, total_flops = bench_moe(args, fg, torch, workloads)
+    torch.cuda.empty_cache()
+
+    decode = None
+    if args.workload in ("prefill", "decode") and not args.no_decode:
+        decode = bench_decode(fg, torch)
+        for r in decode:
+            log(f"decode M=1 N={r['n']} K={r['k']}: graph {r['graph_us']} us {r['graph_gbs']} GB/s; "
+                f"eager {r['eager_us']} us")
+
+    cpu = None
+    if args.workload == "prefill" and not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(linears)
+
+    per_out = [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items() if not k.startswith("_")}
+               for r in per]
+    line = {
+        "metric": "FP8 block-scaled GEMM TFLOPS (% dense FP8 peak); decode M=1 GB/s (% HBM)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) activations with 0.1% x20 outliers, N(0,0.02) weights; no trained weights)",
+        "config": {
+            "workload": workload,
+            "steps_are": "act-quant (1x128) + block-scaled FP8 GEMM (bf16 out) for every linear; weights pre-quantized",
+            "linears": per_out,
+            "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
+            "gemm_only_tflops": round(total_flops / gemm_s / 1e12, 2) if gemm_s else None,
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "decode": decode,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_moe(args, fg, torch, workloads):
+    g = workloads.moe_grouped()
+    x = dev_bf16(g.a, torch)
+    q, sa = fg.quantize_fp8_groups(x)
+    w = dev_bf16(g.b.reshape(g.num_groups * g.n, g.k), torch)
+    qb, sb = fg.quantize_fp8_blocks(w)
+    del w
+    qb = qb.view(g.num_groups, g.n, g.k)
+    sb = sb.view(g.num_groups, g.n // 128, g.k // 128)
+    idx = torch.from_numpy(g.m_indices).cuda()
+    d = torch.empty((g.m, g.n), dtype=torch.bfloat16, device="cuda")
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fg.quantize_fp8_groups(x, out=(q, sa))
+        if ev:
+            ev[1].record()
+        fg.m_grouped_fp8_gemm_nt_contiguous((q, sa), (qb, sb), d, idx)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gt = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    qt = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    flops = g.useful_flops
+    per = [{"name": g.name, "m_pad": g.m, "n": g.n, "k": g.k, "groups": g.num_groups, "quant_us": qt * 1e6,
+            "gemm_us": gt * 1e6, "gemm_tflops_useful": flops / gt / 1e12,
+            "gemm_tflops_padded": 2 * g.m * g.n * g.k / gt / 1e12, "_gemm_s": gt}]
+    roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x2>", "achieved": round(flops / gt / 1e12, 1),
+            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / gt / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "traffic": None, "mean_launch_us": round(gt * 1e6, 2)}
+    return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gt, flops
+
+
+if __name__ == "__main__":
+    main()

@@ -14,8 +14,13 @@
 // row of A (l % 16) and four columns of B.  That makes the promotion scale
 // sa[row] * sb[block] a single per-lane value for the whole 16x16 tile.
 // Within a wave tile of NT 16-column MFMA tiles, MFMA tile t's column c is
-// mapped to wave column NT*c + t, so each lane ends up owning 4*NT
-// consecutive output columns of its row (a 64- or 32-byte contiguous store).
+// mapped to a wave column chosen so that each 16-byte store of the epilogue
+// writes 8 consecutive columns and the four lanes of a row cover 64
+// contiguous bytes.  The B tile is stored in LDS with its columns permuted
+// to match, so that every MFMA tile reads 16 consecutive LDS rows, exactly
+// like the A fragments.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -32,15 +37,20 @@ struct Tile {
   static constexpr int TN = BN / WAVES_N;  // wave tile columns (inside one 128-column scale block)
   static constexpr int MT = TM / 16;
   static constexpr int NT = TN / 16;
+  // LDS: the two stages of each operand sit one operand-tile apart, so that
+  // with the K loop unrolled by two every fragment address is a
+  // loop-invariant register plus an immediate (< 64 KB) offset.
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int S_BYTES = 1024;  // one stage's activation scales (<= 256 floats)
   static constexpr int A_OFF = 0;
-  static constexpr int B_OFF = BM * 128;
-  static constexpr int S_OFF = B_OFF + BN * 128;
-  static constexpr int S_BYTES = BM * 4 < 1024 ? 1024 : BM * 4;
-  static constexpr int STAGE = S_OFF + S_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int B_OFF = 2 * A_BYTES;
+  static constexpr int S_OFF = B_OFF + 2 * B_BYTES;
+  static constexpr int LDS = S_OFF + 2 * S_BYTES;
   static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-  static_assert(BM * 4 <= 1024, "one wave loads a stage's activation scales");
+  static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "segments divide evenly among waves");
+  static_assert(BM * 4 <= S_BYTES, "one wave loads a stage's activation scales");
+  static_assert(A_BYTES <= 32768 && B_BYTES <= 32768, "stage offsets must fit a 16-bit LDS immediate");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -49,43 +59,102 @@ using Tile128x256 = Tile<128, 256, 2, 2>;
 using Tile256x128 = Tile<256, 128, 4, 1>;
 using Tile128x128 = Tile<128, 128, 2, 2>;
 
-// LDS layout of a K chunk: row r of a tile is 128 bytes (8 slots of 16 bytes);
-// logical slot c of row r is stored at slot c ^ swz(r).  The XOR with both
-// r's low bits and its next three makes the 16-byte fragment reads
-// conflict-free both for 8 consecutive rows (A fragments) and for rows
-// NT apart (B fragments of the column-interleaved mapping).
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// LDS layout of a K chunk: row r of a tile is 128 bytes (8 slots of 16
+// bytes); logical slot c of row r is stored at slot c ^ swz(r).  Fragment
+// reads always cover 16 consecutive rows (a 16-row-aligned group) per
+// instruction, and swz depends only on r mod 16, so a fragment's address is
+// a per-lane base plus a compile-time offset (2 KB per 16-row tile, 32 KB per
+// stage) -- no address arithmetic in the main loop.  With (r ^ r>>3) over the
+// low four bits the 16-row reads run at ~85% of the conflict-free
+// ds_read_b128 rate on gfx950 (measured), well above what the loop needs.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Output column of MFMA tile t, position c (c = 4*lg + r for output lane
+// (li, lg), register r), within a wave's TN-column region: the lane's 4*NT
+// values j = NT*r + t go to columns 32*(j/8) + 8*lg + (j%8), so the four lanes
+// of a row together write 64 contiguous bytes per 16-byte store.
+template <class C>
+__device__ __forceinline__ int wave_col(int c, int t) {
+  const int j = C::NT * (c & 3) + t;
+  return 32 * (j >> 3) + 8 * (c >> 2) + (j & 7);
+}
+
+// LDS row rho of the B tile holds tile column b_col_of_row(rho): within each
+// wave's TN-column region, row 16*t + c holds wave_col(c, t), so MFMA tile t
+// reads the 16 consecutive rows 16t .. 16t+15.
+template <class C>
+__device__ __forceinline__ int b_col_of_row(int rho) {
+  const int w = rho / C::TN, rl = rho % C::TN;
+  return w * C::TN + wave_col<C>(rl & 15, rl >> 4);
+}
 
 // All waves cooperatively copy chunk kb of the A tile, the B tile and the
-// tile's activation scales into one LDS stage, with direct global->LDS
-// buffer loads (1 KB = 8 tile rows per wave instruction; rows past the
-// matrix edge read as zero).
+// tile's activation scales into one LDS stage with direct global->LDS buffer
+// loads (1 KB = 8 LDS rows per wave instruction; rows past the matrix edge
+// read as zero).  Wave w copies segments w, w + WAVES, ... of A and of B
+// (both counts divide evenly), and wave 0 the scales.  voff[] holds the
+// per-lane byte offsets of those segments for chunk 0; the chunk's column
+// offset is the scalar offset of each load.
 template <class C>
-__device__ __forceinline__ void load_stage(uint8_t* st, rsrc_t ra, rsrc_t rb, rsrc_t rs, uint32_t K, int kb,
-                                           uint32_t sa_ld_bytes, int wave, int lane) {
-  constexpr int AS = C::BM / 8, BS = C::BN / 8, SEGS = AS + BS + 1;
+struct StageLoader {
+  static constexpr int AN = C::BM / 8 / C::WAVES, BN_ = C::BN / 8 / C::WAVES, NSEG = AN + BN_;
+  uint8_t* lds;
+  rsrc_t ra, rb, rs;
+  const uint32_t* voff;
+  uint32_t sa_ld_bytes;
+  int wave, lane;
+  // Segment i (< NSEG) of chunk kb into `stage`; segment NSEG is the scales
+  // (wave 0 only).
+  __device__ __forceinline__ void issue(int i, int stage, int kb) const {
+    const uint32_t koff = (uint32_t)kb * 128u;
+    if (i < AN)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_void_t*)(lds + C::A_OFF + stage * C::A_BYTES + (wave + C::WAVES * i) * 1024), 16, voff[i], koff,
+          0, 0);
+    else if (i < NSEG)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_void_t*)(lds + C::B_OFF + stage * C::B_BYTES + (wave + C::WAVES * (i - AN)) * 1024), 16, voff[i],
+          koff, 0, 0);
+    else if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES), 16,
+                                               (uint32_t)lane * 16u, (uint32_t)kb * sa_ld_bytes, 0, 0);
+  }
+  __device__ __forceinline__ void all(int stage, int kb) const {
+#pragma unroll
+    for (int i = 0; i <= NSEG; i++) issue(i, stage, kb);
+  }
+};
+
+template <class C>
+__device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wave, int lane) {
+  constexpr int AN = C::BM / 8 / C::WAVES, BN_ = C::BN / 8 / C::WAVES;
   const int r8 = lane >> 3, cs = lane & 7;
 #pragma unroll
-  for (int s0 = 0; s0 < SEGS; s0 += C::WAVES) {
-    const int s = s0 + wave;
-    if (s < AS) {
-      const int r = s * 8 + r8;
-      load_lds16(ra, st + C::A_OFF + s * 1024, (uint32_t)r * K + kb * 128 + ((cs ^ swz(r)) << 4));
-    } else if (s < AS + BS) {
-      const int r = (s - AS) * 8 + r8;
-      load_lds16(rb, st + C::B_OFF + (s - AS) * 1024, (uint32_t)r * K + kb * 128 + ((cs ^ swz(r)) << 4));
-    } else if (s == AS + BS) {
-      load_lds16(rs, st + C::S_OFF, (uint32_t)kb * sa_ld_bytes + lane * 16);
-    }
+  for (int i = 0; i < AN; i++) {
+    const int rho = (wave + C::WAVES * i) * 8 + r8;
+    voff[i] = (uint32_t)rho * K + ((cs ^ swz(rho)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < BN_; i++) {
+    const int rho = (wave + C::WAVES * i) * 8 + r8;
+    voff[AN + i] = (uint32_t)b_col_of_row<C>(rho) * K + ((cs ^ swz(rho)) << 4);
   }
 }
 
-// The 32 bytes lane (row r, k-group lg) contributes to a 16x16x128 MFMA.
-__device__ __forceinline__ v8i_t read_frag(const uint8_t* base, int r, int lg) {
-  const uint8_t* row = base + r * 128;
-  const int sw = swz(r);
-  const uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * lg) ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * lg + 1) ^ sw) << 4));
+// LDS byte offsets of the two 16-byte slots lane (li, lg) reads for a
+// 16x16x128 MFMA fragment of rows base_row .. base_row+15 (base_row a
+// multiple of 16, so the swizzle depends on li only).  Adding 2048 selects
+// the next 16-row tile, adding an operand-tile size the other stage.
+struct FragAddr {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ FragAddr frag_addr(uint32_t region, int base_row, int li, int lg) {
+  const uint32_t row = region + (uint32_t)(base_row + li) * 128u;
+  return {row + (uint32_t)(((2 * lg) ^ swz(li)) << 4), row + (uint32_t)(((2 * lg + 1) ^ swz(li)) << 4)};
+}
+__device__ __forceinline__ v8i_t read_frag(const uint8_t* lds, const FragAddr& a, uint32_t cst) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(lds + a.lo + cst);
+  const uint4 hi = *reinterpret_cast<const uint4*>(lds + a.hi + cst);
   v8i_t f;
   f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
   f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
@@ -105,29 +174,73 @@ __device__ __forceinline__ void promote(v4f_t& acc, const v4f_t& p, float s) {
   acc[3] = __builtin_fmaf(p[3], s, acc[3]);
 }
 
+// B fragment of column tile t for lane c = li: LDS row 16*t + c of the wave's
+// region, which holds wave column wave_col(c, t).  acc[mt][t][r] of output
+// lane (li, lg) is therefore wave column wave_col(4*lg + r, t).
 template <class C>
-__device__ __forceinline__ void compute_stage(const uint8_t* st, float sbv, int wm, int wn, int lane,
-                                              v4f_t (&acc)[C::MT][C::NT]) {
-  const int li = lane & 15, lg = lane >> 4;
-  const float* sas = reinterpret_cast<const float*>(st + C::S_OFF);
-  v8i_t af[C::MT];
-  float sc[C::MT];
+__device__ __forceinline__ v8i_t read_b(const uint8_t* lds, const FragAddr& ba, int stage, int t) {
+  return read_frag(lds, ba, (uint32_t)(stage * C::B_BYTES + 2048 * t));
+}
+
+// A fragments and promotion scales (sa[row] * sb) of one chunk.
+template <class C>
+__device__ __forceinline__ void read_a(const uint8_t* lds, const FragAddr& aa, uint32_t sa_addr, int stage,
+                                       float sbv, v8i_t (&af)[C::MT], float (&sc)[C::MT]) {
 #pragma unroll
   for (int mt = 0; mt < C::MT; mt++) {
-    const int r = wm * C::TM + 16 * mt + li;
-    af[mt] = read_frag(st + C::A_OFF, r, lg);
-    sc[mt] = sas[r] * sbv;
-  }
-#pragma unroll
-  for (int t = 0; t < C::NT; t++) {
-    const v8i_t bfr = read_frag(st + C::B_OFF, wn * C::TN + C::NT * li + t, lg);
-#pragma unroll
-    for (int mt = 0; mt < C::MT; mt++) promote(acc[mt][t], mfma_fp8(bfr, af[mt]), sc[mt]);
+    af[mt] = read_frag(lds, aa, (uint32_t)(stage * C::A_BYTES + 2048 * mt));
+    sc[mt] = *reinterpret_cast<const float*>(lds + sa_addr + stage * C::S_BYTES + 64 * mt) * sbv;
   }
 }
 
-// Main loop + epilogue for one (m0, n0) output tile.  a / b point at the
-// tile's first row of A / B; sb_base at the first scale row of B's matrix.
+// Column tiles [T0, T1) of a chunk, software-pipelined one MFMA deep: MFMA i
+// is issued, then the FP32 promotion of MFMA i-1's partial runs on the VALU
+// (independent of MFMA i, so the two overlap), and the B fragment of the next
+// column tile is read one tile ahead (from LDS, or from registers when PRE).
+template <class C, int T0, int T1, bool PRE, bool LD>
+__device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& ba, int stage,
+                                           const v8i_t (&af)[C::MT], const float (&sc)[C::MT], const v8i_t* pre,
+                                           v4f_t (&acc)[C::MT][C::NT], const StageLoader<C>& ld, int next_kb) {
+  // With LD, the next chunk's global->LDS copies (NSEG instructions per
+  // wave) are spread over the first half of the column tiles, so that no
+  // wave stalls for long on a full vector-memory queue, and they still land
+  // well before the next barrier.
+  constexpr int NL = StageLoader<C>::NSEG, HALF = (T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1;
+  constexpr int PER = (NL + HALF - 1) / HALF;
+  constexpr int N_MFMA = (T1 - T0) * C::MT;
+  v8i_t bfr[2];
+  v4f_t part[2];
+  bfr[0] = PRE ? pre[0] : read_b<C>(lds, ba, stage, T0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; i++) {
+    const int u = i / C::MT, mt = i % C::MT, t = T0 + u;
+    if (LD && mt == 0) {
+#pragma unroll
+      for (int q = 0; q < PER; q++)
+        if (u * PER + q < NL) ld.issue(u * PER + q, stage ^ 1, next_kb);
+    }
+    if (mt == 0 && t + 1 < T1) bfr[(u + 1) & 1] = PRE ? pre[u + 1] : read_b<C>(lds, ba, stage, t + 1);
+    part[i & 1] = mfma_fp8(bfr[u & 1], af[mt]);
+    if (i > 0) {
+      const int pu = (i - 1) / C::MT, pm = (i - 1) % C::MT;
+      promote(acc[pm][T0 + pu], part[(i - 1) & 1], sc[pm]);
+    }
+    // Keep this order in the final schedule: the next B fragment's two LDS
+    // reads, then per MFMA the promotion of the previous partial.  Without
+    // it the scheduler hoists every fragment read of the chunk and runs out
+    // of registers.
+    if (LD && mt == 0) {
+#pragma unroll
+      for (int q = 0; q < PER; q++)
+        if (u * PER + q < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    if (mt == 0 && t + 1 < T1 && !PRE) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+  promote(acc[C::MT - 1][T1 - 1], part[(N_MFMA - 1) & 1], sc[C::MT - 1]);
+}
+
 template <class C>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
                                           const float* sb_base, uint16_t* __restrict__ d, int64_t M, int64_t N,
@@ -152,42 +265,60 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
 #pragma unroll
     for (int j = 0; j < C::NT; j++) acc[i][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
 
-  load_stage<C>(lds, ra, rb, rs, (uint32_t)K, 0, (uint32_t)(sa_ld * 4), wave, lane);
-  for (int kb = 0; kb < KB; kb++) {
-    const float sbv = sbw[kb];
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies into the stage have landed
-    __syncthreads();                     // ... and every other wave's; stage kb-1 is free again
-    if (kb + 1 < KB)
-      load_stage<C>(lds + ((kb + 1) & 1) * C::STAGE, ra, rb, rs, (uint32_t)K, kb + 1, (uint32_t)(sa_ld * 4), wave,
-                    lane);
-    compute_stage<C>(lds + (kb & 1) * C::STAGE, sbv, wm, wn, lane, acc);
-  }
-
-  // Epilogue: lane (li, lg) owns row m0 + wm*TM + 16*mt + li, columns
-  // c0 .. c0 + 4*NT - 1; acc[mt][t][r] is column c0 + NT*r + t.
   const int li = lane & 15, lg = lane >> 4;
+  v8i_t af[C::MT];
+  float sc[C::MT];
+  uint32_t voff[StageLoader<C>::NSEG];
+  stage_offsets<C>(voff, (uint32_t)K, wave, lane);
+  const StageLoader<C> loader{lds, ra, rb, rs, voff, (uint32_t)(sa_ld * 4), wave, lane};
+  const FragAddr aa = frag_addr(C::A_OFF, wm * C::TM, li, lg);
+  const FragAddr ba = frag_addr(C::B_OFF, wn * C::TN, li, lg);
+  const uint32_t sa_addr = C::S_OFF + (uint32_t)(wm * C::TM + li) * 4u;
+  // One chunk: wait for this wave's copies into `stage`, barrier (every
+  // wave's copies have landed and the other stage is no longer read), then
+  // compute chunk kb while refilling the other stage with chunk kb+1.
+  loader.all(0, 0);
+  for (int kb = 0; kb < KB; kb++) {
+    const int stage = kb & 1;
+    const float sbv = sbw[kb];
+    // The last chunk refills the free stage with a copy of itself (valid
+    // addresses, never read) so that the loop body has no branch.
+    const int next = kb + 1 < KB ? kb + 1 : kb;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (wave == 0) loader.issue(StageLoader<C>::NSEG, stage ^ 1, next);  // scales
+    read_a<C>(lds, aa, sa_addr, stage, sbv, af, sc);
+    mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, af, sc, nullptr, acc, loader, next);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
+
+  // Epilogue: lane (li, lg) owns row m0 + wm*TM + 16*mt + li; its values
+  // j = 8*s + e (s < NT/2, e < 8) go to column n0 + wn*TN + 32*s + 8*lg + e,
+  // held in acc[mt][j % NT][j / NT].
   const bool vec = (N % 8) == 0;
 #pragma unroll
   for (int mt = 0; mt < C::MT; mt++) {
     const int64_t row = m0 + wm * C::TM + 16 * mt + li;
     if (row >= M) continue;
-    const int64_t c0 = n0 + wn * C::TN + 4 * C::NT * lg;
     uint16_t* drow = d + row * N;
-    if (vec && c0 + 4 * C::NT <= N) {
 #pragma unroll
-      for (int s = 0; s < C::NT / 2; s++) {
+    for (int s = 0; s < C::NT / 2; s++) {
+      const int64_t c0 = n0 + wn * C::TN + 32 * s + 8 * lg;
+      if (vec && c0 + 8 <= N) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int j0 = 8 * s + 2 * e, j1 = j0 + 1;
           w[e] = pack_bf16x2(acc[mt][j0 % C::NT][j0 / C::NT], acc[mt][j1 % C::NT][j1 / C::NT]);
         }
-        *reinterpret_cast<uint4*>(drow + c0 + 8 * s) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    } else {
+        *reinterpret_cast<uint4*>(drow + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4 * C::NT; j++)
-        if (c0 + j < N) drow[c0 + j] = (uint16_t)bf16_rne(acc[mt][j % C::NT][j / C::NT]);
+        for (int e = 0; e < 8; e++) {
+          const int j = 8 * s + e;
+          if (c0 + e < N) drow[c0 + e] = (uint16_t)bf16_rne(acc[mt][j % C::NT][j / C::NT]);
+        }
+      }
     }
   }
 }
