@@ -225,18 +225,13 @@ __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& b
       const int pu = (i - 1) / C::MT, pm = (i - 1) % C::MT;
       promote(acc[pm][T0 + pu], part[(i - 1) & 1], sc[pm]);
     }
-    // Keep this order in the final schedule: the next B fragment's two LDS
-    // reads, then per MFMA the promotion of the previous partial.  Without
-    // it the scheduler hoists every fragment read of the chunk and runs out
-    // of registers.
-    if (LD && mt == 0) {
-#pragma unroll
-      for (int q = 0; q < PER; q++)
-        if (u * PER + q < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    if (mt == 0 && t + 1 < T1 && !PRE) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    // Keep the written order: MFMA i is issued before the promotion of
+    // partial i-1, so one wave alone issues MFMAs back to back (the VALU work
+    // of the previous partial fills the gap) instead of stalling on the
+    // result of the MFMA it just issued.
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   promote(acc[C::MT - 1][T1 - 1], part[(N_MFMA - 1) & 1], sc[C::MT - 1]);
 }
