@@ -14,46 +14,63 @@
 namespace fgfp8 {
 
 // ---------------------------------------------------------------- groups
-// One wave quantizes four (row, group) slots: the 16 lanes of DPP row j hold
-// row 4q+j of group g, 8 bf16 (16 bytes) per lane, so the group's amax is a
-// 16-lane DPP reduction.  Slot quads are numbered group-major, so a wave's
-// four scales are four consecutive floats of one MN-major scale column.  The
-// kernel is bound by HBM: 2 bytes in and 1 byte out per element.
+// A wave quantizes a block of 4 rows x 4 groups.  In step i it reads row
+// r0 + i, groups g0 .. g0+3: 1 KB contiguous, the 16 lanes of DPP row j
+// holding group g0 + j (8 bf16 = 16 bytes per lane), so a group's amax is a
+// 16-lane DPP reduction.  All four rows are loaded before any is quantized
+// (four 16-byte loads in flight per lane).  After the four steps, lane 16j
+// holds the scales of group g0 + j for rows r0 .. r0+3 -- four consecutive
+// floats of the MN-major scale column -- and stores them at once.  Waves are
+// numbered row-block-major so that neighbouring waves read neighbouring
+// kilobytes of the same rows.  The kernel is bound by HBM: 2 bytes in and 1
+// byte out per element.
 constexpr int kQgWaves = 4;
 
 __global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const uint16_t* __restrict__ x,
                                                                          uint8_t* __restrict__ q,
                                                                          float* __restrict__ sa, int64_t m, int64_t k,
-                                                                         int64_t sa_ld, int64_t quads_per_group,
-                                                                         int64_t total_quads) {
+                                                                         int64_t sa_ld, int64_t group_quads,
+                                                                         int64_t total_blocks) {
   const int lane = threadIdx.x & 63;
-  const int64_t quad = (int64_t)blockIdx.x * kQgWaves + (threadIdx.x >> 6);
-  if (quad >= total_quads) return;  // wave-uniform
-  const int64_t g = quad / quads_per_group;
-  const int64_t row = (quad - g * quads_per_group) * 4 + (lane >> 4);
-  const bool valid = row < m;
-  const int64_t off = row * k + g * kGroup + (lane & 15) * 8;
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (valid) v = *reinterpret_cast<const uint4*>(x + off);
-  const uint32_t amax_bits = row16_max_u32(absmax8_bits(v));
-  const float s = group_scale(__uint_as_float(amax_bits));
-  const double r = 1.0 / (double)s;
-  const uint2 o = quantize8(v, r);
-  if (valid) {
-    *reinterpret_cast<uint2*>(q + off) = o;
-    if ((lane & 15) == 0) sa[g * sa_ld + row] = s;
+  const int64_t blk = (int64_t)blockIdx.x * kQgWaves + (threadIdx.x >> 6);
+  if (blk >= total_blocks) return;  // wave-uniform
+  const int64_t r0 = (blk / group_quads) * 4;
+  const int64_t g = (blk % group_quads) * 4 + (lane >> 4);
+  const bool g_ok = g < k / kGroup;
+  const int64_t col = g * kGroup + (lane & 15) * 8;
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    v[i] = (g_ok && r0 + i < m) ? *reinterpret_cast<const uint4*>(x + (r0 + i) * k + col) : make_uint4(0, 0, 0, 0);
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t amax_bits = row16_max_u32(absmax8_bits(v[i]));
+    s[i] = group_scale(__uint_as_float(amax_bits));
+    const double r = 1.0 / (double)s[i];
+    const uint2 o = quantize8(v[i], r);
+    if (g_ok && r0 + i < m) *reinterpret_cast<uint2*>(q + (r0 + i) * k + col) = o;
+  }
+  if (g_ok && (lane & 15) == 0) {
+    float* dst = sa + g * sa_ld + r0;
+    if (r0 + 4 <= m) {
+      *reinterpret_cast<float4*>(dst) = make_float4(s[0], s[1], s[2], s[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (r0 + i < m) dst[i] = s[i];
+    }
   }
 }
 
 hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, float* sa, int64_t sa_ld,
                                   hipStream_t stream) {
-  const int64_t mpad = (m + 3) / 4 * 4;
-  const int64_t quads_per_group = mpad / 4;
-  const int64_t total = quads_per_group * (k / kGroup);
+  const int64_t row_blocks = (m + 3) / 4;
+  const int64_t group_quads = (k / kGroup + 3) / 4;
+  const int64_t total = row_blocks * group_quads;
   const int64_t blocks = (total + kQgWaves - 1) / kQgWaves;
   hipLaunchKernelGGL(quantize_groups_kernel, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, quads_per_group,
-                     total);
+                     static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total);
   return hipGetLastError();
 }
 
