@@ -43,11 +43,12 @@ _lib.quantize_fp8_groups.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_blocks.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
 _lib.m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _vp, _i64, _i64, _i64, _vp]
+_lib.fp8_linear_nt.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _vp]
 _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
-              "fgfp8_describe_gemm"):
+              "fp8_linear_nt", "fgfp8_describe_gemm"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -185,15 +186,47 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Ten
     return d
 
 
+FUSED_MAX_M, FUSED_MAX_K = 4, 32768
+
+
+def fp8_linear_nt(x: torch.Tensor, weight, d: torch.Tensor, act_out=None) -> torch.Tensor:
+    """d[M, N] = quantize_groups(x) . B^T for bf16 x [M, K] and the stored
+    weight (q [N, K], sb).  One fused kernel for M <= 4 (K <= 32768);
+    `act_out` = (q [M, K], sa [K/128, sa_ld]) optionally receives the quantized
+    activation (and is required as workspace for larger M)."""
+    qb, sb = weight
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(qb, "b", _FP8, 2)
+    _need(sb, "sb", (torch.float32,), 2)
+    _need(d, "d", (torch.bfloat16,), 2)
+    m, k = x.shape
+    n = qb.shape[0]
+    if qb.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch among x [M, K], b [N, K], d [M, N]")
+    if act_out is None:
+        q_ptr, sa_ptr, sa_ld = None, None, 0
+    else:
+        q, sa = act_out
+        _need(q, "q", _FP8, 2)
+        _need(sa, "sa", (torch.float32,), 2)
+        q_ptr, sa_ptr, sa_ld = _ptr(q), _ptr(sa), sa.shape[1]
+    _check(_lib.fp8_linear_nt(_ptr(x), m, k, _ptr(qb), _ptr(sb), n, _ptr(d), q_ptr, sa_ptr, sa_ld, _stream(d)))
+    return d
+
+
 def fp8_linear(x: torch.Tensor, weight) -> torch.Tensor:
     """The pages' linear (Linnet DeepGEMM plugin, _BlockProduct.execute): round
     the bf16 input per 1x128 group, then the block-scaled product with the
     pre-quantized weight (q [N, K], sb).  x: bf16 [..., K]; returns bf16 [..., N]."""
     qb, sb = weight
     flat = x.reshape(-1, x.shape[-1])
-    q, sa = quantize_fp8_groups(flat)
-    d = torch.empty((flat.shape[0], qb.shape[0]), dtype=torch.bfloat16, device=x.device)
-    fp8_gemm_nt((q, sa), (qb, sb), d)
+    m, k = flat.shape
+    d = torch.empty((m, qb.shape[0]), dtype=torch.bfloat16, device=x.device)
+    act = None
+    if not (m <= FUSED_MAX_M and k <= FUSED_MAX_K):
+        act = (torch.empty((m, k), dtype=torch.float8_e4m3fn, device=x.device),
+               torch.empty((k // GROUP, padded_rows(m)), dtype=torch.float32, device=x.device))
+    fp8_linear_nt(flat, (qb, sb), d, act)
     return d.reshape(*x.shape[:-1], qb.shape[0])
 
 
@@ -213,6 +246,7 @@ __all__ = [
     "describe_gemm",
     "fp8_gemm_nt",
     "fp8_linear",
+    "fp8_linear_nt",
     "last_error",
     "m_grouped_fp8_gemm_nt_contiguous",
     "padded_rows",

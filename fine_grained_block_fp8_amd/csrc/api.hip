@@ -164,6 +164,40 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
                   who);
 }
 
+int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, const float* sb, int64_t n,
+                  void* d_bf16, void* q_e4m3, float* sa, int64_t sa_ld, void* stream) {
+  const char* who = "fp8_linear_nt";
+  if (m < 0 || m >= kMaxRows || n < 0 || n >= kMaxRows)
+    return fail(FGFP8_EINVAL, "%s: m=%lld n=%lld out of range", who, (long long)m, (long long)n);
+  if (int rc = check_k(who, k)) return rc;
+  if (!x_bf16 || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if ((q_e4m3 == nullptr) != (sa == nullptr))
+    return fail(FGFP8_EINVAL, "%s: q_e4m3 and sa must be given together", who);
+  const bool fused = m <= fgfp8::kFusedMaxM && k <= fgfp8::kFusedMaxK;
+  if (!fused && q_e4m3 == nullptr)
+    return fail(FGFP8_EINVAL, "%s: m=%lld k=%lld needs the q_e4m3/sa workspace", who, (long long)m, (long long)k);
+  if (q_e4m3 != nullptr) {
+    if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+    if (!aligned16(q_e4m3) || !aligned16(sa)) return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  }
+  if (!aligned16(x_bf16) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(d_bf16))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (m == 0 || n == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  if (fused) {
+    if (env_flag("FGFP8_PRINT_CONFIG"))
+      fprintf(stderr, "[fgfp8] fp8_linear_nt m=%lld n=%lld k=%lld: fused decode split=%d\n", (long long)m,
+              (long long)n, (long long)k, fgfp8::decode_split(n, k));
+    return launched(fgfp8::launch_decode_fused(x_bf16, b_e4m3, sb, d_bf16, m, n, k, q_e4m3, sa, sa_ld,
+                                               (hipStream_t)stream),
+                    who);
+  }
+  if (int rc = launched(fgfp8::launch_quantize_groups(x_bf16, m, k, q_e4m3, sa, sa_ld, (hipStream_t)stream), who))
+    return rc;
+  const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
+  return launched(fgfp8::launch_gemm(plan, q_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, (hipStream_t)stream), who);
+}
+
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len) {
   if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: null or empty buffer");
   if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: bad shape");

@@ -1,0 +1,286 @@
+// Decode-shaped block-scaled FP8 products (M <= 16): a stream over the weight.
+//
+// Same definition as the dense product (deepgemm-rust README, "What's
+// implemented" table, fp8_gemm_nt row; per-128-block scale promotion), but
+// with at most 16 activation rows the work is bound by reading B (N*K bytes)
+// from HBM: decode "re-reads the full weight tensor from HBM every generated
+// token" (AReno FP8 decode pull request, Summary).  A workgroup owns 16 output
+// columns -- one 16-row slab of B, contiguous in memory -- and its KS waves
+// split K into contiguous chunk ranges.  Each wave issues the loads of all
+// its chunks (two 16-byte loads per lane per chunk, straight into MFMA
+// fragment registers) before doing anything else, so the whole weight stream
+// is in flight at once; then it forms one 16x16x128 MFMA per chunk with a
+// zero accumulator and promotes it with sa * sb in FP32.  The KS partial
+// tiles are summed through LDS in wave order.
+//
+// The fused variant takes the bf16 activation (M <= 4) and quantizes it per
+// 1x128 group into LDS inside every workgroup, with exactly the arithmetic of
+// quantize_fp8_groups, while the weight loads are in flight: one launch per
+// decode linear instead of two (the pages' decode path spent its time in the
+// per-call activation-quantize chain until that was fused into one kernel:
+// AReno pull request, commit notes on fusing the activation quantize).
+// Both variants share the chunk order and the reduction order, so their
+// outputs are bit-identical.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fgfp8 {
+
+// Chunks of one wave held in registers at a time: 12 with the activation in
+// LDS (fused), 8 when the A fragments are registers too.  Both keep a wave
+// under 168 VGPRs, so three waves fit per SIMD and a grid of three
+// workgroups per CU is resident at once.
+constexpr int kDecodeMaxChunksFused = 12;
+constexpr int kDecodeMaxChunks = 8;
+constexpr int kFusedMaxRows = 4;
+
+__device__ __forceinline__ v8i_t frag_of(uint4 lo, uint4 hi) {
+  v8i_t f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+__device__ __forceinline__ v4f_t mfma_fp8_dec(const v8i_t& x, const v8i_t& y) {
+  const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// FUSED = false: A is E4M3 [M][K] with scales sa [K/128][sa_ld] in global
+// memory.  FUSED = true: X is bf16 [M][K] (M <= 4), quantized here; if q_out
+// is non-null, workgroup 0 also writes the quantized activation and its
+// scales (q_out [M][K], sa_out [K/128][sa_out_ld]).
+template <int KS, bool FUSED>
+__global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict__ Ain, const float* __restrict__ SA,
+                                                         int64_t sa_ld, const uint8_t* __restrict__ B,
+                                                         const float* __restrict__ SB, uint16_t* __restrict__ D,
+                                                         int M, int64_t N, int K, uint8_t* __restrict__ q_out,
+                                                         float* __restrict__ sa_out, int64_t sa_out_ld) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int KB = K / kGroup;
+  const int per = (KB + KS - 1) / KS;
+  const int c_begin = wave * per;
+  const int c_end = c_begin + per < KB ? c_begin + per : KB;
+  const uint32_t b_rows = (uint32_t)(N - n0 < 16 ? N - n0 : 16);
+  const rsrc_t rb = make_rsrc(B + n0 * K, b_rows * (uint32_t)K);
+  const uint32_t off = (uint32_t)li * (uint32_t)K + (uint32_t)lg * 32u;
+  const float* sbw = SB + (n0 / kGroup) * KB;
+  const bool row_ok = li < M;
+
+  // LDS: [red: KS x 64 x 16 B][FUSED: qa 4 x K bytes][FUSED: scales KB x 4 floats]
+  v4f_t* red = reinterpret_cast<v4f_t*>(smem);
+  uint8_t* qa = smem + KS * 64 * 16;
+  float* qs = reinterpret_cast<float*>(qa + kFusedMaxRows * K);
+
+  // Every operand of a batch of chunks is requested before any is used, so
+  // a wave waits for memory once per batch, not once per chunk: the B
+  // fragments, the weight scales of the batch (one per lane, broadcast with
+  // readlane) and, without fusion, the A fragments and activation scales.
+  constexpr int MAXC = FUSED ? kDecodeMaxChunksFused : kDecodeMaxChunks;
+  v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 b0[MAXC], b1[MAXC], a0[FUSED ? 1 : MAXC], a1[FUSED ? 1 : MAXC];
+  float sav[FUSED ? 1 : MAXC];
+  float sbv = 0.0f;
+  const uint8_t* Aq = static_cast<const uint8_t*>(Ain);
+  // Small operands first: requests queue in order behind the weight stream,
+  // so anything issued after it would arrive only when the stream has.
+  auto issue = [&](int cb, int nc) {
+    sbv = lane < nc ? sbw[cb + lane] : 0.0f;
+    if (!FUSED) {
+#pragma unroll
+      for (int u = 0; u < MAXC; u++) {
+        if (u < nc) {
+          const int kb = cb + u;
+          if (row_ok) {
+            const uint8_t* p = Aq + (int64_t)li * K + kb * kGroup + lg * 32;
+            a0[u] = *reinterpret_cast<const uint4*>(p);
+            a1[u] = *reinterpret_cast<const uint4*>(p + 16);
+            sav[u] = SA[(int64_t)kb * sa_ld + li];
+          } else {
+            a0[u] = make_uint4(0, 0, 0, 0);
+            a1[u] = make_uint4(0, 0, 0, 0);
+            sav[u] = 0.0f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MAXC; u++) {
+      if (u < nc) {
+        const uint32_t o = off + (uint32_t)(cb + u) * 128u;
+        b0[u] = load_rsrc16(rb, o);
+        b1[u] = load_rsrc16(rb, o + 16);
+      }
+    }
+  };
+  auto compute = [&](int cb, int nc) {
+#pragma unroll
+    for (int u = 0; u < MAXC; u++) {
+      if (u < nc) {
+        const int kb = cb + u;
+        v8i_t af;
+        float sa_u;
+        if (FUSED) {
+          if (row_ok) {
+            const uint8_t* p = qa + li * K + kb * kGroup + lg * 32;
+            af = frag_of(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 16));
+            sa_u = qs[kb * kFusedMaxRows + li];
+          } else {
+            af = frag_of(make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0));
+            sa_u = 0.0f;
+          }
+        } else {
+          af = frag_of(a0[u], a1[u]);
+          sa_u = sav[u];
+        }
+        const v4f_t p = mfma_fp8_dec(frag_of(b0[u], b1[u]), af);
+        const float sc = sa_u * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sbv), u));
+        acc[0] = __builtin_fmaf(p[0], sc, acc[0]);
+        acc[1] = __builtin_fmaf(p[1], sc, acc[1]);
+        acc[2] = __builtin_fmaf(p[2], sc, acc[2]);
+        acc[3] = __builtin_fmaf(p[3], sc, acc[3]);
+      }
+    }
+  };
+
+  int cb = c_begin;
+  int nc = c_end - cb < MAXC ? c_end - cb : MAXC;
+  if (FUSED) {
+    // Every wave helps quantize the activation into LDS (16 lanes per (row,
+    // group), as quantize_fp8_groups).  The first kXAhead activation loads of
+    // each lane go out before the weight loads, and the quantization runs
+    // while the weight stream is in flight.
+    constexpr int kXAhead = 4;
+    const uint16_t* X = static_cast<const uint16_t*>(Ain);
+    const int tasks = M * KB, step = KS * 4, part = threadIdx.x & 15, t0 = (int)(threadIdx.x >> 4);
+    uint4 xv[kXAhead];
+#pragma unroll
+    for (int i = 0; i < kXAhead; i++) {
+      const int task = t0 + i * step;
+      if (task < tasks) {
+        const int m = task / KB, g = task - m * KB;
+        xv[i] = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + g * kGroup + part * 8);
+      }
+    }
+    if (nc > 0) issue(cb, nc);
+    auto quantize_task = [&](int task, const uint4& v) {
+      const int m = task / KB, g = task - m * KB;
+      const uint32_t amax_bits = row16_max_u32(absmax8_bits(v));
+      const float s = group_scale(__uint_as_float(amax_bits));
+      const double r = 1.0 / (double)s;
+      const uint2 o = quantize8(v, r);
+      *reinterpret_cast<uint2*>(qa + m * K + g * kGroup + part * 8) = o;
+      if (part == 0) qs[g * kFusedMaxRows + m] = s;
+      if (q_out != nullptr && blockIdx.x == 0) {
+        *reinterpret_cast<uint2*>(q_out + (int64_t)m * K + g * kGroup + part * 8) = o;
+        if (part == 0) sa_out[(int64_t)g * sa_out_ld + m] = s;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kXAhead; i++) {
+      const int task = t0 + i * step;
+      if (task < tasks) quantize_task(task, xv[i]);
+    }
+    for (int task = t0 + kXAhead * step; task < tasks; task += step) {
+      const int m = task / KB, g = task - m * KB;
+      quantize_task(task, *reinterpret_cast<const uint4*>(X + (int64_t)m * K + g * kGroup + part * 8));
+    }
+    __syncthreads();
+  } else if (nc > 0) {
+    issue(cb, nc);
+  }
+  while (nc > 0) {
+    compute(cb, nc);
+    cb += nc;
+    nc = c_end - cb < MAXC ? c_end - cb : MAXC;
+    if (nc > 0) issue(cb, nc);
+  }
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    v4f_t s = red[lane];
+#pragma unroll
+    for (int w = 1; w < KS; w++) {
+      const v4f_t o = red[w * 64 + lane];
+      s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
+    }
+    // lane (li, lg): output row li, columns n0 + 4*lg .. n0 + 4*lg + 3
+    if (row_ok) {
+      const int64_t c0 = n0 + 4 * lg;
+      uint16_t* drow = D + (int64_t)li * N;
+      if ((N % 4) == 0 && c0 + 4 <= N) {
+        *reinterpret_cast<uint2*>(drow + c0) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          if (c0 + r < N) drow[c0 + r] = (uint16_t)bf16_rne(s[r]);
+      }
+    }
+  }
+}
+
+// K split (1..8 waves per slab): enough waves in flight to cover HBM
+// latency, and at most 12 chunks per wave on the common shapes.
+int decode_split(int64_t n, int64_t k) {
+  const int64_t slabs = (n + 15) / 16, kb = k / kGroup;
+  int ks = 4;
+  while (ks < 8 && (slabs * ks < 2048 || (kb + ks - 1) / ks > 12)) ks *= 2;
+  while (ks > 1 && (kb + ks - 1) / ks < 2) ks /= 2;
+  return ks;
+}
+
+template <int KS, bool FUSED>
+static hipError_t allow_lds() {
+  // The fused variant holds the quantized activation (up to 4 x K bytes) in
+  // LDS; allow dynamic LDS beyond the 64 KB default, once per kernel.
+  static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  return once;
+}
+
+template <int KS, bool FUSED>
+static hipError_t launch_decode_ks(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
+                                   void* d, int64_t m, int64_t n, int64_t k, uint8_t* q_out, float* sa_out,
+                                   int64_t sa_out_ld, hipStream_t stream) {
+  size_t lds = (size_t)KS * 64 * 16;
+  if (FUSED) {
+    lds += (size_t)kFusedMaxRows * k + (size_t)(k / kGroup) * kFusedMaxRows * 4;
+    if (lds > 64 * 1024) {
+      const hipError_t e = allow_lds<KS, FUSED>();
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL((decode_kernel<KS, FUSED>), dim3((uint32_t)((n + 15) / 16)), dim3(KS * 64), lds, stream, a, sa,
+                     sa_ld, static_cast<const uint8_t*>(b), sb, static_cast<uint16_t*>(d), (int)m, n, (int)k, q_out,
+                     sa_out, sa_out_ld);
+  return hipGetLastError();
+}
+
+template <bool FUSED>
+static hipError_t launch_decode_t(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b,
+                                  const float* sb, void* d, int64_t m, int64_t n, int64_t k, uint8_t* q_out,
+                                  float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
+  switch (ks) {
+    case 1: return launch_decode_ks<1, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 2: return launch_decode_ks<2, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 4: return launch_decode_ks<4, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    default: return launch_decode_ks<8, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+  }
+}
+
+hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
+                         void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  return launch_decode_t<false>(ks, a, sa, sa_ld, b, sb, d, m, n, k, nullptr, nullptr, 0, stream);
+}
+
+hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
+                               int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
+  return launch_decode_t<true>(decode_split(n, k), x, nullptr, 0, b, sb, d, m, n, k, static_cast<uint8_t*>(q_out),
+                               sa_out, sa_out_ld, stream);
+}
+
+}  // namespace fgfp8

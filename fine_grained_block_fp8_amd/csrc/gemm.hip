@@ -368,84 +368,6 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_kernel(
                m0, n0);
 }
 
-// ------------------------------------------------------------ decode (M <= 16)
-// The product is a stream over B (N*K bytes) with A's <= 16 rows re-read from
-// L2.  A workgroup owns 16 output columns; its SPLIT waves take interleaved K
-// chunks, each lane loading its own 32-byte MFMA fragments straight from
-// global memory, kU chunks per batch so that several loads are in flight per
-// lane.  The waves' FP32 tiles are then summed through LDS.
-constexpr int kDecodeU = 4;
-
-template <int SPLIT>
-__global__ __launch_bounds__(SPLIT * 64) void gemm_decode_kernel(const uint8_t* __restrict__ A,
-                                                                  const float* __restrict__ SA,
-                                                                  const uint8_t* __restrict__ B,
-                                                                  const float* __restrict__ SB,
-                                                                  uint16_t* __restrict__ D, int M, int64_t N, int K,
-                                                                  int64_t sa_ld) {
-  __shared__ v4f_t red[SPLIT][64];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int KB = K / kGroup;
-  const uint32_t b_rows = (uint32_t)(N - n0 < 16 ? N - n0 : 16);
-  const rsrc_t rb = make_rsrc(B + n0 * K, b_rows * (uint32_t)K);
-  const rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K);
-  const uint32_t off = (uint32_t)li * K + lg * 32;
-  const float* sbw = SB + (n0 / kGroup) * KB;
-  const bool row_ok = li < M;
-  v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kb0 = wave; kb0 < KB; kb0 += SPLIT * kDecodeU) {
-    uint4 b0[kDecodeU], b1[kDecodeU], a0[kDecodeU], a1[kDecodeU];
-    float sv[kDecodeU];
-#pragma unroll
-    for (int u = 0; u < kDecodeU; u++) {
-      const int kb = kb0 + u * SPLIT;
-      if (kb < KB) {
-        b0[u] = load_rsrc16(rb, off + kb * 128);
-        b1[u] = load_rsrc16(rb, off + kb * 128 + 16);
-        a0[u] = load_rsrc16(ra, off + kb * 128);
-        a1[u] = load_rsrc16(ra, off + kb * 128 + 16);
-        sv[u] = (row_ok ? SA[(int64_t)kb * sa_ld + li] : 0.0f) * sbw[kb];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kDecodeU; u++) {
-      const int kb = kb0 + u * SPLIT;
-      if (kb < KB) {
-        v8i_t bf, af;
-        bf[0] = b0[u].x; bf[1] = b0[u].y; bf[2] = b0[u].z; bf[3] = b0[u].w;
-        bf[4] = b1[u].x; bf[5] = b1[u].y; bf[6] = b1[u].z; bf[7] = b1[u].w;
-        af[0] = a0[u].x; af[1] = a0[u].y; af[2] = a0[u].z; af[3] = a0[u].w;
-        af[4] = a1[u].x; af[5] = a1[u].y; af[6] = a1[u].z; af[7] = a1[u].w;
-        promote(acc, mfma_fp8(bf, af), sv[u]);
-      }
-    }
-  }
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    v4f_t s = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < SPLIT; w++) {
-      const v4f_t o = red[w][lane];
-      s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
-    }
-    // lane (li, lg): row li, columns n0 + 4*lg .. n0 + 4*lg + 3
-    if (row_ok) {
-      const int64_t c0 = n0 + 4 * lg;
-      uint16_t* drow = D + (int64_t)li * N;
-      if ((N % 4) == 0 && c0 + 4 <= N) {
-        *reinterpret_cast<uint2*>(drow + c0) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-          if (c0 + r < N) drow[c0 + r] = (uint16_t)bf16_rne(s[r]);
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------ host side
 namespace {
 struct Candidate {
@@ -463,13 +385,7 @@ constexpr int kCUs = 256;
 }  // namespace
 
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
-  if (m <= 16) {
-    const int64_t slabs = (n + 15) / 16;
-    const int64_t kb = k / kGroup;
-    int split = 4;
-    if (slabs < 512 && kb >= 32) split = 8;
-    return {kGemmDecode, split};
-  }
+  if (m <= 16) return {kGemmDecode, decode_split(n, k)};
   GemmPlan best{kGemmTile256x256, 0};
   double best_cost = 1e300;
   for (const Candidate& c : kCandidates) {
@@ -490,7 +406,7 @@ const char* gemm_kind_name(GemmKind kind) {
     case kGemmTile128x256: return "tile128x256_w2x2";
     case kGemmTile256x128: return "tile256x128_w4x1";
     case kGemmTile128x128: return "tile128x128_w2x2";
-    case kGemmDecode: return "decode_slab16";
+    case kGemmDecode: return "decode_splitk_slab16";
   }
   return "?";
 }
@@ -505,15 +421,6 @@ static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, con
   return hipGetLastError();
 }
 
-template <int SPLIT>
-static hipError_t launch_decode(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
-                                void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_decode_kernel<SPLIT>, dim3((uint32_t)((n + 15) / 16)), dim3(SPLIT * 64), 0, stream,
-                     static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb,
-                     static_cast<uint16_t*>(d), (int)m, n, (int)k, sa_ld);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
                        const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   switch (plan.kind) {
@@ -521,9 +428,7 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int
     case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
     case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
     case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
-    case kGemmDecode:
-      return plan.split == 8 ? launch_decode<8>(a, sa, sa_ld, b, sb, d, m, n, k, stream)
-                             : launch_decode<4>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmDecode: return launch_decode(plan.split, a, sa, sa_ld, b, sb, d, m, n, k, stream);
   }
   return hipErrorInvalidValue;
 }

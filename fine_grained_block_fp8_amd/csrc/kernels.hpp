@@ -31,6 +31,16 @@ const char* gemm_kind_name(GemmKind kind);
 hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
                        const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+// Decode-shaped products (M <= 16): K split over ks waves per 16-column slab.
+int decode_split(int64_t n, int64_t k);
+hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
+                         void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+// Fused activation quantization + product for M <= 4 (K <= kFusedMaxK).
+constexpr int64_t kFusedMaxM = 4;
+constexpr int64_t kFusedMaxK = 32768;
+hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
+                               int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
                                const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream);

@@ -129,6 +129,30 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
                                      const void* b_e4m3, const float* sb, int32_t num_groups, void* d_bf16,
                                      int64_t m, int64_t n, int64_t k, void* stream);
 
+/* The linear as the pages run it (Linnet "Backend plugins" page,
+ * _BlockProduct.execute: round the bf16 input per 1x128 group, then
+ * fp8_gemm_nt with the stored weight): D = quantize_groups(x) . B^T.
+ *
+ * For m <= 4 and k <= 32768 this is a single kernel that quantizes x inside
+ * every workgroup while the weight stream is in flight (decode: the
+ * activation-quantize step must not cost a launch of its own; the AReno FP8
+ * decode pull request measured the separate quantize chain holding a decode
+ * linear at ~1.2x until it was fused).  Its result is bit-identical to
+ * quantize_fp8_groups followed by fp8_gemm_nt.  For larger m it runs those
+ * two calls.
+ *
+ * x_bf16  [m][k] bfloat16, input.
+ * b_e4m3  [n][k] E4M3 and sb [ceil(n/128)][k/128] float32: the stored weight
+ *         (as written by quantize_fp8_blocks).
+ * d_bf16  [m][n] bfloat16, output.
+ * q_e4m3, sa, sa_ld: the quantized activation [m][k] and its MN-major scales
+ *         [k/128][sa_ld], exactly as quantize_fp8_groups writes them.
+ *         Optional (both NULL) when m <= 4; required as workspace otherwise.
+ * Requirements: m >= 0, n >= 0, k > 0 and k % 128 == 0; if q_e4m3 is given,
+ * sa_ld % 4 == 0 and sa_ld >= m. */
+int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, const float* sb, int64_t n,
+                  void* d_bf16, void* q_e4m3, float* sa, int64_t sa_ld, void* stream);
+
 /* Message for the most recent non-zero status returned on the calling thread
  * (thread-local; the pointer stays valid until the next failing call on that
  * thread).  Returns "" if no call has failed. */

@@ -33,6 +33,7 @@ def test_library_exports_every_declared_function():
         "m_grouped_fp8_gemm_nt_contiguous",
         "fgfp8_last_error",
         "fgfp8_describe_gemm",
+        "fp8_linear_nt",
     }
     lib = fg.library()
     for n in names:
@@ -119,6 +120,21 @@ def test_grouped_rejects():
     assert call(m=0, sa_ld=4) == fg.FGFP8_OK
 
 
+def test_linear_rejects():
+    lib = _lib()
+
+    def call(m=2, k=256, n=128, q=None, sa=None, sa_ld=0, x=P):
+        return lib.fp8_linear_nt(x, m, k, P, P, n, P, q, sa, sa_ld, None)
+
+    assert call(k=100) == fg.FGFP8_EINVAL
+    assert call(m=8) == fg.FGFP8_EINVAL  # larger m needs the workspace
+    assert "workspace" in fg.last_error()
+    assert call(q=P) == fg.FGFP8_EINVAL  # q without sa
+    assert call(m=8, q=P, sa=P, sa_ld=6) == fg.FGFP8_EINVAL
+    assert call(x=None) == fg.FGFP8_EINVAL
+    assert call(m=0) == fg.FGFP8_OK
+
+
 def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
@@ -133,6 +149,7 @@ def test_no_device_is_reported_not_crashed():
     assert lib.fp8_gemm_nt(P, P, 8, P, P, P, 8, 16, 256, None) == fg.FGFP8_ENODEV
     assert lib.quantize_fp8_blocks(P, 16, 256, P, P, None) == fg.FGFP8_ENODEV
     assert lib.m_grouped_fp8_gemm_nt_contiguous(P, P, 128, P, P, P, 2, P, 128, 64, 128, None) == fg.FGFP8_ENODEV
+    assert lib.fp8_linear_nt(P, 1, 256, P, P, 128, P, None, None, 0, None) == fg.FGFP8_ENODEV
 
 
 def test_describe_gemm_plans():

@@ -150,3 +150,31 @@ def test_runs_on_a_side_stream():
         fg.fp8_gemm_nt((q, sa), (qb, sb), d2)
     s.synchronize()
     assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288), (200, 384), (1000, 128)])
+def test_fused_linear_matches_two_calls_and_oracle(m, n, k):
+    """fp8_linear_nt (one fused kernel for m <= 4) writes the same quantized
+    activation as quantize_fp8_groups (checked bit-exact against the oracle)
+    and the same output bits as quantize_fp8_groups + fp8_gemm_nt."""
+    lin = workloads.decode_linear(m, n, k) if (n, k) in workloads.DECODE_SHAPES else workloads.random_linear(m, n, k, seed=m + n)
+    q, sa, qb, sb, d_two = gpu_hot_path(lin)
+    x = torch.from_numpy(lin.a.view(np.int16)).view(torch.bfloat16).cuda()
+    d = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q2 = torch.full((m, k), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sa2 = torch.full((k // 128, fg.padded_rows(m)), float("nan"), dtype=torch.float32, device="cuda")
+    fg.fp8_linear_nt(x, (qb, sb), d, (q2, sa2))
+    torch.cuda.synchronize()
+    oq, osa = oracle.quantize_groups(lin.a)
+    assert np.array_equal(codes(q2), oq)
+    assert np.array_equal(sa2[:, :m].cpu().numpy().view(np.uint32), osa[:, :m].view(np.uint32))
+    assert torch.equal(d.view(torch.int16), d_two.view(torch.int16)), "fused output differs from the two-call path"
+    # and without the optional activation outputs
+    d3 = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if m <= 4:
+        fg.fp8_linear_nt(x, (qb, sb), d3)
+        torch.cuda.synchronize()
+        assert torch.equal(d3.view(torch.int16), d_two.view(torch.int16))
+    rng = np.random.default_rng(5)
+    check_sampled(lin, q, sa, qb, sb, d, np.arange(m), sample_col_blocks(n, 8, rng), f"fused {m}x{n}x{k}")
