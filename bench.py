@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "moe", "square8k", "square16k"])
+    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "moe", "square8k", "square16k", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     return p.parse_args()
@@ -137,27 +137,62 @@ def bench_linears(linears, steps, warmup, fg, torch):
     return preps, elapsed, per
 
 
+def kernel_sources_hash() -> str:
+    """SHA-256 prefix over the kernel sources, to tie a counter record in
+    profiles/ to the code it was measured on."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "fine_grained_block_fp8_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE / WRITE_SIZE
+    counter runs summarised in profiles/ (scaled by a plain-copy
+    calibration), or None when no record matches the current sources."""
+    import glob
+
+    want = kernel_sources_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic-record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("kernel") == kernel and rec.get("sources") == want:
+                        return rec["bytes_per_launch"]
+    return None
+
+
 def roofline_of(per):
     """Dominant kernel (largest total time among the GEMM kernels): its
     algorithmic FLOPs per launch over its mean launch duration."""
     by = {}
     for r in per:
-        e = by.setdefault(r["_kernel"], {"flops": 0, "s": 0.0, "n": 0})
+        e = by.setdefault(r["_kernel"], {"flops": 0, "s": 0.0, "n": 0, "bytes": 0})
         e["flops"] += r["_flops"]
+        e["bytes"] += gemm_bytes(r["m"], r["n"], r["k"])
         e["s"] += r["_gemm_s"]
         e["n"] += 1
     name, e = max(by.items(), key=lambda kv: kv[1]["s"])
     flops_per_launch = e["flops"] / e["n"]
     mean_s = e["s"] / e["n"]
     achieved = flops_per_launch / mean_s / 1e12
+    kernel = f"gemm_nt_kernel<{name}>"
     return {
         "bound": "mfma",
-        "kernel": f"gemm_nt_kernel<{name}>",
+        "kernel": kernel,
         "achieved": round(achieved, 1),
         "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-        "traffic": None,
+        "traffic": recorded_traffic(kernel),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "algorithmic_bytes_per_launch": round(e["bytes"] / e["n"]),
         "launches_per_step": e["n"],
         "mean_launch_us": round(mean_s * 1e6, 2),
         "algorithmic_gflop_per_launch": round(flops_per_launch / 1e9, 3),
@@ -270,6 +305,21 @@ def cpu_baseline(linears, rows=None, cols=2048):
     }
 
 
+# ------------------------------------------------------- counter calibration
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(args, torch):
+    """A plain device-to-device copy of 256 MiB, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters: each launch moves exactly COPY_BYTES each way."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup + args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copy", "bytes_each_way": COPY_BYTES, "launches": args.warmup + args.steps}))
+
+
 # --------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -290,6 +340,9 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')}")
 
+    if args.workload == "copy":
+        copy_calibration(args, torch)
+        return
     if args.workload == "prefill":
         linears = workloads.prefill_linears()
         workload = "qwen3_8b_prefill_linears_m2048"
