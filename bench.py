@@ -450,7 +450,7 @@ def bench_moe(args, fg, torch, workloads):
     per = [{"name": g.name, "m_pad": g.m, "n": g.n, "k": g.k, "groups": g.num_groups, "quant_us": qt * 1e6,
             "gemm_us": gt * 1e6, "gemm_tflops_useful": flops / gt / 1e12,
             "gemm_tflops_padded": 2 * g.m * g.n * g.k / gt / 1e12, "_gemm_s": gt}]
-    roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x2>", "achieved": round(flops / gt / 1e12, 1),
+    roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x4>", "achieved": round(flops / gt / 1e12, 1),
             "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / gt / 1e12 / PEAK_FP8_TFLOPS, 4),
             "traffic": None, "mean_launch_us": round(gt * 1e6, 2)}
     return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gt, flops

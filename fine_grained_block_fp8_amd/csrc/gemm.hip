@@ -20,6 +20,8 @@
 // to match, so that every MFMA tile reads 16 consecutive LDS rows, exactly
 // like the A fragments.
 
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "common.hpp"
@@ -41,7 +43,11 @@ struct Tile {
   // with the K loop unrolled by two every fragment address is a
   // loop-invariant register plus an immediate (< 64 KB) offset.
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  static constexpr int S_BYTES = 1024;  // one stage's activation scales (<= 256 floats)
+  // One stage's scales: the tile's activation scales (<= 256 floats) at +0,
+  // and at +1024 one 4-byte slot per lane of the weight-scale copy, slot j
+  // holding the weight scale of the tile's column block j.
+  static constexpr int S_BYTES = 1024 + 256;
+  static constexpr int SB_IN_S = 1024;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = 2 * A_BYTES;
   static constexpr int S_OFF = B_OFF + 2 * B_BYTES;
@@ -49,14 +55,17 @@ struct Tile {
   static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
   static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "segments divide evenly among waves");
-  static_assert(BM * 4 <= S_BYTES, "one wave loads a stage's activation scales");
+  static_assert(BM * 4 <= SB_IN_S, "one wave loads a stage's activation scales");
   static_assert(A_BYTES <= 32768 && B_BYTES <= 32768, "stage offsets must fit a 16-bit LDS immediate");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
+// Two waves per SIMD (8 per workgroup) hide each other's LDS and barrier
+// stalls; the 64x128 and 64x64 wave tiles keep the FP32 accumulators in
+// architectural VGPRs, where the promotion FMAs can reach them.
 using Tile256x256 = Tile<256, 256, 4, 2>;
-using Tile128x256 = Tile<128, 256, 2, 2>;
-using Tile256x128 = Tile<256, 128, 4, 1>;
+using Tile128x256 = Tile<128, 256, 2, 4>;
+using Tile256x128 = Tile<256, 128, 4, 2>;
 using Tile128x128 = Tile<128, 128, 2, 2>;
 
 // LDS layout of a K chunk: row r of a tile is 128 bytes (8 slots of 16
@@ -89,19 +98,23 @@ __device__ __forceinline__ int b_col_of_row(int rho) {
 }
 
 // All waves cooperatively copy chunk kb of the A tile, the B tile and the
-// tile's activation scales into one LDS stage with direct global->LDS buffer
-// loads (1 KB = 8 LDS rows per wave instruction; rows past the matrix edge
-// read as zero).  Wave w copies segments w, w + WAVES, ... of A and of B
-// (both counts divide evenly), and wave 0 the scales.  voff[] holds the
-// per-lane byte offsets of those segments for chunk 0; the chunk's column
-// offset is the scalar offset of each load.
+// tile's scales into one LDS stage with direct global->LDS buffer loads (1 KB
+// = 8 LDS rows per wave instruction; rows past the matrix edge read as zero).
+// Wave w copies segments w, w + WAVES, ... of A and of B (both counts divide
+// evenly), wave 0 the activation scales and wave 1 the weight scales of the
+// tile's column blocks.  voff[] holds the per-lane byte offsets of those
+// segments for chunk 0; the chunk's column offset is the scalar offset of
+// each load.  Staging the weight scales through LDS keeps scalar memory loads
+// out of the loop: their completion shares a counter with the LDS reads and
+// would force every fragment read of the chunk to drain before the first
+// MFMA.
 template <class C>
 struct StageLoader {
   static constexpr int AN = C::BM / 8 / C::WAVES, BN_ = C::BN / 8 / C::WAVES, NSEG = AN + BN_;
   uint8_t* lds;
-  rsrc_t ra, rb, rs;
+  rsrc_t ra, rb, rs, rsb;
   const uint32_t* voff;
-  uint32_t sa_ld_bytes;
+  uint32_t sa_ld_bytes, vsb;
   int wave, lane;
   // Segment i (< NSEG) of chunk kb into `stage`; segment NSEG is the scales
   // (wave 0 only).
@@ -118,6 +131,9 @@ struct StageLoader {
     else if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES), 16,
                                                (uint32_t)lane * 16u, (uint32_t)kb * sa_ld_bytes, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES + C::SB_IN_S),
+                                               4, vsb, (uint32_t)kb * 4u, 0, 0);
   }
   __device__ __forceinline__ void all(int stage, int kb) const {
 #pragma unroll
@@ -184,8 +200,9 @@ __device__ __forceinline__ v8i_t read_b(const uint8_t* lds, const FragAddr& ba, 
 
 // A fragments and promotion scales (sa[row] * sb) of one chunk.
 template <class C>
-__device__ __forceinline__ void read_a(const uint8_t* lds, const FragAddr& aa, uint32_t sa_addr, int stage,
-                                       float sbv, v8i_t (&af)[C::MT], float (&sc)[C::MT]) {
+__device__ __forceinline__ void read_a(const uint8_t* lds, const FragAddr& aa, uint32_t sa_addr, uint32_t sb_addr,
+                                       int stage, v8i_t (&af)[C::MT], float (&sc)[C::MT]) {
+  const float sbv = *reinterpret_cast<const float*>(lds + sb_addr + stage * C::S_BYTES);
 #pragma unroll
   for (int mt = 0; mt < C::MT; mt++) {
     af[mt] = read_frag(lds, aa, (uint32_t)(stage * C::A_BYTES + 2048 * mt));
@@ -249,10 +266,14 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   const rsrc_t ra = make_rsrc(a, a_rows * (uint32_t)K);
   const rsrc_t rb = make_rsrc(b, b_rows * (uint32_t)K);
   const rsrc_t rs = make_rsrc(sa + m0, (uint32_t)(((int64_t)KB * sa_ld - m0) * 4));
+  // Weight scales: lane j of wave 1 copies the scale of column block
+  // n0/128 + j (clamped to the last block: a wave entirely past N never
+  // stores its results).
   const int64_t nblocks = (N + kGroup - 1) / kGroup;
-  int64_t nb = (n0 + wn * C::TN) / kGroup;
-  if (nb >= nblocks) nb = nblocks - 1;  // a wave entirely past N: its results are never stored
-  const float* sbw = sb_base + nb * KB;
+  int64_t nb_lane = n0 / kGroup + lane;
+  if (nb_lane >= nblocks) nb_lane = nblocks - 1;
+  const rsrc_t rsb = make_rsrc(sb_base, (uint32_t)(nblocks * KB * 4));
+  const uint32_t vsb = (uint32_t)(nb_lane * KB * 4);
 
   v4f_t acc[C::MT][C::NT];
 #pragma unroll
@@ -265,24 +286,24 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   float sc[C::MT];
   uint32_t voff[StageLoader<C>::NSEG];
   stage_offsets<C>(voff, (uint32_t)K, wave, lane);
-  const StageLoader<C> loader{lds, ra, rb, rs, voff, (uint32_t)(sa_ld * 4), wave, lane};
+  const StageLoader<C> loader{lds, ra, rb, rs, rsb, voff, (uint32_t)(sa_ld * 4), vsb, wave, lane};
   const FragAddr aa = frag_addr(C::A_OFF, wm * C::TM, li, lg);
   const FragAddr ba = frag_addr(C::B_OFF, wn * C::TN, li, lg);
   const uint32_t sa_addr = C::S_OFF + (uint32_t)(wm * C::TM + li) * 4u;
+  const uint32_t sb_addr = C::S_OFF + C::SB_IN_S + (uint32_t)((wn * C::TN) / kGroup) * 4u;
   // One chunk: wait for this wave's copies into `stage`, barrier (every
   // wave's copies have landed and the other stage is no longer read), then
   // compute chunk kb while refilling the other stage with chunk kb+1.
   loader.all(0, 0);
   for (int kb = 0; kb < KB; kb++) {
     const int stage = kb & 1;
-    const float sbv = sbw[kb];
     // The last chunk refills the free stage with a copy of itself (valid
     // addresses, never read) so that the loop body has no branch.
     const int next = kb + 1 < KB ? kb + 1 : kb;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (wave == 0) loader.issue(StageLoader<C>::NSEG, stage ^ 1, next);  // scales
-    read_a<C>(lds, aa, sa_addr, stage, sbv, af, sc);
+    if (wave < 2) loader.issue(StageLoader<C>::NSEG, stage ^ 1, next);  // scales
+    read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
     mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, af, sc, nullptr, acc, loader, next);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
@@ -373,19 +394,24 @@ namespace {
 struct Candidate {
   GemmKind kind;
   int bm, bn;
-  double eff;  // relative per-tile efficiency (larger tiles reuse more)
+  double eff;  // throughput per CU relative to the 256x256 tile (measured, 8192^3)
 };
 constexpr Candidate kCandidates[] = {
     {kGemmTile256x256, 256, 256, 1.00},
-    {kGemmTile256x128, 256, 128, 0.90},
-    {kGemmTile128x256, 128, 256, 0.90},
-    {kGemmTile128x128, 128, 128, 0.75},
+    {kGemmTile256x128, 256, 128, 0.97},
+    {kGemmTile128x256, 128, 256, 0.97},
+    {kGemmTile128x128, 128, 128, 0.72},
 };
 constexpr int kCUs = 256;
 }  // namespace
 
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
   if (m <= 16) return {kGemmDecode, decode_split(n, k)};
+  // Tuning and test override: FGFP8_GEMM_TILE=<tile name> forces a tile.
+  if (const char* force = getenv("FGFP8_GEMM_TILE")) {
+    for (const Candidate& c : kCandidates)
+      if (strcmp(force, gemm_kind_name(c.kind)) == 0) return {c.kind, 0};
+  }
   GemmPlan best{kGemmTile256x256, 0};
   double best_cost = 1e300;
   for (const Candidate& c : kCandidates) {
@@ -403,8 +429,8 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
 const char* gemm_kind_name(GemmKind kind) {
   switch (kind) {
     case kGemmTile256x256: return "tile256x256_w4x2";
-    case kGemmTile128x256: return "tile128x256_w2x2";
-    case kGemmTile256x128: return "tile256x128_w4x1";
+    case kGemmTile128x256: return "tile128x256_w2x4";
+    case kGemmTile256x128: return "tile256x128_w4x2";
     case kGemmTile128x128: return "tile128x128_w2x2";
     case kGemmDecode: return "decode_splitk_slab16";
   }

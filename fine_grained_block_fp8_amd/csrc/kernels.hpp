@@ -14,8 +14,8 @@ hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, 
 // Kernel configurations of the dense product.
 enum GemmKind : int {
   kGemmTile256x256 = 0,  // 256x256 workgroup tile, 8 waves of 64x128
-  kGemmTile128x256 = 1,  // 128x256, 4 waves of 64x128
-  kGemmTile256x128 = 2,  // 256x128, 4 waves of 64x128
+  kGemmTile128x256 = 1,  // 128x256, 8 waves of 64x64
+  kGemmTile256x128 = 2,  // 256x128, 8 waves of 64x64
   kGemmTile128x128 = 3,  // 128x128, 4 waves of 64x64
   kGemmDecode = 4,       // M <= 16: 16-column slabs, K split across waves
 };

@@ -162,7 +162,11 @@ const char* fgfp8_last_error(void);
  * fp8_gemm_nt would use for (m, n, k) into buf (at most len bytes, truncated)
  * and returns FGFP8_OK; host-only, enqueues nothing, touches no device.
  * Mirrors the pages' habit of printing every tile decision next to the
- * number it produced (deepgemm-rust README, "Benchmark"). */
+ * number it produced (deepgemm-rust README, "Benchmark").  For m > 16 the
+ * environment variable FGFP8_GEMM_TILE, set to one of the tile names
+ * (tile256x256_w4x2, tile256x128_w4x2, tile128x256_w2x4, tile128x128_w2x2),
+ * forces that tile in fp8_gemm_nt (tuning and tests); other values are
+ * ignored. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
 
 #ifdef __cplusplus

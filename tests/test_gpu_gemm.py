@@ -178,3 +178,25 @@ def test_fused_linear_matches_two_calls_and_oracle(m, n, k):
         assert torch.equal(d3.view(torch.int16), d_two.view(torch.int16))
     rng = np.random.default_rng(5)
     check_sampled(lin, q, sa, qb, sb, d, np.arange(m), sample_col_blocks(n, 8, rng), f"fused {m}x{n}x{k}")
+
+
+TILES = ["tile256x256_w4x2", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("m,n,k", [(17, 136, 128), (129, 1000, 384), (300, 520, 768), (513, 264, 1152)])
+def test_every_tile_config(tile, m, n, k, monkeypatch):
+    """Each tile configuration, forced through FGFP8_GEMM_TILE, on shapes with
+    ragged M, N edges and several K chunks."""
+    monkeypatch.setenv("FGFP8_GEMM_TILE", tile)
+    assert fg.describe_gemm(m, n, k).startswith(tile)
+    full_check(workloads.random_linear(m, n, k, seed=m + 3 * n + k), f"{tile} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_every_tile_config_prefill_o(tile, monkeypatch):
+    monkeypatch.setenv("FGFP8_GEMM_TILE", tile)
+    (lin,) = workloads.prefill_linears(names=["o"])
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    rng = np.random.default_rng(7)
+    check_sampled(lin, q, sa, qb, sb, d, sample_rows(lin.m, 24, rng), sample_col_blocks(lin.n, 6, rng), f"o {tile}")
