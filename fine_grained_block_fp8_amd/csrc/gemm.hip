@@ -30,18 +30,18 @@
 namespace fgfp8 {
 
 // ------------------------------------------------------------ tile configs
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  // LDS stages of the K loop: chunk kb + STAGES - 1 is copied while chunk kb
+  // is multiplied, so a copy has STAGES - 1 chunk times to arrive.
+  static constexpr int STAGES = STAGES_;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int TM = BM / WAVES_M;  // wave tile rows
   static constexpr int TN = BN / WAVES_N;  // wave tile columns (inside one 128-column scale block)
   static constexpr int MT = TM / 16;
   static constexpr int NT = TN / 16;
-  // LDS: the two stages of each operand sit one operand-tile apart, so that
-  // with the K loop unrolled by two every fragment address is a
-  // loop-invariant register plus an immediate (< 64 KB) offset.
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   // One stage's scales: the tile's activation scales (<= 256 floats) at +0,
   // and at +1024 one 4-byte slot per lane of the weight-scale copy, slot j
@@ -49,24 +49,27 @@ struct Tile {
   static constexpr int S_BYTES = 1024 + 256;
   static constexpr int SB_IN_S = 1024;
   static constexpr int A_OFF = 0;
-  static constexpr int B_OFF = 2 * A_BYTES;
-  static constexpr int S_OFF = B_OFF + 2 * B_BYTES;
-  static constexpr int LDS = S_OFF + 2 * S_BYTES;
+  static constexpr int B_OFF = STAGES * A_BYTES;
+  static constexpr int S_OFF = B_OFF + STAGES * B_BYTES;
+  static constexpr int LDS = S_OFF + STAGES * S_BYTES;
   static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
   static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "segments divide evenly among waves");
   static_assert(BM * 4 <= SB_IN_S, "one wave loads a stage's activation scales");
-  static_assert(A_BYTES <= 32768 && B_BYTES <= 32768, "stage offsets must fit a 16-bit LDS immediate");
+  static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 // Two waves per SIMD (8 per workgroup) hide each other's LDS and barrier
 // stalls; the 64x128 and 64x64 wave tiles keep the FP32 accumulators in
-// architectural VGPRs, where the promotion FMAs can reach them.
-using Tile256x256 = Tile<256, 256, 4, 2>;
-using Tile128x256 = Tile<128, 256, 2, 4>;
-using Tile256x128 = Tile<256, 128, 4, 2>;
-using Tile128x128 = Tile<128, 128, 2, 2>;
+// architectural VGPRs, where the promotion FMAs can reach them.  Tiles whose
+// stage is at most 48 KB take three stages (a longer prefetch distance, which
+// matters when B streams from HBM rather than the last-level cache, as the
+// per-expert weights of the grouped product do); 256x256 fits two.
+using Tile256x256 = Tile<256, 256, 4, 2, 2>;
+using Tile128x256 = Tile<128, 256, 2, 4, 3>;
+using Tile256x128 = Tile<256, 128, 4, 2, 3>;
+using Tile128x128 = Tile<128, 128, 2, 2, 3>;
 
 // LDS layout of a K chunk: row r of a tile is 128 bytes (8 slots of 16
 // bytes); logical slot c of row r is stored at slot c ^ swz(r).  Fragment
@@ -111,6 +114,7 @@ __device__ __forceinline__ int b_col_of_row(int rho) {
 template <class C>
 struct StageLoader {
   static constexpr int AN = C::BM / 8 / C::WAVES, BN_ = C::BN / 8 / C::WAVES, NSEG = AN + BN_;
+  static_assert(NSEG + 1 < 16, "a chunk's copies must fit the 4-bit vmcnt field used by the waits");
   uint8_t* lds;
   rsrc_t ra, rb, rs, rsb;
   const uint32_t* voff;
@@ -140,6 +144,19 @@ struct StageLoader {
     for (int i = 0; i <= NSEG; i++) issue(i, stage, kb);
   }
 };
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// waits for every outstanding global->LDS copy (vmcnt(0)) and would drain the
+// copies of the chunks ahead, reducing three stages to two.  The K loop
+// orders LDS traffic itself (explicit vmcnt waits for the copies; every
+// fragment read of a stage is consumed by an MFMA before the barrier after
+// which the stage is refilled); the empty asm statements keep the compiler
+// from moving memory operations across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <class C>
 __device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wave, int lane) {
@@ -215,7 +232,7 @@ __device__ __forceinline__ void read_a(const uint8_t* lds, const FragAddr& aa, u
 // (independent of MFMA i, so the two overlap), and the B fragment of the next
 // column tile is read one tile ahead (from LDS, or from registers when PRE).
 template <class C, int T0, int T1, bool PRE, bool LD>
-__device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& ba, int stage,
+__device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& ba, int stage, int load_stage,
                                            const v8i_t (&af)[C::MT], const float (&sc)[C::MT], const v8i_t* pre,
                                            v4f_t (&acc)[C::MT][C::NT], const StageLoader<C>& ld, int next_kb) {
   // With LD, the next chunk's global->LDS copies (NSEG instructions per
@@ -234,7 +251,7 @@ __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& b
     if (LD && mt == 0) {
 #pragma unroll
       for (int q = 0; q < PER; q++)
-        if (u * PER + q < NL) ld.issue(u * PER + q, stage ^ 1, next_kb);
+        if (u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
     }
     if (mt == 0 && t + 1 < T1) bfr[(u + 1) & 1] = PRE ? pre[u + 1] : read_b<C>(lds, ba, stage, t + 1);
     part[i & 1] = mfma_fp8(bfr[u & 1], af[mt]);
@@ -291,20 +308,33 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   const FragAddr ba = frag_addr(C::B_OFF, wn * C::TN, li, lg);
   const uint32_t sa_addr = C::S_OFF + (uint32_t)(wm * C::TM + li) * 4u;
   const uint32_t sb_addr = C::S_OFF + C::SB_IN_S + (uint32_t)((wn * C::TN) / kGroup) * 4u;
-  // One chunk: wait for this wave's copies into `stage`, barrier (every
-  // wave's copies have landed and the other stage is no longer read), then
-  // compute chunk kb while refilling the other stage with chunk kb+1.
+  // One chunk: wait for this wave's copies of chunk kb, barrier (every
+  // wave's copies have landed, and the stage chunk kb - 1 occupied is no
+  // longer read), then compute chunk kb while filling that stage with chunk
+  // kb + STAGES - 1.  Near the end the copy repeats the last chunk (valid
+  // addresses, into a stage that is not read again), so the loop body has no
+  // branch.  Copies return in issue order, so "chunk kb has landed" is "at
+  // most the copies of the chunks after it are outstanding": none with two
+  // stages; with three, one chunk's NSEG segments plus the scale copy that
+  // waves 0 and 1 issue.
   loader.all(0, 0);
+  if (C::STAGES == 3) loader.all(1, KB > 1 ? 1 : 0);
+  int stage = 0;
   for (int kb = 0; kb < KB; kb++) {
-    const int stage = kb & 1;
-    // The last chunk refills the free stage with a copy of itself (valid
-    // addresses, never read) so that the loop body has no branch.
-    const int next = kb + 1 < KB ? kb + 1 : kb;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (wave < 2) loader.issue(StageLoader<C>::NSEG, stage ^ 1, next);  // scales
+    const int load_stage = stage == 0 ? C::STAGES - 1 : stage - 1;
+    const int next = kb + C::STAGES - 1 < KB ? kb + C::STAGES - 1 : KB - 1;
+    if (C::STAGES == 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    } else if (wave < 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (StageLoader<C>::NSEG + 1));  // vmcnt(NSEG + 1)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | StageLoader<C>::NSEG);  // vmcnt(NSEG)
+    }
+    barrier_no_fence();
+    if (wave < 2) loader.issue(StageLoader<C>::NSEG, load_stage, next);  // scales
     read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
-    mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, af, sc, nullptr, acc, loader, next);
+    mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, load_stage, af, sc, nullptr, acc, loader, next);
+    stage = stage + 1 == C::STAGES ? 0 : stage + 1;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
 

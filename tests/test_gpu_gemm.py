@@ -184,7 +184,7 @@ TILES = ["tile256x256_w4x2", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x12
 
 
 @pytest.mark.parametrize("tile", TILES)
-@pytest.mark.parametrize("m,n,k", [(17, 136, 128), (129, 1000, 384), (300, 520, 768), (513, 264, 1152)])
+@pytest.mark.parametrize("m,n,k", [(17, 136, 128), (200, 300, 256), (129, 1000, 384), (300, 520, 768), (513, 264, 1152)])
 def test_every_tile_config(tile, m, n, k, monkeypatch):
     """Each tile configuration, forced through FGFP8_GEMM_TILE, on shapes with
     ragged M, N edges and several K chunks."""
