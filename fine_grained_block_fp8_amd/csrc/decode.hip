@@ -27,12 +27,13 @@
 
 namespace fgfp8 {
 
-// Chunks of one wave held in registers at a time: 12 with the activation in
-// LDS (fused), 8 when the A fragments are registers too.  Both keep a wave
-// under 168 VGPRs, so three waves fit per SIMD and a grid of three
-// workgroups per CU is resident at once.
-constexpr int kDecodeMaxChunksFused = 12;
-constexpr int kDecodeMaxChunks = 8;
+// Chunks of one wave held in registers at a time.  With KS <= 4 (the split
+// of the wide shapes, N = 12288 at K = 4096: 768 slabs, three workgroups per
+// CU) a wave holds 8 chunks and stays within 168 VGPRs, so three waves fit
+// per SIMD; with KS = 8 (N = 4096, K = 12288: two waves per SIMD) it holds 12.
+// The A fragments of the non-fused form take registers too: it holds 8.
+template <int KS, bool FUSED>
+constexpr int decode_max_chunks() { return FUSED && KS >= 8 ? 12 : 8; }
 constexpr int kFusedMaxRows = 4;
 
 __device__ __forceinline__ v8i_t frag_of(uint4 lo, uint4 hi) {
@@ -80,23 +81,36 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
   // a wave waits for memory once per batch, not once per chunk: the B
   // fragments, the weight scales of the batch (one per lane, broadcast with
   // readlane) and, without fusion, the A fragments and activation scales.
-  constexpr int MAXC = FUSED ? kDecodeMaxChunksFused : kDecodeMaxChunks;
+  // Every load is issued unconditionally, as a buffer load: one past the end
+  // of its operand (a chunk beyond the batch, a row beyond M) gets an offset
+  // outside the resource and returns zeros without touching memory.  The
+  // number of loads in flight is then the same on every path, so the
+  // compiler waits for exactly the load an instruction needs -- a branch
+  // around a load would make it wait for all of them (the whole weight
+  // stream) before the first use.
+  constexpr uint32_t kOob = 0x80000000u;
+  constexpr int MAXC = decode_max_chunks<KS, FUSED>();
   v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   uint4 b0[MAXC], b1[MAXC], a0[FUSED ? 1 : MAXC], a1[FUSED ? 1 : MAXC];
   float sav[FUSED ? 1 : MAXC];
   float sbv = 0.0f;
-  const uint8_t* Aq = static_cast<const uint8_t*>(Ain);
+  const rsrc_t rsb = make_rsrc(sbw, (uint32_t)KB * 4u);
   // Small operands first: requests queue in order behind the weight stream,
   // so anything issued after it would arrive only when the stream has.
   auto issue = [&](int cb, int nc) {
-    sbv = lane < nc ? sbw[cb + lane] : 0.0f;
+    sbv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rsb, lane < nc ? (uint32_t)(cb + lane) * 4u : kOob, 0, 0));
     if (!FUSED) {
+      // A fragments and scales: only lanes of rows < M load (the texture
+      // unit then handles M lanes of each request, not 64).  The branches
+      // make the compiler wait for all of a batch's loads before its first
+      // MFMA, which costs less here than 64-lane requests would.
 #pragma unroll
       for (int u = 0; u < MAXC; u++) {
         if (u < nc) {
           const int kb = cb + u;
           if (row_ok) {
-            const uint8_t* p = Aq + (int64_t)li * K + kb * kGroup + lg * 32;
+            const uint8_t* p = static_cast<const uint8_t*>(Ain) + (int64_t)li * K + kb * kGroup + lg * 32;
             a0[u] = *reinterpret_cast<const uint4*>(p);
             a1[u] = *reinterpret_cast<const uint4*>(p + 16);
             sav[u] = SA[(int64_t)kb * sa_ld + li];
@@ -110,16 +124,21 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
     }
 #pragma unroll
     for (int u = 0; u < MAXC; u++) {
-      if (u < nc) {
-        const uint32_t o = off + (uint32_t)(cb + u) * 128u;
+      if (FUSED || u < nc) {  // (the non-fused form waits for all loads anyway)
+        const uint32_t o = u < nc ? off + (uint32_t)(cb + u) * 128u : kOob;
         b0[u] = load_rsrc16(rb, o);
-        b1[u] = load_rsrc16(rb, o + 16);
+        b1[u] = load_rsrc16(rb, u < nc ? o + 16u : kOob);
       }
     }
   };
+  // One MFMA per chunk into alternating partial registers, each promoted
+  // after the next MFMA is issued (so the MFMAs do not wait on each other);
+  // chunks are added to acc in order.
   auto compute = [&](int cb, int nc) {
+    v4f_t part[2];
+    float scl[2];
 #pragma unroll
-    for (int u = 0; u < MAXC; u++) {
+    for (int u = 0; u <= MAXC; u++) {
       if (u < nc) {
         const int kb = cb + u;
         v8i_t af;
@@ -137,8 +156,20 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
           af = frag_of(a0[u], a1[u]);
           sa_u = sav[u];
         }
-        const v4f_t p = mfma_fp8_dec(frag_of(b0[u], b1[u]), af);
-        const float sc = sa_u * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sbv), u));
+        part[u & 1] = mfma_fp8_dec(frag_of(b0[u], b1[u]), af);
+        scl[u & 1] = sa_u * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sbv), u));
+        if (!FUSED) {  // registers are scarcer here: promote at once
+          const v4f_t& p = part[u & 1];
+          const float sc = scl[u & 1];
+          acc[0] = __builtin_fmaf(p[0], sc, acc[0]);
+          acc[1] = __builtin_fmaf(p[1], sc, acc[1]);
+          acc[2] = __builtin_fmaf(p[2], sc, acc[2]);
+          acc[3] = __builtin_fmaf(p[3], sc, acc[3]);
+        }
+      }
+      if (FUSED && u > 0 && u - 1 < nc) {
+        const v4f_t& p = part[(u - 1) & 1];
+        const float sc = scl[(u - 1) & 1];
         acc[0] = __builtin_fmaf(p[0], sc, acc[0]);
         acc[1] = __builtin_fmaf(p[1], sc, acc[1]);
         acc[2] = __builtin_fmaf(p[2], sc, acc[2]);
@@ -154,19 +185,18 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
     // group), as quantize_fp8_groups).  The first kXAhead activation loads of
     // each lane go out before the weight loads, and the quantization runs
     // while the weight stream is in flight.
-    constexpr int kXAhead = 4;
+    constexpr int kXAhead = 3;
     const uint16_t* X = static_cast<const uint16_t*>(Ain);
     const int tasks = M * KB, step = KS * 4, part = threadIdx.x & 15, t0 = (int)(threadIdx.x >> 4);
+    const rsrc_t rx = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
     uint4 xv[kXAhead];
 #pragma unroll
     for (int i = 0; i < kXAhead; i++) {
       const int task = t0 + i * step;
-      if (task < tasks) {
-        const int m = task / KB, g = task - m * KB;
-        xv[i] = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + g * kGroup + part * 8);
-      }
+      const int m = task / KB, g = task - m * KB;
+      xv[i] = load_rsrc16(rx, task < tasks ? (uint32_t)(m * K + g * kGroup + part * 8) * 2u : kOob);
     }
-    if (nc > 0) issue(cb, nc);
+    issue(cb, nc);  // even with nc == 0 (every load out of range): no branch around loads
     auto quantize_task = [&](int task, const uint4& v) {
       const int m = task / KB, g = task - m * KB;
       const uint32_t amax_bits = row16_max_u32(absmax8_bits(v));
@@ -190,7 +220,7 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
       quantize_task(task, *reinterpret_cast<const uint4*>(X + (int64_t)m * K + g * kGroup + part * 8));
     }
     __syncthreads();
-  } else if (nc > 0) {
+  } else {
     issue(cb, nc);
   }
   while (nc > 0) {
