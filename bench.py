@@ -26,8 +26,9 @@ graph see the same device time).  Also reported:
   timed by graph replay over 8 rotating weight sets so that the weights stream
   from HBM rather than the 256 MB last-level cache;
 * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
-Other --workload values (decode, moe, square8k, square16k) time one shape
-for profiling.
+Other --workload values time one shape for profiling: decode (M=1 linears),
+moe (contiguous grouped, 32 experts), moe_masked (masked grouped over a
+decode-time dispatch buffer), square8k, square16k, copy (counter calibration).
 """
 
 from __future__ import annotations
@@ -52,7 +53,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "moe", "square8k", "square16k", "copy"])
+    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "moe", "moe_masked", "square8k", "square16k", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     return p.parse_args()
@@ -449,6 +450,9 @@ def main():
     elif args.workload == "square16k":
         linears = [workloads.square_linear(16384, 16384, 8192)]
         workload = "square_16384x16384x8192"
+    elif args.workload == "moe_masked":
+        linears = None
+        workload = "moe_masked_32experts_1024tok_zipf1.1_top4_k7168_n4096"
     else:
         linears = None
         workload = "moe_32experts_zipf1.1_top4_k7168_n4096"
@@ -462,6 +466,8 @@ def main():
         gemm_s = sum(r["_gemm_s"] for r in per)
         roof = roofline_of(per)
         del preps
+    elif args.workload == "moe_masked":
+        value, ms_per_step, per, roof, gemm_s, total_flops = bench_masked(args, fg, torch, workloads)
     else:
         value, ms_per_step, per, roof, gemm_s, total_flops = bench_moe(args, fg, torch, workloads)
     torch.cuda.empty_cache()
@@ -554,6 +560,70 @@ def bench_moe(args, fg, torch, workloads):
     roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x4>", "achieved": round(flops / gt / 1e12, 1),
             "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / gt / 1e12 / PEAK_FP8_TFLOPS, 4),
             "traffic": None, "mean_launch_us": round(gt * 1e6, 2)}
+    return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gt, flops
+
+
+
+def bench_masked(args, fg, torch, workloads):
+    """Decode-time MoE: the masked grouped product over a dispatch buffer
+    (32 experts, 1024 tokens routed top-4 by Zipf(1.1), K = 7168, N = 4096);
+    one step = quantize the buffer + the masked product."""
+    c = workloads.moe_masked()
+    g, mm, n, k = c.num_groups, c.max_m, c.n, c.k
+    x = dev_bf16(c.a.reshape(g * mm, k), torch)
+    q, sa = fg.quantize_fp8_groups(x)
+    w = dev_bf16(c.b.reshape(g * n, k), torch)
+    qb, sb = fg.quantize_fp8_blocks(w)
+    del w
+    qb, sb = qb.view(g, n, k), sb.view(g, n // 128, k // 128)
+    masked = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
+    d = torch.empty((g, mm, n), dtype=torch.bfloat16, device="cuda")
+    qv = q.view(g, mm, k)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fg.quantize_fp8_groups(x, out=(q, sa))
+        if ev:
+            ev[1].record()
+        fg.m_grouped_fp8_gemm_nt_masked((qv, sa), (qb, sb), d, masked, c.expected_m)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[HipEvent(torch) for _ in range(3)] for _ in range(args.steps)]
+    ahead = GpuAhead(torch)
+    probe = [HipEvent(torch) for _ in range(3)]
+    host_step = host_enqueue_seconds(lambda: step(probe), torch)
+    e_first, e_last = HipEvent(torch), HipEvent(torch)
+    torch.cuda.synchronize()
+    ahead.spin(1.5 * host_step * args.steps + 2e-3)
+    e_first.record()
+    for s in range(args.steps):
+        step(evs[s])
+    e_last.record()
+    torch.cuda.synchronize()
+    elapsed = e_first.elapsed_time(e_last) * 1e-3
+    gt = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    qt = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    flops = float(2 * int(c.masked_m.sum()) * n * k)
+    kernel = "masked_gemm_nt_kernel (128-row tile chosen from expected_m)"
+    per = [{"name": c.name, "max_m": mm, "expected_m": c.expected_m, "rows": int(c.masked_m.sum()), "n": n, "k": k,
+            "groups": g, "quant_us": qt * 1e6, "gemm_us": gt * 1e6, "gemm_tflops_useful": flops / gt / 1e12,
+            "_gemm_s": gt}]
+    # At ~128 rows per expert the product reads every expert's weight once
+    # (940 MB) for ~240 GFLOP: ~250 FLOP/B, below the MFMA ridge (~625), so
+    # the bound is HBM.  Algorithmic bytes: the weights and weight scales of
+    # the experts with rows, their activation rows and scales, their outputs.
+    rows = int(c.masked_m.sum())
+    active = int((c.masked_m > 0).sum())
+    nbytes = active * (n * k + 4 * (n // 128) * (k // 128)) + rows * k + 4 * rows * (k // 128) + 2 * rows * n
+    gbs = nbytes / gt / 1e9
+    roof = {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+            "useful_tflops": round(flops / gt / 1e12, 1), "mean_launch_us": round(gt * 1e6, 2)}
     return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gt, flops
 
 

@@ -14,6 +14,7 @@ Linnet DeepGEMM plugin source):
     qb, sb = quantize_fp8_blocks(w)                  # w: bf16 [N, K]
     fp8_gemm_nt((q, sa), (qb, sb), d)                # d: bf16 [M, N], in place
     m_grouped_fp8_gemm_nt_contiguous((q, sa), (qb, sb), d, m_indices)
+    m_grouped_fp8_gemm_nt_masked((q, sa), (qb, sb), d, masked_m, expected_m)
 """
 
 from __future__ import annotations
@@ -44,11 +45,12 @@ _lib.quantize_fp8_blocks.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
 _lib.m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _vp, _i64, _i64, _i64, _vp]
 _lib.fp8_linear_nt.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _vp]
+_lib.m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _i64, _i64, _vp, _i64, _i64, _vp]
 _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
-              "fp8_linear_nt", "fgfp8_describe_gemm"):
+              "m_grouped_fp8_gemm_nt_masked", "fp8_linear_nt", "fgfp8_describe_gemm"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -192,6 +194,36 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Ten
     return d
 
 
+def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor, expected_m: int | None = None):
+    """Masked grouped product: A = (q [G, max_m, K], sa [K/128, sa_ld]) with the
+    group folded into the scale column (row g*max_m + r), B = (q [G, N, K], sb
+    [G, ceil(N/128), K/128]), masked_m int32 [G] on the device, d bf16
+    [G, max_m, N] (rows past masked_m[g] are not written).  expected_m is a
+    host-side hint for the tile choice."""
+    (qa, sa), (qb, sb) = a, b
+    _need(qa, "a", _FP8, 3)
+    _need(qb, "b", _FP8, 3)
+    _need(sa, "sa", (torch.float32,), 2)
+    _need(sb, "sb", (torch.float32,), 3)
+    _need(d, "d", (torch.bfloat16,), 3)
+    _need(masked_m, "masked_m", (torch.int32,), 1)
+    g, max_m, k = qa.shape
+    g2, n, k2 = qb.shape
+    if g2 != g or k2 != k or tuple(d.shape) != (g, max_m, n) or masked_m.shape[0] != g:
+        raise ValueError("shape mismatch among a [G, max_m, K], b [G, N, K], d [G, max_m, N], masked_m [G]")
+    if k % GROUP == 0 and tuple(sb.shape) != (g, -(-n // GROUP), k // GROUP):
+        raise ValueError("sb must be [G, ceil(N/128), K/128]")
+    if k % GROUP == 0 and sa.shape[0] != k // GROUP:
+        raise ValueError("sa must be [K/128, sa_ld]")
+    em = 0 if expected_m is None else int(expected_m)
+    _check(
+        _lib.m_grouped_fp8_gemm_nt_masked(
+            _ptr(qa), _ptr(sa), sa.shape[1], _ptr(masked_m), _ptr(qb), _ptr(sb), g, max_m, em, _ptr(d), n, k, _stream(d)
+        )
+    )
+    return d
+
+
 FUSED_MAX_M, FUSED_MAX_K = 4, 32768
 
 
@@ -255,6 +287,7 @@ __all__ = [
     "fp8_linear_nt",
     "last_error",
     "m_grouped_fp8_gemm_nt_contiguous",
+    "m_grouped_fp8_gemm_nt_masked",
     "padded_rows",
     "quantize_fp8_blocks",
     "quantize_fp8_groups",

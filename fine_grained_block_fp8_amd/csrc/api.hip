@@ -157,10 +157,37 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
   if (m == 0 || n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   if (env_flag("FGFP8_PRINT_CONFIG"))
-    fprintf(stderr, "[fgfp8] m_grouped_fp8_gemm_nt_contiguous m=%lld n=%lld k=%lld groups=%d: tile128x256_w2x2\n",
-            (long long)m, (long long)n, (long long)k, (int)num_groups);
+    fprintf(stderr, "[fgfp8] m_grouped_fp8_gemm_nt_contiguous m=%lld n=%lld k=%lld groups=%d: %s\n", (long long)m,
+            (long long)n, (long long)k, (int)num_groups, fgfp8::gemm_kind_name(fgfp8::kGemmTile128x256));
   return launched(fgfp8::launch_grouped_gemm(a_e4m3, sa, sa_ld, m_indices, b_e4m3, sb, num_groups, d_bf16, m, n, k,
                                              (hipStream_t)stream),
+                  who);
+}
+
+int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                                 const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
+                                 int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* stream) {
+  const char* who = "m_grouped_fp8_gemm_nt_masked";
+  if (num_groups < 1) return fail(FGFP8_EINVAL, "%s: num_groups=%d must be >= 1", who, (int)num_groups);
+  if (max_m < 0 || max_m % 4 != 0 || (int64_t)num_groups * max_m >= kMaxRows)
+    return fail(FGFP8_EINVAL, "%s: max_m=%lld must be a non-negative multiple of 4 (and num_groups * max_m < 2^31)",
+                who, (long long)max_m);
+  if (n < 0 || n >= kMaxRows) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, (int64_t)num_groups * max_m, k, sa_ld)) return rc;
+  if (!a_e4m3 || !sa || !masked_m || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(masked_m) || !aligned16(b_e4m3) || !aligned16(sb) ||
+      !aligned16(d_bf16))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (max_m == 0 || n == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  const fgfp8::GemmKind kind = fgfp8::plan_masked(num_groups, max_m, expected_m, n);
+  if (env_flag("FGFP8_PRINT_CONFIG"))
+    fprintf(stderr, "[fgfp8] m_grouped_fp8_gemm_nt_masked groups=%d max_m=%lld expected_m=%lld n=%lld k=%lld: %s\n",
+            (int)num_groups, (long long)max_m, (long long)expected_m, (long long)n, (long long)k,
+            fgfp8::gemm_kind_name(kind));
+  return launched(fgfp8::launch_masked_gemm(kind, a_e4m3, sa, sa_ld, masked_m, b_e4m3, sb, num_groups, max_m, d_bf16,
+                                            n, k, (hipStream_t)stream),
                   who);
 }
 

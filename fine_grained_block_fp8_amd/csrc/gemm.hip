@@ -419,6 +419,32 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_kernel(
                m0, n0);
 }
 
+// Masked: group g owns rows [g*max_m, g*max_m + max_m) of A and D (a
+// dispatch buffer with a fixed stride per group), of which only the first
+// masked_m[g] are real.  The grid covers every group's max_m rows; a block
+// reads its group's count on the device (no host synchronisation) and exits
+// when its rows are all past it.  Rows past the count read as zero and are
+// never stored.  A count outside [0, max_m] is clamped to it.
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void masked_gemm_nt_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ SA, const int32_t* __restrict__ masked_m,
+    const uint8_t* __restrict__ B, const float* __restrict__ SB, uint16_t* __restrict__ D, int64_t max_m, int64_t N,
+    int K, int64_t sa_ld, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  const int per_group = tiles_m * tiles_n;
+  const int g = blockIdx.x / per_group;
+  int tm, tn;
+  tile_coords(blockIdx.x - g * per_group, per_group, tiles_m, tiles_n, tm, tn);
+  int rows = __builtin_amdgcn_readfirstlane(masked_m[g]);
+  rows = rows < 0 ? 0 : (rows > max_m ? (int)max_m : rows);
+  if ((int64_t)tm * C::BM >= rows) return;  // uniform across the workgroup, before any barrier
+  const int64_t base = (int64_t)g * max_m;
+  const int64_t m0 = base + (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+  const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
+  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, D, base + rows, N, K,
+               sa_ld, m0, n0);
+}
+
 // ------------------------------------------------------------ host side
 namespace {
 struct Candidate {
@@ -487,6 +513,50 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int
     case kGemmDecode: return launch_decode(plan.split, a, sa, sa_ld, b, sb, d, m, n, k, stream);
   }
   return hipErrorInvalidValue;
+}
+
+GemmKind plan_masked(int32_t num_groups, int64_t max_m, int64_t expected_m, int64_t n) {
+  // Tiles of 128 rows (the smallest that keeps two waves per SIMD); the
+  // column width from the expected work: rounds of 256 CUs over
+  // num_groups * ceil(expected_m / 128) row tiles, as in plan_gemm.
+  const int64_t em = expected_m > 0 && expected_m < max_m ? expected_m : max_m;
+  const int64_t row_tiles = (int64_t)num_groups * ((em + 127) / 128);
+  GemmKind best = kGemmTile128x256;
+  double best_cost = 1e300;
+  for (const Candidate& c : kCandidates) {
+    if (c.bm != 128) continue;
+    const int64_t tiles = row_tiles * ((n + c.bn - 1) / c.bn);
+    const double cost = (double)((tiles + kCUs - 1) / kCUs) * c.bm * c.bn / c.eff;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = c.kind;
+    }
+  }
+  return best;
+}
+
+template <class C>
+static hipError_t launch_masked_tile(const void* a, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                                     const void* b, const float* sb, int32_t num_groups, int64_t max_m, void* d,
+                                     int64_t n, int64_t k, hipStream_t stream) {
+  const int tiles_m = (int)((max_m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL(masked_gemm_nt_kernel<C>, dim3((uint32_t)num_groups * tiles_m * tiles_n), dim3(C::THREADS), 0,
+                     stream, static_cast<const uint8_t*>(a), sa, masked_m, static_cast<const uint8_t*>(b), sb,
+                     static_cast<uint16_t*>(d), max_m, n, (int)k, sa_ld, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_masked_gemm(GemmKind kind, const void* a, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                              const void* b, const float* sb, int32_t num_groups, int64_t max_m, void* d, int64_t n,
+                              int64_t k, hipStream_t stream) {
+  switch (kind) {
+    case kGemmTile128x256:
+      return launch_masked_tile<Tile128x256>(a, sa, sa_ld, masked_m, b, sb, num_groups, max_m, d, n, k, stream);
+    case kGemmTile128x128:
+      return launch_masked_tile<Tile128x128>(a, sa, sa_ld, masked_m, b, sb, num_groups, max_m, d, n, k, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,

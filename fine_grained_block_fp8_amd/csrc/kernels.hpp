@@ -45,4 +45,11 @@ hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, co
                                const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream);
 
+// Masked grouped product: a 128-row tile chosen from the expected rows per
+// group (a host-side hint; the per-group counts stay on the device).
+GemmKind plan_masked(int32_t num_groups, int64_t max_m, int64_t expected_m, int64_t n);
+hipError_t launch_masked_gemm(GemmKind kind, const void* a, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                              const void* b, const float* sb, int32_t num_groups, int64_t max_m, void* d, int64_t n,
+                              int64_t k, hipStream_t stream);
+
 }  // namespace fgfp8

@@ -129,6 +129,31 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
                                      const void* b_e4m3, const float* sb, int32_t num_groups, void* d_bf16,
                                      int64_t m, int64_t n, int64_t k, void* stream);
 
+/* M-grouped masked variant for mixture-of-experts layers at decode time
+ * (deepgemm-rust README, "What's implemented", m_grouped_fp8_gemm_nt_masked
+ * row: the same kernel with a masked_m scheduler, for a DeepEP-style dispatch
+ * output, with expected_m guiding the schedule and no host synchronisation).
+ * Every group owns max_m rows of a dispatch buffer, of which only the first
+ * masked_m[g] are real; the counts are device data, never read on the host.
+ *
+ * a_e4m3     [num_groups][max_m][k] E4M3: group g's row r is buffer row
+ *            g * max_m + r.
+ * sa         [k/128][sa_ld] float32: the MN-major scales of the buffer viewed
+ *            as one (num_groups * max_m) x k matrix, i.e. the group folded
+ *            into the scale column (what quantize_fp8_groups writes for it).
+ * masked_m   [num_groups] int32: rows of each group to compute (values
+ *            outside [0, max_m] are clamped to it).
+ * b_e4m3     [num_groups][n][k] E4M3; sb [num_groups][ceil(n/128)][k/128].
+ * expected_m host-side hint: the typical count, used only to choose the tile
+ *            (<= 0: assume max_m).  Any value gives the same results.
+ * d_bf16     [num_groups][max_m][n] bfloat16 output; rows r >= masked_m[g]
+ *            of group g are not written.
+ * Requirements: num_groups >= 1, max_m >= 0 and max_m % 4 == 0, n >= 0,
+ * k > 0 and k % 128 == 0, sa_ld % 4 == 0, sa_ld >= num_groups * max_m. */
+int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                                 const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
+                                 int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* stream);
+
 /* The linear as the pages run it (Linnet "Backend plugins" page,
  * _BlockProduct.execute: round the bf16 input per 1x128 group, then
  * fp8_gemm_nt with the stored weight): D = quantize_groups(x) . B^T.

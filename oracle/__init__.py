@@ -21,7 +21,8 @@ What it computes, and where the pages define it:
 * ``gemm``      the block-scaled product D = A.B^T with both scale sets applied
                 once per 128-wide K chunk, in FP64, and its M-grouped contiguous
                 variant (deepgemm-rust README, "What's implemented" table and
-                "Quick start" grouped example).
+                "Quick start" grouped example), and its masked variant (same
+                table, m_grouped_fp8_gemm_nt_masked row).
 
 Every function works in float64 (or exact integer / float32 steps where the
 method fixes float32), favouring obviousness over speed.
@@ -36,6 +37,7 @@ from .gemm import (
     gemm_nt,
     gemm_nt_dequantized,
     grouped_gemm_nt,
+    masked_grouped_gemm_nt,
     round_to_bf16,
 )
 from .quantize import GROUP, quantize_blocks, quantize_groups
@@ -49,6 +51,7 @@ __all__ = [
     "gemm_nt",
     "gemm_nt_dequantized",
     "grouped_gemm_nt",
+    "masked_grouped_gemm_nt",
     "quantize_blocks",
     "quantize_groups",
     "round_to_bf16",

@@ -1,4 +1,5 @@
-"""The block-scaled FP8 product D = A.B^T, dense and M-grouped, in FP64.
+"""The block-scaled FP8 product D = A.B^T, dense and M-grouped (contiguous and
+masked), in FP64.
 
 Test infrastructure (see the package docstring): not part of the product path.
 
@@ -108,6 +109,36 @@ def grouped_gemm_nt(qa, sa, m_indices, qb, sb, num_groups: int) -> np.ndarray:
         if rows.size == 0:
             continue
         d[rows] = gemm_nt(qa[rows], sa[:, rows], qb[g], sb[g])
+    return d
+
+
+def masked_grouped_gemm_nt(qa, sa, masked_m, qb, sb) -> np.ndarray:
+    """M-grouped masked product (deepgemm-rust README, "What's implemented",
+    m_grouped_fp8_gemm_nt_masked row: the same product with a masked_m
+    scheduler, for a dispatch buffer that holds every group's rows at a fixed
+    stride; only the first masked_m[g] rows of group g are real).
+
+    qa [G][max_m][K]; sa [K/128][>= G*max_m], the activation scales of the
+    buffer viewed as one (G*max_m) x K matrix (the group folded into the
+    scale column: row r of group g is column g*max_m + r); masked_m [G];
+    qb [G][N][K]; sb [G][ceil(N/128)][K/128].  Returns D [G][max_m][N] with
+    row r < masked_m[g] of group g the dense product of that row with group
+    g's weight, and NaN elsewhere (those rows carry no defined value).
+    """
+    qa = np.asarray(qa, dtype=np.uint8)
+    g_count, max_m, k = qa.shape
+    qb = np.asarray(qb, dtype=np.uint8).reshape(g_count, -1, k)
+    n = qb.shape[1]
+    sb = np.asarray(sb, dtype=np.float32).reshape(g_count, -(-n // GROUP), k // GROUP)
+    sa = np.asarray(sa, dtype=np.float32)
+    masked_m = np.asarray(masked_m, dtype=np.int64)
+    d = np.full((g_count, max_m, n), np.nan, dtype=np.float64)
+    for g in range(g_count):
+        rows = int(masked_m[g])
+        if rows <= 0:
+            continue
+        cols = g * max_m + np.arange(rows)
+        d[g, :rows] = gemm_nt(qa[g, :rows], sa[:, cols], qb[g], sb[g])
     return d
 
 

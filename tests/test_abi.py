@@ -34,6 +34,7 @@ def test_library_exports_every_declared_function():
         "fgfp8_last_error",
         "fgfp8_describe_gemm",
         "fp8_linear_nt",
+        "m_grouped_fp8_gemm_nt_masked",
     }
     lib = fg.library()
     for n in names:
@@ -120,6 +121,22 @@ def test_grouped_rejects():
     assert call(m=0, sa_ld=4) == fg.FGFP8_OK
 
 
+def test_masked_rejects():
+    lib = _lib()
+
+    def call(g=4, max_m=64, n=128, k=256, sa_ld=256, mm=P, em=32):
+        return lib.m_grouped_fp8_gemm_nt_masked(P, P, sa_ld, mm, P, P, g, max_m, em, P, n, k, None)
+
+    assert call(max_m=62) == fg.FGFP8_EINVAL
+    assert "multiple of 4" in fg.last_error()
+    assert call(g=0) == fg.FGFP8_EINVAL
+    assert call(sa_ld=252) == fg.FGFP8_EINVAL  # sa_ld < num_groups * max_m
+    assert call(mm=None) == fg.FGFP8_EINVAL
+    assert call(k=200) == fg.FGFP8_EINVAL
+    assert call(max_m=0, sa_ld=4) == fg.FGFP8_OK
+    assert call(n=0) == fg.FGFP8_OK
+
+
 def test_linear_rejects():
     lib = _lib()
 
@@ -150,6 +167,7 @@ def test_no_device_is_reported_not_crashed():
     assert lib.quantize_fp8_blocks(P, 16, 256, P, P, None) == fg.FGFP8_ENODEV
     assert lib.m_grouped_fp8_gemm_nt_contiguous(P, P, 128, P, P, P, 2, P, 128, 64, 128, None) == fg.FGFP8_ENODEV
     assert lib.fp8_linear_nt(P, 1, 256, P, P, 128, P, None, None, 0, None) == fg.FGFP8_ENODEV
+    assert lib.m_grouped_fp8_gemm_nt_masked(P, P, 256, P, P, P, 4, 64, 32, P, 128, 256, None) == fg.FGFP8_ENODEV
 
 
 def test_describe_gemm_plans():

@@ -1,0 +1,134 @@
+"""GPU parity of m_grouped_fp8_gemm_nt_masked against the oracle.
+
+The activation buffer [G][max_m][K] is quantized as one (G*max_m) x K matrix
+(checked bit-exact), the weights expert by expert; every computed row is held
+to the product criteria of tests/parity.py, rows past a group's count must
+stay untouched (NaN-poisoned output), and a full-groups case must equal the
+contiguous grouped kernel bit for bit (same MFMA chunks, same promotion
+order)."""
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_fp8_amd as fg
+import oracle
+import workloads
+from tests.parity import bits32, check_gemm, codes, d_to_f64, magnitude_sum, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_masked(c: workloads.Masked, masked_dev=None, expected_m=None):
+    g, mm, n, k = c.num_groups, c.max_m, c.n, c.k
+    x = to_dev_bf16(c.a.reshape(g * mm, k))
+    q, sa = fg.quantize_fp8_groups(x)
+    w = to_dev_bf16(c.b.reshape(g * n, k))
+    if n % 128 == 0:
+        qb, sb = fg.quantize_fp8_blocks(w)
+        qb, sb = qb.view(g, n, k), sb.view(g, n // 128, k // 128)
+    else:
+        qb = torch.empty((g, n, k), dtype=torch.float8_e4m3fn, device="cuda")
+        sb = torch.empty((g, -(-n // 128), k // 128), dtype=torch.float32, device="cuda")
+        for e in range(g):  # per expert (a block must not straddle two experts), via aligned temporaries
+            qe, se = fg.quantize_fp8_blocks(w[e * n : (e + 1) * n])
+            qb[e].copy_(qe)
+            sb[e].copy_(se)
+    if masked_dev is None:
+        masked_dev = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
+    d = torch.full((g, mm, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.m_grouped_fp8_gemm_nt_masked((q.view(g, mm, k), sa), (qb, sb), d, masked_dev,
+                                    c.expected_m if expected_m is None else expected_m)
+    torch.cuda.synchronize()
+    return q, sa, qb, sb, d
+
+
+def check_masked(c, q, sa, qb, sb, d, groups=None, rows_per_group=None, cblocks=None, rng=None):
+    rng = rng or np.random.default_rng(0)
+    g_all, mm, n, k = c.num_groups, c.max_m, c.n, c.k
+    groups = range(g_all) if groups is None else groups
+    cblocks = np.arange(-(-n // 128)) if cblocks is None else np.asarray(cblocks)
+    cols = np.concatenate([np.arange(b * 128, min(n, b * 128 + 128)) for b in cblocks])
+    counts = np.clip(c.masked_m, 0, mm)
+    for e in groups:
+        rows = np.arange(int(counts[e]))
+        if rows_per_group and rows.size > rows_per_group:
+            rows = np.unique(np.concatenate([rows[[0, -1]], rng.choice(rows, rows_per_group - 2, replace=False)]))
+        buf_rows = e * mm + rows
+        if rows.size:
+            oq, osa = oracle.quantize_groups(c.a[e][rows])
+            oqb, osb = oracle.quantize_blocks(c.b[e][cols])
+            ri = torch.as_tensor(buf_rows, device="cuda")
+            assert np.array_equal(codes(q.view(torch.uint8).index_select(0, ri)), oq)
+            assert np.array_equal(bits32(sa.index_select(1, ri)), bits32(osa[:, : rows.size]))
+            assert np.array_equal(codes(qb[e].view(torch.uint8).index_select(0, torch.as_tensor(cols, device="cuda"))), oqb)
+            ref = oracle.gemm_nt(oq, osa, oqb, osb)
+            got = d_to_f64(d[e].index_select(0, torch.as_tensor(rows, device="cuda")).index_select(1, torch.as_tensor(cols, device="cuda")))
+            check_gemm(got, ref, magnitude_sum(oq, osa, oqb, osb), k, f"group {e}")
+        # rows past the count are never written
+        assert torch.isnan(d[e, int(counts[e]):].float()).all(), f"group {e}: rows past masked_m written"
+
+
+@pytest.mark.parametrize(
+    "counts,max_m,n,k",
+    [
+        ([0, 137, 200], 200, 264, 384),
+        ([64, 1, 17, 0, 33], 64, 128, 256),
+        ([300, 129, 128, 256], 300, 512, 640),
+        ([5], 8, 16, 128),
+    ],
+)
+def test_small_masked_cases(counts, max_m, n, k):
+    c = workloads.small_masked(counts, max_m, n, k, seed=sum(counts) + max_m + n + k)
+    q, sa, qb, sb, d = gpu_masked(c)
+    check_masked(c, q, sa, qb, sb, d)
+
+
+def test_oracle_function_agrees_on_a_small_case():
+    """The oracle's masked form itself (folded scale columns) on the GPU's
+    quantized bytes."""
+    c = workloads.small_masked([3, 0, 8], 8, 136, 256, seed=71)
+    q, sa, qb, sb, d = gpu_masked(c)
+    g, mm, n, k = c.num_groups, c.max_m, c.n, c.k
+    ref = oracle.masked_grouped_gemm_nt(codes(q).reshape(g, mm, k), sa.cpu().numpy(), c.masked_m,
+                                        codes(qb).reshape(g, n, k), sb.cpu().numpy())
+    got = d_to_f64(d.reshape(g * mm, n)).reshape(g, mm, n)
+    qa_all, sa_all = codes(q).reshape(g, mm, k), sa.cpu().numpy()
+    qb_all, sb_all = codes(qb).reshape(g, n, k), sb.cpu().numpy()
+    for e in range(g):
+        r = int(c.masked_m[e])
+        if r:
+            s = magnitude_sum(qa_all[e, :r], sa_all[:, e * mm : e * mm + r], qb_all[e], sb_all[e])
+            check_gemm(got[e, :r], ref[e, :r], s, k, f"group {e}")
+
+
+def test_counts_outside_range_are_clamped():
+    c = workloads.small_masked([-3, 40, 7], 32, 128, 256, seed=73)
+    q, sa, qb, sb, d = gpu_masked(c)
+    c2 = workloads.Masked(c.name, c.num_groups, c.max_m, c.n, c.k, np.array([0, 32, 7], np.int32), c.expected_m, c.a, c.b)
+    check_masked(c2, q, sa, qb, sb, d)
+
+
+@pytest.mark.parametrize("expected_m", [1, 128, 4096])
+def test_full_groups_equal_contiguous_bitwise(expected_m):
+    """max_m a multiple of 128 and every group full: the buffer is the
+    contiguous layout, and the results must be the same bits whatever tile the
+    hint selects."""
+    c = workloads.small_masked([256, 256, 256], 256, 384, 512, seed=79)
+    q, sa, qb, sb, d = gpu_masked(c, expected_m=expected_m)
+    idx = torch.repeat_interleave(torch.arange(3, dtype=torch.int32, device="cuda"), 256)
+    d2 = torch.full((768, c.n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.m_grouped_fp8_gemm_nt_contiguous((q, sa), (qb, sb), d2, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(d.reshape(768, c.n).view(torch.int16), d2.view(torch.int16))
+
+
+def test_decode_moe_dispatch_buffer_sampled():
+    """The 32-expert, K = 7168, N = 4096 decode dispatch buffer (1024 tokens,
+    Zipf(1.1) top-4): sampled rows of several groups against the oracle."""
+    c = workloads.moe_masked()
+    q, sa, qb, sb, d = gpu_masked(c)
+    rng = np.random.default_rng(11)
+    check_masked(c, q, sa, qb, sb, d, groups=[0, 1, 7, 20, 31], rows_per_group=6, cblocks=[0, 13, 31], rng=rng)
+    for e in range(c.num_groups):
+        assert torch.isfinite(d[e, : int(c.masked_m[e])].float()).all()

@@ -198,3 +198,68 @@ def test_round_to_bf16_matches_exact_rounding():
             assert np.isinf(gv)
         else:
             assert Fraction(float(gv)) == r, v
+
+
+def _masked_operands(rng, g_count, max_m, n, k):
+    qa = rng.choice(FINITE, size=(g_count, max_m, k)).astype(np.uint8)
+    qb = rng.choice(FINITE, size=(g_count, n, k)).astype(np.uint8)
+    sa = (rng.random((k // 128, g_count * max_m)) * 2.0 ** rng.integers(-8, 4, size=(k // 128, g_count * max_m))).astype(np.float32)
+    sb = (rng.random((g_count, -(-n // 128), k // 128)) + 0.25).astype(np.float32)
+    return qa, sa, qb, sb
+
+
+def test_masked_matches_rational_brute_force():
+    """Tiny masked case against exact rationals, element by element: the
+    group's weight and scale block, the folded activation-scale column
+    g*max_m + r, and the row mask."""
+    rng = np.random.default_rng(43)
+    g_count, max_m, n, k = 3, 4, 3, 256
+    qa, sa, qb, sb = _masked_operands(rng, g_count, max_m, n, k)
+    masked = np.array([2, 0, 4])
+    d = oracle.masked_grouped_gemm_nt(qa, sa, masked, qb, sb)
+    t = oracle.e4m3_table()
+    for g in range(g_count):
+        for r in range(max_m):
+            if r >= masked[g]:
+                assert np.all(np.isnan(d[g, r]))
+                continue
+            for j in range(n):
+                exact = Fraction(0)
+                mag = 0.0
+                for kb in range(k // 128):
+                    s = Fraction(float(sa[kb, g * max_m + r])) * Fraction(float(sb[g, j // 128, kb]))
+                    part = sum(Fraction(float(t[qa[g, r, kk]])) * Fraction(float(t[qb[g, j, kk]])) for kk in range(kb * 128, (kb + 1) * 128))
+                    exact += s * part
+                    mag += float(s) * sum(abs(float(t[qa[g, r, kk]]) * float(t[qb[g, j, kk]])) for kk in range(kb * 128, (kb + 1) * 128))
+                assert abs(Fraction(d[g, r, j]) - exact) <= Fraction(2.0**-50) * Fraction(mag) + Fraction(2.0**-1000)
+
+
+def test_masked_full_groups_equal_contiguous_layout():
+    """With every group full (masked_m = max_m, max_m a multiple of 128) the
+    dispatch buffer is exactly the contiguous layout with m_indices = g on
+    group g's rows: the independently pinned contiguous form must agree."""
+    rng = np.random.default_rng(47)
+    g_count, max_m, n, k = 3, 128, 136, 256
+    qa, sa, qb, sb = _masked_operands(rng, g_count, max_m, n, k)
+    d = oracle.masked_grouped_gemm_nt(qa, sa, np.full(g_count, max_m), qb, sb)
+    m_idx = np.repeat(np.arange(g_count, dtype=np.int32), max_m)
+    d_c = oracle.grouped_gemm_nt(qa.reshape(g_count * max_m, k), sa, m_idx, qb, sb, g_count)
+    assert np.array_equal(d.reshape(g_count * max_m, n), d_c)
+
+
+def test_masked_groups_are_isolated_and_mask_is_a_prefix():
+    """Changing one group's weight or its rows past masked_m changes nothing
+    in the other groups, nor in the masked-off rows."""
+    rng = np.random.default_rng(53)
+    g_count, max_m, n, k = 4, 8, 130, 128
+    qa, sa, qb, sb = _masked_operands(rng, g_count, max_m, n, k)
+    masked = np.array([8, 3, 0, 5])
+    d = oracle.masked_grouped_gemm_nt(qa, sa, masked, qb, sb)
+    qb2, qa2 = qb.copy(), qa.copy()
+    qb2[1] = rng.choice(FINITE, size=(n, k))
+    qa2[3, 5:] = rng.choice(FINITE, size=(max_m - 5, k))
+    d2 = oracle.masked_grouped_gemm_nt(qa2, sa, masked, qb2, sb)
+    for g in (0, 2, 3):
+        assert np.array_equal(np.nan_to_num(d[g], nan=7.0), np.nan_to_num(d2[g], nan=7.0))
+    assert not np.array_equal(d[1, :3], d2[1, :3])
+    assert np.all(np.isnan(d[2])) and np.all(np.isnan(d[3, 5:]))

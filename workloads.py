@@ -212,3 +212,53 @@ def small_grouped(sizes, n: int, k: int, seed: int) -> Grouped:
     b = gaussian_bf16(r_w, (len(sizes), n, k), 0.02)
     token_of_row = np.where(m_indices >= 0, np.arange(m_indices.shape[0]), -1)
     return Grouped(f"grouped_{len(sizes)}x{n}x{k}", len(sizes), n, k, sizes, starts, m_indices, a, b, token_of_row)
+
+
+# -------------------------------------------------------------------- masked
+@dataclass
+class Masked:
+    """A masked grouped (dispatch-buffer) case: group g's rows are buffer rows
+    g*max_m .. g*max_m + max_m - 1, the first masked_m[g] of them real."""
+
+    name: str
+    num_groups: int
+    max_m: int
+    n: int
+    k: int
+    masked_m: np.ndarray  # int32 [G]
+    expected_m: int
+    a: np.ndarray  # uint16 [G][max_m][K]; rows past masked_m hold unrelated values
+    b: np.ndarray  # uint16 [G][N][K]
+
+
+def small_masked(masked_m, max_m: int, n: int, k: int, seed: int) -> Masked:
+    """Given per-group counts; every row of the buffer (real or not) ~ N(0,1),
+    so rows past the count carry values a kernel must ignore."""
+    r_x, r_w = _rngs(seed, 2)
+    masked_m = np.asarray(masked_m, dtype=np.int32)
+    g = masked_m.shape[0]
+    a = gaussian_bf16(r_x, (g, max_m, k), 1.0)
+    b = gaussian_bf16(r_w, (g, n, k), 0.02)
+    em = int(np.clip(masked_m, 0, max_m).mean()) if g else 0
+    return Masked(f"masked_{g}x{max_m}x{n}x{k}", g, max_m, n, k, masked_m, em, a, b)
+
+
+def moe_masked(seed: int = 5, experts: int = 32, tokens: int = 1024, topk: int = 4, alpha: float = 1.1,
+               n: int = 4096, k: int = 7168, with_weights: bool = True) -> Masked:
+    """Decode-time MoE dispatch buffer: `tokens` tokens routed top-k by the
+    seeded Zipf(alpha) expert choice (as moe_grouped); expert g receives
+    masked_m[g] of them; max_m is the largest count rounded up to 128;
+    expected_m the mean count (the hint a dispatcher knows ahead of time).
+    Rows past a group's count are zero, as a freshly cleared buffer."""
+    r_route, r_x, r_w = _rngs(seed, 3)
+    choice = zipf_topk_routing(r_route, tokens, experts, topk, alpha)
+    counts = np.array([(choice == g).any(axis=1).sum() for g in range(experts)], dtype=np.int32)
+    max_m = int(-(-counts.max() // ALIGN) * ALIGN)
+    x = gaussian_bf16(r_x, (tokens, k), 1.0)
+    a = np.zeros((experts, max_m, k), dtype=np.uint16)
+    for g in range(experts):
+        toks = np.nonzero((choice == g).any(axis=1))[0]
+        a[g, : toks.size] = x[toks]
+    b = gaussian_bf16(r_w, (experts, n, k), 0.02) if with_weights else np.zeros((0,), np.uint16)
+    return Masked(f"moe_masked_{experts}x{n}x{k}_zipf{alpha}_top{topk}_{tokens}tok", experts, max_m, n, k, counts,
+                  int(round(counts.mean())), a, b)
