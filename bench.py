@@ -56,6 +56,7 @@ def parse():
     p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "moe", "moe_masked", "square8k", "square16k", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--decode-reps", type=int, default=50, help="rounds over the 8 weight sets per decode timing")
     return p.parse_args()
 
 
@@ -474,7 +475,7 @@ def main():
 
     decode = None
     if args.workload in ("prefill", "decode") and not args.no_decode:
-        decode = bench_decode(fg, torch)
+        decode = bench_decode(fg, torch, reps=args.decode_reps)
         for r in decode:
             log(f"decode M=1 N={r['n']} K={r['k']}: graph {r['graph_us']} us {r['graph_gbs']} GB/s; "
                 f"eager {r['eager_us']} us")
