@@ -45,12 +45,13 @@ _lib.quantize_fp8_blocks.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
 _lib.m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _vp, _i64, _i64, _i64, _vp]
 _lib.fp8_linear_nt.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _vp]
+_lib.fp8_gemm_nt_fp8_out.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _fp, _i64, _vp, _i64, _i64, _i64, _vp]
 _lib.m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _i64, _i64, _vp, _i64, _i64, _vp]
 _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
-              "m_grouped_fp8_gemm_nt_masked", "fp8_linear_nt", "fgfp8_describe_gemm"):
+              "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -170,6 +171,44 @@ def fp8_gemm_nt(a, b, d: torch.Tensor) -> torch.Tensor:
     return d
 
 
+def fp8_gemm_nt_fp8_out(a, b, out=None, d: torch.Tensor | None = None):
+    """The product of fp8_gemm_nt, quantized per 1x128 group of each row for
+    the next layer: returns (q float8_e4m3fn [M, N], sd float32 [N/128,
+    sd_ld]), bit-identical to quantize_fp8_groups(fp8_gemm_nt(a, b)); d, if
+    given, also receives the bf16 product.  N must be a multiple of 128."""
+    (qa, sa), (qb, sb) = a, b
+    _need(qa, "a", _FP8, 2)
+    _need(qb, "b", _FP8, 2)
+    _need(sa, "sa", (torch.float32,), 2)
+    _need(sb, "sb", (torch.float32,), 2)
+    m, k = qa.shape
+    n = qb.shape[0]
+    if qb.shape[1] != k:
+        raise ValueError("a and b must share K")
+    if out is None:
+        q = torch.empty((m, n), dtype=torch.float8_e4m3fn, device=qa.device)
+        sd = torch.empty((n // GROUP if n % GROUP == 0 else 0, padded_rows(m)), dtype=torch.float32, device=qa.device)
+    else:
+        q, sd = out
+        _need(q, "q", _FP8, 2)
+        _need(sd, "sd", (torch.float32,), 2)
+        if tuple(q.shape) != (m, n):
+            raise ValueError(f"q must be [{m}, {n}]")
+    d_ptr = None
+    if d is not None:
+        _need(d, "d", (torch.bfloat16,), 2)
+        if tuple(d.shape) != (m, n):
+            raise ValueError(f"d must be [{m}, {n}]")
+        d_ptr = _ptr(d)
+    _check(
+        _lib.fp8_gemm_nt_fp8_out(
+            _ptr(qa), _ptr(sa), sa.shape[1], _ptr(qb), _ptr(sb), _ptr(q), _ptr(sd), sd.shape[1], d_ptr, m, n, k,
+            _stream(qa),
+        )
+    )
+    return q, sd
+
+
 def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Tensor) -> torch.Tensor:
     """Grouped product: A = (q [M, K], sa), B = (q [G, N, K], sb [G, ceil(N/128), K/128]),
     m_indices int32 [M] (group of each row, -1 for padding), d bf16 [M, N]."""
@@ -283,6 +322,7 @@ __all__ = [
     "declared_functions",
     "describe_gemm",
     "fp8_gemm_nt",
+    "fp8_gemm_nt_fp8_out",
     "fp8_linear",
     "fp8_linear_nt",
     "last_error",

@@ -164,6 +164,33 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
                   who);
 }
 
+int fp8_gemm_nt_fp8_out(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                        void* q_e4m3, float* sd, int64_t sd_ld, void* d_bf16, int64_t m, int64_t n, int64_t k,
+                        void* stream) {
+  const char* who = "fp8_gemm_nt_fp8_out";
+  if (m < 0 || m >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m=%lld out of range", who, (long long)m);
+  if (n < 0 || n >= kMaxRows || n % 128 != 0)
+    return fail(FGFP8_EINVAL, "%s: n=%lld must be a non-negative multiple of 128", who, (long long)n);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (sd_ld < m || sd_ld % 4 != 0 || sd_ld <= 0 || (n / 128) * sd_ld * 4 >= (int64_t(1) << 31))
+    return fail(FGFP8_EINVAL, "%s: sd_ld=%lld must be a positive multiple of 4, >= m=%lld (and n/128 * sd_ld < 2^29)",
+                who, (long long)sd_ld, (long long)m);
+  if (!a_e4m3 || !sa || !b_e4m3 || !sb || !q_e4m3 || !sd) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(q_e4m3) ||
+      !aligned16(sd) || (d_bf16 && !aligned16(d_bf16)))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (m == 0 || n == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  const fgfp8::GemmKind kind = fgfp8::plan_tiles(m, n, k);
+  if (env_flag("FGFP8_PRINT_CONFIG"))
+    fprintf(stderr, "[fgfp8] fp8_gemm_nt_fp8_out m=%lld n=%lld k=%lld: %s\n", (long long)m, (long long)n,
+            (long long)k, fgfp8::gemm_kind_name(kind));
+  return launched(fgfp8::launch_gemm_fp8out(kind, a_e4m3, sa, sa_ld, b_e4m3, sb, q_e4m3, sd, sd_ld, d_bf16, m, n, k,
+                                            (hipStream_t)stream),
+                  who);
+}
+
 int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
                                  const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
                                  int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* stream) {

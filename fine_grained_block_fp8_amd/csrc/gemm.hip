@@ -51,7 +51,10 @@ struct Tile {
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = STAGES * A_BYTES;
   static constexpr int S_OFF = B_OFF + STAGES * B_BYTES;
-  static constexpr int LDS = S_OFF + STAGES * S_BYTES;
+  // FP8-output epilogue: one float per (wave, row) for the partner-wave amax
+  // exchange of 64-column wave tiles.
+  static constexpr int EPI_OFF = S_OFF + STAGES * S_BYTES;
+  static constexpr int LDS = EPI_OFF + WAVES * TM * 4;
   static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
   static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "segments divide evenly among waves");
@@ -270,9 +273,31 @@ __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& b
   promote(acc[C::MT - 1][T1 - 1], part[(N_MFMA - 1) & 1], sc[C::MT - 1]);
 }
 
+// The 8 values of epilogue slot s of an MFMA row tile, rounded to bf16 and
+// packed in column order (see the epilogue).
 template <class C>
+__device__ __forceinline__ uint4 pack8(const v4f_t (&a)[C::NT], int s) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int j0 = 8 * s + 2 * e, j1 = j0 + 1;
+    w[e] = pack_bf16x2(a[j0 % C::NT][j0 / C::NT], a[j1 % C::NT][j1 / C::NT]);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Where a tile's results go: bf16 D (d, optional when q is given) and, for
+// the FP8-output form, E4M3 Q with its MN-major 1x128 scales (sd, sd_ld).
+struct TileOut {
+  uint16_t* d;
+  uint8_t* q;
+  float* sd;
+  int64_t sd_ld;
+};
+
+template <class C, bool FP8OUT = false>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
-                                          const float* sb_base, uint16_t* __restrict__ d, int64_t M, int64_t N,
+                                          const float* sb_base, const TileOut& out, int64_t M, int64_t N,
                                           int K, int64_t sa_ld, int64_t m0, int64_t n0) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -340,32 +365,76 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
 
   // Epilogue: lane (li, lg) owns row m0 + wm*TM + 16*mt + li; its values
   // j = 8*s + e (s < NT/2, e < 8) go to column n0 + wn*TN + 32*s + 8*lg + e,
-  // held in acc[mt][j % NT][j / NT].
-  const bool vec = (N % 8) == 0;
+  // held in acc[mt][j % NT][j / NT].  They are rounded to bf16 (RNE) and
+  // packed 8 to a 16-byte word, w[s].
+  uint16_t* __restrict__ d = out.d;
+  if constexpr (!FP8OUT) {
+    const bool vec = (N % 8) == 0;
 #pragma unroll
-  for (int mt = 0; mt < C::MT; mt++) {
-    const int64_t row = m0 + wm * C::TM + 16 * mt + li;
-    if (row >= M) continue;
-    uint16_t* drow = d + row * N;
+    for (int mt = 0; mt < C::MT; mt++) {
+      const int64_t row = m0 + wm * C::TM + 16 * mt + li;
+      if (row >= M) continue;
+      uint16_t* drow = d + row * N;
 #pragma unroll
-    for (int s = 0; s < C::NT / 2; s++) {
-      const int64_t c0 = n0 + wn * C::TN + 32 * s + 8 * lg;
-      if (vec && c0 + 8 <= N) {
-        uint32_t w[4];
+      for (int s = 0; s < C::NT / 2; s++) {
+        const int64_t c0 = n0 + wn * C::TN + 32 * s + 8 * lg;
+        if (vec && c0 + 8 <= N) {
+          *reinterpret_cast<uint4*>(drow + c0) = pack8<C>(acc[mt], s);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int j0 = 8 * s + 2 * e, j1 = j0 + 1;
-          w[e] = pack_bf16x2(acc[mt][j0 % C::NT][j0 / C::NT], acc[mt][j1 % C::NT][j1 / C::NT]);
-        }
-        *reinterpret_cast<uint4*>(drow + c0) = make_uint4(w[0], w[1], w[2], w[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const int j = 8 * s + e;
-          if (c0 + e < N) drow[c0 + e] = (uint16_t)bf16_rne(acc[mt][j % C::NT][j / C::NT]);
+          for (int e = 0; e < 8; e++) {
+            const int j = 8 * s + e;
+            if (c0 + e < N) drow[c0 + e] = (uint16_t)bf16_rne(acc[mt][j % C::NT][j / C::NT]);
+          }
         }
       }
     }
+    return;
+  } else {
+  // FP8 output (N % 128 == 0): the bf16 values above, quantized per 1x128
+  // group of each row exactly as quantize_fp8_groups quantizes a bf16
+  // input -- amax over the group, s = fl32(amax/448) (1 for a zero group),
+  // E4M3(fl32(x / s)) -- so the result equals that call applied to the bf16
+  // output, bit for bit.  A row's group is spread over the four lanes li +
+  // 16 lg of a wave (TN = 128), or of two partner waves wn, wn ^ 1 (TN = 64,
+  // amax exchanged through LDS).
+  uint32_t am[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; mt++) {
+    uint32_t m_ = 0;
+#pragma unroll
+    for (int s = 0; s < C::NT / 2; s++) m_ = max(m_, absmax8_bits(pack8<C>(acc[mt], s)));
+    m_ = max(m_, (uint32_t)__shfl_xor((int)m_, 16));
+    m_ = max(m_, (uint32_t)__shfl_xor((int)m_, 32));
+    am[mt] = m_;
+  }
+  if constexpr (C::TN == 64) {
+    uint32_t* ex = reinterpret_cast<uint32_t*>(lds + C::EPI_OFF);
+    if (lg == 0) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; mt++) ex[wave * C::TM + 16 * mt + li] = am[mt];
+    }
+    __syncthreads();
+    const int partner = wm + C::WAVES_M * (wn ^ 1);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; mt++) am[mt] = max(am[mt], ex[partner * C::TM + 16 * mt + li]);
+  }
+  const int64_t cw = n0 + wn * C::TN;  // first column of this wave
+#pragma unroll
+  for (int mt = 0; mt < C::MT; mt++) {
+    const int64_t row = m0 + wm * C::TM + 16 * mt + li;
+    if (row >= M || cw >= N) continue;
+    const float sc = group_scale(__uint_as_float(am[mt]));
+    const double r = 1.0 / (double)sc;
+#pragma unroll
+    for (int s = 0; s < C::NT / 2; s++) {
+      const int64_t c0 = cw + 32 * s + 8 * lg;
+      const uint4 w = pack8<C>(acc[mt], s);
+      *reinterpret_cast<uint2*>(out.q + row * N + c0) = quantize8(w, r);
+      if (d != nullptr) *reinterpret_cast<uint4*>(d + row * N + c0) = w;
+    }
+    if (lg == 0 && (C::TN == 128 || (wn & 1) == 0)) out.sd[(cw / kGroup) * out.sd_ld + row] = sc;
+  }
   }
 }
 
@@ -386,17 +455,17 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
   tn = r / rows;
 }
 
-template <class C>
+template <class C, bool FP8OUT>
 __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __restrict__ A, const float* __restrict__ SA,
                                                              const uint8_t* __restrict__ B,
-                                                             const float* __restrict__ SB, uint16_t* __restrict__ D,
-                                                             int64_t M, int64_t N, int K, int64_t sa_ld, int tiles_m,
+                                                             const float* __restrict__ SB, TileOut out, int64_t M,
+                                                             int64_t N, int K, int64_t sa_ld, int tiles_m,
                                                              int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-  gemm_tile<C>(lds, A + m0 * K, B + n0 * K, SA, SB, D, M, N, K, sa_ld, m0, n0);
+  gemm_tile<C, FP8OUT>(lds, A + m0 * K, B + n0 * K, SA, SB, out, M, N, K, sa_ld, m0, n0);
 }
 
 // Grouped: every BM-row block lies inside one group (groups start at
@@ -415,7 +484,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_kernel(
   const int g = __builtin_amdgcn_readfirstlane(m_indices[m0]);
   if (g < 0 || g >= num_groups) return;  // padding; uniform across the workgroup, before any barrier
   const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
-  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, D, M, N, K, sa_ld,
+  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, TileOut{D, nullptr, nullptr, 0}, M, N, K, sa_ld,
                m0, n0);
 }
 
@@ -441,7 +510,8 @@ __global__ __launch_bounds__(C::THREADS) void masked_gemm_nt_kernel(
   const int64_t base = (int64_t)g * max_m;
   const int64_t m0 = base + (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
   const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
-  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, D, base + rows, N, K,
+  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB,
+               TileOut{D, nullptr, nullptr, 0}, base + rows, N, K,
                sa_ld, m0, n0);
 }
 
@@ -494,22 +564,28 @@ const char* gemm_kind_name(GemmKind kind) {
 }
 
 template <class C>
-static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb, void* d,
-                              int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
+                              const TileOut& out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const int tiles_m = (int)((m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL(gemm_nt_kernel<C>, dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
-                     static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb,
-                     static_cast<uint16_t*>(d), m, n, (int)k, sa_ld, tiles_m, tiles_n);
+  if (out.q != nullptr)
+    hipLaunchKernelGGL((gemm_nt_kernel<C, true>), dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
+                       static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb, out, m, n, (int)k,
+                       sa_ld, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_nt_kernel<C, false>), dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
+                       static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb, out, m, n, (int)k,
+                       sa_ld, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
                        const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  const TileOut out{static_cast<uint16_t*>(d), nullptr, nullptr, 0};
   switch (plan.kind) {
-    case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
-    case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
-    case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
-    case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmDecode: return launch_decode(plan.split, a, sa, sa_ld, b, sb, d, m, n, k, stream);
   }
   return hipErrorInvalidValue;
@@ -557,6 +633,24 @@ hipError_t launch_masked_gemm(GemmKind kind, const void* a, const float* sa, int
     default:
       return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_fp8out(GemmKind kind, const void* a, const float* sa, int64_t sa_ld, const void* b,
+                              const float* sb, void* q, float* sd, int64_t sd_ld, void* d, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream) {
+  const TileOut out{static_cast<uint16_t*>(d), static_cast<uint8_t*>(q), sd, sd_ld};
+  switch (kind) {
+    case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+GemmKind plan_tiles(int64_t m, int64_t n, int64_t k) {
+  const GemmPlan p = plan_gemm(m > 16 ? m : 17, n, k);
+  return p.kind == kGemmDecode ? kGemmTile128x128 : p.kind;
 }
 
 hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,

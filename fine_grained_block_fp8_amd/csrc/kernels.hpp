@@ -31,6 +31,14 @@ const char* gemm_kind_name(GemmKind kind);
 hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
                        const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+// FP8-output product (n % 128 == 0): q = quantize_groups(bf16(A . B^T)) per
+// 1x128 group of each row with MN-major scales sd [n/128][sd_ld]; d (bf16)
+// optional.  Tile kernels only; plan_tiles gives the tile for any m.
+GemmKind plan_tiles(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_fp8out(GemmKind kind, const void* a, const float* sa, int64_t sa_ld, const void* b,
+                              const float* sb, void* q, float* sd, int64_t sd_ld, void* d, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream);
+
 // Decode-shaped products (M <= 16): K split over ks waves per 16-column slab.
 int decode_split(int64_t n, int64_t k);
 hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,

@@ -107,6 +107,26 @@ int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, 
 int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
                 void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream);
 
+/* Block-scaled product with an FP8 output for the next layer: the bf16
+ * result of fp8_gemm_nt, quantized per 1x128 group of each row exactly as
+ * quantize_fp8_groups quantizes a bf16 input, inside the product's epilogue
+ * (the pages' Blackwell path offers a quantize-to-FP8 epilogue with per-row
+ * output scale factors: deepgemm-rust README, key techniques, "Epilogues";
+ * here at 1x128 granularity with FP32 scales, the activation recipe of the
+ * next linear).  The result is bit-identical to fp8_gemm_nt followed by
+ * quantize_fp8_groups on its output.
+ *
+ * a_e4m3, sa, sa_ld, b_e4m3, sb, m, n, k: as fp8_gemm_nt.
+ * q_e4m3  [m][n] E4M3 output.
+ * sd      [n/128][sd_ld] float32 output, MN-major (the layout of sa, so q and
+ *         sd feed the next fp8_gemm_nt as its A operand).
+ * d_bf16  [m][n] bfloat16 output of the same product, or NULL.
+ * Requirements: as fp8_gemm_nt, plus n % 128 == 0, sd_ld % 4 == 0 and
+ * sd_ld >= m.  Uses the tile kernels for every m (no decode form). */
+int fp8_gemm_nt_fp8_out(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                        void* q_e4m3, float* sd, int64_t sd_ld, void* d_bf16, int64_t m, int64_t n, int64_t k,
+                        void* stream);
+
 /* M-grouped contiguous variant for mixture-of-experts layers (deepgemm-rust
  * README, "What's implemented", m_grouped_fp8_gemm_nt_contiguous row: the
  * tokens of all experts concatenated, 128-row group alignment; "Quick start",

@@ -35,6 +35,7 @@ def test_library_exports_every_declared_function():
         "fgfp8_describe_gemm",
         "fp8_linear_nt",
         "m_grouped_fp8_gemm_nt_masked",
+        "fp8_gemm_nt_fp8_out",
     }
     lib = fg.library()
     for n in names:
@@ -137,6 +138,20 @@ def test_masked_rejects():
     assert call(n=0) == fg.FGFP8_OK
 
 
+def test_fp8_out_rejects():
+    lib = _lib()
+
+    def call(m=8, n=256, k=256, sa_ld=8, sd_ld=8, q=P, sd=P, d=None):
+        return lib.fp8_gemm_nt_fp8_out(P, P, sa_ld, P, P, q, sd, sd_ld, d, m, n, k, None)
+
+    assert call(n=200) == fg.FGFP8_EINVAL
+    assert "multiple of 128" in fg.last_error()
+    assert call(sd_ld=4) == fg.FGFP8_EINVAL
+    assert call(q=None) == fg.FGFP8_EINVAL
+    assert call(d=P + 4) == fg.FGFP8_EINVAL
+    assert call(m=0) == fg.FGFP8_OK
+
+
 def test_linear_rejects():
     lib = _lib()
 
@@ -168,6 +183,7 @@ def test_no_device_is_reported_not_crashed():
     assert lib.m_grouped_fp8_gemm_nt_contiguous(P, P, 128, P, P, P, 2, P, 128, 64, 128, None) == fg.FGFP8_ENODEV
     assert lib.fp8_linear_nt(P, 1, 256, P, P, 128, P, None, None, 0, None) == fg.FGFP8_ENODEV
     assert lib.m_grouped_fp8_gemm_nt_masked(P, P, 256, P, P, P, 4, 64, 32, P, 128, 256, None) == fg.FGFP8_ENODEV
+    assert lib.fp8_gemm_nt_fp8_out(P, P, 8, P, P, P, P, 8, None, 8, 256, 256, None) == fg.FGFP8_ENODEV
 
 
 def test_describe_gemm_plans():

@@ -200,3 +200,52 @@ def test_every_tile_config_prefill_o(tile, monkeypatch):
     q, sa, qb, sb, d = gpu_hot_path(lin)
     rng = np.random.default_rng(7)
     check_sampled(lin, q, sa, qb, sb, d, sample_rows(lin.m, 24, rng), sample_col_blocks(lin.n, 6, rng), f"o {tile}")
+
+
+def test_graph_replays_match_eager():
+    """The calls are legal under HIP graph capture (no allocation, no host
+    synchronisation, no memset nodes): capture the fused decode linear and the
+    quantize + product pair, replay several times with eager work and
+    synchronisations in between, and compare every replay with the eager
+    result bit for bit."""
+    dec = workloads.decode_linear(1, 4096, 12288)
+    big = workloads.random_linear(300, 520, 768, seed=123)
+    xs, ws, outs, eager = [], [], [], []
+    for lin in (dec, big):
+        x = torch.from_numpy(lin.a.view(np.int16)).view(torch.bfloat16).cuda()
+        w = torch.from_numpy(lin.b.view(np.int16)).view(torch.bfloat16).cuda()
+        qb, sb = fg.quantize_fp8_blocks(w)
+        xs.append(x)
+        ws.append((qb, sb))
+    q = torch.empty((big.m, big.k), dtype=torch.float8_e4m3fn, device="cuda")
+    sa = torch.empty((big.k // 128, fg.padded_rows(big.m)), dtype=torch.float32, device="cuda")
+    d_dec = torch.empty((1, dec.n), dtype=torch.bfloat16, device="cuda")
+    d_big = torch.empty((big.m, big.n), dtype=torch.bfloat16, device="cuda")
+
+    def work():
+        fg.fp8_linear_nt(xs[0], ws[0], d_dec)
+        fg.quantize_fp8_groups(xs[1], out=(q, sa))
+        fg.fp8_gemm_nt((q, sa), ws[1], d_big)
+
+    work()
+    torch.cuda.synchronize()
+    ref_dec, ref_big = d_dec.clone(), d_big.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        work()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.synchronize()
+    for i in range(4):
+        d_dec.fill_(float("nan"))
+        d_big.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d_dec.view(torch.int16), ref_dec.view(torch.int16)), f"replay {i}: decode differs"
+        assert torch.equal(d_big.view(torch.int16), ref_big.view(torch.int16)), f"replay {i}: gemm differs"
+        work()  # eager work between replays
+        torch.cuda.synchronize()
