@@ -145,8 +145,9 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if HipEvent._hip is not None and self.ev:
-            HipEvent._hip.hipEventDestroy(self.ev)
+        hip = getattr(HipEvent, "_hip", None) if HipEvent is not None else None
+        if hip is not None and getattr(self, "ev", None):
+            hip.hipEventDestroy(self.ev)
 
 
 class GpuAhead:
