@@ -26,7 +26,8 @@ graph see the same device time).  Also reported:
   timed by graph replay over 8 rotating weight sets so that the weights stream
   from HBM rather than the 256 MB last-level cache;
 * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
-Other --workload values time one shape for profiling: decode (M=1 linears),
+Other --workload values time one shape for profiling: prefill_ue8m0 (the
+same step with power-of-two scales, the matrix cores applying them), decode (M=1 linears),
 moe (contiguous grouped, 32 experts), moe_masked (masked grouped over a
 decode-time dispatch buffer), square8k, square16k, copy (counter calibration).
 """
@@ -53,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "moe", "moe_masked", "square8k", "square16k", "copy"])
+    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "decode", "moe", "moe_masked", "square8k", "square16k", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-reps", type=int, default=50, help="rounds over the 8 weight sets per decode timing")
@@ -73,11 +74,12 @@ class PreparedLinear:
     """Device buffers for one linear: bf16 activation, pre-quantized weight,
     and preallocated outputs (nothing is allocated inside the timed region)."""
 
-    def __init__(self, lin, fg, torch):
+    def __init__(self, lin, fg, torch, ue8m0=False):
         self.lin = lin
+        self.ue8m0 = ue8m0
         self.x = dev_bf16(lin.a, torch)
         w = dev_bf16(lin.b, torch)
-        self.qb, self.sb = fg.quantize_fp8_blocks(w)
+        self.qb, self.sb = fg.quantize_fp8_blocks(w, ue8m0=ue8m0)
         del w
         m, k = lin.m, lin.k
         self.q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device="cuda")
@@ -89,10 +91,10 @@ class PreparedLinear:
     def run(self, fg, ev=None):
         if ev is not None:
             ev[0].record()
-        fg.quantize_fp8_groups(self.x, out=(self.q, self.sa))
+        fg.quantize_fp8_groups(self.x, out=(self.q, self.sa), ue8m0=self.ue8m0)
         if ev is not None:
             ev[1].record()
-        fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d)
+        fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d, ue8m0=self.ue8m0)
         if ev is not None:
             ev[2].record()
 
@@ -185,8 +187,8 @@ def host_enqueue_seconds(fn, torch, reps=3):
     return worst
 
 
-def bench_linears(linears, steps, warmup, fg, torch):
-    preps = [PreparedLinear(l, fg, torch) for l in linears]
+def bench_linears(linears, steps, warmup, fg, torch, ue8m0=False):
+    preps = [PreparedLinear(l, fg, torch, ue8m0) for l in linears]
     torch.cuda.synchronize()
     for _ in range(warmup):
         for p in preps:
@@ -440,9 +442,9 @@ def main():
     if args.workload == "copy":
         copy_calibration(args, torch)
         return
-    if args.workload == "prefill":
+    if args.workload in ("prefill", "prefill_ue8m0"):
         linears = workloads.prefill_linears()
-        workload = "qwen3_8b_prefill_linears_m2048"
+        workload = "qwen3_8b_prefill_linears_m2048" + ("_ue8m0_recipe" if args.workload == "prefill_ue8m0" else "")
     elif args.workload == "decode":
         linears = [workloads.decode_linear(1, 12288, 4096), workloads.decode_linear(1, 4096, 12288)]
         workload = "decode_m1_linears"
@@ -461,7 +463,8 @@ def main():
 
     if linears is not None:
         log(f"workload {workload}: " + ", ".join(f"{l.name} [{fg.describe_gemm(l.m, l.n, l.k)}]" for l in linears))
-        preps, elapsed, per = bench_linears(linears, args.steps, args.warmup, fg, torch)
+        preps, elapsed, per = bench_linears(linears, args.steps, args.warmup, fg, torch,
+                                            ue8m0=args.workload == "prefill_ue8m0")
         total_flops = sum(l.flops for l in linears)
         ms_per_step = elapsed / args.steps * 1e3
         value = total_flops * args.steps / elapsed / 1e12

@@ -47,11 +47,15 @@ _lib.m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp,
 _lib.fp8_linear_nt.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _vp]
 _lib.fp8_gemm_nt_fp8_out.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _fp, _i64, _vp, _i64, _i64, _i64, _vp]
 _lib.m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _i64, _i64, _vp, _i64, _i64, _vp]
+_lib.quantize_fp8_groups_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
+_lib.quantize_fp8_blocks_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
+_lib.fp8_gemm_nt_ue8m0.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
 _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
-              "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm"):
+              "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
+              "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -117,9 +121,10 @@ def padded_rows(m: int) -> int:
     return -(-m // 4) * 4
 
 
-def quantize_fp8_groups(x: torch.Tensor, sa_ld: int | None = None, out=None):
+def quantize_fp8_groups(x: torch.Tensor, sa_ld: int | None = None, out=None, ue8m0: bool = False):
     """Per-(1x128) activation quantization.  x: bf16 [M, K].  Returns
-    (q float8_e4m3fn [M, K], sa float32 [K/128, sa_ld]), sa MN-major."""
+    (q float8_e4m3fn [M, K], sa float32 [K/128, sa_ld]), sa MN-major.
+    ue8m0=True rounds every scale up to a power of two (the UE8M0 recipe)."""
     _need(x, "x", (torch.bfloat16,), 2)
     m, k = x.shape
     sa_ld = padded_rows(m) if sa_ld is None else int(sa_ld)
@@ -132,13 +137,15 @@ def quantize_fp8_groups(x: torch.Tensor, sa_ld: int | None = None, out=None):
         _need(sa, "sa", (torch.float32,), 2)
         if tuple(q.shape) != (m, k) or tuple(sa.shape) != (k // GROUP, sa_ld):
             raise ValueError("output shapes must be q [M, K] and sa [K/128, sa_ld]")
-    _check(_lib.quantize_fp8_groups(_ptr(x), m, k, _ptr(q), _ptr(sa), sa_ld, _stream(x)))
+    fn = _lib.quantize_fp8_groups_ue8m0 if ue8m0 else _lib.quantize_fp8_groups
+    _check(fn(_ptr(x), m, k, _ptr(q), _ptr(sa), sa_ld, _stream(x)))
     return q, sa
 
 
-def quantize_fp8_blocks(w: torch.Tensor, out=None):
+def quantize_fp8_blocks(w: torch.Tensor, out=None, ue8m0: bool = False):
     """Per-(128x128) weight quantization.  w: bf16 [N, K].  Returns
-    (q float8_e4m3fn [N, K], sb float32 [ceil(N/128), K/128])."""
+    (q float8_e4m3fn [N, K], sb float32 [ceil(N/128), K/128]); ue8m0=True:
+    power-of-two scales."""
     _need(w, "w", (torch.bfloat16,), 2)
     n, k = w.shape
     if out is None:
@@ -146,13 +153,15 @@ def quantize_fp8_blocks(w: torch.Tensor, out=None):
         sb = torch.empty((-(-n // GROUP), k // GROUP if k % GROUP == 0 else 0), dtype=torch.float32, device=w.device)
     else:
         q, sb = out
-    _check(_lib.quantize_fp8_blocks(_ptr(w), n, k, _ptr(q), _ptr(sb), _stream(w)))
+    fn = _lib.quantize_fp8_blocks_ue8m0 if ue8m0 else _lib.quantize_fp8_blocks
+    _check(fn(_ptr(w), n, k, _ptr(q), _ptr(sb), _stream(w)))
     return q, sb
 
 
-def fp8_gemm_nt(a, b, d: torch.Tensor) -> torch.Tensor:
+def fp8_gemm_nt(a, b, d: torch.Tensor, ue8m0: bool = False) -> torch.Tensor:
     """d[M, N] (bf16, written in place) = A . B^T with A = (q [M, K], sa
-    [K/128, sa_ld]) and B = (q [N, K], sb [ceil(N/128), K/128])."""
+    [K/128, sa_ld]) and B = (q [N, K], sb [ceil(N/128), K/128]).  ue8m0=True
+    runs fp8_gemm_nt_ue8m0 (every scale must be a power of two)."""
     (qa, sa), (qb, sb) = a, b
     _need(qa, "a", _FP8, 2)
     _need(qb, "b", _FP8, 2)
@@ -167,7 +176,8 @@ def fp8_gemm_nt(a, b, d: torch.Tensor) -> torch.Tensor:
         raise ValueError(f"d must be [{m}, {n}]")
     if k % GROUP == 0 and (sa.shape[0] != k // GROUP or tuple(sb.shape) != (-(-n // GROUP), k // GROUP)):
         raise ValueError("scale shapes must be sa [K/128, sa_ld] and sb [ceil(N/128), K/128]")
-    _check(_lib.fp8_gemm_nt(_ptr(qa), _ptr(sa), sa.shape[1], _ptr(qb), _ptr(sb), _ptr(d), m, n, k, _stream(d)))
+    fn = _lib.fp8_gemm_nt_ue8m0 if ue8m0 else _lib.fp8_gemm_nt
+    _check(fn(_ptr(qa), _ptr(sa), sa.shape[1], _ptr(qb), _ptr(sb), _ptr(d), m, n, k, _stream(d)))
     return d
 
 

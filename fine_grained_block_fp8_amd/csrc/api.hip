@@ -94,9 +94,10 @@ extern "C" {
 
 const char* fgfp8_last_error(void) { return g_last_error.c_str(); }
 
-int quantize_fp8_groups(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, float* sa, int64_t sa_ld,
-                        void* stream) {
-  const char* who = "quantize_fp8_groups";
+namespace {
+
+int quantize_groups_impl(const char* who, bool ue8m0, const void* x_bf16, int64_t m, int64_t k, void* q_e4m3,
+                         float* sa, int64_t sa_ld, void* stream) {
   if (m < 0 || m >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m=%lld out of range", who, (long long)m);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, m, k, sa_ld)) return rc;
@@ -105,11 +106,11 @@ int quantize_fp8_groups(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, 
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
   if (m == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
-  return launched(fgfp8::launch_quantize_groups(x_bf16, m, k, q_e4m3, sa, sa_ld, (hipStream_t)stream), who);
+  return launched(fgfp8::launch_quantize_groups(x_bf16, m, k, q_e4m3, sa, sa_ld, (hipStream_t)stream, ue8m0), who);
 }
 
-int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, float* sb, void* stream) {
-  const char* who = "quantize_fp8_blocks";
+int quantize_blocks_impl(const char* who, bool ue8m0, const void* w_bf16, int64_t n, int64_t k, void* q_e4m3,
+                         float* sb, void* stream) {
   if (n < 0 || (n + 127) / 128 > 65535) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);
   if (int rc = check_k(who, k)) return rc;
   if (!w_bf16 || !q_e4m3 || !sb) return fail(FGFP8_EINVAL, "%s: null pointer", who);
@@ -117,12 +118,11 @@ int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, 
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
   if (n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
-  return launched(fgfp8::launch_quantize_blocks(w_bf16, n, k, q_e4m3, sb, (hipStream_t)stream), who);
+  return launched(fgfp8::launch_quantize_blocks(w_bf16, n, k, q_e4m3, sb, (hipStream_t)stream, ue8m0), who);
 }
 
-int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
-                void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
-  const char* who = "fp8_gemm_nt";
+int gemm_impl(const char* who, bool ue8m0, const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3,
+              const float* sb, void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
   if (m < 0 || m >= kMaxRows || n < 0 || n >= kMaxRows)
     return fail(FGFP8_EINVAL, "%s: m=%lld n=%lld out of range", who, (long long)m, (long long)n);
   if (int rc = check_k(who, k)) return rc;
@@ -134,10 +134,42 @@ int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* 
   if (int rc = check_device(who)) return rc;
   const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
   if (env_flag("FGFP8_PRINT_CONFIG"))
-    fprintf(stderr, "[fgfp8] fp8_gemm_nt m=%lld n=%lld k=%lld: %s split=%d\n", (long long)m, (long long)n,
-            (long long)k, fgfp8::gemm_kind_name(plan.kind), plan.split);
-  return launched(fgfp8::launch_gemm(plan, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, (hipStream_t)stream),
+    fprintf(stderr, "[fgfp8] %s m=%lld n=%lld k=%lld: %s split=%d\n", who, (long long)m, (long long)n, (long long)k,
+            fgfp8::gemm_kind_name(plan.kind), plan.split);
+  const hipStream_t st = (hipStream_t)stream;
+  return launched(ue8m0 ? fgfp8::launch_gemm_ue8m0(plan, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, st)
+                        : fgfp8::launch_gemm(plan, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, st),
                   who);
+}
+
+}  // namespace
+
+int quantize_fp8_groups(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, float* sa, int64_t sa_ld,
+                        void* stream) {
+  return quantize_groups_impl("quantize_fp8_groups", false, x_bf16, m, k, q_e4m3, sa, sa_ld, stream);
+}
+
+int quantize_fp8_groups_ue8m0(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, float* sa, int64_t sa_ld,
+                              void* stream) {
+  return quantize_groups_impl("quantize_fp8_groups_ue8m0", true, x_bf16, m, k, q_e4m3, sa, sa_ld, stream);
+}
+
+int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, float* sb, void* stream) {
+  return quantize_blocks_impl("quantize_fp8_blocks", false, w_bf16, n, k, q_e4m3, sb, stream);
+}
+
+int quantize_fp8_blocks_ue8m0(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, float* sb, void* stream) {
+  return quantize_blocks_impl("quantize_fp8_blocks_ue8m0", true, w_bf16, n, k, q_e4m3, sb, stream);
+}
+
+int fp8_gemm_nt_ue8m0(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                      void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
+  return gemm_impl("fp8_gemm_nt_ue8m0", true, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, stream);
+}
+
+int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
+  return gemm_impl("fp8_gemm_nt", false, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, stream);
 }
 
 int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* m_indices,

@@ -58,6 +58,27 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
 // rounded float division), or 1 for an all-zero group.
 __device__ __forceinline__ float group_scale(float amax) { return amax == 0.0f ? 1.0f : amax / kE4m3Max; }
 
+// Power-of-two (UE8M0) scale: group_scale rounded up to the next power of
+// two, within the E8M0 range [2^-127, 2^127].  2^-127 is the float32
+// subnormal 0x00400000, so its exponent field (0) is again the E8M0 code.
+__device__ __forceinline__ float group_scale_ue8m0(float amax) {
+  const uint32_t b = __float_as_uint(group_scale(amax));
+  const uint32_t e = b >> 23, man = b & 0x7fffffu;
+  uint32_t out;
+  if (e == 0) {
+    out = man <= 0x400000u ? 0x400000u : 0x800000u;  // (0, 2^-127] -> 2^-127, (2^-127, 2^-126) -> 2^-126
+  } else {
+    uint32_t f = e + (man != 0u ? 1u : 0u);
+    if (f > 254u) f = 254u;
+    out = f << 23;
+  }
+  return __uint_as_float(out);
+}
+
+// The E8M0 code of a power-of-two float32 scale (its exponent field; the
+// mantissa of a non-power-of-two is ignored).
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
+
 // fl32(x / s) for every float32 x given r = 1/s in double.  x * r carries a
 // relative error below 2^-52, while a float32 quotient x/s with a normal
 // result is never within 2^-49 (relative) of a float32 rounding boundary

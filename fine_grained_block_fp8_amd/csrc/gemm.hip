@@ -273,6 +273,48 @@ __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& b
   promote(acc[C::MT - 1][T1 - 1], part[(N_MFMA - 1) & 1], sc[C::MT - 1]);
 }
 
+// UE8M0 recipe: with power-of-two scales the scaling is exact, so the
+// matrix core applies it -- v_mfma_scale takes one E8M0 exponent per operand
+// row and 32-wide K block (lane l supplies row l % 16, block l / 16, which is
+// the lane's own fragment), and the product accumulates across chunks in the
+// MFMA accumulator itself: acc = MFMA(B, A, acc) * 2^(eb + ea), with no FP32
+// promotion.  Per chunk, a lane's A exponent is that of its row's scale and
+// the B exponent that of the wave's column block (uniform).
+template <class C>
+__device__ __forceinline__ void read_a_ue8m0(const uint8_t* lds, const FragAddr& aa, uint32_t sa_addr,
+                                             uint32_t sb_addr, int stage, v8i_t (&af)[C::MT], int (&ea)[C::MT],
+                                             int& eb) {
+  eb = e8m0_of(*reinterpret_cast<const float*>(lds + sb_addr + stage * C::S_BYTES));
+#pragma unroll
+  for (int mt = 0; mt < C::MT; mt++) {
+    af[mt] = read_frag(lds, aa, (uint32_t)(stage * C::A_BYTES + 2048 * mt));
+    ea[mt] = e8m0_of(*reinterpret_cast<const float*>(lds + sa_addr + stage * C::S_BYTES + 64 * mt));
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_tiles_ue8m0(const uint8_t* lds, const FragAddr& ba, int stage, int load_stage,
+                                                 const v8i_t (&af)[C::MT], const int (&ea)[C::MT], int eb,
+                                                 v4f_t (&acc)[C::MT][C::NT], const StageLoader<C>& ld, int next_kb) {
+  constexpr int NL = StageLoader<C>::NSEG, HALF = C::NT / 2 > 0 ? C::NT / 2 : 1;
+  constexpr int PER = (NL + HALF - 1) / HALF;
+  constexpr int N_MFMA = C::NT * C::MT;
+  v8i_t bfr[2];
+  bfr[0] = read_b<C>(lds, ba, stage, 0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; i++) {
+    const int u = i / C::MT, mt = i % C::MT;
+    if (mt == 0) {
+#pragma unroll
+      for (int q = 0; q < PER; q++)
+        if (u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
+      if (u + 1 < C::NT) bfr[(u + 1) & 1] = read_b<C>(lds, ba, stage, u + 1);
+    }
+    acc[mt][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[u & 1], af[mt], acc[mt][u], 0, 0, 0, eb, 0,
+                                                                  ea[mt]);
+  }
+}
+
 // The 8 values of epilogue slot s of an MFMA row tile, rounded to bf16 and
 // packed in column order (see the epilogue).
 template <class C>
@@ -295,7 +337,7 @@ struct TileOut {
   int64_t sd_ld;
 };
 
-template <class C, bool FP8OUT = false>
+template <class C, bool FP8OUT = false, bool UE8M0 = false>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
                                           const float* sb_base, const TileOut& out, int64_t M, int64_t N,
                                           int K, int64_t sa_ld, int64_t m0, int64_t n0) {
@@ -357,8 +399,14 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
     }
     barrier_no_fence();
     if (wave < 2) loader.issue(StageLoader<C>::NSEG, load_stage, next);  // scales
-    read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
-    mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, load_stage, af, sc, nullptr, acc, loader, next);
+    if constexpr (UE8M0) {
+      int ea[C::MT], eb;
+      read_a_ue8m0<C>(lds, aa, sa_addr, sb_addr, stage, af, ea, eb);
+      mfma_tiles_ue8m0<C>(lds, ba, stage, load_stage, af, ea, eb, acc, loader, next);
+    } else {
+      read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
+      mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, load_stage, af, sc, nullptr, acc, loader, next);
+    }
     stage = stage + 1 == C::STAGES ? 0 : stage + 1;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
@@ -455,7 +503,7 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
   tn = r / rows;
 }
 
-template <class C, bool FP8OUT>
+template <class C, bool FP8OUT, bool UE8M0>
 __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __restrict__ A, const float* __restrict__ SA,
                                                              const uint8_t* __restrict__ B,
                                                              const float* __restrict__ SB, TileOut out, int64_t M,
@@ -465,7 +513,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __re
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-  gemm_tile<C, FP8OUT>(lds, A + m0 * K, B + n0 * K, SA, SB, out, M, N, K, sa_ld, m0, n0);
+  gemm_tile<C, FP8OUT, UE8M0>(lds, A + m0 * K, B + n0 * K, SA, SB, out, M, N, K, sa_ld, m0, n0);
 }
 
 // Grouped: every BM-row block lies inside one group (groups start at
@@ -565,15 +613,19 @@ const char* gemm_kind_name(GemmKind kind) {
 
 template <class C>
 static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
-                              const TileOut& out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+                              const TileOut& out, int64_t m, int64_t n, int64_t k, hipStream_t stream,
+                              bool ue8m0 = false) {
   const int tiles_m = (int)((m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
-  if (out.q != nullptr)
-    hipLaunchKernelGGL((gemm_nt_kernel<C, true>), dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
-                       static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb, out, m, n, (int)k,
+  const dim3 grid((uint32_t)tiles_m * tiles_n), block(C::THREADS);
+  const uint8_t *pa = static_cast<const uint8_t*>(a), *pb = static_cast<const uint8_t*>(b);
+  if (ue8m0)
+    hipLaunchKernelGGL((gemm_nt_kernel<C, false, true>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
+                       sa_ld, tiles_m, tiles_n);
+  else if (out.q != nullptr)
+    hipLaunchKernelGGL((gemm_nt_kernel<C, true, false>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
                        sa_ld, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((gemm_nt_kernel<C, false>), dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
-                       static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb, out, m, n, (int)k,
+    hipLaunchKernelGGL((gemm_nt_kernel<C, false, false>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
                        sa_ld, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -646,6 +698,20 @@ hipError_t launch_gemm_fp8out(GemmKind kind, const void* a, const float* sa, int
     case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_ue8m0(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
+                             const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  const TileOut out{static_cast<uint16_t*>(d), nullptr, nullptr, 0};
+  switch (plan.kind) {
+    case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
+    case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
+    case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
+    case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
+    // decode shapes: the promote path is exact for power-of-two scales
+    case kGemmDecode: return launch_decode(plan.split, a, sa, sa_ld, b, sb, d, m, n, k, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 GemmKind plan_tiles(int64_t m, int64_t n, int64_t k) {

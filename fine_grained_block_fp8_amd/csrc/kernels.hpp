@@ -8,8 +8,9 @@
 namespace fgfp8 {
 
 hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, float* sa, int64_t sa_ld,
-                                  hipStream_t stream);
-hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream);
+                                  hipStream_t stream, bool ue8m0 = false);
+hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream,
+                                  bool ue8m0 = false);
 
 // Kernel configurations of the dense product.
 enum GemmKind : int {
@@ -30,6 +31,12 @@ const char* gemm_kind_name(GemmKind kind);
 
 hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
                        const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+// UE8M0 recipe (every scale a power of two): the tile kernels let the matrix
+// core apply the scales and accumulate across chunks (no FP32 promotion);
+// decode shapes use the decode kernel, exact for such scales.
+hipError_t launch_gemm_ue8m0(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
+                             const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
 // FP8-output product (n % 128 == 0): q = quantize_groups(bf16(A . B^T)) per
 // 1x128 group of each row with MN-major scales sd [n/128][sd_ld]; d (bf16)

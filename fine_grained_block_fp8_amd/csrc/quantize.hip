@@ -6,7 +6,9 @@
 // 128 inputs of a row rounded to FP8 with a scale of their own, the scales
 // stored column by column with rows padded to a multiple of four (Linnet
 // "Backend plugins" page, plugin module docstring).  Scale s = fl32(amax/448),
-// 1 for an all-zero group; element code = E4M3_RNE(fl32(x / s)).
+// 1 for an all-zero group; element code = E4M3_RNE(fl32(x / s)).  The UE8M0
+// variants round s up to a power of two (the Blackwell path's UE8M0 scale
+// factors, deepgemm-rust README key techniques) and are otherwise the same.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -26,6 +28,7 @@ namespace fgfp8 {
 // byte out per element.
 constexpr int kQgWaves = 4;
 
+template <bool UE8M0>
 __global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const uint16_t* __restrict__ x,
                                                                          uint8_t* __restrict__ q,
                                                                          float* __restrict__ sa, int64_t m, int64_t k,
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const ui
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const uint32_t amax_bits = row16_max_u32(absmax8_bits(v[i]));
-    s[i] = group_scale(__uint_as_float(amax_bits));
+    s[i] = UE8M0 ? group_scale_ue8m0(__uint_as_float(amax_bits)) : group_scale(__uint_as_float(amax_bits));
     const double r = 1.0 / (double)s[i];
     const uint2 o = quantize8(v[i], r);
     if (g_ok && r0 + i < m) *reinterpret_cast<uint2*>(q + (r0 + i) * k + col) = o;
@@ -64,13 +67,17 @@ __global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const ui
 }
 
 hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, float* sa, int64_t sa_ld,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, bool ue8m0) {
   const int64_t row_blocks = (m + 3) / 4;
   const int64_t group_quads = (k / kGroup + 3) / 4;
   const int64_t total = row_blocks * group_quads;
   const int64_t blocks = (total + kQgWaves - 1) / kQgWaves;
-  hipLaunchKernelGGL(quantize_groups_kernel, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total);
+  if (ue8m0)
+    hipLaunchKernelGGL(quantize_groups_kernel<true>, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total);
+  else
+    hipLaunchKernelGGL(quantize_groups_kernel<false>, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total);
   return hipGetLastError();
 }
 
@@ -78,6 +85,7 @@ hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, 
 // One workgroup per 128x128 block: thread t owns 64 elements of row t/2; the
 // block amax is a wave shuffle reduction followed by an LDS combine across the
 // four waves.  Offline (weights are quantized once), so simplicity wins.
+template <bool UE8M0>
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ q,
                                                               float* __restrict__ sb, int64_t n, int64_t k) {
   __shared__ uint32_t red[4];
@@ -98,7 +106,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(const uint16_t* __
   if ((t & 63) == 0) red[t >> 6] = am;
   __syncthreads();
   am = max(max(red[0], red[1]), max(red[2], red[3]));
-  const float s = group_scale(__uint_as_float(am));
+  const float s = UE8M0 ? group_scale_ue8m0(__uint_as_float(am)) : group_scale(__uint_as_float(am));
   const double r = 1.0 / (double)s;
   if (valid) {
 #pragma unroll
@@ -110,10 +118,15 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(const uint16_t* __
   if (t == 0) sb[nb * (k / kGroup) + kb] = s;
 }
 
-hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream) {
+hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream,
+                                  bool ue8m0) {
   const int64_t nbk = k / kGroup, nbn = (n + kGroup - 1) / kGroup;
-  hipLaunchKernelGGL(quantize_blocks_kernel, dim3((uint32_t)nbk, (uint32_t)nbn), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(w), static_cast<uint8_t*>(q), sb, n, k);
+  if (ue8m0)
+    hipLaunchKernelGGL(quantize_blocks_kernel<true>, dim3((uint32_t)nbk, (uint32_t)nbn), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(w), static_cast<uint8_t*>(q), sb, n, k);
+  else
+    hipLaunchKernelGGL(quantize_blocks_kernel<false>, dim3((uint32_t)nbk, (uint32_t)nbn), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(w), static_cast<uint8_t*>(q), sb, n, k);
   return hipGetLastError();
 }
 

@@ -198,6 +198,24 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
 int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, const float* sb, int64_t n,
                   void* d_bf16, void* q_e4m3, float* sa, int64_t sa_ld, void* stream);
 
+/* UE8M0 recipe: power-of-two scales (the Blackwell path of the pages keeps
+ * its scale factors as UE8M0 powers of two and bridges FP32 scales to them:
+ * deepgemm-rust README, key techniques and the note on the SM100 device API).
+ * A different recipe from the calls above -- each scale is fl32(amax/448)
+ * rounded up to a power of two within [2^-127, 2^127] (1 for a zero group),
+ * the element E4M3(x / s) -- with the same layouts and requirements.
+ * quantize_fp8_groups_ue8m0 / quantize_fp8_blocks_ue8m0: as the FP32-scale
+ * quantizers.  fp8_gemm_nt_ue8m0: as fp8_gemm_nt, for operands whose every
+ * scale is such a power of two (only the exponent field of each scale is
+ * read); the matrix cores apply the scales and accumulate across the K
+ * chunks, so no FP32 promotion is needed.  Results agree with fp8_gemm_nt on
+ * the same operands up to FP32 summation order. */
+int quantize_fp8_groups_ue8m0(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, float* sa, int64_t sa_ld,
+                              void* stream);
+int quantize_fp8_blocks_ue8m0(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, float* sb, void* stream);
+int fp8_gemm_nt_ue8m0(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                      void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream);
+
 /* Message for the most recent non-zero status returned on the calling thread
  * (thread-local; the pointer stays valid until the next failing call on that
  * thread).  Returns "" if no call has failed. */

@@ -18,6 +18,9 @@ What it computes, and where the pages define it:
                 quantization with FP32 scales = amax / 448 (deepgemm-rust README,
                 "What's implemented" table, fp8_gemm_nt row; Linnet page, module
                 docstring of the DeepGEMM plugin source).
+                The UE8M0 variants round each scale up to a power of two
+                (deepgemm-rust README, Blackwell key techniques: UE8M0 scale
+                factors; FP32 scales bridged to packed UE8M0).
 * ``gemm``      the block-scaled product D = A.B^T with both scale sets applied
                 once per 128-wide K chunk, in FP64, and its M-grouped contiguous
                 variant (deepgemm-rust README, "What's implemented" table and
@@ -40,7 +43,7 @@ from .gemm import (
     masked_grouped_gemm_nt,
     round_to_bf16,
 )
-from .quantize import GROUP, quantize_blocks, quantize_groups
+from .quantize import GROUP, quantize_blocks, quantize_blocks_ue8m0, quantize_groups, quantize_groups_ue8m0
 
 __all__ = [
     "E4M3_MAX",
@@ -54,5 +57,7 @@ __all__ = [
     "masked_grouped_gemm_nt",
     "quantize_blocks",
     "quantize_groups",
+    "quantize_groups_ue8m0",
+    "quantize_blocks_ue8m0",
     "round_to_bf16",
 ]

@@ -95,3 +95,58 @@ def quantize_blocks(w_bf16: np.ndarray):
             sb[i, j] = s
             q[rows, cols] = e4m3_encode((block / s).astype(np.float32))
     return q, sb
+
+
+def _scale_of_ue8m0(amax: np.ndarray) -> np.ndarray:
+    """Power-of-two (UE8M0) scale: the FP32 scale fl32(amax/448) (1 for a zero
+    group) rounded up to a power of two, 2^ceil(log2 s), kept within the E8M0
+    range [2^-127, 2^127]."""
+    s32 = _scale_of(amax).astype(np.float64)
+    f, e = np.frexp(s32)  # s32 = f * 2^e, f in [0.5, 1)
+    e = np.where(f == 0.5, e - 1, e)  # exact powers of two stay
+    e = np.clip(e, -127, 127)
+    return np.ldexp(1.0, e).astype(np.float32)
+
+
+def quantize_groups_ue8m0(x_bf16: np.ndarray, sa_ld: int | None = None):
+    """quantize_groups with power-of-two scales (the UE8M0 recipe of the
+    Blackwell path: deepgemm-rust README, key techniques, scale factors as
+    UE8M0 powers of two; and its note that FP32 scales are bridged to packed
+    UE8M0).  The element is y = x / s (exact for a power of two unless it
+    underflows float32), then E4M3; scales stay float32 values, powers of two."""
+    x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
+    m, k = x_bf16.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    if sa_ld is None:
+        sa_ld = -(-m // 4) * 4
+    x = bf16_bits_to_f32(x_bf16).reshape(m, k // GROUP, GROUP)
+    amax = np.max(np.abs(x), axis=2) if m else np.zeros((0, k // GROUP), np.float32)
+    s = _scale_of_ue8m0(amax)
+    y = (x / s[:, :, None]).astype(np.float32)
+    q = e4m3_encode(y).reshape(m, k)
+    sa = np.full((k // GROUP, sa_ld), np.nan, dtype=np.float32)
+    sa[:, :m] = s.T
+    return q, sa
+
+
+def quantize_blocks_ue8m0(w_bf16: np.ndarray):
+    """quantize_blocks with power-of-two (UE8M0) scales."""
+    w_bf16 = np.asarray(w_bf16, dtype=np.uint16)
+    n, k = w_bf16.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    w = bf16_bits_to_f32(w_bf16)
+    nb, kb = -(-n // GROUP), k // GROUP
+    q = np.empty((n, k), dtype=np.uint8)
+    sb = np.empty((nb, kb), dtype=np.float32)
+    for i in range(nb):
+        rows = slice(i * GROUP, min(n, (i + 1) * GROUP))
+        for j in range(kb):
+            cols = slice(j * GROUP, (j + 1) * GROUP)
+            block = w[rows, cols]
+            s = _scale_of_ue8m0(np.max(np.abs(block)))
+            sb[i, j] = s
+            q[rows, cols] = e4m3_encode((block / s).astype(np.float32))
+    return q, sb
+

@@ -106,12 +106,14 @@ def block_rows(n: int, cblocks: np.ndarray) -> np.ndarray:
     return np.concatenate([np.arange(c * 128, min(n, c * 128 + 128)) for c in cblocks])
 
 
-def check_sampled(lin, q, sa, qb, sb, d, rows, cblocks, label=""):
+def check_sampled(lin, q, sa, qb, sb, d, rows, cblocks, label="", quantizers=None):
     """Oracle on a sample: rows of A (row-independent quantization) and whole
-    128-row blocks of B (so the oracle's blocks are the GPU's blocks)."""
+    128-row blocks of B (so the oracle's blocks are the GPU's blocks).
+    quantizers: the oracle's (groups, blocks) pair, FP32-scale by default."""
+    qg, qbk = quantizers or (oracle.quantize_groups, oracle.quantize_blocks)
     cols = block_rows(lin.n, cblocks)
-    oq, osa = oracle.quantize_groups(lin.a[rows])
-    oqb, osb = oracle.quantize_blocks(lin.b[cols])
+    oq, osa = qg(lin.a[rows])
+    oqb, osb = qbk(lin.b[cols])
     ri = torch.as_tensor(rows, device=d.device)
     ci = torch.as_tensor(cols, device=d.device)
     assert np.array_equal(codes(q.view(torch.uint8).index_select(0, ri)), oq), f"{label}: activation codes differ"

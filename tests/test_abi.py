@@ -36,6 +36,9 @@ def test_library_exports_every_declared_function():
         "fp8_linear_nt",
         "m_grouped_fp8_gemm_nt_masked",
         "fp8_gemm_nt_fp8_out",
+        "quantize_fp8_groups_ue8m0",
+        "quantize_fp8_blocks_ue8m0",
+        "fp8_gemm_nt_ue8m0",
     }
     lib = fg.library()
     for n in names:
@@ -79,6 +82,16 @@ def test_quantize_groups_rejects(args, needle):
     rc = _lib().quantize_fp8_groups(*args)
     assert rc == fg.FGFP8_EINVAL
     assert needle in fg.last_error()
+
+
+def test_ue8m0_calls_validate_like_the_fp32_ones():
+    lib = _lib()
+    assert lib.quantize_fp8_groups_ue8m0(P, 4, 100, P, P, 4, None) == fg.FGFP8_EINVAL
+    assert "multiple of 128" in fg.last_error()
+    assert lib.quantize_fp8_blocks_ue8m0(P, 10, 128, None, P, None) == fg.FGFP8_EINVAL
+    assert lib.fp8_gemm_nt_ue8m0(P, P, 6, P, P, P, 8, 16, 256, None) == fg.FGFP8_EINVAL
+    assert "fp8_gemm_nt_ue8m0" in fg.last_error()
+    assert lib.fp8_gemm_nt_ue8m0(P, P, 8, P, P, P, 0, 16, 256, None) == fg.FGFP8_OK
 
 
 def test_quantize_blocks_rejects():

@@ -196,3 +196,79 @@ def test_rejects_k_not_multiple_of_128():
         oracle.quantize_groups(np.zeros((2, 100), np.uint16))
     with pytest.raises(ValueError):
         oracle.quantize_blocks(np.zeros((2, 100), np.uint16))
+
+
+# ------------------------------------------------------------- UE8M0 scales
+def exact_group_ue8m0(xs):
+    """Power-of-two scale and codes with exact rationals: s32 = RN32(amax/448)
+    (1 if amax == 0), s = the least power of two >= s32 within [2^-127, 2^127];
+    code_i = E4M3(RN32(x_i / s))."""
+    amax = max(abs(f32_fraction(x)) for x in xs)
+    s32 = Fraction(1) if amax == 0 else to_f32(amax / 448)
+    s = Fraction(2) ** -127
+    while s < s32 and s < Fraction(2) ** 127:
+        s *= 2
+    codes = [e4m3_code(to_f32(f32_fraction(x) / s), bool(np.signbit(x))) for x in xs]
+    return s, codes
+
+
+def test_ue8m0_random_groups_match_exact_rationals():
+    rng = np.random.default_rng(111)
+    for trial in range(40):
+        scale = float(2.0 ** rng.integers(-40, 40))
+        x = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32) * np.float32(scale)))
+        q, sa = oracle.quantize_groups_ue8m0(workloads.f32_to_bf16_bits(x)[None, :])
+        s, codes = exact_group_ue8m0(x)
+        assert Fraction(float(sa[0, 0])) == s
+        assert list(q[0]) == codes
+
+
+def test_ue8m0_subnormal_and_zero_groups():
+    rng = np.random.default_rng(112)
+    mags = rng.integers(0, 128, size=128).astype(np.float64) * 2.0**-133
+    x = (mags * np.where(rng.random(128) < 0.5, -1.0, 1.0)).astype(np.float32)
+    q, sa = oracle.quantize_groups_ue8m0(bf16(x)[None, :])
+    s, codes = exact_group_ue8m0(x)
+    assert Fraction(float(sa[0, 0])) == s == Fraction(2) ** -127  # clamped to the E8M0 minimum
+    assert list(q[0]) == codes
+    q0, s0 = oracle.quantize_groups_ue8m0(np.zeros((1, 128), np.uint16))
+    assert s0[0, 0] == 1.0 and not q0.any()
+
+
+@pytest.mark.parametrize("j", [-20, 0, 7])
+def test_ue8m0_equals_fp32_recipe_when_the_scale_is_a_power_of_two(j):
+    """With amax = 448 * 2^j the FP32 scale is already 2^j: both recipes agree."""
+    rng = np.random.default_rng(200 + j)
+    t = oracle.e4m3_table()
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = rng.choice(finite, size=(4, 128))
+    codes[:, 5] = 0x7E
+    x = (t[codes] * 2.0**j).astype(np.float32)
+    q1, s1 = oracle.quantize_groups(bf16(x))
+    q2, s2 = oracle.quantize_groups_ue8m0(bf16(x))
+    assert np.array_equal(q1, q2) and np.array_equal(s1[:, :4], s2[:, :4])
+
+
+def test_ue8m0_scales_are_powers_of_two_bounding_amax():
+    (lin,) = workloads.prefill_linears(names=["o"])
+    q, sa = oracle.quantize_groups_ue8m0(lin.a[:64])
+    s = sa[:, :64].astype(np.float64)
+    mant, _ = np.frexp(s)
+    assert np.all(mant == 0.5), "scales must be powers of two"
+    x = workloads.bf16_bits_to_f32(lin.a[:64]).reshape(64, -1, 128)
+    amax = np.abs(x).max(axis=2).T.astype(np.float64)
+    assert np.all(amax / 448 <= s * (1 + 2.0**-23)) and np.all(s < 2 * amax / 448 * (1 + 2.0**-23))
+
+
+def test_ue8m0_blocks_match_exact_rationals():
+    rng = np.random.default_rng(113)
+    w = (rng.standard_normal((130, 256)) * 0.02).astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(w)
+    q, sb = oracle.quantize_blocks_ue8m0(bits)
+    wf = workloads.bf16_bits_to_f32(bits)
+    for i, rows in enumerate([slice(0, 128), slice(128, 130)]):
+        for j in range(2):
+            block = wf[rows, j * 128 : (j + 1) * 128]
+            s, codes = exact_group_ue8m0(block.ravel())
+            assert Fraction(float(sb[i, j])) == s
+            assert list(q[rows, j * 128 : (j + 1) * 128].ravel()) == codes
