@@ -337,10 +337,18 @@ struct TileOut {
   int64_t sd_ld;
 };
 
+// The bf16 output is a separate __restrict__ parameter (d == out.d): inlining
+// a function with a noalias pointer argument tags every memory access of the
+// tile body with alias metadata, and without any such metadata the
+// wait-count pass treats each LDS read as a possible reader of every
+// in-flight global->LDS copy and drains all of them (vmcnt(0)) before it,
+// which serialises the K pipeline.  The pipeline orders those copies before
+// the reads itself (explicit vmcnt waits and a barrier per K block).  The
+// codegen test checks the count of full drains per kernel.
 template <class C, bool FP8OUT = false, bool UE8M0 = false>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
-                                          const float* sb_base, const TileOut& out, int64_t M, int64_t N,
-                                          int K, int64_t sa_ld, int64_t m0, int64_t n0) {
+                                          const float* sb_base, uint16_t* __restrict__ d, const TileOut& out,
+                                          int64_t M, int64_t N, int K, int64_t sa_ld, int64_t m0, int64_t n0) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
@@ -415,7 +423,6 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   // j = 8*s + e (s < NT/2, e < 8) go to column n0 + wn*TN + 32*s + 8*lg + e,
   // held in acc[mt][j % NT][j / NT].  They are rounded to bf16 (RNE) and
   // packed 8 to a 16-byte word, w[s].
-  uint16_t* __restrict__ d = out.d;
   if constexpr (!FP8OUT) {
     const bool vec = (N % 8) == 0;
 #pragma unroll
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __re
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-  gemm_tile<C, FP8OUT, UE8M0>(lds, A + m0 * K, B + n0 * K, SA, SB, out, M, N, K, sa_ld, m0, n0);
+  gemm_tile<C, FP8OUT, UE8M0>(lds, A + m0 * K, B + n0 * K, SA, SB, out.d, out, M, N, K, sa_ld, m0, n0);
 }
 
 // Grouped: every BM-row block lies inside one group (groups start at
@@ -532,8 +539,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_kernel(
   const int g = __builtin_amdgcn_readfirstlane(m_indices[m0]);
   if (g < 0 || g >= num_groups) return;  // padding; uniform across the workgroup, before any barrier
   const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
-  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, TileOut{D, nullptr, nullptr, 0}, M, N, K, sa_ld,
-               m0, n0);
+  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, D,
+               TileOut{D, nullptr, nullptr, 0}, M, N, K, sa_ld, m0, n0);
 }
 
 // Masked: group g owns rows [g*max_m, g*max_m + max_m) of A and D (a
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(C::THREADS) void masked_gemm_nt_kernel(
   const int64_t base = (int64_t)g * max_m;
   const int64_t m0 = base + (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
   const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
-  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB,
+  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, D,
                TileOut{D, nullptr, nullptr, 0}, base + rows, N, K,
                sa_ld, m0, n0);
 }
