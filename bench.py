@@ -29,7 +29,9 @@ graph see the same device time).  Also reported:
 Other --workload values time one shape for profiling: prefill_ue8m0 (the
 same step with power-of-two scales, the matrix cores applying them), decode (M=1 linears),
 moe (contiguous grouped, 32 experts), moe_masked (masked grouped over a
-decode-time dispatch buffer), square8k, square16k, copy (counter calibration).
+decode-time dispatch buffer), moe_layer (the whole MoE layer: routing, gather,
+two grouped products, SiLU-times-up and combine, 8192 tokens top-4 over 32
+experts, H = 7168, I = 2048), square8k, square16k, copy (counter calibration).
 """
 
 from __future__ import annotations
@@ -47,6 +49,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 (E4M3) MFMA peak
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+STEPS_ARE = {
+    "prefill": "act-quant (1x128) + block-scaled FP8 GEMM (bf16 out) for every linear; weights pre-quantized",
+    "moe_layer": "route + gather/act-quant + grouped GEMM (gate_up) + SiLU*up/act-quant + grouped GEMM (down) + "
+                 "weighted combine; expert weights pre-quantized; value counts routed rows only",
+}
 
 
 def parse():
@@ -54,7 +61,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "decode", "moe", "moe_masked", "square8k", "square16k", "copy"])
+    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-reps", type=int, default=50, help="rounds over the 8 weight sets per decode timing")
@@ -457,6 +464,9 @@ def main():
     elif args.workload == "moe_masked":
         linears = None
         workload = "moe_masked_32experts_1024tok_zipf1.1_top4_k7168_n4096"
+    elif args.workload == "moe_layer":
+        linears = None
+        workload = "moe_layer_32experts_8192tok_zipf1.1_top4_h7168_i2048"
     else:
         linears = None
         workload = "moe_32experts_zipf1.1_top4_k7168_n4096"
@@ -473,6 +483,8 @@ def main():
         del preps
     elif args.workload == "moe_masked":
         value, ms_per_step, per, roof, gemm_s, total_flops = bench_masked(args, fg, torch, workloads)
+    elif args.workload == "moe_layer":
+        value, ms_per_step, per, roof, gemm_s, total_flops = bench_moe_layer(args, fg, torch, workloads)
     else:
         value, ms_per_step, per, roof, gemm_s, total_flops = bench_moe(args, fg, torch, workloads)
     torch.cuda.empty_cache()
@@ -506,7 +518,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations with 0.1% x20 outliers, N(0,0.02) weights; no trained weights)",
         "config": {
             "workload": workload,
-            "steps_are": "act-quant (1x128) + block-scaled FP8 GEMM (bf16 out) for every linear; weights pre-quantized",
+            "steps_are": STEPS_ARE.get(args.workload, STEPS_ARE["prefill"]),
             "linears": per_out,
             "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
             "gemm_only_tflops": round(total_flops / gemm_s / 1e12, 2) if gemm_s else None,
@@ -630,6 +642,103 @@ def bench_masked(args, fg, torch, workloads):
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes_per_launch": nbytes,
             "useful_tflops": round(flops / gt / 1e12, 1), "mean_launch_us": round(gt * 1e6, 2)}
     return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gt, flops
+
+
+def bench_moe_layer(args, fg, torch, workloads):
+    """The FP8 MoE layer: one step = route -> gather+quantize -> grouped
+    product (gate_up, N = 2I) -> SiLU-times-up+quantize -> grouped product
+    (down, N = H) -> weighted combine, every buffer sized by the padded-row
+    upper bound so that nothing waits for the host.  Value: useful TFLOP/s of
+    the two products (routed rows only) over the whole step."""
+    c = workloads.moe_layer()
+    g, hd, it, t, tk = c.experts, c.hidden, c.inter, c.tokens, c.topk
+    x = dev_bf16(c.x, torch)
+    idx = torch.from_numpy(c.topk_idx.astype(np.int32)).cuda()
+    wts = torch.from_numpy(c.topk_weights).cuda()
+    q1 = torch.empty((g, 2 * it, hd), dtype=torch.float8_e4m3fn, device="cuda")
+    s1 = torch.empty((g, 2 * it // 128, hd // 128), dtype=torch.float32, device="cuda")
+    q2 = torch.empty((g, hd, it), dtype=torch.float8_e4m3fn, device="cuda")
+    s2 = torch.empty((g, hd // 128, it // 128), dtype=torch.float32, device="cuda")
+    for e in range(g):
+        qa, sa = fg.quantize_fp8_blocks(dev_bf16(c.w1[e], torch))
+        q1[e].copy_(qa)
+        s1[e].copy_(sa)
+        qa, sa = fg.quantize_fp8_blocks(dev_bf16(c.w2[e], torch))
+        q2[e].copy_(qa)
+        s2[e].copy_(sa)
+    del qa, sa
+    c.w1 = c.w2 = None
+    m = fg.moe_max_padded_rows(t, tk, g)
+    dev = "cuda"
+    route = (torch.empty(g, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.int32, device=dev),
+             torch.empty(m, dtype=torch.int32, device=dev), torch.empty((t, tk), dtype=torch.int32, device=dev),
+             torch.empty(max(fg.moe_route_workspace_bytes(t, g), 16), dtype=torch.uint8, device=dev))
+    a1 = (torch.empty((m, hd), dtype=torch.float8_e4m3fn, device=dev),
+          torch.empty((hd // 128, m), dtype=torch.float32, device=dev))
+    h = torch.empty((m, 2 * it), dtype=torch.bfloat16, device=dev)
+    a2 = (torch.empty((m, it), dtype=torch.float8_e4m3fn, device=dev),
+          torch.empty((it // 128, m), dtype=torch.float32, device=dev))
+    y = torch.empty((m, hd), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((t, hd), dtype=torch.bfloat16, device=dev)
+    names = ["route", "gather_quant", "gemm_gate_up", "silu_mul_quant", "gemm_down", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev:
+                ev[i].record()
+        mark(0)
+        _counts, m_idx, tok, row_of = fg.moe_route_contiguous(idx, g, out=route)
+        mark(1)
+        fg.moe_gather_quantize(x, tok, out=a1)
+        mark(2)
+        fg.m_grouped_fp8_gemm_nt_contiguous(a1, (q1, s1), h, m_idx)
+        mark(3)
+        fg.silu_mul_quantize(h, m_idx, out=a2)
+        mark(4)
+        fg.m_grouped_fp8_gemm_nt_contiguous(a2, (q2, s2), y, m_idx)
+        mark(5)
+        fg.moe_combine(y, row_of, wts, out=out)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[HipEvent(torch) for _ in range(7)] for _ in range(args.steps)]
+    ahead = GpuAhead(torch)
+    probe = [HipEvent(torch) for _ in range(7)]
+    host_step = host_enqueue_seconds(lambda: step(probe), torch)
+    e_first, e_last = HipEvent(torch), HipEvent(torch)
+    torch.cuda.synchronize()
+    ahead.spin(1.5 * host_step * args.steps + 2e-3)
+    e_first.record()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    e_last.record()
+    torch.cuda.synchronize()
+    elapsed = e_first.elapsed_time(e_last) * 1e-3
+    stage = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e-3 for i, n in enumerate(names)}
+    pairs = int(c.topk_idx.size)
+    f1 = 2.0 * pairs * (2 * it) * hd
+    f2 = 2.0 * pairs * hd * it
+    flops = f1 + f2
+    m_real = padded_rows_of(route[0])
+    per = [{"name": c.name, "m_pad_max": m, "m_pad": m_real, "pairs": pairs, "hidden": hd, "inter": it, "experts": g,
+            **{f"{n}_us": stage[n] * 1e6 for n in names},
+            "gate_up_tflops_useful": f1 / stage["gemm_gate_up"] / 1e12,
+            "down_tflops_useful": f2 / stage["gemm_down"] / 1e12, "_gemm_s": stage["gemm_gate_up"] + stage["gemm_down"]}]
+    gemm_s = stage["gemm_gate_up"] + stage["gemm_down"]
+    # both products run the same kernel: its per-launch average over the two
+    roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x4> (gate_up and down launches averaged)",
+            "achieved": round(flops / gemm_s / 1e12, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(flops / gemm_s / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops / 2, "mean_launch_us": round(gemm_s / 2 * 1e6, 2)}
+    return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gemm_s, flops
+
+
+def padded_rows_of(counts):
+    """Rows the layout really uses: every expert's count rounded up to 128
+    (read after the timed region)."""
+    return int((((counts.long() + 127) // 128) * 128).sum().item())
 
 
 if __name__ == "__main__":

@@ -15,6 +15,7 @@ Linnet DeepGEMM plugin source):
     fp8_gemm_nt((q, sa), (qb, sb), d)                # d: bf16 [M, N], in place
     m_grouped_fp8_gemm_nt_contiguous((q, sa), (qb, sb), d, m_indices)
     m_grouped_fp8_gemm_nt_masked((q, sa), (qb, sb), d, masked_m, expected_m)
+    out = moe_fp8_layer(x, topk_idx, topk_weights, w1, w2)   # the MoE layer
 """
 
 from __future__ import annotations
@@ -50,12 +51,21 @@ _lib.m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i3
 _lib.quantize_fp8_groups_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_blocks_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt_ue8m0.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
+_lib.moe_max_padded_rows.argtypes = [_i64, _i32, _i32]
+_lib.moe_max_padded_rows.restype = ctypes.c_int64
+_lib.moe_route_workspace_bytes.argtypes = [_i64, _i32]
+_lib.moe_route_workspace_bytes.restype = ctypes.c_int64
+_lib.moe_route_contiguous.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]
+_lib.moe_gather_quantize.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _fp, _i64, _vp]
+_lib.silu_mul_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp, _fp, _i64, _vp]
+_lib.moe_combine.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _i32, _vp, _vp]
 _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
               "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
-              "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0"):
+              "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
+              "moe_gather_quantize", "silu_mul_quantize", "moe_combine"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -79,7 +89,7 @@ def declared_functions() -> list[str]:
     with open(HEADER_PATH) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
 
 
 def library() -> ctypes.CDLL:
@@ -317,6 +327,147 @@ def fp8_linear(x: torch.Tensor, weight) -> torch.Tensor:
     return d.reshape(*x.shape[:-1], qb.shape[0])
 
 
+# ----------------------------------------------------------------- MoE layer
+def moe_max_padded_rows(tokens: int, topk: int, num_experts: int) -> int:
+    """Upper bound of the contiguous layout's rows: roundup(T*topk + G*127, 128)."""
+    r = _lib.moe_max_padded_rows(tokens, topk, num_experts)
+    if r < 0:
+        raise ValueError("bad MoE sizes")
+    return r
+
+
+def moe_route_contiguous(topk_idx: torch.Tensor, num_experts: int, m_pad_max: int | None = None, out=None):
+    """Routing layout from topk_idx int32 [T, topk].  Returns (counts [G],
+    m_indices [m_pad_max], token_of_row [m_pad_max], row_of [T, topk]), all
+    int32 on the device and computed without a host synchronisation.  `out`
+    optionally holds those four tensors plus a uint8 workspace of at least
+    moe_route_workspace_bytes(T, G) bytes, to be reused across calls."""
+    _need(topk_idx, "topk_idx", (torch.int32,), 2)
+    tokens, topk = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        if m_pad_max is None:
+            m_pad_max = moe_max_padded_rows(tokens, topk, num_experts)
+        ws_bytes = _lib.moe_route_workspace_bytes(tokens, num_experts)
+        if ws_bytes < 0:
+            raise ValueError("bad MoE sizes")
+        out = (torch.empty(num_experts, dtype=torch.int32, device=dev),
+               torch.empty(m_pad_max, dtype=torch.int32, device=dev),
+               torch.empty(m_pad_max, dtype=torch.int32, device=dev),
+               torch.empty((tokens, topk), dtype=torch.int32, device=dev),
+               torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev))
+    counts, m_indices, token_of_row, row_of, ws = out
+    for t, name in ((counts, "counts"), (m_indices, "m_indices"), (token_of_row, "token_of_row")):
+        _need(t, name, (torch.int32,), 1)
+    _need(row_of, "row_of", (torch.int32,), 2)
+    if counts.shape[0] != num_experts or token_of_row.shape != m_indices.shape or tuple(row_of.shape) != (tokens, topk):
+        raise ValueError("routing buffers do not match (G, m_pad_max, [T, topk])")
+    _check(
+        _lib.moe_route_contiguous(
+            _ptr(topk_idx), tokens, topk, num_experts, _ptr(counts), _ptr(m_indices), _ptr(token_of_row),
+            _ptr(row_of), m_indices.shape[0], _ptr(ws), ws.numel(), _stream(topk_idx)
+        )
+    )
+    return counts, m_indices, token_of_row, row_of
+
+
+def moe_route_workspace_bytes(tokens: int, num_experts: int) -> int:
+    r = _lib.moe_route_workspace_bytes(tokens, num_experts)
+    if r < 0:
+        raise ValueError("bad MoE sizes")
+    return r
+
+
+def moe_gather_quantize(x: torch.Tensor, token_of_row: torch.Tensor, out=None):
+    """Rows x[token_of_row[r]] (zeros for an index outside [0, T)) quantized per 1x128 group.
+    x: bf16 [T, K].  Returns (q float8_e4m3fn [m_pad_max, K], sa float32
+    [K/128, m_pad_max'] with the rows padded to a multiple of four)."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(token_of_row, "token_of_row", (torch.int32,), 1)
+    k = x.shape[1]
+    m = token_of_row.shape[0]
+    if out is None:
+        out = (torch.empty((m, k), dtype=torch.float8_e4m3fn, device=x.device),
+               torch.empty((k // GROUP, padded_rows(m)), dtype=torch.float32, device=x.device))
+    q, sa = out
+    _need(q, "q", _FP8, 2)
+    _need(sa, "sa", (torch.float32,), 2)
+    if tuple(q.shape) != (m, k):
+        raise ValueError("q must be [m_pad_max, K]")
+    _check(_lib.moe_gather_quantize(_ptr(x), x.shape[0], k, _ptr(token_of_row), m, _ptr(q), _ptr(sa), sa.shape[1],
+                                    _stream(x)))
+    return q, sa
+
+
+def silu_mul_quantize(h: torch.Tensor, m_indices: torch.Tensor, out=None):
+    """act = bf16(silu(h[:, :I]) * h[:, I:]) quantized per 1x128 group (rows
+    with m_indices < 0 give zeros).  h: bf16 [M, 2I].  Returns (q [M, I], sa
+    [I/128, roundup(M, 4)])."""
+    _need(h, "h", (torch.bfloat16,), 2)
+    _need(m_indices, "m_indices", (torch.int32,), 1)
+    m, two_i = h.shape
+    if two_i % 2 or m_indices.shape[0] != m:
+        raise ValueError("h must be [M, 2I] and m_indices [M]")
+    inter = two_i // 2
+    if out is None:
+        out = (torch.empty((m, inter), dtype=torch.float8_e4m3fn, device=h.device),
+               torch.empty((inter // GROUP, padded_rows(m)), dtype=torch.float32, device=h.device))
+    q, sa = out
+    _need(q, "q", _FP8, 2)
+    _need(sa, "sa", (torch.float32,), 2)
+    if tuple(q.shape) != (m, inter):
+        raise ValueError("q must be [M, I]")
+    _check(_lib.silu_mul_quantize(_ptr(h), m, inter, _ptr(m_indices), _ptr(q), _ptr(sa), sa.shape[1], _stream(h)))
+    return q, sa
+
+
+def moe_combine(y: torch.Tensor, row_of: torch.Tensor, topk_weights: torch.Tensor, out=None) -> torch.Tensor:
+    """out[t] = bf16(sum_j topk_weights[t, j] * y[row_of[t, j]]) in FP32, slot
+    order; slots whose row lies outside [0, rows) are skipped.  y bf16 [rows, H], row_of int32 [T, topk], topk_weights float32 [T, topk]."""
+    _need(y, "y", (torch.bfloat16,), 2)
+    _need(row_of, "row_of", (torch.int32,), 2)
+    _need(topk_weights, "topk_weights", (torch.float32,), 2)
+    tokens, topk = row_of.shape
+    if tuple(topk_weights.shape) != (tokens, topk):
+        raise ValueError("topk_weights must match row_of [T, topk]")
+    hdim = y.shape[1]
+    if out is None:
+        out = torch.empty((tokens, hdim), dtype=torch.bfloat16, device=y.device)
+    _need(out, "out", (torch.bfloat16,), 2)
+    if tuple(out.shape) != (tokens, hdim):
+        raise ValueError("out must be [T, H]")
+    _check(_lib.moe_combine(_ptr(y), y.shape[0], hdim, _ptr(row_of), _ptr(topk_weights), tokens, topk, _ptr(out),
+                            _stream(y)))
+    return out
+
+
+def moe_fp8_layer(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor, w1, w2) -> torch.Tensor:
+    """The FP8 MoE layer (deepgemm-rust README, "What's implemented",
+    moe_fp8_layer row), every step on the device with no host synchronisation:
+    route -> gather+quantize -> grouped product with w1 -> SiLU.mul+quantize ->
+    grouped product with w2 -> weighted combine.
+
+    x bf16 [T, H]; topk_idx int32 [T, topk]; topk_weights float32 [T, topk];
+    w1 = (q [G, 2I, H], sb [G, 2I/128, H/128]) with the gate rows first, then
+    the up rows; w2 = (q [G, H, I], sb [G, H/128, I/128]).  Returns bf16 [T, H]."""
+    (q1, s1), (q2, s2) = w1, w2
+    _need(q1, "w1", _FP8, 3)
+    _need(q2, "w2", _FP8, 3)
+    tokens, hdim = x.shape
+    g, two_i, h1 = q1.shape
+    if h1 != hdim or tuple(q2.shape) != (g, hdim, two_i // 2):
+        raise ValueError("w1 must be [G, 2I, H] and w2 [G, H, I]")
+    counts, m_indices, token_of_row, row_of = moe_route_contiguous(topk_idx, g)
+    m = m_indices.shape[0]
+    a1 = moe_gather_quantize(x, token_of_row)
+    hbuf = torch.empty((m, two_i), dtype=torch.bfloat16, device=x.device)
+    m_grouped_fp8_gemm_nt_contiguous(a1, (q1, s1), hbuf, m_indices)
+    a2 = silu_mul_quantize(hbuf, m_indices)
+    y = torch.empty((m, hdim), dtype=torch.bfloat16, device=x.device)
+    m_grouped_fp8_gemm_nt_contiguous(a2, (q2, s2), y, m_indices)
+    return moe_combine(y, row_of, topk_weights)
+
+
 def describe_gemm(m: int, n: int, k: int) -> str:
     buf = ctypes.create_string_buffer(128)
     _check(_lib.fgfp8_describe_gemm(m, n, k, buf, 128))
@@ -338,7 +489,14 @@ __all__ = [
     "last_error",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
+    "moe_combine",
+    "moe_fp8_layer",
+    "moe_gather_quantize",
+    "moe_max_padded_rows",
+    "moe_route_contiguous",
+    "moe_route_workspace_bytes",
     "padded_rows",
     "quantize_fp8_blocks",
     "quantize_fp8_groups",
+    "silu_mul_quantize",
 ]

@@ -250,6 +250,90 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
                   who);
 }
 
+int64_t moe_route_workspace_bytes(int64_t tokens, int32_t num_experts) {
+  if (tokens < 0 || num_experts < 1) return -1;
+  return fgfp8::moe_route_workspace_bytes(tokens, num_experts);
+}
+
+int64_t moe_max_padded_rows(int64_t tokens, int32_t topk, int32_t num_experts) {
+  if (tokens < 0 || topk < 1 || num_experts < 1) return -1;
+  return (tokens * topk + (int64_t)num_experts * 127 + 127) / 128 * 128;
+}
+
+int moe_route_contiguous(const int32_t* topk_idx, int64_t tokens, int32_t topk, int32_t num_experts, int32_t* counts,
+                         int32_t* m_indices, int32_t* token_of_row, int32_t* row_of, int64_t m_pad_max,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  const char* who = "moe_route_contiguous";
+  if (tokens < 0 || tokens >= kMaxRows) return fail(FGFP8_EINVAL, "%s: tokens=%lld out of range", who, (long long)tokens);
+  if (topk < 1 || topk > 8) return fail(FGFP8_EINVAL, "%s: topk=%d must be 1..8", who, (int)topk);
+  if (num_experts < 1 || num_experts > 2048)
+    return fail(FGFP8_EINVAL, "%s: num_experts=%d must be 1..2048", who, (int)num_experts);
+  const int64_t need_rows = moe_max_padded_rows(tokens, topk, num_experts);
+  if (m_pad_max < need_rows || m_pad_max % 128 != 0 || m_pad_max >= kMaxRows)
+    return fail(FGFP8_EINVAL, "%s: m_pad_max=%lld must be a multiple of 128 and >= %lld", who, (long long)m_pad_max,
+                (long long)need_rows);
+  if (workspace_bytes < fgfp8::moe_route_workspace_bytes(tokens, num_experts))
+    return fail(FGFP8_EINVAL, "%s: workspace of %lld bytes, need %lld", who, (long long)workspace_bytes,
+                (long long)fgfp8::moe_route_workspace_bytes(tokens, num_experts));
+  if (!counts || !m_indices || !token_of_row || !workspace || (tokens > 0 && (!topk_idx || !row_of)))
+    return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_moe_route(topk_idx, tokens, topk, num_experts, counts, m_indices, token_of_row, row_of,
+                                          m_pad_max, workspace, (hipStream_t)stream),
+                  who);
+}
+
+int moe_gather_quantize(const void* x_bf16, int64_t tokens, int64_t k, const int32_t* token_of_row, int64_t m_pad_max,
+                        void* q_e4m3, float* sa, int64_t sa_ld, void* stream) {
+  const char* who = "moe_gather_quantize";
+  if (m_pad_max < 0 || m_pad_max >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m_pad_max out of range", who);
+  if (tokens < 0 || tokens >= kMaxRows) return fail(FGFP8_EINVAL, "%s: tokens out of range", who);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m_pad_max, k, sa_ld)) return rc;
+  if ((tokens > 0 && !x_bf16) || !token_of_row || !q_e4m3 || !sa) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(sa))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (m_pad_max == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_moe_gather_quantize(x_bf16, tokens, k, token_of_row, m_pad_max, q_e4m3, sa, sa_ld,
+                                                    (hipStream_t)stream),
+                  who);
+}
+
+int silu_mul_quantize(const void* h_bf16, int64_t m, int64_t inter, const int32_t* m_indices, void* q_e4m3, float* sa,
+                      int64_t sa_ld, void* stream) {
+  const char* who = "silu_mul_quantize";
+  if (m < 0 || m >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m=%lld out of range", who, (long long)m);
+  if (int rc = check_k(who, inter)) return rc;
+  if (int rc = check_sa(who, m, inter, sa_ld)) return rc;
+  if (!h_bf16 || !m_indices || !q_e4m3 || !sa) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(h_bf16) || !aligned16(q_e4m3) || !aligned16(sa))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (m == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_moe_silu_mul_quantize(h_bf16, m, inter, m_indices, q_e4m3, sa, sa_ld,
+                                                      (hipStream_t)stream),
+                  who);
+}
+
+int moe_combine(const void* y_bf16, int64_t y_rows, int64_t hdim, const int32_t* row_of, const float* topk_weights,
+                int64_t tokens, int32_t topk, void* out_bf16, void* stream) {
+  const char* who = "moe_combine";
+  if (y_rows < 0 || y_rows >= kMaxRows) return fail(FGFP8_EINVAL, "%s: y_rows out of range", who);
+  if (tokens < 0 || tokens >= kMaxRows) return fail(FGFP8_EINVAL, "%s: tokens out of range", who);
+  if (topk < 1 || topk > 8) return fail(FGFP8_EINVAL, "%s: topk=%d must be 1..8", who, (int)topk);
+  if (hdim <= 0 || hdim % 8 != 0) return fail(FGFP8_EINVAL, "%s: hdim=%lld must be a positive multiple of 8", who, (long long)hdim);
+  if ((y_rows > 0 && !y_bf16) || !row_of || !topk_weights || !out_bf16)
+    return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(y_bf16) || !aligned16(out_bf16))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (tokens == 0) return FGFP8_OK;
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_moe_combine(y_bf16, y_rows, hdim, row_of, topk_weights, tokens, topk, out_bf16,
+                                            (hipStream_t)stream),
+                  who);
+}
+
 int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, const float* sb, int64_t n,
                   void* d_bf16, void* q_e4m3, float* sa, int64_t sa_ld, void* stream) {
   const char* who = "fp8_linear_nt";

@@ -67,4 +67,16 @@ hipError_t launch_masked_gemm(GemmKind kind, const void* a, const float* sa, int
                               const void* b, const float* sb, int32_t num_groups, int64_t max_m, void* d, int64_t n,
                               int64_t k, hipStream_t stream);
 
+// Mixture-of-experts layer steps around the grouped product.
+int64_t moe_route_workspace_bytes(int64_t tokens, int experts);
+hipError_t launch_moe_route(const int32_t* topk_idx, int64_t tokens, int topk, int experts, int32_t* counts,
+                            int32_t* m_indices, int32_t* token_of_row, int32_t* row_of, int64_t m_pad_max,
+                            void* workspace, hipStream_t stream);
+hipError_t launch_moe_gather_quantize(const void* x, int64_t tokens, int64_t k, const int32_t* token_of_row,
+                                      int64_t m_pad_max, void* q, float* sa, int64_t sa_ld, hipStream_t stream);
+hipError_t launch_moe_silu_mul_quantize(const void* h, int64_t m, int64_t inter, const int32_t* m_indices, void* q,
+                                        float* sa, int64_t sa_ld, hipStream_t stream);
+hipError_t launch_moe_combine(const void* y, int64_t y_rows, int64_t hdim, const int32_t* row_of, const float* w,
+                              int64_t tokens, int topk, void* out, hipStream_t stream);
+
 }  // namespace fgfp8

@@ -216,6 +216,62 @@ int quantize_fp8_blocks_ue8m0(const void* w_bf16, int64_t n, int64_t k, void* q_
 int fp8_gemm_nt_ue8m0(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
                       void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream);
 
+/* The FP8 mixture-of-experts layer around the grouped product, step by step,
+ * with no device-to-host synchronisation (deepgemm-rust README, "What's
+ * implemented", moe_fp8_layer row: histogram -> offsets -> gather -> grouped
+ * GEMM -> SiLU.mul -> grouped GEMM -> weighted combine).  With tokens T,
+ * slots per token topk, experts G, hidden size H and expert width I:
+ *   moe_route_contiguous   topk_idx -> layout (counts, m_indices, rows)
+ *   moe_gather_quantize    x [T][H] -> A1 (E4M3 [m_pad_max][H], scales)
+ *   m_grouped_fp8_gemm_nt_contiguous  A1 x W1 [G][2I][H] -> h [m_pad_max][2I]
+ *   silu_mul_quantize      h -> A2 = quantize(bf16(silu(h[:, :I]) * h[:, I:]))
+ *   m_grouped_fp8_gemm_nt_contiguous  A2 x W2 [G][H][I] -> y [m_pad_max][H]
+ *   moe_combine            y -> out [T][H]
+ * Every buffer is sized by m_pad_max = moe_max_padded_rows(T, topk, G), an
+ * upper bound of the padded row count; rows past the real count carry group
+ * -1 and are skipped by the grouped product. */
+
+/* Upper bound of the padded rows: roundup(T*topk + G*127, 128) (or -1 on
+ * bad arguments).  Host-only. */
+int64_t moe_max_padded_rows(int64_t tokens, int32_t topk, int32_t num_experts);
+/* Bytes of device workspace moe_route_contiguous needs (or -1).  Host-only. */
+int64_t moe_route_workspace_bytes(int64_t tokens, int32_t num_experts);
+
+/* Routing layout.  topk_idx [tokens][topk] int32, the experts of each token
+ * (values outside [0, num_experts) drop that slot).  Outputs (device):
+ * counts [num_experts] pairs per expert; m_indices [m_pad_max] the expert of
+ * each row or -1 (expert e owns rows starts[e] .. starts[e] + counts[e] - 1,
+ * starts 128-aligned, experts in order); token_of_row [m_pad_max] the token of
+ * each row or -1; row_of [tokens][topk] the row of each pair or -1.  Within an
+ * expert, pairs are ordered by (token, slot).  workspace: device scratch of
+ * workspace_bytes >= moe_route_workspace_bytes(tokens, num_experts).
+ * Requirements: 1 <= topk <= 8, 1 <= num_experts <= 2048, m_pad_max a
+ * multiple of 128 and >= moe_max_padded_rows(tokens, topk, num_experts). */
+int moe_route_contiguous(const int32_t* topk_idx, int64_t tokens, int32_t topk, int32_t num_experts, int32_t* counts,
+                         int32_t* m_indices, int32_t* token_of_row, int32_t* row_of, int64_t m_pad_max,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Row r of the layout = x[token_of_row[r]] (a zero row for an index outside
+ * [0, tokens)), quantized exactly as quantize_fp8_groups.  x [tokens][k] bf16;
+ * q [m_pad_max][k] E4M3; sa [k/128][sa_ld], sa_ld >= m_pad_max, sa_ld % 4 == 0;
+ * k % 128 == 0. */
+int moe_gather_quantize(const void* x_bf16, int64_t tokens, int64_t k, const int32_t* token_of_row, int64_t m_pad_max,
+                        void* q_e4m3, float* sa, int64_t sa_ld, void* stream);
+
+/* act[r][c] = bf16(silu(h[r][c]) * h[r][inter + c]) in FP32 (silu(g) =
+ * g / (1 + exp(-g)), the gate half first), quantized per 1x128 group as
+ * quantize_fp8_groups: q [m][inter], sa [inter/128][sa_ld].  Rows whose
+ * m_indices entry is negative are zero rows.  h [m][2*inter] bf16. */
+int silu_mul_quantize(const void* h_bf16, int64_t m, int64_t inter, const int32_t* m_indices, void* q_e4m3, float* sa,
+                      int64_t sa_ld, void* stream);
+
+/* out[t][c] = bf16(sum_{j < topk} topk_weights[t][j] * y[row_of[t][j]][c]),
+ * summed in FP32 in slot order; slots whose row lies outside [0, y_rows) are
+ * skipped.  y [y_rows][hdim] bf16, row_of and topk_weights [tokens][topk],
+ * out [tokens][hdim] bf16, hdim % 8 == 0, 1 <= topk <= 8. */
+int moe_combine(const void* y_bf16, int64_t y_rows, int64_t hdim, const int32_t* row_of, const float* topk_weights,
+                int64_t tokens, int32_t topk, void* out_bf16, void* stream);
+
 /* Message for the most recent non-zero status returned on the calling thread
  * (thread-local; the pointer stays valid until the next failing call on that
  * thread).  Returns "" if no call has failed. */

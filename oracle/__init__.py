@@ -26,6 +26,9 @@ What it computes, and where the pages define it:
                 variant (deepgemm-rust README, "What's implemented" table and
                 "Quick start" grouped example), and its masked variant (same
                 table, m_grouped_fp8_gemm_nt_masked row).
+* ``moe``       the FP8 mixture-of-experts layer around the grouped product:
+                routing layout, gather, SiLU-times-up, weighted combine and the
+                whole layer (same table, moe_fp8_layer row).
 
 Every function works in float64 (or exact integer / float32 steps where the
 method fixes float32), favouring obviousness over speed.
@@ -43,6 +46,7 @@ from .gemm import (
     masked_grouped_gemm_nt,
     round_to_bf16,
 )
+from . import moe
 from .quantize import GROUP, quantize_blocks, quantize_blocks_ue8m0, quantize_groups, quantize_groups_ue8m0
 
 __all__ = [
@@ -55,6 +59,7 @@ __all__ = [
     "gemm_nt_dequantized",
     "grouped_gemm_nt",
     "masked_grouped_gemm_nt",
+    "moe",
     "quantize_blocks",
     "quantize_groups",
     "quantize_groups_ue8m0",

@@ -39,6 +39,12 @@ def test_library_exports_every_declared_function():
         "quantize_fp8_groups_ue8m0",
         "quantize_fp8_blocks_ue8m0",
         "fp8_gemm_nt_ue8m0",
+        "moe_max_padded_rows",
+        "moe_route_workspace_bytes",
+        "moe_route_contiguous",
+        "moe_gather_quantize",
+        "silu_mul_quantize",
+        "moe_combine",
     }
     lib = fg.library()
     for n in names:
@@ -165,6 +171,51 @@ def test_fp8_out_rejects():
     assert call(m=0) == fg.FGFP8_OK
 
 
+def test_moe_sizes():
+    lib = _lib()
+    assert lib.moe_max_padded_rows(8192, 4, 32) == (8192 * 4 + 32 * 127 + 127) // 128 * 128
+    assert lib.moe_max_padded_rows(0, 1, 1) == 128
+    assert lib.moe_max_padded_rows(-1, 4, 32) == -1
+    assert lib.moe_route_workspace_bytes(257, 32) == 2 * 32 * 4 + 32 * 4
+    assert lib.moe_route_workspace_bytes(0, 3) == 12
+    assert lib.moe_route_workspace_bytes(4, 0) == -1
+
+
+def test_moe_calls_reject():
+    lib = _lib()
+    mpm = lib.moe_max_padded_rows(100, 4, 8)
+    ws = lib.moe_route_workspace_bytes(100, 8)
+
+    def route(tokens=100, topk=4, g=8, m_pad_max=mpm, wsb=ws, idx=P):
+        return lib.moe_route_contiguous(idx, tokens, topk, g, P, P, P, P, m_pad_max, P, wsb, None)
+
+    assert route(topk=9) == fg.FGFP8_EINVAL
+    assert "topk" in fg.last_error()
+    assert route(g=0) == fg.FGFP8_EINVAL
+    assert route(g=4096) == fg.FGFP8_EINVAL
+    assert route(m_pad_max=mpm - 128) == fg.FGFP8_EINVAL
+    assert "m_pad_max" in fg.last_error()
+    assert route(m_pad_max=mpm + 4) == fg.FGFP8_EINVAL
+    assert route(wsb=ws - 4) == fg.FGFP8_EINVAL
+    assert "workspace" in fg.last_error()
+    assert route(idx=None) == fg.FGFP8_EINVAL
+
+    assert lib.moe_gather_quantize(P, 10, 100, P, 256, P, P, 256, None) == fg.FGFP8_EINVAL
+    assert lib.moe_gather_quantize(P, 10, 128, P, 256, P, P, 252, None) == fg.FGFP8_EINVAL
+    assert lib.moe_gather_quantize(P, 10, 128, None, 256, P, P, 256, None) == fg.FGFP8_EINVAL
+    assert lib.moe_gather_quantize(P, -1, 128, P, 256, P, P, 256, None) == fg.FGFP8_EINVAL
+    assert lib.moe_gather_quantize(P, 10, 128, P, 0, P, P, 4, None) == fg.FGFP8_OK
+    assert lib.silu_mul_quantize(P, 256, 64, P, P, P, 256, None) == fg.FGFP8_EINVAL
+    assert lib.silu_mul_quantize(P + 2, 256, 128, P, P, P, 256, None) == fg.FGFP8_EINVAL
+    assert lib.silu_mul_quantize(P, 0, 128, P, P, P, 4, None) == fg.FGFP8_OK
+    assert lib.moe_combine(P, 64, 100, P, P, 8, 4, P, None) == fg.FGFP8_EINVAL
+    assert "multiple of 8" in fg.last_error()
+    assert lib.moe_combine(P, 64, 128, P, P, 8, 0, P, None) == fg.FGFP8_EINVAL
+    assert lib.moe_combine(P, 64, 128, None, P, 8, 4, P, None) == fg.FGFP8_EINVAL
+    assert lib.moe_combine(P, -1, 128, P, P, 8, 4, P, None) == fg.FGFP8_EINVAL
+    assert lib.moe_combine(P, 64, 128, P, P, 0, 4, P, None) == fg.FGFP8_OK
+
+
 def test_linear_rejects():
     lib = _lib()
 
@@ -197,6 +248,11 @@ def test_no_device_is_reported_not_crashed():
     assert lib.fp8_linear_nt(P, 1, 256, P, P, 128, P, None, None, 0, None) == fg.FGFP8_ENODEV
     assert lib.m_grouped_fp8_gemm_nt_masked(P, P, 256, P, P, P, 4, 64, 32, P, 128, 256, None) == fg.FGFP8_ENODEV
     assert lib.fp8_gemm_nt_fp8_out(P, P, 8, P, P, P, P, 8, None, 8, 256, 256, None) == fg.FGFP8_ENODEV
+    mpm, ws = lib.moe_max_padded_rows(100, 4, 8), lib.moe_route_workspace_bytes(100, 8)
+    assert lib.moe_route_contiguous(P, 100, 4, 8, P, P, P, P, mpm, P, ws, None) == fg.FGFP8_ENODEV
+    assert lib.moe_gather_quantize(P, 10, 128, P, 256, P, P, 256, None) == fg.FGFP8_ENODEV
+    assert lib.silu_mul_quantize(P, 256, 128, P, P, P, 256, None) == fg.FGFP8_ENODEV
+    assert lib.moe_combine(P, 64, 128, P, P, 8, 4, P, None) == fg.FGFP8_ENODEV
 
 
 def test_describe_gemm_plans():

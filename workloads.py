@@ -262,3 +262,48 @@ def moe_masked(seed: int = 5, experts: int = 32, tokens: int = 1024, topk: int =
     b = gaussian_bf16(r_w, (experts, n, k), 0.02) if with_weights else np.zeros((0,), np.uint16)
     return Masked(f"moe_masked_{experts}x{n}x{k}_zipf{alpha}_top{topk}_{tokens}tok", experts, max_m, n, k, counts,
                   int(round(counts.mean())), a, b)
+
+
+# ----------------------------------------------------------------- MoE layer
+@dataclass
+class MoeLayer:
+    name: str
+    tokens: int
+    experts: int
+    topk: int
+    hidden: int  # H
+    inter: int  # I: w1 is [G][2I][H] (gate rows, then up rows), w2 [G][H][I]
+    x: np.ndarray  # uint16 [T][H]
+    topk_idx: np.ndarray  # int32 [T][topk]
+    topk_weights: np.ndarray  # float32 [T][topk]
+    w1: np.ndarray = field(default=None)  # uint16 [G][2I][H]
+    w2: np.ndarray = field(default=None)  # uint16 [G][H][I]
+
+    @property
+    def useful_flops(self) -> int:
+        """Both products over the routed pairs (padding rows excluded)."""
+        pairs = int(((self.topk_idx >= 0) & (self.topk_idx < self.experts)).sum())
+        return 2 * pairs * (2 * self.inter) * self.hidden + 2 * pairs * self.hidden * self.inter
+
+
+def moe_layer(seed: int = 6, experts: int = 32, tokens: int = 8192, topk: int = 4, hidden: int = 7168,
+              inter: int = 2048, alpha: float = 1.1, with_weights: bool = True) -> MoeLayer:
+    """A MoE layer input: tokens x_t ~ N(0, 1) [T][H]; top-k distinct experts
+    per token by the seeded Zipf(alpha) choice; routing weights = softmax of
+    N(0, 1) logits over the token's k slots (float32, positive, summing to one);
+    expert weights w1 [G][2I][H] and w2 [G][H][I] ~ N(0, 0.02)."""
+    r_route, r_x, r_w1, r_w2, r_p = _rngs(seed, 5)
+    choice = zipf_topk_routing(r_route, tokens, experts, topk, alpha).astype(np.int32)
+    x = gaussian_bf16(r_x, (tokens, hidden), 1.0)
+    logits = r_p.standard_normal(size=(tokens, topk)).astype(np.float64)
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    weights = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+    w1 = w2 = None
+    if with_weights:
+        w1 = np.empty((experts, 2 * inter, hidden), dtype=np.uint16)
+        w2 = np.empty((experts, hidden, inter), dtype=np.uint16)
+        for g in range(experts):
+            w1[g] = gaussian_bf16(r_w1, (2 * inter, hidden), 0.02)
+            w2[g] = gaussian_bf16(r_w2, (hidden, inter), 0.02)
+    return MoeLayer(f"moe_layer_{experts}e_top{topk}_{tokens}tok_h{hidden}_i{inter}", tokens, experts, topk, hidden,
+                    inter, x, choice, weights, w1, w2)
