@@ -510,6 +510,268 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
   tn = r / rows;
 }
 
+// ------------------------------------------------------------- persistent
+// tile_coords over a tile count padded to a multiple of 8: false for an id
+// past the tiles_m x tiles_n tiles.
+__device__ __forceinline__ bool tile_coords_padded(int t, int t_pad, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int v = (t & 7) * (t_pad >> 3) + (t >> 3);
+  if (v >= tiles_m * tiles_n) return false;
+  constexpr int kBand = 8;
+  const int per_band = kBand * tiles_n;
+  const int band = v / per_band;
+  const int first = band * kBand;
+  const int rows = tiles_m - first < kBand ? tiles_m - first : kBand;
+  const int r = v - band * per_band;
+  tm = first + r % rows;
+  tn = r / rows;
+  return true;
+}
+
+// One output tile of a persistent walk: its corner and operand bases.
+struct TileRef {
+  int64_t m0, n0;
+  const uint8_t* a;   // A + m0 * K
+  const uint8_t* b;   // B (of the tile's group) + n0 * K
+  const float* sb;    // weight scales of the tile's group
+};
+
+// Dense tiles: every id below tiles_m x tiles_n is a tile.
+struct DenseTiles {
+  const uint8_t* A;
+  const uint8_t* B;
+  const float* SB;
+  int64_t K;
+  int tiles_m, tiles_n, t_pad, bm, bn;
+  __device__ __forceinline__ bool get(int t, TileRef& r) const {
+    int tm, tn;
+    if (!tile_coords_padded(t, t_pad, tiles_m, tiles_n, tm, tn)) return false;
+    r.m0 = (int64_t)tm * bm;
+    r.n0 = (int64_t)tn * bn;
+    r.a = A + r.m0 * K;
+    r.b = B + r.n0 * K;
+    r.sb = SB;
+    return true;
+  }
+};
+
+// Grouped tiles: 128-row blocks of a 128-aligned group layout; a block whose
+// first row is padding (-1 or out of range) is not a tile.
+struct GroupedTiles {
+  const uint8_t* A;
+  const uint8_t* B;
+  const float* SB;
+  const int32_t* m_indices;
+  int64_t M, N, K;
+  int num_groups, tiles_m, tiles_n, t_pad;
+  __device__ __forceinline__ bool get(int t, TileRef& r) const {
+    int tm, tn;
+    if (!tile_coords_padded(t, t_pad, tiles_m, tiles_n, tm, tn)) return false;
+    r.m0 = (int64_t)tm * 128;
+    // A scalar load (constant address space, uniform address): a vector load
+    // here would make its use wait for every copy in flight, the next tile's
+    // prefetch included.
+    const int g = ((const __attribute__((address_space(4))) int32_t*)m_indices)[r.m0];
+    if (g < 0 || g >= num_groups) return false;
+    r.n0 = (int64_t)tn * 256;
+    r.a = A + r.m0 * K;
+    r.b = B + (int64_t)g * N * K + r.n0 * K;
+    const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
+    r.sb = SB + (int64_t)g * NB * KB;
+    return true;
+  }
+};
+
+// The first tile id >= t (stepping by the grid) that is a tile, or t_pad.
+template <class Src>
+__device__ __forceinline__ int next_tile(const Src& src, int t, TileRef& r) {
+  for (; t < src.t_pad; t += (int)gridDim.x)
+    if (src.get(t, r)) return t;
+  return src.t_pad;
+}
+
+template <class C>
+__device__ __forceinline__ StageLoader<C> tile_loader(uint8_t* lds, const TileRef& t, const float* sa, int64_t sa_ld,
+                                                      int64_t M, int64_t N, int K, const uint32_t* voff, int wave,
+                                                      int lane) {
+  const int KB = K / kGroup;
+  const uint32_t a_rows = (uint32_t)(M - t.m0 < C::BM ? M - t.m0 : C::BM);
+  const uint32_t b_rows = (uint32_t)(N - t.n0 < C::BN ? N - t.n0 : C::BN);
+  const int64_t nblocks = (N + kGroup - 1) / kGroup;
+  int64_t nb_lane = t.n0 / kGroup + lane;
+  if (nb_lane >= nblocks) nb_lane = nblocks - 1;
+  return StageLoader<C>{lds,
+                        make_rsrc(t.a, a_rows * (uint32_t)K),
+                        make_rsrc(t.b, b_rows * (uint32_t)K),
+                        make_rsrc(sa + t.m0, (uint32_t)(((int64_t)KB * sa_ld - t.m0) * 4)),
+                        make_rsrc(t.sb, (uint32_t)(nblocks * KB * 4)),
+                        voff,
+                        (uint32_t)(sa_ld * 4),
+                        (uint32_t)(nb_lane * KB * 4),
+                        wave,
+                        lane};
+}
+
+__device__ __forceinline__ TileRef select_tile(bool first, const TileRef& x, const TileRef& y) {
+  TileRef r = y;
+  if (first) r = x;
+  return r;
+}
+
+// The bf16 results of a finished tile, packed while the next tile starts.
+template <class C>
+__device__ __forceinline__ void store_packed(uint16_t* __restrict__ d, const uint4 (&w)[C::MT][C::NT / 2],
+                                             int64_t M, int64_t N, int64_t m0, int64_t n0, int wm, int wn, int li,
+                                             int lg) {
+  const bool vec = (N % 8) == 0;
+#pragma unroll
+  for (int mt = 0; mt < C::MT; mt++) {
+    const int64_t row = m0 + wm * C::TM + 16 * mt + li;
+    if (row >= M) continue;
+    uint16_t* drow = d + row * N;
+#pragma unroll
+    for (int s = 0; s < C::NT / 2; s++) {
+      const int64_t c0 = n0 + wn * C::TN + 32 * s + 8 * lg;
+      if (vec && c0 + 8 <= N) {
+        *reinterpret_cast<uint4*>(drow + c0) = w[mt][s];
+      } else {
+        const uint32_t v[4] = {w[mt][s].x, w[mt][s].y, w[mt][s].z, w[mt][s].w};
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          if (c0 + e < N) drow[c0 + e] = (uint16_t)(e & 1 ? v[e / 2] >> 16 : v[e / 2] & 0xffff);
+      }
+    }
+  }
+}
+
+// Persistent walk over the tiles of `src`: workgroup w takes tiles w, w + G,
+// w + 2G, ... (G = the grid, a multiple of 8, so every tile of a workgroup
+// falls in its XCD's run).  The K pipeline runs on across tiles: during the
+// last STAGES - 1 chunks of a tile the copies already fetch the first chunks
+// of the next one, so no tile starts with an empty pipeline.  A finished
+// tile's results are rounded and packed to registers, and (three stages)
+// stored after the next chunk's barrier; the chunk after that waits for every
+// outstanding memory operation (the stores included) before its barrier.
+// With two stages every chunk already starts with that wait, so the results
+// are stored as soon as they are packed.  Needs
+// K / 128 >= STAGES - 1.  Per output element the arithmetic is that of
+// gemm_tile, so the results are bit-identical.
+template <class C, class Src>
+__device__ __forceinline__ void gemm_persistent(uint8_t* lds, const Src& src, const float* sa, int64_t sa_ld,
+                                                uint16_t* __restrict__ d, int64_t M, int64_t N, int K) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
+  const int li = lane & 15, lg = lane >> 4;
+  const int KB = K / kGroup;
+  const int G = (int)gridDim.x;
+
+  TileRef cur, nxt;
+  int t = next_tile(src, (int)blockIdx.x, cur);
+  if (t >= src.t_pad) return;  // uniform, before any barrier
+  int tn_ = next_tile(src, t + G, nxt);
+  bool has_next = tn_ < src.t_pad;
+  if (!has_next) nxt = cur;
+
+  uint32_t voff[StageLoader<C>::NSEG];
+  stage_offsets<C>(voff, (uint32_t)K, wave, lane);
+  const FragAddr aa = frag_addr(C::A_OFF, wm * C::TM, li, lg);
+  const FragAddr ba = frag_addr(C::B_OFF, wn * C::TN, li, lg);
+  const uint32_t sa_addr = C::S_OFF + (uint32_t)(wm * C::TM + li) * 4u;
+  const uint32_t sb_addr = C::S_OFF + C::SB_IN_S + (uint32_t)((wn * C::TN) / kGroup) * 4u;
+
+  v4f_t acc[C::MT][C::NT];
+#pragma unroll
+  for (int i = 0; i < C::MT; i++)
+#pragma unroll
+    for (int j = 0; j < C::NT; j++) acc[i][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+  v8i_t af[C::MT];
+  float sc[C::MT];
+  uint4 pend[C::MT][C::NT / 2];
+  int64_t pend_m0 = 0, pend_n0 = 0;
+
+  {
+    const StageLoader<C> l0 = tile_loader<C>(lds, cur, sa, sa_ld, M, N, K, voff, wave, lane);
+    l0.all(0, 0);
+    if (C::STAGES == 3) l0.all(1, 1);
+  }
+  int pending = 0;  // three stages: 1 = packed results to store, 2 = their stores in flight
+  int stage = 0, kb = 0;
+  while (true) {
+    const int load_stage = stage == 0 ? C::STAGES - 1 : stage - 1;
+    // The chunk this iteration copies: STAGES - 1 ahead, in this tile or the
+    // next (the last tile repeats its last chunk into a stage never read).
+    const int q = kb + C::STAGES - 1;
+    const bool in_cur = q < KB || !has_next;
+    const int next_kb = q < KB ? q : (has_next ? q - KB : KB - 1);
+    const StageLoader<C> ld = tile_loader<C>(lds, select_tile(in_cur, cur, nxt), sa, sa_ld, M, N, K, voff, wave,
+                                             lane);
+    if (C::STAGES == 2 || pending == 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (pending == 2) pending = 0;
+    } else if (wave < 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (StageLoader<C>::NSEG + 1));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | StageLoader<C>::NSEG);
+    }
+    barrier_no_fence();
+    if (pending == 1) {
+      store_packed<C>(d, pend, M, N, pend_m0, pend_n0, wm, wn, li, lg);
+      pending = 2;
+    }
+    if (wave < 2) ld.issue(StageLoader<C>::NSEG, load_stage, next_kb);  // scales
+    read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
+    mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, load_stage, af, sc, nullptr, acc, ld, next_kb);
+    stage = stage + 1 == C::STAGES ? 0 : stage + 1;
+    if (kb + 1 < KB) {
+      kb++;
+      continue;
+    }
+    // Tile done: pack its results (two stages: store them at once, the next
+    // chunk drains every outstanding operation anyway), start the next tile.
+#pragma unroll
+    for (int mt = 0; mt < C::MT; mt++) {
+#pragma unroll
+      for (int s2 = 0; s2 < C::NT / 2; s2++) pend[mt][s2] = pack8<C>(acc[mt], s2);
+#pragma unroll
+      for (int j = 0; j < C::NT; j++) acc[mt][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    if constexpr (C::STAGES == 2) {
+      store_packed<C>(d, pend, M, N, cur.m0, cur.n0, wm, wn, li, lg);
+    } else {
+      pend_m0 = cur.m0;
+      pend_n0 = cur.n0;
+      pending = 1;
+    }
+    if (!has_next) break;
+    cur = nxt;
+    t = tn_;
+    tn_ = next_tile(src, t + G, nxt);
+    has_next = tn_ < src.t_pad;
+    if (!has_next) nxt = cur;
+    kb = 0;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
+  if constexpr (C::STAGES == 3) store_packed<C>(d, pend, M, N, pend_m0, pend_n0, wm, wn, li, lg);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_nt_persistent_kernel(DenseTiles src, const float* __restrict__ SA,
+                                                                        uint16_t* __restrict__ D, int64_t M,
+                                                                        int64_t N, int K, int64_t sa_ld) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  gemm_persistent<C>(lds, src, SA, sa_ld, D, M, N, K);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_persistent_kernel(GroupedTiles src,
+                                                                                const float* __restrict__ SA,
+                                                                                uint16_t* __restrict__ D, int64_t M,
+                                                                                int64_t N, int K, int64_t sa_ld) {
+  static_assert(C::BM == 128 && C::BN == 256, "grouped tiles are 128x256");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  gemm_persistent<C>(lds, src, SA, sa_ld, D, M, N, K);
+}
+
 template <class C, bool FP8OUT, bool UE8M0>
 __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __restrict__ A, const float* __restrict__ SA,
                                                              const uint8_t* __restrict__ B,
@@ -618,6 +880,31 @@ const char* gemm_kind_name(GemmKind kind) {
   return "?";
 }
 
+// Persistent walk (gemm_persistent) or one workgroup per tile.  Tuning and
+// test override: FGFP8_PERSISTENT=0|1.  The walk needs K >= 256 (two chunks
+// per tile keep a finished tile's stores ahead of the next pack).
+bool use_persistent(int64_t k) {
+  if (k < 2 * kGroup) return false;
+  if (const char* force = getenv("FGFP8_PERSISTENT")) return strcmp(force, "0") != 0;
+  return false;
+}
+
+// Workgroups of a persistent launch: one per compute unit (the tiles' LDS
+// allows one per CU), a multiple of 8, at most the padded tile count.
+static int persistent_grid(int t_pad) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kCUs;
+    cus[dev] = n;
+  }
+  int g = cus[dev] / 8 * 8;
+  if (g < 8) g = 8;
+  return g < t_pad ? g : t_pad;
+}
+
 template <class C>
 static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
                               const TileOut& out, int64_t m, int64_t n, int64_t k, hipStream_t stream,
@@ -625,6 +912,13 @@ static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, con
   const int tiles_m = (int)((m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
   const dim3 grid((uint32_t)tiles_m * tiles_n), block(C::THREADS);
   const uint8_t *pa = static_cast<const uint8_t*>(a), *pb = static_cast<const uint8_t*>(b);
+  if (!ue8m0 && out.q == nullptr && use_persistent(k)) {
+    const int t_pad = (tiles_m * tiles_n + 7) / 8 * 8;
+    const DenseTiles src{pa, pb, sb, k, tiles_m, tiles_n, t_pad, C::BM, C::BN};
+    hipLaunchKernelGGL(gemm_nt_persistent_kernel<C>, dim3((uint32_t)persistent_grid(t_pad)), block, 0, stream, src,
+                       sa, out.d, m, n, (int)k, sa_ld);
+    return hipGetLastError();
+  }
   if (ue8m0)
     hipLaunchKernelGGL((gemm_nt_kernel<C, false, true>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
                        sa_ld, tiles_m, tiles_n);
@@ -731,6 +1025,14 @@ hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, co
                                int64_t k, hipStream_t stream) {
   using C = Tile128x256;
   const int tiles_m = (int)(m / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
+  if (use_persistent(k)) {
+    const int t_pad = (tiles_m * tiles_n + 7) / 8 * 8;
+    const GroupedTiles src{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), sb, m_indices, m, n, k,
+                           (int)num_groups, tiles_m, tiles_n, t_pad};
+    hipLaunchKernelGGL(grouped_gemm_nt_persistent_kernel<C>, dim3((uint32_t)persistent_grid(t_pad)),
+                       dim3(C::THREADS), 0, stream, src, sa, static_cast<uint16_t*>(d), m, n, (int)k, sa_ld);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(grouped_gemm_nt_kernel<C>, dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
                      static_cast<const uint8_t*>(a), sa, m_indices, static_cast<const uint8_t*>(b), sb,
                      static_cast<uint16_t*>(d), m, n, (int)k, sa_ld, (int)num_groups, tiles_m, tiles_n);

@@ -56,6 +56,8 @@ constexpr int64_t kFusedMaxK = 32768;
 hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
                                int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream);
 
+// Whether a product with this K runs the persistent tile walk.
+bool use_persistent(int64_t k);
 hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
                                const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream);

@@ -249,3 +249,27 @@ def test_graph_replays_match_eager():
         assert torch.equal(d_big.view(torch.int16), ref_big.view(torch.int16)), f"replay {i}: gemm differs"
         work()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def _product(lin, env, monkeypatch):
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    _q, _sa, _qb, _sb, d = gpu_hot_path(lin)
+    return d
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("m,n,k", [(200, 300, 256), (2100, 1800, 384), (513, 4000, 640), (4096, 3000, 1280)])
+def test_persistent_walk_matches_per_tile_kernel(tile, m, n, k, monkeypatch):
+    """The persistent tile walk (several tiles per workgroup, the next tile's
+    chunks fetched during the current tile's last ones, ragged M and N edges,
+    the minimum K of two chunks) gives the same bits as one workgroup per
+    tile, and meets the oracle on sampled rows."""
+    lin = workloads.random_linear(m, n, k, seed=m + n + k + len(tile))
+    print(f"persistent {tile} {m}x{n}x{k}", flush=True)
+    base = _product(lin, {"FGFP8_GEMM_TILE": tile, "FGFP8_PERSISTENT": "0"}, monkeypatch)
+    monkeypatch.setenv("FGFP8_PERSISTENT", "1")
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    assert torch.equal(base.view(torch.int16), d.view(torch.int16))
+    rng = np.random.default_rng(m)
+    check_sampled(lin, q, sa, qb, sb, d, sample_rows(m, 16, rng), sample_col_blocks(n, 4, rng), f"persistent {tile}")

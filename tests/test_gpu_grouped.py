@@ -66,6 +66,7 @@ def check_groups(g, q, sa, qb, sb, d, groups=None, rows_per_group=None, cblocks=
         ([300, 129, 64, 0, 1], 200, 512),
         ([128], 384, 256),
         ([1] * 9, 128, 128),
+        ([700, 1000, 260, 0, 513], 512, 384),
     ],
 )
 def test_small_grouped_cases(sizes, n, k):
@@ -110,3 +111,21 @@ def test_grouped_deterministic():
     _, _, _, _, d2 = gpu_grouped(g)
     real = torch.from_numpy(g.m_indices >= 0).cuda()
     assert torch.equal(d1[real].view(torch.int16), d2[real].view(torch.int16))
+
+
+@pytest.mark.parametrize(
+    "sizes,n,k",
+    [([300, 129, 64, 0, 1], 512, 256), ([700, 1000, 260, 0, 513], 768, 384), ([5, 0, 2000, 1, 128, 900], 4096, 640)],
+)
+def test_persistent_walk_matches_per_block_kernel(sizes, n, k, monkeypatch):
+    """The persistent walk over the grouped layout (padding blocks skipped,
+    several tiles per workgroup) gives the same bits as one workgroup per
+    block."""
+    g = workloads.small_grouped(sizes, n, k, seed=sum(sizes) + 7)
+    monkeypatch.setenv("FGFP8_PERSISTENT", "0")
+    _, _, _, _, d1 = gpu_grouped(g)
+    monkeypatch.setenv("FGFP8_PERSISTENT", "1")
+    q, sa, qb, sb, d2 = gpu_grouped(g)
+    real = torch.from_numpy(g.m_indices >= 0).cuda()
+    assert torch.equal(d1[real].view(torch.int16), d2[real].view(torch.int16))
+    check_groups(g, q, sa, qb, sb, d2, rows_per_group=16)
