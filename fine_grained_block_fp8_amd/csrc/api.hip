@@ -63,9 +63,10 @@ int launched(hipError_t e, const char* who) {
   return FGFP8_OK;
 }
 
-// K is at most 2^24 so that tile offsets (<= 256 rows * K) fit the 32-bit
-// buffer offsets the kernels use.
-constexpr int64_t kMaxK = int64_t(1) << 24;
+// K is below 2^24 so that a tile's operand bytes (256 rows * K) fit the
+// 32-bit record counts and offsets of the buffer resources the kernels use
+// (at K = 2^24 exactly, 256 * K wraps to zero).
+constexpr int64_t kMaxK = (int64_t(1) << 24) - 128;
 constexpr int64_t kMaxRows = int64_t(1) << 31;
 
 int check_k(const char* who, int64_t k) {

@@ -17,8 +17,8 @@
  * Conventions shared by every call:
  *  - Every pointer argument is a DEVICE pointer (memory of the current HIP
  *    device), owned by the caller.  The library never allocates, frees or
- *    synchronizes, never reads device data on the host, and keeps no state
- *    between calls; every call is legal under HIP graph capture.
+ *    synchronizes, never reads device data on the host, and keeps no device
+ *    state between calls; every call is legal under HIP graph capture.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *    legacy default stream) and runs asynchronously: a return of FGFP8_OK
  *    means the work was enqueued, not that it finished.
@@ -29,6 +29,10 @@
  *    enqueued and fgfp8_last_error() describes the cause.  No C++ exception
  *    crosses this interface.
  *  - Empty problems (m == 0 or n == 0) enqueue nothing and return FGFP8_OK.
+ *  - Size limits (the kernels address a tile with 32-bit buffer offsets):
+ *    row counts below 2^31; k a positive multiple of 128 below 2^24; an
+ *    activation scale array (k/128 * sa_ld floats) below 2 GiB.  Larger
+ *    sizes are rejected with FGFP8_EINVAL.
  *  - Calls on one stream are ordered; calls on different streams that write
  *    the same output race.
  */

@@ -122,6 +122,8 @@ def test_gemm_rejects():
     assert call(b=P + 2) == fg.FGFP8_EINVAL
     assert call(n=-3) == fg.FGFP8_EINVAL
     assert call(k=1 << 25) == fg.FGFP8_EINVAL
+    assert call(k=1 << 24) == fg.FGFP8_EINVAL  # 256 rows * K would wrap the 32-bit buffer size
+    assert "exceeds" in fg.last_error()
     # empty problems are a valid no-op, even without a device
     assert call(m=0) == fg.FGFP8_OK
     assert call(n=0) == fg.FGFP8_OK
