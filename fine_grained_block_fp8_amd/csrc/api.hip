@@ -76,8 +76,8 @@ int check_k(const char* who, int64_t k) {
 }
 
 int check_sa(const char* who, int64_t m, int64_t k, int64_t sa_ld) {
-  if (sa_ld < m || sa_ld % 4 != 0 || sa_ld <= 0)
-    return fail(FGFP8_EINVAL, "%s: sa_ld=%lld must be a positive multiple of 4 and >= m=%lld", who,
+  if (sa_ld < m || sa_ld % 4 != 0 || sa_ld < 0)
+    return fail(FGFP8_EINVAL, "%s: sa_ld=%lld must be a non-negative multiple of 4 and >= m=%lld", who,
                 (long long)sa_ld, (long long)m);
   if ((k / 128) * sa_ld * 4 >= (int64_t(1) << 31))
     return fail(FGFP8_EINVAL, "%s: activation scale array (k/128 * sa_ld floats) exceeds 2 GiB", who);
@@ -102,10 +102,10 @@ int quantize_groups_impl(const char* who, bool ue8m0, const void* x_bf16, int64_
   if (m < 0 || m >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m=%lld out of range", who, (long long)m);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (m == 0) return FGFP8_OK;  // empty: nothing to enqueue, pointers may be null
   if (!x_bf16 || !q_e4m3 || !sa) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(sa))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (m == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   return launched(fgfp8::launch_quantize_groups(x_bf16, m, k, q_e4m3, sa, sa_ld, (hipStream_t)stream, ue8m0), who);
 }
@@ -114,10 +114,10 @@ int quantize_blocks_impl(const char* who, bool ue8m0, const void* w_bf16, int64_
                          float* sb, void* stream) {
   if (n < 0 || (n + 127) / 128 > 65535) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);
   if (int rc = check_k(who, k)) return rc;
+  if (n == 0) return FGFP8_OK;
   if (!w_bf16 || !q_e4m3 || !sb) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(w_bf16) || !aligned16(q_e4m3) || !aligned16(sb))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   return launched(fgfp8::launch_quantize_blocks(w_bf16, n, k, q_e4m3, sb, (hipStream_t)stream, ue8m0), who);
 }
@@ -128,10 +128,10 @@ int gemm_impl(const char* who, bool ue8m0, const void* a_e4m3, const float* sa, 
     return fail(FGFP8_EINVAL, "%s: m=%lld n=%lld out of range", who, (long long)m, (long long)n);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (m == 0 || n == 0) return FGFP8_OK;
   if (!a_e4m3 || !sa || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(d_bf16))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (m == 0 || n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
   if (env_flag("FGFP8_PRINT_CONFIG"))
@@ -183,11 +183,11 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
   if (num_groups < 1) return fail(FGFP8_EINVAL, "%s: num_groups=%d must be >= 1", who, (int)num_groups);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (m == 0 || n == 0) return FGFP8_OK;
   if (!a_e4m3 || !sa || !m_indices || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(m_indices) || !aligned16(b_e4m3) || !aligned16(sb) ||
       !aligned16(d_bf16))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (m == 0 || n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   if (env_flag("FGFP8_PRINT_CONFIG"))
     fprintf(stderr, "[fgfp8] m_grouped_fp8_gemm_nt_contiguous m=%lld n=%lld k=%lld groups=%d: %s\n", (long long)m,
@@ -206,14 +206,15 @@ int fp8_gemm_nt_fp8_out(const void* a_e4m3, const float* sa, int64_t sa_ld, cons
     return fail(FGFP8_EINVAL, "%s: n=%lld must be a non-negative multiple of 128", who, (long long)n);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, m, k, sa_ld)) return rc;
-  if (sd_ld < m || sd_ld % 4 != 0 || sd_ld <= 0 || (n / 128) * sd_ld * 4 >= (int64_t(1) << 31))
-    return fail(FGFP8_EINVAL, "%s: sd_ld=%lld must be a positive multiple of 4, >= m=%lld (and n/128 * sd_ld < 2^29)",
-                who, (long long)sd_ld, (long long)m);
+  if (sd_ld < m || sd_ld % 4 != 0 || sd_ld < 0 || (n / 128) * sd_ld * 4 >= (int64_t(1) << 31))
+    return fail(FGFP8_EINVAL,
+                "%s: sd_ld=%lld must be a non-negative multiple of 4, >= m=%lld (and n/128 * sd_ld < 2^29)", who,
+                (long long)sd_ld, (long long)m);
+  if (m == 0 || n == 0) return FGFP8_OK;
   if (!a_e4m3 || !sa || !b_e4m3 || !sb || !q_e4m3 || !sd) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(q_e4m3) ||
       !aligned16(sd) || (d_bf16 && !aligned16(d_bf16)))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (m == 0 || n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   const fgfp8::GemmKind kind = fgfp8::plan_tiles(m, n, k);
   if (env_flag("FGFP8_PRINT_CONFIG"))
@@ -235,11 +236,11 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
   if (n < 0 || n >= kMaxRows) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, (int64_t)num_groups * max_m, k, sa_ld)) return rc;
+  if (max_m == 0 || n == 0) return FGFP8_OK;
   if (!a_e4m3 || !sa || !masked_m || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(masked_m) || !aligned16(b_e4m3) || !aligned16(sb) ||
       !aligned16(d_bf16))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (max_m == 0 || n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   const fgfp8::GemmKind kind = fgfp8::plan_masked(num_groups, max_m, expected_m, n);
   if (env_flag("FGFP8_PRINT_CONFIG"))
@@ -291,10 +292,10 @@ int moe_gather_quantize(const void* x_bf16, int64_t tokens, int64_t k, const int
   if (tokens < 0 || tokens >= kMaxRows) return fail(FGFP8_EINVAL, "%s: tokens out of range", who);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, m_pad_max, k, sa_ld)) return rc;
+  if (m_pad_max == 0) return FGFP8_OK;
   if ((tokens > 0 && !x_bf16) || !token_of_row || !q_e4m3 || !sa) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(sa))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (m_pad_max == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   return launched(fgfp8::launch_moe_gather_quantize(x_bf16, tokens, k, token_of_row, m_pad_max, q_e4m3, sa, sa_ld,
                                                     (hipStream_t)stream),
@@ -307,10 +308,10 @@ int silu_mul_quantize(const void* h_bf16, int64_t m, int64_t inter, const int32_
   if (m < 0 || m >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m=%lld out of range", who, (long long)m);
   if (int rc = check_k(who, inter)) return rc;
   if (int rc = check_sa(who, m, inter, sa_ld)) return rc;
+  if (m == 0) return FGFP8_OK;
   if (!h_bf16 || !m_indices || !q_e4m3 || !sa) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(h_bf16) || !aligned16(q_e4m3) || !aligned16(sa))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (m == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   return launched(fgfp8::launch_moe_silu_mul_quantize(h_bf16, m, inter, m_indices, q_e4m3, sa, sa_ld,
                                                       (hipStream_t)stream),
@@ -324,11 +325,11 @@ int moe_combine(const void* y_bf16, int64_t y_rows, int64_t hdim, const int32_t*
   if (tokens < 0 || tokens >= kMaxRows) return fail(FGFP8_EINVAL, "%s: tokens out of range", who);
   if (topk < 1 || topk > 8) return fail(FGFP8_EINVAL, "%s: topk=%d must be 1..8", who, (int)topk);
   if (hdim <= 0 || hdim % 8 != 0) return fail(FGFP8_EINVAL, "%s: hdim=%lld must be a positive multiple of 8", who, (long long)hdim);
+  if (tokens == 0) return FGFP8_OK;
   if ((y_rows > 0 && !y_bf16) || !row_of || !topk_weights || !out_bf16)
     return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(y_bf16) || !aligned16(out_bf16))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (tokens == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   return launched(fgfp8::launch_moe_combine(y_bf16, y_rows, hdim, row_of, topk_weights, tokens, topk, out_bf16,
                                             (hipStream_t)stream),
@@ -341,6 +342,7 @@ int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, 
   if (m < 0 || m >= kMaxRows || n < 0 || n >= kMaxRows)
     return fail(FGFP8_EINVAL, "%s: m=%lld n=%lld out of range", who, (long long)m, (long long)n);
   if (int rc = check_k(who, k)) return rc;
+  if (m == 0 || n == 0) return FGFP8_OK;
   if (!x_bf16 || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if ((q_e4m3 == nullptr) != (sa == nullptr))
     return fail(FGFP8_EINVAL, "%s: q_e4m3 and sa must be given together", who);
@@ -353,7 +355,6 @@ int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, 
   }
   if (!aligned16(x_bf16) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(d_bf16))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
-  if (m == 0 || n == 0) return FGFP8_OK;
   if (int rc = check_device(who)) return rc;
   if (fused) {
     if (env_flag("FGFP8_PRINT_CONFIG"))

@@ -28,7 +28,8 @@
  *  - Return value: FGFP8_OK (0) or an error code below; on error nothing was
  *    enqueued and fgfp8_last_error() describes the cause.  No C++ exception
  *    crosses this interface.
- *  - Empty problems (m == 0 or n == 0) enqueue nothing and return FGFP8_OK.
+ *  - Empty problems (m == 0 or n == 0) enqueue nothing and return FGFP8_OK
+ *    once the sizes are valid; their array pointers may then be null.
  *  - Size limits (the kernels address a tile with 32-bit buffer offsets):
  *    row counts below 2^31; k a positive multiple of 128 below 2^24; an
  *    activation scale array (k/128 * sa_ld floats) below 2 GiB.  Larger

@@ -218,6 +218,27 @@ def test_moe_calls_reject():
     assert lib.moe_combine(P, 64, 128, P, P, 0, 4, P, None) == fg.FGFP8_OK
 
 
+def test_empty_problems_accept_null_pointers():
+    """An empty problem validates its sizes, then returns FGFP8_OK without
+    looking at its (possibly null) pointers -- what an empty tensor passes."""
+    lib = _lib()
+    N = None
+    assert lib.quantize_fp8_groups(N, 0, 256, N, N, 0, None) == fg.FGFP8_OK
+    assert lib.quantize_fp8_groups_ue8m0(N, 0, 256, N, N, 0, None) == fg.FGFP8_OK
+    assert lib.quantize_fp8_groups(N, 0, 200, N, N, 0, None) == fg.FGFP8_EINVAL  # sizes still checked
+    assert lib.quantize_fp8_blocks(N, 0, 256, N, N, None) == fg.FGFP8_OK
+    assert lib.fp8_gemm_nt(N, N, 0, N, N, N, 0, 16, 256, None) == fg.FGFP8_OK
+    assert lib.fp8_gemm_nt(N, N, 8, N, N, N, 8, 0, 256, None) == fg.FGFP8_OK
+    assert lib.fp8_gemm_nt_ue8m0(N, N, 0, N, N, N, 0, 16, 256, None) == fg.FGFP8_OK
+    assert lib.m_grouped_fp8_gemm_nt_contiguous(N, N, 0, N, N, N, 4, N, 0, 128, 256, None) == fg.FGFP8_OK
+    assert lib.m_grouped_fp8_gemm_nt_masked(N, N, 0, N, N, N, 4, 0, 0, N, 128, 256, None) == fg.FGFP8_OK
+    assert lib.fp8_gemm_nt_fp8_out(N, N, 0, N, N, N, N, 0, N, 0, 256, 256, None) == fg.FGFP8_OK
+    assert lib.fp8_linear_nt(N, 0, 256, N, N, 128, N, N, N, 0, None) == fg.FGFP8_OK
+    assert lib.moe_gather_quantize(N, 0, 256, N, 0, N, N, 0, None) == fg.FGFP8_OK
+    assert lib.silu_mul_quantize(N, 0, 128, N, N, N, 0, None) == fg.FGFP8_OK
+    assert lib.moe_combine(N, 0, 128, N, N, 0, 4, N, None) == fg.FGFP8_OK
+
+
 def test_linear_rejects():
     lib = _lib()
 

@@ -19,6 +19,7 @@ from tests.parity import (
     magnitude_sum,
     sample_col_blocks,
     sample_rows,
+    to_dev_bf16,
     to_dev_u8_fp8,
 )
 
@@ -273,3 +274,37 @@ def test_persistent_walk_matches_per_tile_kernel(tile, m, n, k, monkeypatch):
     assert torch.equal(base.view(torch.int16), d.view(torch.int16))
     rng = np.random.default_rng(m)
     check_sampled(lin, q, sa, qb, sb, d, sample_rows(m, 16, rng), sample_col_blocks(n, 4, rng), f"persistent {tile}")
+
+
+def test_empty_problems_through_the_binding():
+    """Zero rows (or columns) through every call: nothing is written, no error."""
+    dev = "cuda"
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    q, sa = fg.quantize_fp8_groups(x)
+    assert q.shape == (0, 256) and sa.shape == (2, 0)
+    q8, sa8 = fg.quantize_fp8_groups(x, ue8m0=True)
+    assert q8.shape == (0, 256)
+    qb, sb = fg.quantize_fp8_blocks(torch.empty((0, 256), dtype=torch.bfloat16, device=dev))
+    assert qb.shape == (0, 256)
+    lin = workloads.random_linear(8, 128, 256, seed=5)
+    wq, ws = fg.quantize_fp8_blocks(to_dev_bf16(lin.b))
+    d = torch.empty((0, 128), dtype=torch.bfloat16, device=dev)
+    fg.fp8_gemm_nt((q, sa), (wq, ws), d)
+    fg.fp8_gemm_nt((q, sa), (wq, ws), d, ue8m0=True)
+    assert fg.fp8_linear(x, (wq, ws)).shape == (0, 128)
+    qo, so = fg.fp8_gemm_nt_fp8_out((q, sa), (wq, ws))
+    assert qo.shape == (0, 128)
+    xa = to_dev_bf16(lin.a)
+    qa, saa = fg.quantize_fp8_groups(xa)
+    d0 = torch.empty((8, 0), dtype=torch.bfloat16, device=dev)
+    fg.fp8_gemm_nt((qa, saa), (wq[:0], ws[:0]), d0)
+    # the MoE layer with no tokens
+    idx = torch.empty((0, 2), dtype=torch.int32, device=dev)
+    wts = torch.empty((0, 2), dtype=torch.float32, device=dev)
+    w1 = fg.quantize_fp8_blocks(torch.zeros((2 * 256, 256), dtype=torch.bfloat16, device=dev))
+    w2 = fg.quantize_fp8_blocks(torch.zeros((2 * 256, 128), dtype=torch.bfloat16, device=dev))
+    w1 = (w1[0].view(2, 256, 256), w1[1].view(2, 2, 2))
+    w2 = (w2[0].view(2, 256, 128), w2[1].view(2, 2, 1))
+    out = fg.moe_fp8_layer(torch.empty((0, 256), dtype=torch.bfloat16, device=dev), idx, wts, w1, w2)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
