@@ -22,7 +22,7 @@ graph see the same device time).  Also reported:
 * roofline: the dominant kernel's algorithmic TFLOP/s from HIP events on the
   launch stream (created without the system-scope fence, so that recording
   them barely disturbs the step), against the 5.0 PFLOP/s dense FP8 peak;
-* decode: M=1 linears (act-quant included per call) in GB/s against 8 TB/s,
+* decode: M = 1, 4, 16 linears (act-quant included per call) in GB/s against 8 TB/s,
   timed by graph replay over 8 rotating weight sets so that the weights stream
   from HBM rather than the 256 MB last-level cache;
 * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
@@ -306,13 +306,15 @@ def roofline_of(per):
 
 
 # ------------------------------------------------------------------- decode
-def bench_decode(fg, torch, m=1, shapes=((12288, 4096), (4096, 12288)), sets=8, reps=50):
-    """Act-quant + product per call, M=1; 8 rotating weight sets (8 x 50 MB >
-    256 MB last-level cache) replayed from a HIP graph, and eagerly."""
+def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288)), sets=8, reps=50):
+    """Act-quant + product per call at M = 1, 4, 16; 8 rotating weight sets
+    (8 x 50 MB > 256 MB last-level cache) replayed from a HIP graph, and
+    eagerly.  M <= 4 runs the fused kernel; M = 16 the quantizer and the
+    decode product (two launches)."""
     import workloads
 
     out = []
-    for n, k in shapes:
+    for m, (n, k) in [(m_, sh) for m_ in ms for sh in shapes]:
         lin = workloads.decode_linear(m, n, k)
         x = dev_bf16(lin.a, torch)
         w = dev_bf16(lin.b, torch)
@@ -320,11 +322,14 @@ def bench_decode(fg, torch, m=1, shapes=((12288, 4096), (4096, 12288)), sets=8, 
         del w
         weights = [(qb0, sb0)] + [(qb0.clone(), sb0.clone()) for _ in range(sets - 1)]
         d = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        fused = m <= fg.FUSED_MAX_M and k <= fg.FUSED_MAX_K
+        act = None if fused else (torch.empty((m, k), dtype=torch.float8_e4m3fn, device="cuda"),
+                                  torch.empty((k // 128, fg.padded_rows(m)), dtype=torch.float32, device="cuda"))
 
         def one_round():
-            # act-quant + product: one fused kernel per call (fp8_linear_nt)
+            # act-quant + product (one fused kernel per call for M <= 4)
             for qb, sb in weights:
-                fg.fp8_linear_nt(x, (qb, sb), d)
+                fg.fp8_linear_nt(x, (qb, sb), d, act)
 
         for _ in range(3):
             one_round()
@@ -362,7 +367,7 @@ def bench_decode(fg, torch, m=1, shapes=((12288, 4096), (4096, 12288)), sets=8, 
                 "m": m,
                 "n": n,
                 "k": k,
-                "kernel": "fused act-quant + " + fg.describe_gemm(m, n, k),
+                "kernel": ("fused act-quant + " if fused else "act-quant kernel + ") + fg.describe_gemm(m, n, k),
                 "bytes_per_call": nbytes,
                 "graph_us": round(graph_s * 1e6, 3),
                 "graph_gbs": round(nbytes / graph_s / 1e9, 1),
@@ -493,7 +498,7 @@ def main():
     if args.workload in ("prefill", "decode") and not args.no_decode:
         decode = bench_decode(fg, torch, reps=args.decode_reps)
         for r in decode:
-            log(f"decode M=1 N={r['n']} K={r['k']}: graph {r['graph_us']} us {r['graph_gbs']} GB/s; "
+            log(f"decode M={r['m']} N={r['n']} K={r['k']}: graph {r['graph_us']} us {r['graph_gbs']} GB/s; "
                 f"eager {r['eager_us']} us")
 
     cpu = None

@@ -51,8 +51,11 @@ __device__ __forceinline__ v4f_t mfma_fp8_dec(const v8i_t& x, const v8i_t& y) {
 // FUSED = false: A is E4M3 [M][K] with scales sa [K/128][sa_ld] in global
 // memory.  FUSED = true: X is bf16 [M][K] (M <= 4), quantized here; if q_out
 // is non-null, workgroup 0 also writes the quantized activation and its
-// scales (q_out [M][K], sa_out [K/128][sa_out_ld]).
-template <int KS, bool FUSED>
+// scales (q_out [M][K], sa_out [K/128][sa_out_ld]).  XA: activation loads per
+// lane issued ahead of the weight stream (loads complete in issue order, so
+// one issued after the stream can only be used once the whole stream has
+// arrived): 3 covers M = 1; 12 covers M <= 4 at the common K.
+template <int KS, bool FUSED, int XA = 3>
 __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict__ Ain, const float* __restrict__ SA,
                                                          int64_t sa_ld, const uint8_t* __restrict__ B,
                                                          const float* __restrict__ SB, uint16_t* __restrict__ D,
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
     // group), as quantize_fp8_groups).  The first kXAhead activation loads of
     // each lane go out before the weight loads, and the quantization runs
     // while the weight stream is in flight.
-    constexpr int kXAhead = 3;
+    constexpr int kXAhead = XA;
     const uint16_t* X = static_cast<const uint16_t*>(Ain);
     const int tasks = M * KB, step = KS * 4, part = threadIdx.x & 15, t0 = (int)(threadIdx.x >> 4);
     const rsrc_t rx = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
@@ -263,16 +266,16 @@ int decode_split(int64_t n, int64_t k) {
   return ks;
 }
 
-template <int KS, bool FUSED>
+template <int KS, bool FUSED, int XA>
 static hipError_t allow_lds() {
   // The fused variant holds the quantized activation (up to 4 x K bytes) in
   // LDS; allow dynamic LDS beyond the 64 KB default, once per kernel.
-  static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED>),
+  static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED, XA>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   return once;
 }
 
-template <int KS, bool FUSED>
+template <int KS, bool FUSED, int XA = 3>
 static hipError_t launch_decode_ks(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
                                    void* d, int64_t m, int64_t n, int64_t k, uint8_t* q_out, float* sa_out,
                                    int64_t sa_out_ld, hipStream_t stream) {
@@ -280,25 +283,25 @@ static hipError_t launch_decode_ks(const void* a, const float* sa, int64_t sa_ld
   if (FUSED) {
     lds += (size_t)kFusedMaxRows * k + (size_t)(k / kGroup) * kFusedMaxRows * 4;
     if (lds > 64 * 1024) {
-      const hipError_t e = allow_lds<KS, FUSED>();
+      const hipError_t e = allow_lds<KS, FUSED, XA>();
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL((decode_kernel<KS, FUSED>), dim3((uint32_t)((n + 15) / 16)), dim3(KS * 64), lds, stream, a, sa,
+  hipLaunchKernelGGL((decode_kernel<KS, FUSED, XA>), dim3((uint32_t)((n + 15) / 16)), dim3(KS * 64), lds, stream, a, sa,
                      sa_ld, static_cast<const uint8_t*>(b), sb, static_cast<uint16_t*>(d), (int)m, n, (int)k, q_out,
                      sa_out, sa_out_ld);
   return hipGetLastError();
 }
 
-template <bool FUSED>
+template <bool FUSED, int XA = 3>
 static hipError_t launch_decode_t(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b,
                                   const float* sb, void* d, int64_t m, int64_t n, int64_t k, uint8_t* q_out,
                                   float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
   switch (ks) {
-    case 1: return launch_decode_ks<1, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
-    case 2: return launch_decode_ks<2, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
-    case 4: return launch_decode_ks<4, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
-    default: return launch_decode_ks<8, FUSED>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 1: return launch_decode_ks<1, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 2: return launch_decode_ks<2, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 4: return launch_decode_ks<4, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    default: return launch_decode_ks<8, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
   }
 }
 
@@ -309,8 +312,15 @@ hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, 
 
 hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
                                int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
-  return launch_decode_t<true>(decode_split(n, k), x, nullptr, 0, b, sb, d, m, n, k, static_cast<uint8_t*>(q_out),
-                               sa_out, sa_out_ld, stream);
+  const int ks = decode_split(n, k);
+  // Activation quantize tasks (row, 128-group) per lane: M * K/128 over the
+  // workgroup's KS * 4 lanes-of-16.  When more than three, issue up to 12
+  // ahead of the weight stream.
+  const int64_t per_lane = (m * (k / kGroup) + ks * 4 - 1) / (ks * 4);
+  uint8_t* q = static_cast<uint8_t*>(q_out);
+  if (per_lane > 3 && per_lane <= 12)
+    return launch_decode_t<true, 12>(ks, x, nullptr, 0, b, sb, d, m, n, k, q, sa_out, sa_out_ld, stream);
+  return launch_decode_t<true>(ks, x, nullptr, 0, b, sb, d, m, n, k, q, sa_out, sa_out_ld, stream);
 }
 
 }  // namespace fgfp8
