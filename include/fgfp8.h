@@ -290,7 +290,12 @@ const char* fgfp8_last_error(void);
  * environment variable FGFP8_GEMM_TILE, set to one of the tile names
  * (tile256x256_w4x2, tile256x128_w4x2, tile128x256_w2x4, tile128x128_w2x2),
  * forces that tile in fp8_gemm_nt (tuning and tests); other values are
- * ignored. */
+ * ignored.  FGFP8_PERSISTENT=1 makes fp8_gemm_nt (bf16 output, FP32 scales)
+ * and m_grouped_fp8_gemm_nt_contiguous walk their tiles persistently (one
+ * workgroup per compute unit, the K pipeline continuing across tiles; same
+ * results bit for bit) for k >= 256; by default every tile is a workgroup of
+ * its own, which measured faster.  FGFP8_PRINT_CONFIG=1 prints each call's
+ * kernel choice to stderr. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
 
 #ifdef __cplusplus
