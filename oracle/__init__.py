@@ -20,12 +20,15 @@ What it computes, and where the pages define it:
                 docstring of the DeepGEMM plugin source).
                 The UE8M0 variants round each scale up to a power of two
                 (deepgemm-rust README, Blackwell key techniques: UE8M0 scale
-                factors; FP32 scales bridged to packed UE8M0).
+                factors; FP32 scales bridged to packed UE8M0); the MX variant
+                takes one such scale per 1x32 block (the README's gran-32
+                recipe), packed as E8M0 codes.
 * ``gemm``      the block-scaled product D = A.B^T with both scale sets applied
                 once per 128-wide K chunk, in FP64, and its M-grouped contiguous
                 variant (deepgemm-rust README, "What's implemented" table and
                 "Quick start" grouped example), and its masked variant (same
-                table, m_grouped_fp8_gemm_nt_masked row).
+                table, m_grouped_fp8_gemm_nt_masked row); and the MX product
+                with per-1x32 power-of-two scales on both operands.
 * ``moe``       the FP8 mixture-of-experts layer around the grouped product:
                 routing layout, gather, SiLU-times-up, weighted combine and the
                 whole layer (same table, moe_fp8_layer row).
@@ -41,13 +44,22 @@ force, closed forms and invariants).  No function is "parity unpinned".
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_table
 from .gemm import (
     gemm_nt,
+    gemm_nt_mx,
     gemm_nt_dequantized,
     grouped_gemm_nt,
     masked_grouped_gemm_nt,
     round_to_bf16,
 )
 from . import moe
-from .quantize import GROUP, quantize_blocks, quantize_blocks_ue8m0, quantize_groups, quantize_groups_ue8m0
+from .quantize import (
+    GROUP,
+    quantize_blocks,
+    quantize_blocks_ue8m0,
+    quantize_groups,
+    quantize_groups_ue8m0,
+    quantize_mx,
+    unpack_mx_scales,
+)
 
 __all__ = [
     "E4M3_MAX",
@@ -56,6 +68,7 @@ __all__ = [
     "e4m3_encode",
     "e4m3_table",
     "gemm_nt",
+    "gemm_nt_mx",
     "gemm_nt_dequantized",
     "grouped_gemm_nt",
     "masked_grouped_gemm_nt",
@@ -64,5 +77,7 @@ __all__ = [
     "quantize_groups",
     "quantize_groups_ue8m0",
     "quantize_blocks_ue8m0",
+    "quantize_mx",
+    "unpack_mx_scales",
     "round_to_bf16",
 ]

@@ -32,6 +32,7 @@ from __future__ import annotations
 import numpy as np
 
 from .e4m3 import e4m3_decode
+from .quantize import unpack_mx_scales
 
 GROUP = 128
 
@@ -158,3 +159,32 @@ def round_to_bf16(d: np.ndarray) -> np.ndarray:
         out = np.where(finite, out, d)
     bits = (out.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     return bits
+
+
+def gemm_nt_mx(qa, sa_packed, qb, sb_packed) -> np.ndarray:
+    """The MXFP8 product in FP64: with one power-of-two scale per 1x32 block
+    of each row of A and of B (E8M0 codes packed four to an int32, see
+    quantize_mx),
+
+        D[m, n] = sum_b 2^(ea[m, b] - 127) * 2^(eb[n, b] - 127) * P[m, n, b],
+        P[m, n, b] = sum_{k in block b} dec(qa[m, k]) * dec(qb[n, k]).
+
+    Every term is exact in FP64 (a block partial is a multiple of 2^-18 below
+    2^23, the scales are powers of two), so the only roundings are one per
+    accumulated term."""
+    qa = np.asarray(qa, dtype=np.uint8)
+    qb = np.asarray(qb, dtype=np.uint8)
+    m, k = qa.shape
+    n, k2 = qb.shape
+    if k != k2 or k % GROUP:
+        raise ValueError("A and B must share K, a multiple of 128")
+    ea = unpack_mx_scales(sa_packed, m)
+    eb = unpack_mx_scales(sb_packed, n)
+    a = e4m3_decode(qa)
+    b = e4m3_decode(qb)
+    d = np.zeros((m, n), dtype=np.float64)
+    for blk in range(k // 32):
+        cols = slice(32 * blk, 32 * blk + 32)
+        p = a[:, cols] @ b[:, cols].T  # exact
+        d += np.ldexp(p, (ea[:, blk] - 127)[:, None] + (eb[:, blk] - 127)[None, :])
+    return d

@@ -150,3 +150,51 @@ def quantize_blocks_ue8m0(w_bf16: np.ndarray):
             q[rows, cols] = e4m3_encode((block / s).astype(np.float32))
     return q, sb
 
+
+
+MX_BLOCK = 32
+
+
+def e8m0_code(s: np.ndarray) -> np.ndarray:
+    """E8M0 code (exponent + 127) of power-of-two float32 scales in
+    [2^-127, 2^127]."""
+    f, e = np.frexp(np.asarray(s, dtype=np.float64))  # s = 0.5 * 2^e exactly
+    if not np.all(f == 0.5):
+        raise ValueError("scales must be powers of two")
+    return (e - 1 + 127).astype(np.int64)
+
+
+def quantize_mx(x_bf16: np.ndarray, s_ld: int | None = None):
+    """MXFP8 recipe: one power-of-two scale per 1x32 block of each row (the
+    gran-32 recipe of the deepgemm-rust README, "Full recipes"; the scale rule
+    is _scale_of_ue8m0 over the block's amax, the same rule as the UE8M0
+    recipe at gran-128), element code E4M3(x / s).  Scales are stored as E8M0
+    codes, the four of a 128-column chunk packed in one int32 (byte j holds
+    block 4c + j; the pages' packed UE8M0 scale factors), MN-major:
+    s[c][row].  Entries of rows >= M are -1 (unspecified).
+
+    x_bf16: uint16 [M][K], K a multiple of 128.  Returns (q uint8 [M][K],
+    s int32 [K/128][s_ld]).  The same function quantizes a weight [N][K] (one
+    scale per 1x32 block of each weight row)."""
+    x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
+    m, k = x_bf16.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    if s_ld is None:
+        s_ld = -(-m // 4) * 4
+    x = bf16_bits_to_f32(x_bf16).reshape(m, k // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(x), axis=2) if m else np.zeros((0, k // MX_BLOCK), np.float32)
+    s = _scale_of_ue8m0(amax)
+    q = e4m3_encode((x / s[:, :, None]).astype(np.float32)).reshape(m, k)
+    codes = e8m0_code(s).reshape(m, k // GROUP, 4) if m else np.zeros((0, k // GROUP, 4), np.int64)
+    packed = codes[:, :, 0] | (codes[:, :, 1] << 8) | (codes[:, :, 2] << 16) | (codes[:, :, 3] << 24)
+    out = np.full((k // GROUP, s_ld), -1, dtype=np.int32)
+    out[:, :m] = packed.T.astype(np.uint32).view(np.int32)
+    return q, out
+
+
+def unpack_mx_scales(s_packed: np.ndarray, rows: int) -> np.ndarray:
+    """E8M0 codes [rows][K/32] of a packed scale array [K/128][>= rows]."""
+    p = np.asarray(s_packed, dtype=np.int32)[:, :rows].astype(np.uint32).T  # [rows][K/128]
+    codes = np.stack([(p >> (8 * j)) & 0xFF for j in range(4)], axis=2)  # [rows][K/128][4]
+    return codes.reshape(rows, -1).astype(np.int64)
