@@ -51,6 +51,8 @@ _lib.m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i3
 _lib.quantize_fp8_groups_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_blocks_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt_ue8m0.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
+_lib.quantize_fp8_mx.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp]
+_lib.fp8_gemm_nt_mx.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]
 _lib.moe_max_padded_rows.argtypes = [_i64, _i32, _i32]
 _lib.moe_max_padded_rows.restype = ctypes.c_int64
 _lib.moe_route_workspace_bytes.argtypes = [_i64, _i32]
@@ -65,7 +67,7 @@ _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
               "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
-              "moe_gather_quantize", "silu_mul_quantize", "moe_combine"):
+              "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -327,6 +329,43 @@ def fp8_linear(x: torch.Tensor, weight) -> torch.Tensor:
     return d.reshape(*x.shape[:-1], qb.shape[0])
 
 
+# ---------------------------------------------------------------- MX recipe
+def quantize_fp8_mx(x: torch.Tensor, s_ld: int | None = None, out=None):
+    """MXFP8 quantization: one power-of-two scale per 1x32 block of each row.
+    x: bf16 [M, K] (an activation, or a weight [N, K]).  Returns (q
+    float8_e4m3fn [M, K], s int32 [K/128, s_ld]) with the four E8M0 codes of
+    a 128-column chunk packed in each int32."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    m, k = x.shape
+    s_ld = padded_rows(m) if s_ld is None else int(s_ld)
+    if out is None:
+        out = (torch.empty((m, k), dtype=torch.float8_e4m3fn, device=x.device),
+               torch.empty((k // GROUP, s_ld), dtype=torch.int32, device=x.device))
+    q, sc = out
+    _need(q, "q", _FP8, 2)
+    _need(sc, "s", (torch.int32,), 2)
+    _check(_lib.quantize_fp8_mx(_ptr(x), m, k, _ptr(q), _ptr(sc), sc.shape[1], _stream(x)))
+    return q, sc
+
+
+def fp8_gemm_nt_mx(a, b, d: torch.Tensor) -> torch.Tensor:
+    """MXFP8 product: a = (q [M, K], s int32 [K/128, sa_ld]), b = (q [N, K],
+    s int32 [K/128, sb_ld]) from quantize_fp8_mx; d bf16 [M, N] in place."""
+    (qa, sa), (qb, sb) = a, b
+    _need(qa, "a", _FP8, 2)
+    _need(qb, "b", _FP8, 2)
+    _need(sa, "sa", (torch.int32,), 2)
+    _need(sb, "sb", (torch.int32,), 2)
+    _need(d, "d", (torch.bfloat16,), 2)
+    m, k = qa.shape
+    n = qb.shape[0]
+    if qb.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch among a [M, K], b [N, K], d [M, N]")
+    _check(_lib.fp8_gemm_nt_mx(_ptr(qa), _ptr(sa), sa.shape[1], _ptr(qb), _ptr(sb), sb.shape[1], _ptr(d), m, n, k,
+                               _stream(d)))
+    return d
+
+
 # ----------------------------------------------------------------- MoE layer
 def moe_max_padded_rows(tokens: int, topk: int, num_experts: int) -> int:
     """Upper bound of the contiguous layout's rows: roundup(T*topk + G*127, 128)."""
@@ -484,6 +523,7 @@ __all__ = [
     "describe_gemm",
     "fp8_gemm_nt",
     "fp8_gemm_nt_fp8_out",
+    "fp8_gemm_nt_mx",
     "fp8_linear",
     "fp8_linear_nt",
     "last_error",
@@ -498,5 +538,6 @@ __all__ = [
     "padded_rows",
     "quantize_fp8_blocks",
     "quantize_fp8_groups",
+    "quantize_fp8_mx",
     "silu_mul_quantize",
 ]

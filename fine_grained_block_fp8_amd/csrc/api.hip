@@ -252,6 +252,44 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
                   who);
 }
 
+int quantize_fp8_mx(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, int32_t* s, int64_t s_ld,
+                    void* stream) {
+  const char* who = "quantize_fp8_mx";
+  if (m < 0 || m >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m=%lld out of range", who, (long long)m);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m, k, s_ld)) return rc;
+  if (m == 0) return FGFP8_OK;
+  if (!x_bf16 || !q_e4m3 || !s) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(s))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_quantize_mx(x_bf16, m, k, q_e4m3, s, s_ld, (hipStream_t)stream), who);
+}
+
+int fp8_gemm_nt_mx(const void* a_e4m3, const int32_t* sa, int64_t sa_ld, const void* b_e4m3, const int32_t* sb,
+                   int64_t sb_ld, void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
+  const char* who = "fp8_gemm_nt_mx";
+  if (m < 0 || m >= kMaxRows || n < 0 || n >= kMaxRows)
+    return fail(FGFP8_EINVAL, "%s: m=%lld n=%lld out of range", who, (long long)m, (long long)n);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (sb_ld < n || sb_ld % 4 != 0 || sb_ld < 0 || (k / 128) * sb_ld * 4 >= (int64_t(1) << 31))
+    return fail(FGFP8_EINVAL, "%s: sb_ld=%lld must be a non-negative multiple of 4, >= n=%lld (and k/128 * sb_ld < 2^29)",
+                who, (long long)sb_ld, (long long)n);
+  if (m == 0 || n == 0) return FGFP8_OK;
+  if (!a_e4m3 || !sa || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(d_bf16))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (int rc = check_device(who)) return rc;
+  const fgfp8::GemmKind kind = fgfp8::plan_tiles(m, n, k);
+  if (env_flag("FGFP8_PRINT_CONFIG"))
+    fprintf(stderr, "[fgfp8] fp8_gemm_nt_mx m=%lld n=%lld k=%lld: %s\n", (long long)m, (long long)n, (long long)k,
+            fgfp8::gemm_kind_name(kind));
+  return launched(fgfp8::launch_gemm_mx(kind, a_e4m3, sa, sa_ld, b_e4m3, sb, sb_ld, d_bf16, m, n, k,
+                                        (hipStream_t)stream),
+                  who);
+}
+
 int64_t moe_route_workspace_bytes(int64_t tokens, int32_t num_experts) {
   if (tokens < 0 || num_experts < 1) return -1;
   return fgfp8::moe_route_workspace_bytes(tokens, num_experts);

@@ -43,10 +43,11 @@ struct Tile {
   static constexpr int MT = TM / 16;
   static constexpr int NT = TN / 16;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  // One stage's scales: the tile's activation scales (<= 256 floats) at +0,
-  // and at +1024 one 4-byte slot per lane of the weight-scale copy, slot j
-  // holding the weight scale of the tile's column block j.
-  static constexpr int S_BYTES = 1024 + 256;
+  // One stage's scales: the tile's activation scales (<= 256 floats, or
+  // packed E8M0 words of the MX recipe) at +0, and at +1024 the weight
+  // scales: one 4-byte slot per lane of the copy, slot j holding the scale
+  // of the tile's column block j, or (MX) the tile's BN packed E8M0 words.
+  static constexpr int S_BYTES = 1024 + 1024;
   static constexpr int SB_IN_S = 1024;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = STAGES * A_BYTES;
@@ -59,6 +60,7 @@ struct Tile {
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
   static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "segments divide evenly among waves");
   static_assert(BM * 4 <= SB_IN_S, "one wave loads a stage's activation scales");
+  static_assert(BN * 4 <= S_BYTES - SB_IN_S, "one wave loads a stage's MX weight scales");
   static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -123,6 +125,9 @@ struct StageLoader {
   const uint32_t* voff;
   uint32_t sa_ld_bytes, vsb;
   int wave, lane;
+  // 0: the weight-scale copy is one 4-byte block scale per lane; else the MX
+  // recipe's packed words, 16 bytes per lane, rows sb_row_bytes apart per chunk.
+  uint32_t sb_row_bytes = 0;
   // Segment i (< NSEG) of chunk kb into `stage`; segment NSEG is the scales
   // (wave 0 only).
   __device__ __forceinline__ void issue(int i, int stage, int kb) const {
@@ -138,9 +143,12 @@ struct StageLoader {
     else if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES), 16,
                                                (uint32_t)lane * 16u, (uint32_t)kb * sa_ld_bytes, 0, 0);
-    else if (wave == 1)
+    else if (wave == 1 && sb_row_bytes == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES + C::SB_IN_S),
                                                4, vsb, (uint32_t)kb * 4u, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES + C::SB_IN_S),
+                                               16, vsb, (uint32_t)kb * sb_row_bytes, 0, 0);
   }
   __device__ __forceinline__ void all(int stage, int kb) const {
 #pragma unroll
@@ -179,14 +187,21 @@ __device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wa
 
 // LDS byte offsets of the two 16-byte slots lane (li, lg) reads for a
 // 16x16x128 MFMA fragment of rows base_row .. base_row+15 (base_row a
-// multiple of 16, so the swizzle depends on li only).  Adding 2048 selects
-// the next 16-row tile, adding an operand-tile size the other stage.
+// multiple of 16, so the swizzle depends on li only).  The matrix core takes
+// K positions [16*lg, 16*lg + 16) of row li from a lane's first four
+// registers and [64 + 16*lg, 64 + 16*lg + 16) from its last four (fitted on
+// gfx950 from the per-block scale each K byte receives), so the lane reads
+// logical slots lg and lg + 4 and the instruction's K order is the memory
+// order.  For a fixed lg the 16 lanes still read all eight slot columns
+// twice over (slot ^ swz(li)), the same bank pattern as any other slot pair.
+// Adding 2048 selects the next 16-row tile, adding an operand-tile size the
+// other stage.
 struct FragAddr {
   uint32_t lo, hi;
 };
 __device__ __forceinline__ FragAddr frag_addr(uint32_t region, int base_row, int li, int lg) {
   const uint32_t row = region + (uint32_t)(base_row + li) * 128u;
-  return {row + (uint32_t)(((2 * lg) ^ swz(li)) << 4), row + (uint32_t)(((2 * lg + 1) ^ swz(li)) << 4)};
+  return {row + (uint32_t)((lg ^ swz(li)) << 4), row + (uint32_t)(((lg + 4) ^ swz(li)) << 4)};
 }
 __device__ __forceinline__ v8i_t read_frag(const uint8_t* lds, const FragAddr& a, uint32_t cst) {
   const uint4 lo = *reinterpret_cast<const uint4*>(lds + a.lo + cst);
@@ -275,8 +290,8 @@ __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& b
 
 // UE8M0 recipe: with power-of-two scales the scaling is exact, so the
 // matrix core applies it -- v_mfma_scale takes one E8M0 exponent per operand
-// row and 32-wide K block (lane l supplies row l % 16, block l / 16, which is
-// the lane's own fragment), and the product accumulates across chunks in the
+// row and 32-wide K block (lane l supplies row l % 16, block l / 16; here the
+// four blocks of a row share one exponent), and the product accumulates across chunks in the
 // MFMA accumulator itself: acc = MFMA(B, A, acc) * 2^(eb + ea), with no FP32
 // promotion.  Per chunk, a lane's A exponent is that of its row's scale and
 // the B exponent that of the wave's column block (uniform).
@@ -315,6 +330,60 @@ __device__ __forceinline__ void mfma_tiles_ue8m0(const uint8_t* lds, const FragA
   }
 }
 
+// MX recipe: one E8M0 scale per operand row and 32-wide K block, which is
+// exactly what v_mfma_scale takes per lane (lane i + 16b supplies row i,
+// K block b, i.e. K [32b, 32b + 32) of the chunk in memory order, which the
+// fragment layout above keeps).  A lane's A scale is byte lg of its
+// row's packed word; its B scale for column tile t is byte lg of the packed
+// word of the tile column its B fragment row holds (ebo[t], a byte offset
+// into the stage's weight-scale area).  The product accumulates across all
+// of K in the MFMA accumulator: no FP32 promotion.
+template <class C>
+__device__ __forceinline__ void read_a_mx(const uint8_t* lds, const FragAddr& aa, uint32_t sa_addr, int stage,
+                                          int lg, v8i_t (&af)[C::MT], int (&ea)[C::MT]) {
+#pragma unroll
+  for (int mt = 0; mt < C::MT; mt++) {
+    af[mt] = read_frag(lds, aa, (uint32_t)(stage * C::A_BYTES + 2048 * mt));
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(lds + sa_addr + stage * C::S_BYTES + 64 * mt);
+    ea[mt] = (int)((w >> (8 * lg)) & 0xffu);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ int read_eb_mx(const uint8_t* lds, const uint32_t (&ebo)[C::NT], int stage, int t, int lg) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(lds + ebo[t] + stage * C::S_BYTES);
+  return (int)((w >> (8 * lg)) & 0xffu);
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_tiles_mx(const uint8_t* lds, const FragAddr& ba, const uint32_t (&ebo)[C::NT],
+                                              int stage, int load_stage, int lg, const v8i_t (&af)[C::MT],
+                                              const int (&ea)[C::MT], v4f_t (&acc)[C::MT][C::NT],
+                                              const StageLoader<C>& ld, int next_kb) {
+  constexpr int NL = StageLoader<C>::NSEG, HALF = C::NT / 2 > 0 ? C::NT / 2 : 1;
+  constexpr int PER = (NL + HALF - 1) / HALF;
+  constexpr int N_MFMA = C::NT * C::MT;
+  v8i_t bfr[2];
+  int ebr[2];
+  bfr[0] = read_b<C>(lds, ba, stage, 0);
+  ebr[0] = read_eb_mx<C>(lds, ebo, stage, 0, lg);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; i++) {
+    const int u = i / C::MT, mt = i % C::MT;
+    if (mt == 0) {
+#pragma unroll
+      for (int q = 0; q < PER; q++)
+        if (u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
+      if (u + 1 < C::NT) {
+        bfr[(u + 1) & 1] = read_b<C>(lds, ba, stage, u + 1);
+        ebr[(u + 1) & 1] = read_eb_mx<C>(lds, ebo, stage, u + 1, lg);
+      }
+    }
+    acc[mt][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[u & 1], af[mt], acc[mt][u], 0, 0, 0,
+                                                                  ebr[u & 1], 0, ea[mt]);
+  }
+}
+
 // The 8 values of epilogue slot s of an MFMA row tile, rounded to bf16 and
 // packed in column order (see the epilogue).
 template <class C>
@@ -345,10 +414,11 @@ struct TileOut {
 // which serialises the K pipeline.  The pipeline orders those copies before
 // the reads itself (explicit vmcnt waits and a barrier per K block).  The
 // codegen test checks the count of full drains per kernel.
-template <class C, bool FP8OUT = false, bool UE8M0 = false>
+template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
                                           const float* sb_base, uint16_t* __restrict__ d, const TileOut& out,
-                                          int64_t M, int64_t N, int K, int64_t sa_ld, int64_t m0, int64_t n0) {
+                                          int64_t M, int64_t N, int K, int64_t sa_ld, int64_t m0, int64_t n0,
+                                          int64_t sb_ld = 0) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
@@ -364,8 +434,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   const int64_t nblocks = (N + kGroup - 1) / kGroup;
   int64_t nb_lane = n0 / kGroup + lane;
   if (nb_lane >= nblocks) nb_lane = nblocks - 1;
-  const rsrc_t rsb = make_rsrc(sb_base, (uint32_t)(nblocks * KB * 4));
-  const uint32_t vsb = (uint32_t)(nb_lane * KB * 4);
+  // MX: lane j copies the packed words of columns n0 + 4j .. n0 + 4j + 3 of
+  // chunk kb (sb_base[kb * sb_ld + column]).
+  const rsrc_t rsb = MX ? make_rsrc(sb_base + n0, (uint32_t)(((int64_t)KB * sb_ld - n0) * 4))
+                        : make_rsrc(sb_base, (uint32_t)(nblocks * KB * 4));
+  const uint32_t vsb = MX ? (uint32_t)lane * 16u : (uint32_t)(nb_lane * KB * 4);
 
   v4f_t acc[C::MT][C::NT];
 #pragma unroll
@@ -378,7 +451,16 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   float sc[C::MT];
   uint32_t voff[StageLoader<C>::NSEG];
   stage_offsets<C>(voff, (uint32_t)K, wave, lane);
-  const StageLoader<C> loader{lds, ra, rb, rs, rsb, voff, (uint32_t)(sa_ld * 4), vsb, wave, lane};
+  const StageLoader<C> loader{lds, ra, rb, rs, rsb, voff, (uint32_t)(sa_ld * 4), vsb, wave, lane,
+                              MX ? (uint32_t)(sb_ld * 4) : 0u};
+  // MX: byte offsets of the packed weight-scale word each lane's B fragment
+  // row refers to, per column tile.
+  uint32_t ebo[C::NT];
+  if constexpr (MX) {
+#pragma unroll
+    for (int t = 0; t < C::NT; t++)
+      ebo[t] = C::S_OFF + C::SB_IN_S + (uint32_t)(wn * C::TN + wave_col<C>(li, t)) * 4u;
+  }
   const FragAddr aa = frag_addr(C::A_OFF, wm * C::TM, li, lg);
   const FragAddr ba = frag_addr(C::B_OFF, wn * C::TN, li, lg);
   const uint32_t sa_addr = C::S_OFF + (uint32_t)(wm * C::TM + li) * 4u;
@@ -407,7 +489,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
     }
     barrier_no_fence();
     if (wave < 2) loader.issue(StageLoader<C>::NSEG, load_stage, next);  // scales
-    if constexpr (UE8M0) {
+    if constexpr (MX) {
+      int ea[C::MT];
+      read_a_mx<C>(lds, aa, sa_addr, stage, lg, af, ea);
+      mfma_tiles_mx<C>(lds, ba, ebo, stage, load_stage, lg, af, ea, acc, loader, next);
+    } else if constexpr (UE8M0) {
       int ea[C::MT], eb;
       read_a_ue8m0<C>(lds, aa, sa_addr, sb_addr, stage, af, ea, eb);
       mfma_tiles_ue8m0<C>(lds, ba, stage, load_stage, af, ea, eb, acc, loader, next);
@@ -772,17 +858,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_persistent_kernel(
   gemm_persistent<C>(lds, src, SA, sa_ld, D, M, N, K);
 }
 
-template <class C, bool FP8OUT, bool UE8M0>
+template <class C, bool FP8OUT, bool UE8M0, bool MX = false>
 __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __restrict__ A, const float* __restrict__ SA,
                                                              const uint8_t* __restrict__ B,
                                                              const float* __restrict__ SB, TileOut out, int64_t M,
                                                              int64_t N, int K, int64_t sa_ld, int tiles_m,
-                                                             int tiles_n) {
+                                                             int tiles_n, int64_t sb_ld = 0) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-  gemm_tile<C, FP8OUT, UE8M0>(lds, A + m0 * K, B + n0 * K, SA, SB, out.d, out, M, N, K, sa_ld, m0, n0);
+  gemm_tile<C, FP8OUT, UE8M0, MX>(lds, A + m0 * K, B + n0 * K, SA, SB, out.d, out, M, N, K, sa_ld, m0, n0, sb_ld);
 }
 
 // Grouped: every BM-row block lies inside one group (groups start at
@@ -1013,6 +1099,32 @@ hipError_t launch_gemm_ue8m0(const GemmPlan& plan, const void* a, const float* s
     case kGemmDecode: return launch_decode(plan.split, a, sa, sa_ld, b, sb, d, m, n, k, stream);
   }
   return hipErrorInvalidValue;
+}
+
+template <class C>
+static hipError_t launch_tile_mx(const void* a, const int32_t* sa, int64_t sa_ld, const void* b, const int32_t* sb,
+                                 int64_t sb_ld, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  const int tiles_m = (int)((m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
+  const TileOut out{static_cast<uint16_t*>(d), nullptr, nullptr, 0};
+  // The packed int32 scale words travel through the float-typed scale
+  // pointers of the tile body, which only copies them as bytes.
+  hipLaunchKernelGGL((gemm_nt_kernel<C, false, false, true>), dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0,
+                     stream, static_cast<const uint8_t*>(a), reinterpret_cast<const float*>(sa),
+                     static_cast<const uint8_t*>(b), reinterpret_cast<const float*>(sb), out, m, n, (int)k, sa_ld,
+                     tiles_m, tiles_n, sb_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(GemmKind kind, const void* a, const int32_t* sa, int64_t sa_ld, const void* b,
+                          const int32_t* sb, int64_t sb_ld, void* d, int64_t m, int64_t n, int64_t k,
+                          hipStream_t stream) {
+  switch (kind) {
+    case kGemmTile256x256: return launch_tile_mx<Tile256x256>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
+    case kGemmTile128x256: return launch_tile_mx<Tile128x256>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
+    case kGemmTile256x128: return launch_tile_mx<Tile256x128>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
+    case kGemmTile128x128: return launch_tile_mx<Tile128x128>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 GemmKind plan_tiles(int64_t m, int64_t n, int64_t k) {

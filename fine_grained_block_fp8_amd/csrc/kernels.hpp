@@ -9,6 +9,10 @@ namespace fgfp8 {
 
 hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, float* sa, int64_t sa_ld,
                                   hipStream_t stream, bool ue8m0 = false);
+// MX recipe: per-1x32 power-of-two scales, E8M0 codes packed four to an
+// int32, s int32 [k/128][s_ld].
+hipError_t launch_quantize_mx(const void* x, int64_t m, int64_t k, void* q, int32_t* s, int64_t s_ld,
+                              hipStream_t stream);
 hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream,
                                   bool ue8m0 = false);
 
@@ -41,6 +45,11 @@ hipError_t launch_gemm_ue8m0(const GemmPlan& plan, const void* a, const float* s
 // FP8-output product (n % 128 == 0): q = quantize_groups(bf16(A . B^T)) per
 // 1x128 group of each row with MN-major scales sd [n/128][sd_ld]; d (bf16)
 // optional.  Tile kernels only; plan_tiles gives the tile for any m.
+// MX product: packed E8M0 scale words sa int32 [k/128][sa_ld] (A rows) and
+// sb int32 [k/128][sb_ld] (B rows, i.e. output columns).
+hipError_t launch_gemm_mx(GemmKind kind, const void* a, const int32_t* sa, int64_t sa_ld, const void* b,
+                          const int32_t* sb, int64_t sb_ld, void* d, int64_t m, int64_t n, int64_t k,
+                          hipStream_t stream);
 GemmKind plan_tiles(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_fp8out(GemmKind kind, const void* a, const float* sa, int64_t sa_ld, const void* b,
                               const float* sb, void* q, float* sd, int64_t sd_ld, void* d, int64_t m, int64_t n,

@@ -8,7 +8,9 @@
 // "Backend plugins" page, plugin module docstring).  Scale s = fl32(amax/448),
 // 1 for an all-zero group; element code = E4M3_RNE(fl32(x / s)).  The UE8M0
 // variants round s up to a power of two (the Blackwell path's UE8M0 scale
-// factors, deepgemm-rust README key techniques) and are otherwise the same.
+// factors, deepgemm-rust README key techniques) and are otherwise the same;
+// the MX variant takes one such scale per 1x32 block (the README's gran-32
+// recipe) and stores E8M0 codes.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -78,6 +80,67 @@ hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, 
   else
     hipLaunchKernelGGL(quantize_groups_kernel<false>, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
                        static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------------- MX
+// The MX recipe: one power-of-two scale per 1x32 block of a row (the UE8M0
+// rule over the block's amax), E8M0 codes packed four to an int32 per row
+// and 128-column chunk (byte j = block 4c + j), MN-major s[c][row].  Same
+// wave layout as quantize_groups_kernel: a 16-lane quarter holds one 128-
+// column chunk of a row, 8 values per lane, so a 4-lane quad holds one
+// 32-block and its amax is a two-step lane exchange; lane 0 of the quarter
+// gathers the four codes.  Serves activations and weights alike (a weight's
+// blocks run along its rows, per output column).
+__global__ __launch_bounds__(kQgWaves * 64) void quantize_mx_kernel(const uint16_t* __restrict__ x,
+                                                                    uint8_t* __restrict__ q, int32_t* __restrict__ s,
+                                                                    int64_t m, int64_t k, int64_t s_ld,
+                                                                    int64_t group_quads, int64_t total_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * kQgWaves + (threadIdx.x >> 6);
+  if (blk >= total_blocks) return;  // wave-uniform
+  const int64_t r0 = (blk / group_quads) * 4;
+  const int64_t g = (blk % group_quads) * 4 + (lane >> 4);
+  const bool g_ok = g < k / kGroup;
+  const int64_t col = g * kGroup + (lane & 15) * 8;
+  const int quarter = lane & ~15;
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    v[i] = (g_ok && r0 + i < m) ? *reinterpret_cast<const uint4*>(x + (r0 + i) * k + col) : make_uint4(0, 0, 0, 0);
+  uint32_t packed[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    uint32_t am = absmax8_bits(v[i]);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+    const float sc = group_scale_ue8m0(__uint_as_float(am));
+    const double r = 1.0 / (double)sc;
+    const uint2 o = quantize8(v[i], r);
+    if (g_ok && r0 + i < m) *reinterpret_cast<uint2*>(q + (r0 + i) * k + col) = o;
+    const int code = e8m0_of(sc);
+    packed[i] = (uint32_t)__shfl(code, quarter) | ((uint32_t)__shfl(code, quarter + 4) << 8) |
+                ((uint32_t)__shfl(code, quarter + 8) << 16) | ((uint32_t)__shfl(code, quarter + 12) << 24);
+  }
+  if (g_ok && (lane & 15) == 0) {
+    int32_t* dst = s + g * s_ld + r0;
+    if (r0 + 4 <= m) {
+      *reinterpret_cast<int4*>(dst) = make_int4((int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (r0 + i < m) dst[i] = (int)packed[i];
+    }
+  }
+}
+
+hipError_t launch_quantize_mx(const void* x, int64_t m, int64_t k, void* q, int32_t* s, int64_t s_ld,
+                              hipStream_t stream) {
+  const int64_t group_quads = (k / kGroup + 3) / 4;
+  const int64_t total = (m + 3) / 4 * group_quads;
+  const int64_t blocks = (total + kQgWaves - 1) / kQgWaves;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), s, m, k, s_ld, group_quads, total);
   return hipGetLastError();
 }
 

@@ -221,6 +221,29 @@ int quantize_fp8_blocks_ue8m0(const void* w_bf16, int64_t n, int64_t k, void* q_
 int fp8_gemm_nt_ue8m0(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
                       void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream);
 
+/* The MXFP8 recipe: one power-of-two scale per 1x32 block along K, on both
+ * operands (deepgemm-rust README, "Full recipes": gran-32 scale factors on
+ * either side; the scales are UE8M0 powers of two, "Blackwell-native"
+ * techniques).  The scale of a block is the UE8M0 rule of
+ * quantize_fp8_groups_ue8m0 over its 32 values; the element is
+ * E4M3(x / s).  Scales are stored as E8M0 codes (exponent + 127), the four
+ * of a 128-column chunk packed in one int32 (byte j = block 4c + j),
+ * MN-major: s[c * s_ld + row].
+ *
+ * quantize_fp8_mx: x [m][k] bf16 -> q [m][k] E4M3 and s int32 [k/128][s_ld];
+ * k % 128 == 0, s_ld % 4 == 0, s_ld >= m.  The same call quantizes a weight
+ * [n][k] (one scale per 1x32 block of each weight row, i.e. per output
+ * column). */
+int quantize_fp8_mx(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, int32_t* s, int64_t s_ld, void* stream);
+
+/* D[m][n] = sum over 32-blocks b of 2^(ea[m][b]-127) * 2^(eb[n][b]-127) *
+ * sum_{k in b} A[m][k] B[n][k], with A's scales sa [k/128][sa_ld] and B's
+ * sb [k/128][sb_ld] from quantize_fp8_mx.  The matrix cores apply the scales
+ * per 32-block (v_mfma_scale) and accumulate across all of K in FP32; no
+ * per-chunk promotion.  bf16 out; sb_ld % 4 == 0, sb_ld >= n. */
+int fp8_gemm_nt_mx(const void* a_e4m3, const int32_t* sa, int64_t sa_ld, const void* b_e4m3, const int32_t* sb,
+                   int64_t sb_ld, void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream);
+
 /* The FP8 mixture-of-experts layer around the grouped product, step by step,
  * with no device-to-host synchronisation (deepgemm-rust README, "What's
  * implemented", moe_fp8_layer row: histogram -> offsets -> gather -> grouped

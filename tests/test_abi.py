@@ -45,6 +45,8 @@ def test_library_exports_every_declared_function():
         "moe_gather_quantize",
         "silu_mul_quantize",
         "moe_combine",
+        "quantize_fp8_mx",
+        "fp8_gemm_nt_mx",
     }
     lib = fg.library()
     for n in names:
@@ -171,6 +173,18 @@ def test_fp8_out_rejects():
     assert call(q=None) == fg.FGFP8_EINVAL
     assert call(d=P + 4) == fg.FGFP8_EINVAL
     assert call(m=0) == fg.FGFP8_OK
+
+
+def test_mx_calls_validate():
+    lib = _lib()
+    assert lib.quantize_fp8_mx(P, 4, 100, P, P, 4, None) == fg.FGFP8_EINVAL
+    assert lib.quantize_fp8_mx(P, 5, 128, P, P, 5, None) == fg.FGFP8_EINVAL
+    assert lib.quantize_fp8_mx(None, 0, 128, None, None, 0, None) == fg.FGFP8_OK
+    assert lib.fp8_gemm_nt_mx(P, P, 8, P, P, 12, P, 8, 16, 256, None) == fg.FGFP8_EINVAL  # sb_ld % 4
+    assert "sb_ld" in fg.last_error()
+    assert lib.fp8_gemm_nt_mx(P, P, 8, P, P, 8, P, 8, 16, 256, None) == fg.FGFP8_EINVAL  # sb_ld < n
+    assert lib.fp8_gemm_nt_mx(P, P, 8, P, P, 16, P, 8, 16, 200, None) == fg.FGFP8_EINVAL
+    assert lib.fp8_gemm_nt_mx(None, None, 0, None, None, 16, None, 0, 16, 256, None) == fg.FGFP8_OK
 
 
 def test_moe_sizes():
