@@ -27,7 +27,9 @@ graph see the same device time).  Also reported:
   from HBM rather than the 256 MB last-level cache;
 * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 Other --workload values time one shape for profiling: prefill_ue8m0 (the
-same step with power-of-two scales, the matrix cores applying them), decode (M=1 linears),
+same step with power-of-two scales, the matrix cores applying them), prefill_mx
+(the MXFP8 recipe: one power-of-two scale per 1x32 block of every row of both
+operands), decode (M=1 linears),
 moe (contiguous grouped, 32 experts), moe_masked (masked grouped over a
 decode-time dispatch buffer), moe_layer (the whole MoE layer: routing, gather,
 two grouped products, SiLU-times-up and combine, 8192 tokens top-4 over 32
@@ -51,6 +53,7 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 (E4M3) MFMA peak
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 STEPS_ARE = {
     "prefill": "act-quant (1x128) + block-scaled FP8 GEMM (bf16 out) for every linear; weights pre-quantized",
+    "prefill_mx": "act-quant (1x32 E8M0) + MXFP8 GEMM (bf16 out) for every linear; weights pre-quantized (1x32 E8M0)",
     "moe_layer": "route + gather/act-quant + grouped GEMM (gate_up) + SiLU*up/act-quant + grouped GEMM (down) + "
                  "weighted combine; expert weights pre-quantized; value counts routed rows only",
 }
@@ -61,7 +64,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy"])
+    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-reps", type=int, default=50, help="rounds over the 8 weight sets per decode timing")
@@ -81,16 +84,21 @@ class PreparedLinear:
     """Device buffers for one linear: bf16 activation, pre-quantized weight,
     and preallocated outputs (nothing is allocated inside the timed region)."""
 
-    def __init__(self, lin, fg, torch, ue8m0=False):
+    def __init__(self, lin, fg, torch, recipe="fp32"):
         self.lin = lin
-        self.ue8m0 = ue8m0
+        self.recipe = recipe
+        self.ue8m0 = recipe == "ue8m0"
         self.x = dev_bf16(lin.a, torch)
         w = dev_bf16(lin.b, torch)
-        self.qb, self.sb = fg.quantize_fp8_blocks(w, ue8m0=ue8m0)
+        if recipe == "mx":
+            self.qb, self.sb = fg.quantize_fp8_mx(w)
+        else:
+            self.qb, self.sb = fg.quantize_fp8_blocks(w, ue8m0=self.ue8m0)
         del w
         m, k = lin.m, lin.k
         self.q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device="cuda")
-        self.sa = torch.empty((k // 128, fg.padded_rows(m)), dtype=torch.float32, device="cuda")
+        self.sa = torch.empty((k // 128, fg.padded_rows(m)), dtype=torch.int32 if recipe == "mx" else torch.float32,
+                              device="cuda")
         self.d = torch.empty((m, lin.n), dtype=torch.bfloat16, device="cuda")
         self.plan = fg.describe_gemm(m, lin.n, k)
         self.kernel = self.plan.split()[0]
@@ -98,10 +106,16 @@ class PreparedLinear:
     def run(self, fg, ev=None):
         if ev is not None:
             ev[0].record()
-        fg.quantize_fp8_groups(self.x, out=(self.q, self.sa), ue8m0=self.ue8m0)
+        if self.recipe == "mx":
+            fg.quantize_fp8_mx(self.x, out=(self.q, self.sa))
+        else:
+            fg.quantize_fp8_groups(self.x, out=(self.q, self.sa), ue8m0=self.ue8m0)
         if ev is not None:
             ev[1].record()
-        fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d, ue8m0=self.ue8m0)
+        if self.recipe == "mx":
+            fg.fp8_gemm_nt_mx((self.q, self.sa), (self.qb, self.sb), self.d)
+        else:
+            fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d, ue8m0=self.ue8m0)
         if ev is not None:
             ev[2].record()
 
@@ -110,8 +124,11 @@ def quant_bytes(m, k):
     return 3 * m * k + 4 * (-(-m // 4) * 4) * (k // 128)
 
 
-def gemm_bytes(m, n, k):
-    return m * k + 4 * (-(-m // 4) * 4) * (k // 128) + n * k + 4 * (-(-n // 128)) * (k // 128) + 2 * m * n
+def gemm_bytes(m, n, k, mx=False):
+    """A, its scales, B, its scales (one per 128x128 block, or with the MX
+    recipe one packed word per row and chunk) and the bf16 output."""
+    sb_rows = n if mx else -(-n // 128)
+    return m * k + 4 * (-(-m // 4) * 4) * (k // 128) + n * k + 4 * sb_rows * (k // 128) + 2 * m * n
 
 
 # --------------------------------------------------------------- prefill step
@@ -194,8 +211,8 @@ def host_enqueue_seconds(fn, torch, reps=3):
     return worst
 
 
-def bench_linears(linears, steps, warmup, fg, torch, ue8m0=False):
-    preps = [PreparedLinear(l, fg, torch, ue8m0) for l in linears]
+def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32"):
+    preps = [PreparedLinear(l, fg, torch, recipe) for l in linears]
     torch.cuda.synchronize()
     for _ in range(warmup):
         for p in preps:
@@ -235,7 +252,8 @@ def bench_linears(linears, steps, warmup, fg, torch, ue8m0=False):
                 "quant_gbs": quant_bytes(lin.m, lin.k) / qt / 1e9,
                 "gemm_us": gt * 1e6,
                 "gemm_tflops": lin.flops / gt / 1e12,
-                "_kernel": p.kernel,
+                "_kernel": p.kernel + (" mx" if p.recipe == "mx" else ""),
+                "_bytes": gemm_bytes(lin.m, lin.n, lin.k, mx=p.recipe == "mx"),
                 "_flops": lin.flops,
                 "_gemm_s": gt,
             }
@@ -281,14 +299,14 @@ def roofline_of(per):
     for r in per:
         e = by.setdefault(r["_kernel"], {"flops": 0, "s": 0.0, "n": 0, "bytes": 0})
         e["flops"] += r["_flops"]
-        e["bytes"] += gemm_bytes(r["m"], r["n"], r["k"])
+        e["bytes"] += r["_bytes"] if "_bytes" in r else gemm_bytes(r["m"], r["n"], r["k"])
         e["s"] += r["_gemm_s"]
         e["n"] += 1
     name, e = max(by.items(), key=lambda kv: kv[1]["s"])
     flops_per_launch = e["flops"] / e["n"]
     mean_s = e["s"] / e["n"]
     achieved = flops_per_launch / mean_s / 1e12
-    kernel = f"gemm_nt_kernel<{name}>"
+    kernel = f"gemm_nt_kernel<{name.replace(' mx', ', mx')}>"
     return {
         "bound": "mfma",
         "kernel": kernel,
@@ -454,9 +472,10 @@ def main():
     if args.workload == "copy":
         copy_calibration(args, torch)
         return
-    if args.workload in ("prefill", "prefill_ue8m0"):
+    recipe = {"prefill_ue8m0": "ue8m0", "prefill_mx": "mx"}.get(args.workload, "fp32")
+    if args.workload in ("prefill", "prefill_ue8m0", "prefill_mx"):
         linears = workloads.prefill_linears()
-        workload = "qwen3_8b_prefill_linears_m2048" + ("_ue8m0_recipe" if args.workload == "prefill_ue8m0" else "")
+        workload = "qwen3_8b_prefill_linears_m2048" + {"ue8m0": "_ue8m0_recipe", "mx": "_mxfp8_recipe"}.get(recipe, "")
     elif args.workload == "decode":
         linears = [workloads.decode_linear(1, 12288, 4096), workloads.decode_linear(1, 4096, 12288)]
         workload = "decode_m1_linears"
@@ -478,8 +497,7 @@ def main():
 
     if linears is not None:
         log(f"workload {workload}: " + ", ".join(f"{l.name} [{fg.describe_gemm(l.m, l.n, l.k)}]" for l in linears))
-        preps, elapsed, per = bench_linears(linears, args.steps, args.warmup, fg, torch,
-                                            ue8m0=args.workload == "prefill_ue8m0")
+        preps, elapsed, per = bench_linears(linears, args.steps, args.warmup, fg, torch, recipe=recipe)
         total_flops = sum(l.flops for l in linears)
         ms_per_step = elapsed / args.steps * 1e3
         value = total_flops * args.steps / elapsed / 1e12

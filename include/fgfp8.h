@@ -223,8 +223,8 @@ int fp8_gemm_nt_ue8m0(const void* a_e4m3, const float* sa, int64_t sa_ld, const 
 
 /* The MXFP8 recipe: one power-of-two scale per 1x32 block along K, on both
  * operands (deepgemm-rust README, "Full recipes": gran-32 scale factors on
- * either side; the scales are UE8M0 powers of two, "Blackwell-native"
- * techniques).  The scale of a block is the UE8M0 rule of
+ * either side; the scales are UE8M0 powers of two, as on the Blackwell
+ * path's block-scaled MMA).  The scale of a block is the UE8M0 rule of
  * quantize_fp8_groups_ue8m0 over its 32 values; the element is
  * E4M3(x / s).  Scales are stored as E8M0 codes (exponent + 127), the four
  * of a 128-column chunk packed in one int32 (byte j = block 4c + j),
