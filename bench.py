@@ -20,8 +20,9 @@ launch to the end of the last (the host-side Python launch path, ~10-30 us per
 call, is not part of the device's work; callers that launch from C++ or a HIP
 graph see the same device time).  Also reported:
 * roofline: the dominant kernel's algorithmic TFLOP/s from HIP events on the
-  launch stream (created without the system-scope fence, so that recording
-  them barely disturbs the step), against the 5.0 PFLOP/s dense FP8 peak;
+  launch stream, recorded around that kernel's launches only (created without
+  the system-scope fence, so that recording them barely disturbs the step),
+  against the 5.0 PFLOP/s dense FP8 peak;
 * decode: M = 1, 4, 16 linears (act-quant included per call) in GB/s against 8 TB/s,
   timed by graph replay over 8 rotating weight sets so that the weights stream
   from HBM rather than the 256 MB last-level cache;
@@ -104,19 +105,21 @@ class PreparedLinear:
         self.kernel = self.plan.split()[0]
 
     def run(self, fg, ev=None):
-        if ev is not None:
+        """Act-quant then product; ev = (before, between, after) events, any
+        of them None."""
+        if ev is not None and ev[0] is not None:
             ev[0].record()
         if self.recipe == "mx":
             fg.quantize_fp8_mx(self.x, out=(self.q, self.sa))
         else:
             fg.quantize_fp8_groups(self.x, out=(self.q, self.sa), ue8m0=self.ue8m0)
-        if ev is not None:
+        if ev is not None and ev[1] is not None:
             ev[1].record()
         if self.recipe == "mx":
             fg.fp8_gemm_nt_mx((self.q, self.sa), (self.qb, self.sb), self.d)
         else:
             fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d, ue8m0=self.ue8m0)
-        if ev is not None:
+        if ev is not None and ev[2] is not None:
             ev[2].record()
 
 
@@ -135,8 +138,9 @@ def gemm_bytes(m, n, k, mx=False):
 class HipEvent:
     """A HIP timing event created with hipEventDisableSystemFence: recording
     it does not flush caches to system scope, which costs ~5 us of idle GPU
-    time per record with torch's default events (12 records per step would
-    add ~10% to the measured step).  API-compatible with the two methods of
+    time per record with torch's default events.  Even these cost ~1 us of
+    step time per record, so the timed region records only the events the
+    roofline needs.  API-compatible with the two methods of
     torch.cuda.Event used here; records on torch's current stream."""
 
     _hip = None
@@ -211,31 +215,17 @@ def host_enqueue_seconds(fn, torch, reps=3):
     return worst
 
 
-def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32"):
-    preps = [PreparedLinear(l, fg, torch, recipe) for l in linears]
-    torch.cuda.synchronize()
-    for _ in range(warmup):
-        for p in preps:
-            p.run(fg)
-    torch.cuda.synchronize()
+def per_linear_pass(preps, steps, fg, torch, ahead, host_step):
+    """Per-linear breakdown: `steps` steps with three events per linear
+    (before the act-quant, between, after the product).  Runs before the
+    timed region, so its event records do not weigh on the step time."""
     events = [[[HipEvent(torch) for _ in range(3)] for _ in preps] for _ in range(steps)]
-    ahead = GpuAhead(torch)
-    probe = [[HipEvent(torch) for _ in range(3)] for _ in preps]
-    host_step = host_enqueue_seconds(lambda: [p.run(fg, ev) for p, ev in zip(preps, probe)], torch)
-    e_first, e_last = HipEvent(torch), HipEvent(torch)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     ahead.spin(1.5 * host_step * steps + 2e-3)
-    e_first.record()
     for s in range(steps):
         for p, ev in zip(preps, events[s]):
             p.run(fg, ev)
-    e_last.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    elapsed = e_first.elapsed_time(e_last) * 1e-3
-    log(f"timed region: {elapsed * 1e3 / steps:.4f} ms/step on the GPU (events); host enqueue {host_step * 1e3:.3f} ms/step; "
-        f"wall {wall * 1e3:.2f} ms including the spin")
     per = []
     for i, p in enumerate(preps):
         qt = np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(steps)]) * 1e-3
@@ -258,7 +248,53 @@ def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32"):
                 "_gemm_s": gt,
             }
         )
-    return preps, elapsed, per
+    return per
+
+
+def dominant_kernel(per) -> str:
+    """The GEMM kernel with the largest total time over the step."""
+    total = {}
+    for r in per:
+        total[r["_kernel"]] = total.get(r["_kernel"], 0.0) + r["_gemm_s"]
+    return max(total, key=total.get)
+
+
+def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32"):
+    """Warm-up, the per-linear pass, then the timed region: `steps` steps
+    bracketed by two events, with events recorded only around the launches of
+    the dominant kernel (its mean launch duration for the roofline).  Returns
+    (preps, elapsed seconds, per-linear rows, timed dominant-kernel launch)."""
+    preps = [PreparedLinear(l, fg, torch, recipe) for l in linears]
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        for p in preps:
+            p.run(fg)
+    torch.cuda.synchronize()
+    ahead = GpuAhead(torch)
+    probe = [[HipEvent(torch) for _ in range(3)] for _ in preps]
+    host_step = host_enqueue_seconds(lambda: [p.run(fg, ev) for p, ev in zip(preps, probe)], torch)
+    per = per_linear_pass(preps, steps, fg, torch, ahead, host_step)
+    dom = dominant_kernel(per)
+    dom_ev = [[(None, HipEvent(torch), HipEvent(torch)) if r["_kernel"] == dom else None for r in per]
+              for _ in range(steps)]
+    e_first, e_last = HipEvent(torch), HipEvent(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ahead.spin(1.5 * host_step * steps + 2e-3)
+    e_first.record()
+    for s in range(steps):
+        for p, ev in zip(preps, dom_ev[s]):
+            p.run(fg, ev)
+    e_last.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed = e_first.elapsed_time(e_last) * 1e-3
+    launches = [ev[1].elapsed_time(ev[2]) * 1e-3 for row in dom_ev for ev in row if ev is not None]
+    timed = {"kernel": dom, "mean_s": float(np.mean(launches)), "launches": len(launches)}
+    log(f"timed region: {elapsed * 1e3 / steps:.4f} ms/step on the GPU (events); host enqueue {host_step * 1e3:.3f} ms/step; "
+        f"wall {wall * 1e3:.2f} ms including the spin; {dom}: {len(launches)} launches timed, "
+        f"mean {timed['mean_s'] * 1e6:.2f} us")
+    return preps, elapsed, per, timed
 
 
 def kernel_sources_hash() -> str:
@@ -292,9 +328,11 @@ def recorded_traffic(kernel: str):
     return None
 
 
-def roofline_of(per):
+def roofline_of(per, timed=None):
     """Dominant kernel (largest total time among the GEMM kernels): its
-    algorithmic FLOPs per launch over its mean launch duration."""
+    algorithmic FLOPs per launch over its mean launch duration -- from the
+    events around its launches in the timed region when `timed` is given,
+    else from the per-linear rows."""
     by = {}
     for r in per:
         e = by.setdefault(r["_kernel"], {"flops": 0, "s": 0.0, "n": 0, "bytes": 0})
@@ -303,8 +341,10 @@ def roofline_of(per):
         e["s"] += r["_gemm_s"]
         e["n"] += 1
     name, e = max(by.items(), key=lambda kv: kv[1]["s"])
+    if timed is not None:
+        name, e = timed["kernel"], by[timed["kernel"]]
     flops_per_launch = e["flops"] / e["n"]
-    mean_s = e["s"] / e["n"]
+    mean_s = timed["mean_s"] if timed is not None else e["s"] / e["n"]
     achieved = flops_per_launch / mean_s / 1e12
     kernel = f"gemm_nt_kernel<{name.replace(' mx', ', mx')}>"
     return {
@@ -319,6 +359,8 @@ def roofline_of(per):
         "algorithmic_bytes_per_launch": round(e["bytes"] / e["n"]),
         "launches_per_step": e["n"],
         "mean_launch_us": round(mean_s * 1e6, 2),
+        "launch_timing": ("HIP events around each launch of this kernel inside the timed region"
+                          if timed is not None else "HIP events around each launch (per-linear pass)"),
         "algorithmic_gflop_per_launch": round(flops_per_launch / 1e9, 3),
     }
 
@@ -401,10 +443,11 @@ def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288))
 
 
 # ---------------------------------------------------------------- CPU oracle
-def cpu_baseline(linears, rows=None, cols=2048):
-    """The oracle (unchanged) on a bounded sample: every row of each linear's
-    activation, the first `cols` output columns (16 weight blocks) of each
-    linear; timed = activation quantization + block-scaled product."""
+def cpu_baseline(linears, rows=None, cols=6144):
+    """The oracle (unchanged) on a bounded sample of about 10 s: every row of
+    each linear's activation and its first min(N, `cols`) output columns (all
+    of qkv, o and down, a quarter of gate_up at the prefill shapes); timed =
+    activation quantization + block-scaled product."""
     import oracle
     from threadpoolctl import threadpool_info
 
@@ -428,7 +471,7 @@ def cpu_baseline(linears, rows=None, cols=2048):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{m} rows x first {cols} output columns of each of the {len(linears)} linears "
+        "sample": f"{m} rows x the first min(N, {cols}) output columns of each of the {len(linears)} linears "
         f"(quantize_groups + gemm_nt, FP64, numpy+BLAS); {flops / 1e9:.1f} GFLOP in {dt:.1f} s",
         "seconds": round(dt, 2),
     }
@@ -497,12 +540,12 @@ def main():
 
     if linears is not None:
         log(f"workload {workload}: " + ", ".join(f"{l.name} [{fg.describe_gemm(l.m, l.n, l.k)}]" for l in linears))
-        preps, elapsed, per = bench_linears(linears, args.steps, args.warmup, fg, torch, recipe=recipe)
+        preps, elapsed, per, timed = bench_linears(linears, args.steps, args.warmup, fg, torch, recipe=recipe)
         total_flops = sum(l.flops for l in linears)
         ms_per_step = elapsed / args.steps * 1e3
         value = total_flops * args.steps / elapsed / 1e12
         gemm_s = sum(r["_gemm_s"] for r in per)
-        roof = roofline_of(per)
+        roof = roofline_of(per, timed)
         del preps
     elif args.workload == "moe_masked":
         value, ms_per_step, per, roof, gemm_s, total_flops = bench_masked(args, fg, torch, workloads)
@@ -543,6 +586,8 @@ def main():
             "workload": workload,
             "steps_are": STEPS_ARE.get(args.workload, STEPS_ARE["prefill"]),
             "linears": per_out,
+            "linears_timing": "per-linear pass before the timed region (three events per linear); "
+                              "the timed region records events only around the dominant kernel's launches",
             "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
             "gemm_only_tflops": round(total_flops / gemm_s / 1e12, 2) if gemm_s else None,
         },
