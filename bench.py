@@ -443,17 +443,17 @@ def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288))
 
 
 # ---------------------------------------------------------------- CPU oracle
-def cpu_baseline(linears, rows=None, cols=6144):
-    """The oracle (unchanged) on a bounded sample of about 10 s: every row of
-    each linear's activation and its first min(N, `cols`) output columns (all
-    of qkv, o and down, a quarter of gate_up at the prefill shapes); timed =
-    activation quantization + block-scaled product."""
+def cpu_baseline(linears, rows=None, cols=None):
+    """The oracle (unchanged) on a bounded sample: by default one whole step
+    (every row and every output column of each linear, ~10 s on 16 host
+    threads); `rows` / `cols` bound it further.  Timed = activation
+    quantization + block-scaled product."""
     import oracle
     from threadpoolctl import threadpool_info
 
     prepared = []
     for lin in linears:
-        nc = min(cols, lin.n)
+        nc = lin.n if cols is None else min(cols, lin.n)
         qb, sb = oracle.quantize_blocks(lin.b[:nc])  # offline, untimed (as on the GPU side)
         a = lin.a if rows is None else lin.a[:rows]
         prepared.append((a, qb, sb))
@@ -471,8 +471,10 @@ def cpu_baseline(linears, rows=None, cols=6144):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{m} rows x the first min(N, {cols}) output columns of each of the {len(linears)} linears "
-        f"(quantize_groups + gemm_nt, FP64, numpy+BLAS); {flops / 1e9:.1f} GFLOP in {dt:.1f} s",
+        "sample": (f"one whole step: {m} rows x all output columns of each of the {len(linears)} linears"
+                   if cols is None else f"{m} rows x the first min(N, {cols}) output columns of each of the "
+                   f"{len(linears)} linears")
+        + f" (quantize_groups + gemm_nt, FP64, numpy+BLAS); {flops / 1e9:.1f} GFLOP in {dt:.1f} s",
         "seconds": round(dt, 2),
     }
 

@@ -58,7 +58,10 @@ struct Tile {
   static constexpr int LDS = EPI_OFF + WAVES * TM * 4;
   static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-  static_assert((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0, "segments divide evenly among waves");
+  // The copies of a chunk are 8-row segments dealt to the waves in turn; an
+  // uneven deal (some waves copy one segment fewer) needs the vmcnt(0) wait
+  // of the two-stage loop, which does not count copies.
+  static_assert(((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0) || STAGES == 2, "segments divide evenly among waves");
   static_assert(BM * 4 <= SB_IN_S, "one wave loads a stage's activation scales");
   static_assert(BN * 4 <= S_BYTES - SB_IN_S, "one wave loads a stage's MX weight scales");
   static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
@@ -72,6 +75,10 @@ struct Tile {
 // matters when B streams from HBM rather than the last-level cache, as the
 // per-expert weights of the grouped product do); 256x256 fits two.
 using Tile256x256 = Tile<256, 256, 4, 2, 2>;
+// 256x192 with 12 waves (3 per SIMD) of 64x64: 2048 x 6144 is exactly 256
+// such tiles, one per CU.  n0 is a multiple of 64, so every 64-column wave
+// tile still lies inside one 128-column scale block.
+using Tile256x192 = Tile<256, 192, 4, 3, 2>;
 using Tile128x256 = Tile<128, 256, 2, 4, 3>;
 using Tile256x128 = Tile<256, 128, 4, 2, 3>;
 using Tile128x128 = Tile<128, 128, 2, 2, 3>;
@@ -118,7 +125,10 @@ __device__ __forceinline__ int b_col_of_row(int rho) {
 // MFMA.
 template <class C>
 struct StageLoader {
-  static constexpr int AN = C::BM / 8 / C::WAVES, BN_ = C::BN / 8 / C::WAVES, NSEG = AN + BN_;
+  static constexpr int A_SEGS = C::BM / 8, B_SEGS = C::BN / 8;
+  static constexpr int AN = (A_SEGS + C::WAVES - 1) / C::WAVES, BN_ = (B_SEGS + C::WAVES - 1) / C::WAVES,
+                       NSEG = AN + BN_;
+  static constexpr bool EVEN = A_SEGS % C::WAVES == 0 && B_SEGS % C::WAVES == 0;
   static_assert(NSEG + 1 < 16, "a chunk's copies must fit the 4-bit vmcnt field used by the waits");
   uint8_t* lds;
   rsrc_t ra, rb, rs, rsb;
@@ -132,15 +142,17 @@ struct StageLoader {
   // (wave 0 only).
   __device__ __forceinline__ void issue(int i, int stage, int kb) const {
     const uint32_t koff = (uint32_t)kb * 128u;
-    if (i < AN)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void_t*)(lds + C::A_OFF + stage * C::A_BYTES + (wave + C::WAVES * i) * 1024), 16, voff[i], koff,
-          0, 0);
-    else if (i < NSEG)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void_t*)(lds + C::B_OFF + stage * C::B_BYTES + (wave + C::WAVES * (i - AN)) * 1024), 16, voff[i],
-          koff, 0, 0);
-    else if (wave == 0)
+    if (i < AN) {
+      if (EVEN || wave + C::WAVES * i < A_SEGS)  // wave-uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (lds_void_t*)(lds + C::A_OFF + stage * C::A_BYTES + (wave + C::WAVES * i) * 1024), 16, voff[i], koff,
+            0, 0);
+    } else if (i < NSEG) {
+      if (EVEN || wave + C::WAVES * (i - AN) < B_SEGS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (lds_void_t*)(lds + C::B_OFF + stage * C::B_BYTES + (wave + C::WAVES * (i - AN)) * 1024), 16,
+            voff[i], koff, 0, 0);
+    } else if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES), 16,
                                                (uint32_t)lane * 16u, (uint32_t)kb * sa_ld_bytes, 0, 0);
     else if (wave == 1 && sb_row_bytes == 0)
@@ -180,7 +192,9 @@ __device__ __forceinline__ int k_segment(int c) { return (c >> 1) | ((c & 1) << 
 
 template <class C>
 __device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wave, int lane) {
-  constexpr int AN = C::BM / 8 / C::WAVES, BN_ = C::BN / 8 / C::WAVES;
+  // the loader's counts: rounded up, so that an uneven deal still gives
+  // every wave AN A-offsets followed by BN_ B-offsets
+  constexpr int AN = StageLoader<C>::AN, BN_ = StageLoader<C>::BN_;
   const int r8 = lane >> 3, cs = lane & 7;
 #pragma unroll
   for (int i = 0; i < AN; i++) {
@@ -470,7 +484,9 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   const FragAddr aa = frag_addr(C::A_OFF, wm * C::TM, li, lg);
   const FragAddr ba = frag_addr(C::B_OFF, wn * C::TN, li, lg);
   const uint32_t sa_addr = C::S_OFF + (uint32_t)(wm * C::TM + li) * 4u;
-  const uint32_t sb_addr = C::S_OFF + C::SB_IN_S + (uint32_t)((wn * C::TN) / kGroup) * 4u;
+  // The stage's slot j holds column block n0/128 + j (n0 is a multiple of 64).
+  const uint32_t sb_addr =
+      C::S_OFF + C::SB_IN_S + (uint32_t)((n0 + wn * C::TN) / kGroup - n0 / kGroup) * 4u;
   // One chunk: wait for this wave's copies of chunk kb, barrier (every
   // wave's copies have landed, and the stage chunk kb - 1 occupied is no
   // longer read), then compute chunk kb while filling that stage with chunk
@@ -769,6 +785,7 @@ __device__ __forceinline__ void gemm_persistent(uint8_t* lds, const Src& src, co
   const FragAddr aa = frag_addr(C::A_OFF, wm * C::TM, li, lg);
   const FragAddr ba = frag_addr(C::B_OFF, wn * C::TN, li, lg);
   const uint32_t sa_addr = C::S_OFF + (uint32_t)(wm * C::TM + li) * 4u;
+  static_assert(C::BN % kGroup == 0, "the walk takes tiles of whole 128-column blocks");
   const uint32_t sb_addr = C::S_OFF + C::SB_IN_S + (uint32_t)((wn * C::TN) / kGroup) * 4u;
 
   v4f_t acc[C::MT][C::NT];
@@ -933,6 +950,7 @@ struct Candidate {
 };
 constexpr Candidate kCandidates[] = {
     {kGemmTile256x256, 256, 256, 1.00},
+    {kGemmTile256x192, 256, 192, 0.86},  // 12 waves; wins where it fills the CUs (2048 x 6144: 256 tiles)
     {kGemmTile256x128, 256, 128, 0.97},
     {kGemmTile128x256, 128, 256, 0.97},
     {kGemmTile128x128, 128, 128, 0.72},
@@ -964,6 +982,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
 const char* gemm_kind_name(GemmKind kind) {
   switch (kind) {
     case kGemmTile256x256: return "tile256x256_w4x2";
+    case kGemmTile256x192: return "tile256x192_w4x3";
     case kGemmTile128x256: return "tile128x256_w2x4";
     case kGemmTile256x128: return "tile256x128_w4x2";
     case kGemmTile128x128: return "tile128x128_w2x2";
@@ -1004,20 +1023,27 @@ static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, con
   const int tiles_m = (int)((m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
   const dim3 grid((uint32_t)tiles_m * tiles_n), block(C::THREADS);
   const uint8_t *pa = static_cast<const uint8_t*>(a), *pb = static_cast<const uint8_t*>(b);
-  if (!ue8m0 && out.q == nullptr && use_persistent(k)) {
-    const int t_pad = (tiles_m * tiles_n + 7) / 8 * 8;
-    const DenseTiles src{pa, pb, sb, k, tiles_m, tiles_n, t_pad, C::BM, C::BN};
-    hipLaunchKernelGGL(gemm_nt_persistent_kernel<C>, dim3((uint32_t)persistent_grid(t_pad)), block, 0, stream, src,
-                       sa, out.d, m, n, (int)k, sa_ld);
-    return hipGetLastError();
+  // The persistent walk and the FP8-output epilogue take tiles whose
+  // column blocks align with 128 (the epilogue pairs waves wn, wn ^ 1).
+  constexpr bool kAligned = C::BN % kGroup == 0;
+  if constexpr (kAligned) {
+    if (!ue8m0 && out.q == nullptr && use_persistent(k)) {
+      const int t_pad = (tiles_m * tiles_n + 7) / 8 * 8;
+      const DenseTiles src{pa, pb, sb, k, tiles_m, tiles_n, t_pad, C::BM, C::BN};
+      hipLaunchKernelGGL(gemm_nt_persistent_kernel<C>, dim3((uint32_t)persistent_grid(t_pad)), block, 0, stream, src,
+                         sa, out.d, m, n, (int)k, sa_ld);
+      return hipGetLastError();
+    }
   }
-  if (ue8m0)
+  if (ue8m0) {
     hipLaunchKernelGGL((gemm_nt_kernel<C, false, true>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
                        sa_ld, tiles_m, tiles_n);
-  else if (out.q != nullptr)
-    hipLaunchKernelGGL((gemm_nt_kernel<C, true, false>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
-                       sa_ld, tiles_m, tiles_n);
-  else
+  } else if (out.q != nullptr) {
+    if constexpr (!kAligned) return hipErrorInvalidValue;
+    else
+      hipLaunchKernelGGL((gemm_nt_kernel<C, true, false>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
+                         sa_ld, tiles_m, tiles_n);
+  } else
     hipLaunchKernelGGL((gemm_nt_kernel<C, false, false>), grid, block, 0, stream, pa, sa, pb, sb, out, m, n, (int)k,
                        sa_ld, tiles_m, tiles_n);
   return hipGetLastError();
@@ -1028,6 +1054,7 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int
   const TileOut out{static_cast<uint16_t*>(d), nullptr, nullptr, 0};
   switch (plan.kind) {
     case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
+    case kGemmTile256x192: return launch_tile<Tile256x192>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
@@ -1085,6 +1112,7 @@ hipError_t launch_gemm_fp8out(GemmKind kind, const void* a, const float* sa, int
                               int64_t k, hipStream_t stream) {
   const TileOut out{static_cast<uint16_t*>(d), static_cast<uint8_t*>(q), sd, sd_ld};
   switch (kind) {
+    case kGemmTile256x192:  // the epilogue's 1x128 groups need 128-aligned column blocks
     case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
@@ -1098,6 +1126,7 @@ hipError_t launch_gemm_ue8m0(const GemmPlan& plan, const void* a, const float* s
   const TileOut out{static_cast<uint16_t*>(d), nullptr, nullptr, 0};
   switch (plan.kind) {
     case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
+    case kGemmTile256x192: return launch_tile<Tile256x192>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
     case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
     case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
     case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
@@ -1126,6 +1155,7 @@ hipError_t launch_gemm_mx(GemmKind kind, const void* a, const int32_t* sa, int64
                           hipStream_t stream) {
   switch (kind) {
     case kGemmTile256x256: return launch_tile_mx<Tile256x256>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
+    case kGemmTile256x192: return launch_tile_mx<Tile256x192>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
     case kGemmTile128x256: return launch_tile_mx<Tile128x256>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
     case kGemmTile256x128: return launch_tile_mx<Tile256x128>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);
     case kGemmTile128x128: return launch_tile_mx<Tile128x128>(a, sa, sa_ld, b, sb, sb_ld, d, m, n, k, stream);

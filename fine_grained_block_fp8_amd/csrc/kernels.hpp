@@ -23,6 +23,7 @@ enum GemmKind : int {
   kGemmTile256x128 = 2,  // 256x128, 8 waves of 64x64
   kGemmTile128x128 = 3,  // 128x128, 4 waves of 64x64
   kGemmDecode = 4,       // M <= 16: 16-column slabs, K split across waves
+  kGemmTile256x192 = 5,  // 256x192, 12 waves of 64x64
 };
 
 struct GemmPlan {

@@ -16,7 +16,7 @@ from tests.parity import bits32, check_sampled, codes, gpu_hot_path
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["tile256x256_w4x2", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
+TILES = ["tile256x256_w4x2", "tile256x192_w4x3", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
 
 
 def run_and_check(lin, label):

@@ -17,7 +17,7 @@ from tests.parity import check_gemm, codes, d_to_f64, sample_col_blocks, sample_
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["tile256x256_w4x2", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
+TILES = ["tile256x256_w4x2", "tile256x192_w4x3", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
 
 
 def mag_sum_mx(qa, sa, qb, sb):

@@ -15,7 +15,7 @@ from tests.parity import bits32, check_gemm, check_sampled, codes, d_to_f64, mag
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["tile256x256_w4x2", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
+TILES = ["tile256x256_w4x2", "tile256x192_w4x3", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
 
 
 def ue8m0_path(lin):
