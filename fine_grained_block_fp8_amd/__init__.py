@@ -285,14 +285,19 @@ def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor, 
     return d
 
 
-FUSED_MAX_M, FUSED_MAX_K = 4, 32768
+# fp8_linear_nt: one fused kernel up to FUSED_MAX_M rows when no workspace is
+# given; up to FUSED_FAST_MAX_M rows that kernel is also the fastest path
+# (above it, quantize + product with a workspace is faster).
+FUSED_MAX_M, FUSED_FAST_MAX_M = 16, 4
 
 
 def fp8_linear_nt(x: torch.Tensor, weight, d: torch.Tensor, act_out=None) -> torch.Tensor:
     """d[M, N] = quantize_groups(x) . B^T for bf16 x [M, K] and the stored
-    weight (q [N, K], sb).  One fused kernel for M <= 4 (K <= 32768);
-    `act_out` = (q [M, K], sa [K/128, sa_ld]) optionally receives the quantized
-    activation (and is required as workspace for larger M)."""
+    weight (q [N, K], sb).  `act_out` = (q [M, K], sa [K/128, sa_ld])
+    optionally receives the quantized activation.  One fused kernel for
+    M <= 4; for 4 < M <= 16 a fused kernel without `act_out`, the quantizer
+    and the product with it; above 16 rows `act_out` is required.  Every
+    path gives the same bits."""
     qb, sb = weight
     _need(x, "x", (torch.bfloat16,), 2)
     _need(qb, "b", _FP8, 2)
@@ -322,7 +327,7 @@ def fp8_linear(x: torch.Tensor, weight) -> torch.Tensor:
     m, k = flat.shape
     d = torch.empty((m, qb.shape[0]), dtype=torch.bfloat16, device=x.device)
     act = None
-    if not (m <= FUSED_MAX_M and k <= FUSED_MAX_K):
+    if m > FUSED_FAST_MAX_M:  # the two-launch path is the faster one here
         act = (torch.empty((m, k), dtype=torch.float8_e4m3fn, device=x.device),
                torch.empty((k // GROUP, padded_rows(m)), dtype=torch.float32, device=x.device))
     fp8_linear_nt(flat, (qb, sb), d, act)

@@ -384,7 +384,7 @@ int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, 
   if (!x_bf16 || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if ((q_e4m3 == nullptr) != (sa == nullptr))
     return fail(FGFP8_EINVAL, "%s: q_e4m3 and sa must be given together", who);
-  const bool fused = m <= fgfp8::kFusedMaxM && k <= fgfp8::kFusedMaxK;
+  const bool fused = m <= fgfp8::kFusedLdsMaxM || (m <= fgfp8::kFusedMaxM && q_e4m3 == nullptr);
   if (!fused && q_e4m3 == nullptr)
     return fail(FGFP8_EINVAL, "%s: m=%lld k=%lld needs the q_e4m3/sa workspace", who, (long long)m, (long long)k);
   if (q_e4m3 != nullptr) {

@@ -22,6 +22,8 @@
 // Both variants share the chunk order and the reduction order, so their
 // outputs are bit-identical.
 
+#include <cstdlib>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,7 +36,8 @@ namespace fgfp8 {
 // The A fragments of the non-fused form take registers too: it holds 8.
 template <int KS, bool FUSED>
 constexpr int decode_max_chunks() { return FUSED && KS >= 8 ? 12 : 8; }
-constexpr int kFusedMaxRows = 4;
+constexpr int kFusedMaxRows = (int)kFusedLdsMaxM;
+constexpr int64_t kFusedLdsMaxK = 32768;  // 4 x K bytes of LDS per workgroup
 
 __device__ __forceinline__ v8i_t frag_of(uint4 lo, uint4 hi) {
   v8i_t f;
@@ -256,6 +259,134 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
   }
 }
 
+// Fused act-quant + product for M <= 16, with the activation quantized in
+// registers instead of LDS.  Lane (li, lg) of a wave needs, per chunk kb of
+// its K range, the A fragment bytes of row li at K positions kb*128 + 32*lg
+// .. +32 (the same lane layout as the weight fragments).  It loads those 32
+// bf16 values itself; a 1x128 group of row li lies on the four lanes li +
+// 16*lg, so its amax is two lane exchanges, and the lane then encodes its
+// 32 values with the group's scale: exactly quantize_fp8_groups'
+// arithmetic (amax, s = fl32(amax/448), E4M3(fl32(x/s))), so the product is
+// bit-identical to quantize_fp8_groups followed by the decode product (same
+// chunk ranges, promotion order and reduction order).  Rows >= M load
+// nothing (out-of-range buffer offsets) and contribute zeros.  Nothing is
+// held per workgroup, so M and K are not bound by LDS; each wave requests
+// MAXC chunks at a time -- per chunk the four activation loads, then the two
+// weight loads (requests complete in issue order, so a chunk's activation
+// is usable once the previous chunk's weights have arrived).  If q_out is
+// non-null, workgroup 0 also writes the quantized activation and scales.
+template <int KS, int MAXC>
+__global__ __launch_bounds__(KS * 64) void decode_xq_kernel(const uint16_t* __restrict__ X,
+                                                            const uint8_t* __restrict__ B,
+                                                            const float* __restrict__ SB, uint16_t* __restrict__ D,
+                                                            int M, int64_t N, int K, uint8_t* __restrict__ q_out,
+                                                            float* __restrict__ sa_out, int64_t sa_out_ld) {
+  __shared__ v4f_t red[KS * 64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int KB = K / kGroup;
+  const int per = (KB + KS - 1) / KS;
+  const int c_begin = wave * per;
+  const int c_end = c_begin + per < KB ? c_begin + per : KB;
+  const uint32_t b_rows = (uint32_t)(N - n0 < 16 ? N - n0 : 16);
+  const rsrc_t rb = make_rsrc(B + n0 * K, b_rows * (uint32_t)K);
+  const uint32_t off = (uint32_t)li * (uint32_t)K + (uint32_t)lg * 32u;
+  const bool row_ok = li < M;
+  const rsrc_t rx = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+  const uint32_t xoff = off * 2u;  // bytes of bf16 row li, K position 32*lg
+  const rsrc_t rsb = make_rsrc(SB + (n0 / kGroup) * KB, (uint32_t)KB * 4u);
+  const bool writer = q_out != nullptr && blockIdx.x == 0;
+  constexpr uint32_t kOob = 0x80000000u;
+
+  v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xv[MAXC][4], b0[MAXC], b1[MAXC];
+  float sbv = 0.0f;
+  // Every load is issued unconditionally (out-of-range offsets read zeros
+  // without touching memory), so the compiler waits for exactly the load
+  // each instruction needs.
+  auto issue = [&](int cb, int nc) {
+    sbv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rsb, lane < nc ? (uint32_t)(cb + lane) * 4u : kOob, 0, 0));
+#pragma unroll
+    for (int u = 0; u < MAXC; u++) {
+      const bool live = u < nc;
+      const uint32_t xo = live && row_ok ? xoff + (uint32_t)(cb + u) * 256u : kOob;
+#pragma unroll
+      for (int j = 0; j < 4; j++) xv[u][j] = load_rsrc16(rx, xo == kOob ? kOob : xo + 16u * j);
+      const uint32_t o = live ? off + (uint32_t)(cb + u) * 128u : kOob;
+      b0[u] = load_rsrc16(rb, o);
+      b1[u] = load_rsrc16(rb, live ? o + 16u : kOob);
+    }
+  };
+  auto compute = [&](int cb, int nc) {
+    v4f_t part[2];
+    float scl[2];
+#pragma unroll
+    for (int u = 0; u <= MAXC; u++) {
+      if (u < nc) {
+        const int kb = cb + u;
+        uint32_t am = max(max(absmax8_bits(xv[u][0]), absmax8_bits(xv[u][1])),
+                          max(absmax8_bits(xv[u][2]), absmax8_bits(xv[u][3])));
+        am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+        am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+        const float s = group_scale(__uint_as_float(am));
+        const double r = 1.0 / (double)s;
+        const uint2 q0 = quantize8(xv[u][0], r), q1 = quantize8(xv[u][1], r);
+        const uint2 q2 = quantize8(xv[u][2], r), q3 = quantize8(xv[u][3], r);
+        const uint4 lo = make_uint4(q0.x, q0.y, q1.x, q1.y), hi = make_uint4(q2.x, q2.y, q3.x, q3.y);
+        if (writer && row_ok) {
+          uint8_t* qp = q_out + (int64_t)li * K + (int64_t)kb * kGroup + lg * 32;
+          *reinterpret_cast<uint4*>(qp) = lo;
+          *reinterpret_cast<uint4*>(qp + 16) = hi;
+          if (lg == 0) sa_out[(int64_t)kb * sa_out_ld + li] = s;
+        }
+        part[u & 1] = mfma_fp8_dec(frag_of(b0[u], b1[u]), frag_of(lo, hi));
+        scl[u & 1] = (row_ok ? s : 0.0f) *
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sbv), u));
+      }
+      if (u > 0 && u - 1 < nc) {
+        const v4f_t& p = part[(u - 1) & 1];
+        const float sc = scl[(u - 1) & 1];
+        acc[0] = __builtin_fmaf(p[0], sc, acc[0]);
+        acc[1] = __builtin_fmaf(p[1], sc, acc[1]);
+        acc[2] = __builtin_fmaf(p[2], sc, acc[2]);
+        acc[3] = __builtin_fmaf(p[3], sc, acc[3]);
+      }
+    }
+  };
+  int cb = c_begin;
+  int nc = c_end - cb < MAXC ? c_end - cb : MAXC;
+  issue(cb, nc);  // even with nc <= 0 (every load out of range): no branch around loads
+  while (nc > 0) {
+    compute(cb, nc);
+    cb += nc;
+    nc = c_end - cb < MAXC ? c_end - cb : MAXC;
+    if (nc > 0) issue(cb, nc);
+  }
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    v4f_t sum = red[lane];
+#pragma unroll
+    for (int w = 1; w < KS; w++) {
+      const v4f_t o = red[w * 64 + lane];
+      sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+    }
+    if (row_ok) {
+      const int64_t c0 = n0 + 4 * lg;
+      uint16_t* drow = D + (int64_t)li * N;
+      if ((N % 4) == 0 && c0 + 4 <= N) {
+        *reinterpret_cast<uint2*>(drow + c0) = make_uint2(pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          if (c0 + r < N) drow[c0 + r] = (uint16_t)bf16_rne(sum[r]);
+      }
+    }
+  }
+}
+
 // K split (1..8 waves per slab): enough waves in flight to cover HBM
 // latency, and at most 12 chunks per wave on the common shapes.
 int decode_split(int64_t n, int64_t k) {
@@ -310,9 +441,37 @@ hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, 
   return launch_decode_t<false>(ks, a, sa, sa_ld, b, sb, d, m, n, k, nullptr, nullptr, 0, stream);
 }
 
+template <int KS, int MAXC>
+static hipError_t launch_decode_xq_ks(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
+                                      int64_t k, uint8_t* q_out, float* sa_out, int64_t sa_out_ld,
+                                      hipStream_t stream) {
+  hipLaunchKernelGGL((decode_xq_kernel<KS, MAXC>), dim3((uint32_t)((n + 15) / 16)), dim3(KS * 64), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(b), sb, static_cast<uint16_t*>(d),
+                     (int)m, n, (int)k, q_out, sa_out, sa_out_ld);
+  return hipGetLastError();
+}
+
+// Four chunks per request batch (140 VGPRs: three waves per SIMD).  Measured
+// against 6 and 8 chunks and other splits: four is fastest at both decode
+// shapes.  The split is decode_split's, so the result is bit-identical to the
+// two-launch path.
+static hipError_t launch_decode_xq(int ks, const void* x, const void* b, const float* sb, void* d, int64_t m,
+                                   int64_t n, int64_t k, uint8_t* q_out, float* sa_out, int64_t sa_out_ld,
+                                   hipStream_t stream) {
+  switch (ks) {
+    case 1: return launch_decode_xq_ks<1, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 2: return launch_decode_xq_ks<2, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 4: return launch_decode_xq_ks<4, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    default: return launch_decode_xq_ks<8, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+  }
+}
+
 hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
                                int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
   const int ks = decode_split(n, k);
+  // Test override: FGFP8_DECODE_XQ forces the register form at any M.
+  if (m > kFusedMaxRows || k > kFusedLdsMaxK || getenv("FGFP8_DECODE_XQ") != nullptr)
+    return launch_decode_xq(ks, x, b, sb, d, m, n, k, static_cast<uint8_t*>(q_out), sa_out, sa_out_ld, stream);
   // Activation quantize tasks (row, 128-group) per lane: M * K/128 over the
   // workgroup's KS * 4 lanes-of-16.  When more than three, issue up to 12
   // ahead of the weight stream.

@@ -60,9 +60,12 @@ hipError_t launch_gemm_fp8out(GemmKind kind, const void* a, const float* sa, int
 int decode_split(int64_t n, int64_t k);
 hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
                          void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
-// Fused activation quantization + product for M <= 4 (K <= kFusedMaxK).
-constexpr int64_t kFusedMaxM = 4;
-constexpr int64_t kFusedMaxK = 32768;
+// Fused activation quantization + product: one kernel for M <= kFusedMaxM
+// (any K).  Up to kFusedLdsMaxM rows it quantizes into LDS and beats the two
+// launches; above that the register form is slower than them, so it runs
+// only when the caller gives no workspace for the two-launch path.
+constexpr int64_t kFusedMaxM = 16;
+constexpr int64_t kFusedLdsMaxM = 4;
 hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
                                int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream);
 

@@ -183,12 +183,15 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
  * _BlockProduct.execute: round the bf16 input per 1x128 group, then
  * fp8_gemm_nt with the stored weight): D = quantize_groups(x) . B^T.
  *
- * For m <= 4 and k <= 32768 this is a single kernel that quantizes x inside
- * every workgroup while the weight stream is in flight (decode: the
+ * For m <= 4 (k <= 32768) this is a single kernel that quantizes x into LDS
+ * inside every workgroup while the weight stream is in flight (decode: the
  * activation-quantize step must not cost a launch of its own; the AReno FP8
  * decode pull request measured the separate quantize chain holding a decode
- * linear at ~1.2x until it was fused).  Its result is bit-identical to
- * quantize_fp8_groups followed by fp8_gemm_nt.  For larger m it runs those
+ * linear at ~1.2x until it was fused).  For 4 < m <= 16 (or k > 32768) with
+ * q_e4m3/sa NULL it is a single kernel that quantizes x in registers, each
+ * wave its own K range; with q_e4m3/sa given it runs quantize_fp8_groups and
+ * fp8_gemm_nt, which is faster at those m.  Every path is bit-identical to
+ * quantize_fp8_groups followed by fp8_gemm_nt.  Above 16 rows it runs those
  * two calls.
  *
  * x_bf16  [m][k] bfloat16, input.
@@ -197,7 +200,7 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
  * d_bf16  [m][n] bfloat16, output.
  * q_e4m3, sa, sa_ld: the quantized activation [m][k] and its MN-major scales
  *         [k/128][sa_ld], exactly as quantize_fp8_groups writes them.
- *         Optional (both NULL) when m <= 4; required as workspace otherwise.
+ *         Optional (both NULL) when m <= 16; required as workspace otherwise.
  * Requirements: m >= 0, n >= 0, k > 0 and k % 128 == 0; if q_e4m3 is given,
  * sa_ld % 4 == 0 and sa_ld >= m. */
 int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, const float* sb, int64_t n,
@@ -311,14 +314,17 @@ const char* fgfp8_last_error(void);
  * Mirrors the pages' habit of printing every tile decision next to the
  * number it produced (deepgemm-rust README, "Benchmark").  For m > 16 the
  * environment variable FGFP8_GEMM_TILE, set to one of the tile names
- * (tile256x256_w4x2, tile256x128_w4x2, tile128x256_w2x4, tile128x128_w2x2),
- * forces that tile in fp8_gemm_nt (tuning and tests); other values are
- * ignored.  FGFP8_PERSISTENT=1 makes fp8_gemm_nt (bf16 output, FP32 scales)
- * and m_grouped_fp8_gemm_nt_contiguous walk their tiles persistently (one
- * workgroup per compute unit, the K pipeline continuing across tiles; same
- * results bit for bit) for k >= 256; by default every tile is a workgroup of
- * its own, which measured faster.  FGFP8_PRINT_CONFIG=1 prints each call's
- * kernel choice to stderr. */
+ * (tile256x256_w4x2, tile256x192_w4x3, tile256x128_w4x2, tile128x256_w2x4,
+ * tile128x128_w2x2), forces that tile in fp8_gemm_nt (tuning and tests; the
+ * FP8-output call takes tile256x256_w4x2 for tile256x192_w4x3); other values
+ * are ignored.  FGFP8_PERSISTENT=1 makes fp8_gemm_nt (bf16 output, FP32
+ * scales) and m_grouped_fp8_gemm_nt_contiguous walk their tiles
+ * persistently (one workgroup per compute unit, the K pipeline continuing
+ * across tiles; same results bit for bit) for k >= 256; by default every
+ * tile is a workgroup of its own, which measured faster.  FGFP8_DECODE_XQ
+ * (any value) makes fp8_linear_nt's fused path use the register-quantizing
+ * kernel at every m <= 16 (tests; same bits).  FGFP8_PRINT_CONFIG=1 prints
+ * each call's kernel choice to stderr. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
 
 #ifdef __cplusplus

@@ -260,7 +260,7 @@ def test_linear_rejects():
         return lib.fp8_linear_nt(x, m, k, P, P, n, P, q, sa, sa_ld, None)
 
     assert call(k=100) == fg.FGFP8_EINVAL
-    assert call(m=8) == fg.FGFP8_EINVAL  # larger m needs the workspace
+    assert call(m=17) == fg.FGFP8_EINVAL  # above 16 rows the workspace is required
     assert "workspace" in fg.last_error()
     assert call(q=P) == fg.FGFP8_EINVAL  # q without sa
     assert call(m=8, q=P, sa=P, sa_ld=6) == fg.FGFP8_EINVAL

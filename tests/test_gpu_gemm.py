@@ -153,12 +153,13 @@ def test_runs_on_a_side_stream():
     assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288), (200, 384), (1000, 128)])
 def test_fused_linear_matches_two_calls_and_oracle(m, n, k):
-    """fp8_linear_nt (one fused kernel for m <= 4) writes the same quantized
-    activation as quantize_fp8_groups (checked bit-exact against the oracle)
-    and the same output bits as quantize_fp8_groups + fp8_gemm_nt."""
+    """fp8_linear_nt (one fused kernel for m <= 4, and for m <= 16 without the
+    activation outputs) writes the same quantized activation as
+    quantize_fp8_groups (checked bit-exact against the oracle) and the same
+    output bits as quantize_fp8_groups + fp8_gemm_nt."""
     lin = workloads.decode_linear(m, n, k) if (n, k) in workloads.DECODE_SHAPES else workloads.random_linear(m, n, k, seed=m + n)
     q, sa, qb, sb, d_two = gpu_hot_path(lin)
     x = torch.from_numpy(lin.a.view(np.int16)).view(torch.bfloat16).cuda()
@@ -171,14 +172,36 @@ def test_fused_linear_matches_two_calls_and_oracle(m, n, k):
     assert np.array_equal(codes(q2), oq)
     assert np.array_equal(sa2[:, :m].cpu().numpy().view(np.uint32), osa[:, :m].view(np.uint32))
     assert torch.equal(d.view(torch.int16), d_two.view(torch.int16)), "fused output differs from the two-call path"
-    # and without the optional activation outputs
+    # and without the optional activation outputs (for m > 4 the
+    # register-quantizing fused kernel)
     d3 = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
-    if m <= 4:
-        fg.fp8_linear_nt(x, (qb, sb), d3)
-        torch.cuda.synchronize()
-        assert torch.equal(d3.view(torch.int16), d_two.view(torch.int16))
+    fg.fp8_linear_nt(x, (qb, sb), d3)
+    torch.cuda.synchronize()
+    assert torch.equal(d3.view(torch.int16), d_two.view(torch.int16))
     rng = np.random.default_rng(5)
     check_sampled(lin, q, sa, qb, sb, d, np.arange(m), sample_col_blocks(n, 8, rng), f"fused {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [1, 3, 4])
+@pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288), (1000, 384)])
+def test_register_quantizing_kernel_at_small_m(m, n, k, monkeypatch):
+    """The register-quantizing fused kernel forced at m <= 4 (where the LDS
+    form is the default): its quantized activation outputs (written by
+    workgroup 0) are the oracle's bit for bit, and its product is the
+    two-call path's bits."""
+    monkeypatch.setenv("FGFP8_DECODE_XQ", "1")
+    lin = workloads.decode_linear(m, n, k) if (n, k) in workloads.DECODE_SHAPES else workloads.random_linear(m, n, k, seed=m + n)
+    q, sa, qb, sb, d_two = gpu_hot_path(lin)
+    x = to_dev_bf16(lin.a)
+    d = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q2 = torch.full((m, k), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sa2 = torch.full((k // 128, fg.padded_rows(m)), float("nan"), dtype=torch.float32, device="cuda")
+    fg.fp8_linear_nt(x, (qb, sb), d, (q2, sa2))
+    torch.cuda.synchronize()
+    oq, osa = oracle.quantize_groups(lin.a)
+    assert np.array_equal(codes(q2), oq)
+    assert np.array_equal(sa2[:, :m].cpu().numpy().view(np.uint32), osa[:, :m].view(np.uint32))
+    assert torch.equal(d.view(torch.int16), d_two.view(torch.int16))
 
 
 TILES = ["tile256x256_w4x2", "tile256x192_w4x3", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
