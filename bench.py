@@ -297,16 +297,19 @@ def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32"):
     return preps, elapsed, per, timed
 
 
+# The sources the tile GEMM kernels are built from.
+GEMM_SOURCES = ("common.hpp", "gemm.hip", "kernels.hpp")
+
+
 def kernel_sources_hash() -> str:
-    """SHA-256 prefix over the kernel sources, to tie a counter record in
-    profiles/ to the code it was measured on."""
-    import glob
+    """SHA-256 prefix over the GEMM kernels' sources, to tie a counter record
+    in profiles/ to the code it was measured on."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "fine_grained_block_fp8_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in GEMM_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "fine_grained_block_fp8_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
