@@ -503,8 +503,8 @@ def main():
     if args.gpus != 1:
         print(
             json.dumps(
-                {"error": "this build measures one GPU: the block-scaled FP8 linear runs on a single MI355X; "
-                 "multi-GPU sharding is described, not run", "n_gpus": args.gpus}
+                {"error": "fgfp8 runs the block-scaled FP8 linear on one MI355X; sharding over several GPUs "
+                 "is described in the design notes, not run", "n_gpus": args.gpus}
             )
         )
         sys.exit(2)
