@@ -55,8 +55,8 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 STEPS_ARE = {
     "prefill": "act-quant (1x128) + block-scaled FP8 GEMM (bf16 out) for every linear; weights pre-quantized",
     "prefill_mx": "act-quant (1x32 E8M0) + MXFP8 GEMM (bf16 out) for every linear; weights pre-quantized (1x32 E8M0)",
-    "moe_layer": "route + gather/act-quant + grouped GEMM (gate_up) + SiLU*up/act-quant + grouped GEMM (down) + "
-                 "weighted combine; expert weights pre-quantized; value counts routed rows only",
+    "moe_layer": "route + gather/act-quant + grouped GEMM (gate_up) with SiLU*up/act-quant in its epilogue + "
+                 "grouped GEMM (down) + weighted combine; expert weights pre-quantized; value counts routed rows only",
 }
 
 
@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--moe-unfused", action="store_true",
+                   help="moe_layer: run the gate_up product and SiLU.mul+quantize as two launches")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--decode-reps", type=int, default=50, help="rounds over the 8 weight sets per decode timing")
     return p.parse_args()
@@ -719,10 +721,11 @@ def bench_masked(args, fg, torch, workloads):
 
 def bench_moe_layer(args, fg, torch, workloads):
     """The FP8 MoE layer: one step = route -> gather+quantize -> grouped
-    product (gate_up, N = 2I) -> SiLU-times-up+quantize -> grouped product
-    (down, N = H) -> weighted combine, every buffer sized by the padded-row
-    upper bound so that nothing waits for the host.  Value: useful TFLOP/s of
-    the two products (routed rows only) over the whole step."""
+    product (gate_up, N = 2I) with SiLU-times-up+quantize in its epilogue
+    (two launches with --moe-unfused) -> grouped product (down, N = H) ->
+    weighted combine, every buffer sized by the padded-row upper bound so that
+    nothing waits for the host.  Value: useful TFLOP/s of the two products
+    (routed rows only) over the whole step."""
     c = workloads.moe_layer()
     g, hd, it, t, tk = c.experts, c.hidden, c.inter, c.tokens, c.topk
     x = dev_bf16(c.x, torch)
@@ -753,32 +756,40 @@ def bench_moe_layer(args, fg, torch, workloads):
           torch.empty((it // 128, m), dtype=torch.float32, device=dev))
     y = torch.empty((m, hd), dtype=torch.bfloat16, device=dev)
     out = torch.empty((t, hd), dtype=torch.bfloat16, device=dev)
-    names = ["route", "gather_quant", "gemm_gate_up", "silu_mul_quant", "gemm_down", "combine"]
+    fused = not args.moe_unfused
+    names = (["route", "gather_quant", "gemm_gate_up_silu_quant", "gemm_down", "combine"] if fused else
+             ["route", "gather_quant", "gemm_gate_up", "silu_mul_quant", "gemm_down", "combine"])
 
     def step(ev=None):
-        def mark(i):
+        n_ev = [0]
+
+        def mark():
             if ev:
-                ev[i].record()
-        mark(0)
+                ev[n_ev[0]].record()
+            n_ev[0] += 1
+        mark()
         _counts, m_idx, tok, row_of = fg.moe_route_contiguous(idx, g, out=route)
-        mark(1)
+        mark()
         fg.moe_gather_quantize(x, tok, out=a1)
-        mark(2)
-        fg.m_grouped_fp8_gemm_nt_contiguous(a1, (q1, s1), h, m_idx)
-        mark(3)
-        fg.silu_mul_quantize(h, m_idx, out=a2)
-        mark(4)
+        mark()
+        if fused:
+            fg.moe_gate_up_silu_quantize(a1, (q1, s1), m_idx, out=a2)
+        else:
+            fg.m_grouped_fp8_gemm_nt_contiguous(a1, (q1, s1), h, m_idx)
+            mark()
+            fg.silu_mul_quantize(h, m_idx, out=a2)
+        mark()
         fg.m_grouped_fp8_gemm_nt_contiguous(a2, (q2, s2), y, m_idx)
-        mark(5)
+        mark()
         fg.moe_combine(y, row_of, wts, out=out)
-        mark(6)
+        mark()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[HipEvent(torch) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[HipEvent(torch) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     ahead = GpuAhead(torch)
-    probe = [HipEvent(torch) for _ in range(7)]
+    probe = [HipEvent(torch) for _ in range(len(names) + 1)]
     host_step = host_enqueue_seconds(lambda: step(probe), torch)
     e_first, e_last = HipEvent(torch), HipEvent(torch)
     torch.cuda.synchronize()
@@ -795,16 +806,24 @@ def bench_moe_layer(args, fg, torch, workloads):
     f2 = 2.0 * pairs * hd * it
     flops = f1 + f2
     m_real = padded_rows_of(route[0])
+    gu = "gemm_gate_up_silu_quant" if fused else "gemm_gate_up"
     per = [{"name": c.name, "m_pad_max": m, "m_pad": m_real, "pairs": pairs, "hidden": hd, "inter": it, "experts": g,
-            **{f"{n}_us": stage[n] * 1e6 for n in names},
-            "gate_up_tflops_useful": f1 / stage["gemm_gate_up"] / 1e12,
-            "down_tflops_useful": f2 / stage["gemm_down"] / 1e12, "_gemm_s": stage["gemm_gate_up"] + stage["gemm_down"]}]
-    gemm_s = stage["gemm_gate_up"] + stage["gemm_down"]
-    # both products run the same kernel: its per-launch average over the two
-    roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x4> (gate_up and down launches averaged)",
-            "achieved": round(flops / gemm_s / 1e12, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(flops / gemm_s / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": None,
-            "algorithmic_flops_per_launch": flops / 2, "mean_launch_us": round(gemm_s / 2 * 1e6, 2)}
+            "gate_up_fused": fused, **{f"{n}_us": stage[n] * 1e6 for n in names},
+            "gate_up_tflops_useful": f1 / stage[gu] / 1e12,
+            "down_tflops_useful": f2 / stage["gemm_down"] / 1e12, "_gemm_s": stage[gu] + stage["gemm_down"]}]
+    gemm_s = stage[gu] + stage["gemm_down"]
+    if fused:
+        # the dominant kernel: the gate_up product with its SiLU.mul+quantize epilogue
+        roof = {"bound": "mfma", "kernel": "grouped_gemm_silu_kernel<tile128x256_w2x4> (gate_up + SiLU.mul + quantize)",
+                "achieved": round(f1 / stage[gu] / 1e12, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(f1 / stage[gu] / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": f1, "mean_launch_us": round(stage[gu] * 1e6, 2)}
+    else:
+        # both products run the same kernel: its per-launch average over the two
+        roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x4> (gate_up and down launches averaged)",
+                "achieved": round(flops / gemm_s / 1e12, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(flops / gemm_s / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": flops / 2, "mean_launch_us": round(gemm_s / 2 * 1e6, 2)}
     return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gemm_s, flops
 
 

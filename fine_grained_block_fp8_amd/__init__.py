@@ -61,13 +61,15 @@ _lib.moe_route_contiguous.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
 _lib.moe_gather_quantize.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _fp, _i64, _vp]
 _lib.silu_mul_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp, _fp, _i64, _vp]
 _lib.moe_combine.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _i32, _vp, _vp]
+_lib.moe_gate_up_silu_quantize.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _vp, _fp, _i64, _i64, _i64, _i64, _vp]
 _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
               "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
-              "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx"):
+              "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
+              "moe_gate_up_silu_quantize"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -465,6 +467,38 @@ def silu_mul_quantize(h: torch.Tensor, m_indices: torch.Tensor, out=None):
     return q, sa
 
 
+def moe_gate_up_silu_quantize(a, w1, m_indices: torch.Tensor, out=None):
+    """The gate_up grouped product with SiLU.mul and the 1x128 quantizer in
+    its epilogue: a = (q [M, K], sa), w1 = (q [G, 2I, K], sb [G, 2I/128,
+    K/128]) with the gate rows first; returns (q [M, I], sa [I/128,
+    roundup(M, 4)]), the bits m_grouped_fp8_gemm_nt_contiguous followed by
+    silu_mul_quantize give."""
+    (qa, sa), (qw, sw) = a, w1
+    _need(qa, "a", _FP8, 2)
+    _need(sa, "sa", (torch.float32,), 2)
+    _need(qw, "w1", _FP8, 3)
+    _need(sw, "sb1", (torch.float32,), 3)
+    _need(m_indices, "m_indices", (torch.int32,), 1)
+    m, k = qa.shape
+    g, two_i, k2 = qw.shape
+    if k2 != k or two_i % 2 or m_indices.shape[0] != m:
+        raise ValueError("shape mismatch among a [M, K], w1 [G, 2I, K], m_indices [M]")
+    if k % GROUP == 0 and two_i % GROUP == 0 and tuple(sw.shape) != (g, two_i // GROUP, k // GROUP):
+        raise ValueError("sb1 must be [G, 2I/128, K/128]")
+    inter = two_i // 2
+    if out is None:
+        out = (torch.empty((m, inter), dtype=torch.float8_e4m3fn, device=qa.device),
+               torch.empty((inter // GROUP, padded_rows(m)), dtype=torch.float32, device=qa.device))
+    q, sq = out
+    _need(q, "q", _FP8, 2)
+    _need(sq, "sq", (torch.float32,), 2)
+    if tuple(q.shape) != (m, inter):
+        raise ValueError("q must be [M, I]")
+    _check(_lib.moe_gate_up_silu_quantize(_ptr(qa), _ptr(sa), sa.shape[1], _ptr(m_indices), _ptr(qw), _ptr(sw), g,
+                                          _ptr(q), _ptr(sq), sq.shape[1], m, inter, k, _stream(qa)))
+    return q, sq
+
+
 def moe_combine(y: torch.Tensor, row_of: torch.Tensor, topk_weights: torch.Tensor, out=None) -> torch.Tensor:
     """out[t] = bf16(sum_j topk_weights[t, j] * y[row_of[t, j]]) in FP32, slot
     order; slots whose row lies outside [0, rows) are skipped.  y bf16 [rows, H], row_of int32 [T, topk], topk_weights float32 [T, topk]."""
@@ -485,11 +519,13 @@ def moe_combine(y: torch.Tensor, row_of: torch.Tensor, topk_weights: torch.Tenso
     return out
 
 
-def moe_fp8_layer(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor, w1, w2) -> torch.Tensor:
+def moe_fp8_layer(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor, w1, w2,
+                  fused: bool = True) -> torch.Tensor:
     """The FP8 MoE layer (deepgemm-rust README, "What's implemented",
     moe_fp8_layer row), every step on the device with no host synchronisation:
     route -> gather+quantize -> grouped product with w1 -> SiLU.mul+quantize ->
-    grouped product with w2 -> weighted combine.
+    grouped product with w2 -> weighted combine.  With `fused` the w1 product
+    and SiLU.mul+quantize are one kernel (same bits).
 
     x bf16 [T, H]; topk_idx int32 [T, topk]; topk_weights float32 [T, topk];
     w1 = (q [G, 2I, H], sb [G, 2I/128, H/128]) with the gate rows first, then
@@ -504,9 +540,12 @@ def moe_fp8_layer(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.T
     counts, m_indices, token_of_row, row_of = moe_route_contiguous(topk_idx, g)
     m = m_indices.shape[0]
     a1 = moe_gather_quantize(x, token_of_row)
-    hbuf = torch.empty((m, two_i), dtype=torch.bfloat16, device=x.device)
-    m_grouped_fp8_gemm_nt_contiguous(a1, (q1, s1), hbuf, m_indices)
-    a2 = silu_mul_quantize(hbuf, m_indices)
+    if fused:
+        a2 = moe_gate_up_silu_quantize(a1, (q1, s1), m_indices)
+    else:
+        hbuf = torch.empty((m, two_i), dtype=torch.bfloat16, device=x.device)
+        m_grouped_fp8_gemm_nt_contiguous(a1, (q1, s1), hbuf, m_indices)
+        a2 = silu_mul_quantize(hbuf, m_indices)
     y = torch.empty((m, hdim), dtype=torch.bfloat16, device=x.device)
     m_grouped_fp8_gemm_nt_contiguous(a2, (q2, s2), y, m_indices)
     return moe_combine(y, row_of, topk_weights)
@@ -536,6 +575,7 @@ __all__ = [
     "m_grouped_fp8_gemm_nt_masked",
     "moe_combine",
     "moe_fp8_layer",
+    "moe_gate_up_silu_quantize",
     "moe_gather_quantize",
     "moe_max_padded_rows",
     "moe_route_contiguous",

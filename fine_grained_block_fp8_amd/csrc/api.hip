@@ -356,6 +356,31 @@ int silu_mul_quantize(const void* h_bf16, int64_t m, int64_t inter, const int32_
                   who);
 }
 
+int moe_gate_up_silu_quantize(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                              const void* w1_e4m3, const float* sb1, int32_t num_groups, void* q_e4m3, float* sq,
+                              int64_t sq_ld, int64_t m, int64_t inter, int64_t k, void* stream) {
+  const char* who = "moe_gate_up_silu_quantize";
+  if (m < 0 || m >= kMaxRows || m % 128 != 0)
+    return fail(FGFP8_EINVAL, "%s: m=%lld must be a non-negative multiple of 128", who, (long long)m);
+  if (num_groups < 1) return fail(FGFP8_EINVAL, "%s: num_groups=%d must be >= 1", who, (int)num_groups);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_k(who, inter)) return rc;
+  if ((inter + 128) * k >= (int64_t(1) << 31))
+    return fail(FGFP8_EINVAL, "%s: (inter + 128) * k must stay below 2^31", who);
+  if (int rc = check_sa(who, m, k, sa_ld)) return rc;
+  if (int rc = check_sa(who, m, inter, sq_ld)) return rc;
+  if (m == 0) return FGFP8_OK;
+  if (!a_e4m3 || !sa || !m_indices || !w1_e4m3 || !sb1 || !q_e4m3 || !sq)
+    return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(m_indices) || !aligned16(w1_e4m3) || !aligned16(sb1) ||
+      !aligned16(q_e4m3) || !aligned16(sq))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_grouped_gemm_silu(a_e4m3, sa, sa_ld, m_indices, w1_e4m3, sb1, num_groups, q_e4m3,
+                                                  sq, sq_ld, m, inter, k, (hipStream_t)stream),
+                  who);
+}
+
 int moe_combine(const void* y_bf16, int64_t y_rows, int64_t hdim, const int32_t* row_of, const float* topk_weights,
                 int64_t tokens, int32_t topk, void* out_bf16, void* stream) {
   const char* who = "moe_combine";

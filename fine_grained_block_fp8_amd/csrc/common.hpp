@@ -104,6 +104,12 @@ __device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// The MoE layer's activation: silu(g) * u = g / (1 + e^-g) * u, each step in
+// FP32, for the bf16 gate and up projections g and u (the caller rounds the
+// result to bf16).  One definition for the standalone kernel and the fused
+// gate_up epilogue, so that the two agree bit for bit.
+__device__ __forceinline__ float silu_mul_f32(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 // Largest |value| bit pattern among the 8 bf16 in a 16-byte word (as the
 // float32 bit pattern, i.e. shifted into the high half).
 __device__ __forceinline__ uint32_t absmax8_bits(uint4 v) {

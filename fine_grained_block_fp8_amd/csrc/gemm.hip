@@ -190,8 +190,10 @@ __device__ __forceinline__ void barrier_no_fence() {
 // contiguous bytes, in another lane order.
 __device__ __forceinline__ int k_segment(int c) { return (c >> 1) | ((c & 1) << 2); }
 
+// up_rows (the fused gate_up tile only): B rows of tile columns >= 128 lie
+// up_rows further on (the up half of the weight).
 template <class C>
-__device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wave, int lane) {
+__device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wave, int lane, uint32_t up_rows = 0) {
   // the loader's counts: rounded up, so that an uneven deal still gives
   // every wave AN A-offsets followed by BN_ B-offsets
   constexpr int AN = StageLoader<C>::AN, BN_ = StageLoader<C>::BN_;
@@ -204,7 +206,8 @@ __device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wa
 #pragma unroll
   for (int i = 0; i < BN_; i++) {
     const int rho = (wave + C::WAVES * i) * 8 + r8;
-    voff[AN + i] = (uint32_t)b_col_of_row<C>(rho) * K + (k_segment(cs ^ swz(rho)) << 4);
+    const uint32_t col = (uint32_t)b_col_of_row<C>(rho);
+    voff[AN + i] = (col + (col >= (uint32_t)kGroup ? up_rows : 0u)) * K + (k_segment(cs ^ swz(rho)) << 4);
   }
 }
 
@@ -434,17 +437,120 @@ struct TileOut {
 // which serialises the K pipeline.  The pipeline orders those copies before
 // the reads itself (explicit vmcnt waits and a barrier per K block).  The
 // codegen test checks the count of full drains per kernel.
-template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false>
+// The fused gate_up tile of the MoE layer (SILU): tile columns [0, 128) are
+// gate rows gate_block*128 .. of the weight and [128, 256) the matching up
+// rows, up_rows further on (b points at the gate block); the epilogue writes
+// the 1x128-quantized activation bf16(silu(gate) * up) of act columns
+// col0 .. col0 + 127 into q [M][ld] (the tile's output parameter) with
+// scales sq [ld/128][sq_ld], zero for rows whose m_indices entry is negative.
+struct GateUp {
+  uint32_t up_rows = 0;
+  int64_t gate_block = 0, up_block = 0;
+  float* sq = nullptr;
+  int64_t sq_ld = 0, col0 = 0, ld = 0;
+  const int32_t* m_indices = nullptr;
+};
+
+// Epilogue of the fused gate_up tile (waves wn = 0, 1 hold the gate half,
+// wn = 2, 3 the up half, with the same fragment geometry: value (mt, t, r)
+// of lane L of gate wave (wm, h) and of up wave (wm, 2 + h) belong to the
+// same activation column).  Every wave runs the same barriers.
+//  1. The up waves store their bf16-rounded values in LDS by position (the
+//     stages are free once every wave is past its last fragment read).
+//  2. The gate waves form bf16(silu(bf16(gate)) * up) with silu_mul_f32,
+//     zero for rows whose m_indices entry is negative -- the standalone
+//     silu_mul_quantize kernel's values, bit for bit.
+//  3. Each row's 128 activation columns lie on gate waves 0 and 1: their
+//     amax meet through LDS, then each lane quantizes 8-column runs with the
+//     activation quantizer's arithmetic and stores codes and the scale.
+template <class C>
+__device__ __forceinline__ void silu_epilogue(uint8_t* lds, v4f_t (&acc)[C::MT][C::NT], const GateUp& gu,
+                                              uint8_t* q, int64_t m0, int wave, int wm, int wn, int lane) {
+  static_assert(C::BM == 128 && C::BN == 256 && C::TN == 64 && C::WAVES_N == 4, "gate waves 0-1, up waves 2-3");
+  constexpr int VALS = C::MT * C::NT * 4, WORDS = VALS / 8;
+  const int li = lane & 15, lg = lane >> 4;
+  uint4* xch = reinterpret_cast<uint4*>(lds);  // [slot][word][lane], 8 KB per slot
+  const int slot = wm + C::WAVES_M * (wn & 1);
+  // value v of a lane: acc[v / (4 NT)][(v / 4) % NT][v % 4]
+  __syncthreads();  // every wave is past its last fragment read
+  if (wn >= 2) {
+#pragma unroll
+    for (int i = 0; i < WORDS; i++) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int v0 = 8 * i + 2 * e, v1 = v0 + 1;
+        w[e] = pack_bf16x2(acc[v0 / (C::NT * 4)][(v0 / 4) % C::NT][v0 % 4],
+                           acc[v1 / (C::NT * 4)][(v1 / 4) % C::NT][v1 % 4]);
+      }
+      xch[(slot * WORDS + i) * 64 + lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  __syncthreads();
+  uint32_t am[C::MT];
+  if (wn < 2) {
+    bool live[C::MT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; mt++) live[mt] = gu.m_indices[m0 + wm * C::TM + 16 * mt + li] >= 0;
+#pragma unroll
+    for (int i = 0; i < WORDS; i++) {
+      const uint4 u = xch[(slot * WORDS + i) * 64 + lane];
+      const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int v = 8 * i + e, mt = v / (C::NT * 4), t = (v / 4) % C::NT, r = v % 4;
+        const float g = __uint_as_float(bf16_rne(acc[mt][t][r]) << 16);
+        const float up = (e & 1) ? bf16_hi(uw[e >> 1]) : bf16_lo(uw[e >> 1]);
+        const float act = __uint_as_float(bf16_rne(silu_mul_f32(g, up)) << 16);
+        acc[mt][t][r] = live[mt] ? act : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < C::MT; mt++) {
+      uint32_t m_ = 0;
+#pragma unroll
+      for (int s = 0; s < C::NT / 2; s++) m_ = max(m_, absmax8_bits(pack8<C>(acc[mt], s)));
+      m_ = max(m_, (uint32_t)__shfl_xor((int)m_, 16));
+      m_ = max(m_, (uint32_t)__shfl_xor((int)m_, 32));
+      am[mt] = m_;
+    }
+    uint32_t* ex = reinterpret_cast<uint32_t*>(lds + C::EPI_OFF);
+    if (lg == 0) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; mt++) ex[wave * C::TM + 16 * mt + li] = am[mt];
+    }
+  }
+  __syncthreads();
+  if (wn < 2) {
+    const uint32_t* ex = reinterpret_cast<const uint32_t*>(lds + C::EPI_OFF);
+    const int partner = wm + C::WAVES_M * (wn ^ 1);
+    const int64_t cw = gu.col0 + wn * C::TN;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; mt++) {
+      const int64_t row = m0 + wm * C::TM + 16 * mt + li;
+      const float sc = group_scale(__uint_as_float(max(am[mt], ex[partner * C::TM + 16 * mt + li])));
+      const double r = 1.0 / (double)sc;
+#pragma unroll
+      for (int s = 0; s < C::NT / 2; s++) {
+        const int64_t c0 = cw + 32 * s + 8 * lg;
+        *reinterpret_cast<uint2*>(q + row * gu.ld + c0) = quantize8(pack8<C>(acc[mt], s), r);
+      }
+      if (lg == 0 && wn == 0) gu.sq[(gu.col0 / kGroup) * gu.sq_ld + row] = sc;
+    }
+  }
+}
+
+template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false, bool SILU = false>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
                                           const float* sb_base, uint16_t* __restrict__ d, const TileOut& out,
                                           int64_t M, int64_t N, int K, int64_t sa_ld, int64_t m0, int64_t n0,
-                                          int64_t sb_ld = 0) {
+                                          int64_t sb_ld = 0, const GateUp& gu = GateUp{}) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int KB = K / kGroup;
   const uint32_t a_rows = (uint32_t)(M - m0 < C::BM ? M - m0 : C::BM);
-  const uint32_t b_rows = (uint32_t)(N - n0 < C::BN ? N - n0 : C::BN);
+  const uint32_t b_rows = SILU ? gu.up_rows + (uint32_t)C::BN : (uint32_t)(N - n0 < C::BN ? N - n0 : C::BN);
   const rsrc_t ra = make_rsrc(a, a_rows * (uint32_t)K);
   const rsrc_t rb = make_rsrc(b, b_rows * (uint32_t)K);
   const rsrc_t rs = make_rsrc(sa + m0, (uint32_t)(((int64_t)KB * sa_ld - m0) * 4));
@@ -454,6 +560,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   const int64_t nblocks = (N + kGroup - 1) / kGroup;
   int64_t nb_lane = n0 / kGroup + lane;
   if (nb_lane >= nblocks) nb_lane = nblocks - 1;
+  if constexpr (SILU) nb_lane = lane == 0 ? gu.gate_block : gu.up_block;
   // MX: lane j copies the packed words of columns n0 + 4j .. n0 + 4j + 3 of
   // chunk kb (sb_base[kb * sb_ld + column]).
   const rsrc_t rsb = MX ? make_rsrc(sb_base + n0, (uint32_t)(((int64_t)KB * sb_ld - n0) * 4))
@@ -470,7 +577,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   v8i_t af[C::MT];
   float sc[C::MT];
   uint32_t voff[StageLoader<C>::NSEG];
-  stage_offsets<C>(voff, (uint32_t)K, wave, lane);
+  stage_offsets<C>(voff, (uint32_t)K, wave, lane, SILU ? gu.up_rows : 0u);
   const StageLoader<C> loader{lds, ra, rb, rs, rsb, voff, (uint32_t)(sa_ld * 4), vsb, wave, lane,
                               MX ? (uint32_t)(sb_ld * 4) : 0u};
   // MX: byte offsets of the packed weight-scale word each lane's B fragment
@@ -526,6 +633,12 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
     stage = stage + 1 == C::STAGES ? 0 : stage + 1;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
+
+  if constexpr (SILU) {
+    // the codes go through d, the tile's __restrict__ output (see below)
+    silu_epilogue<C>(lds, acc, gu, reinterpret_cast<uint8_t*>(d), m0, wave, wm, wn, lane);
+    return;
+  }
 
   // Epilogue: lane (li, lg) owns row m0 + wm*TM + 16*mt + li; its values
   // j = 8*s + e (s < NT/2, e < 8) go to column n0 + wn*TN + 32*s + 8*lg + e,
@@ -914,6 +1027,46 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_nt_kernel(
                TileOut{D, nullptr, nullptr, 0}, M, N, K, sa_ld, m0, n0);
 }
 
+// The MoE layer's gate_up product with SiLU-times-up and the activation
+// quantizer in its epilogue.  w1 [G][2I][K] holds the gate rows, then the up
+// rows, and sb1 [G][2I/128][K/128] their block scales.  Tile (tm, j) takes
+// the 128 rows m0 = 128 tm and gate block j with up block j, and writes the
+// quantized activation's columns 128 j .. 128 j + 127.  A padding block (its
+// first row's group outside [0, G)) writes zero codes and scale 1, what the
+// standalone kernel writes for rows of group -1.
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_silu_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ SA, const int32_t* __restrict__ m_indices,
+    const uint8_t* __restrict__ B, const float* __restrict__ SB, uint8_t* __restrict__ Q, float* __restrict__ SQ,
+    int64_t sq_ld, int64_t M, int64_t I, int K, int64_t sa_ld, int num_groups, int tiles_m, int tiles_n) {
+  static_assert(C::BM == 128 && C::BN == 2 * kGroup, "a tile is one gate block and one up block");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  int tm, j;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, j);
+  const int64_t m0 = (int64_t)tm * C::BM, col0 = (int64_t)j * kGroup;
+  const int g = __builtin_amdgcn_readfirstlane(m_indices[m0]);
+  if (g < 0 || g >= num_groups) {  // uniform across the workgroup, before any barrier
+    for (int i = threadIdx.x; i < C::BM * 8; i += C::THREADS)  // 128 rows x 8 runs of 16 bytes
+      *reinterpret_cast<uint4*>(Q + (m0 + i / 8) * I + col0 + (i % 8) * 16) = make_uint4(0, 0, 0, 0);
+    for (int i = threadIdx.x; i < C::BM; i += C::THREADS) SQ[(int64_t)j * sq_ld + m0 + i] = 1.0f;
+    return;
+  }
+  const int64_t KB = K / kGroup;
+  GateUp gu;
+  gu.up_rows = (uint32_t)(I - kGroup);
+  gu.gate_block = j;
+  gu.up_block = I / kGroup + j;
+  gu.sq = SQ;
+  gu.sq_ld = sq_ld;
+  gu.col0 = col0;
+  gu.ld = I;
+  gu.m_indices = m_indices;
+  // Q travels as the tile's __restrict__ output parameter d.
+  gemm_tile<C, false, false, false, true>(lds, A + m0 * K, B + (int64_t)g * 2 * I * K + col0 * K, SA,
+                                          SB + (int64_t)g * (2 * I / kGroup) * KB, reinterpret_cast<uint16_t*>(Q),
+                                          TileOut{nullptr, nullptr, nullptr, 0}, M, 2 * I, K, sa_ld, m0, 0, 0, gu);
+}
+
 // Masked: group g owns rows [g*max_m, g*max_m + max_m) of A and D (a
 // dispatch buffer with a fixed stride per group), of which only the first
 // masked_m[g] are real.  The grid covers every group's max_m rows; a block
@@ -1166,6 +1319,17 @@ hipError_t launch_gemm_mx(GemmKind kind, const void* a, const int32_t* sa, int64
 GemmKind plan_tiles(int64_t m, int64_t n, int64_t k) {
   const GemmPlan p = plan_gemm(m > 16 ? m : 17, n, k);
   return p.kind == kGemmDecode ? kGemmTile128x128 : p.kind;
+}
+
+hipError_t launch_grouped_gemm_silu(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                                    const void* w1, const float* sb1, int32_t num_groups, void* q, float* sq,
+                                    int64_t sq_ld, int64_t m, int64_t inter, int64_t k, hipStream_t stream) {
+  using C = Tile128x256;
+  const int tiles_m = (int)(m / C::BM), tiles_n = (int)(inter / kGroup);
+  hipLaunchKernelGGL(grouped_gemm_silu_kernel<C>, dim3((uint32_t)tiles_m * tiles_n), dim3(C::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(a), sa, m_indices, static_cast<const uint8_t*>(w1), sb1,
+                     static_cast<uint8_t*>(q), sq, sq_ld, m, inter, (int)k, sa_ld, (int)num_groups, tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,

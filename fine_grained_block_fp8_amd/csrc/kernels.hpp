@@ -75,6 +75,13 @@ hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, co
                                const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream);
 
+// The MoE gate_up product fused with SiLU-times-up and the 1x128 activation
+// quantizer: w1 [G][2*inter][k] (gate rows, then up rows), sb1
+// [G][2*inter/128][k/128]; writes q [m][inter] (E4M3) and sq [inter/128][sq_ld].
+hipError_t launch_grouped_gemm_silu(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                                    const void* w1, const float* sb1, int32_t num_groups, void* q, float* sq,
+                                    int64_t sq_ld, int64_t m, int64_t inter, int64_t k, hipStream_t stream);
+
 // Masked grouped product: a 128-row tile chosen from the expected rows per
 // group (a host-side hint; the per-group counts stay on the device).
 GemmKind plan_masked(int32_t num_groups, int64_t max_m, int64_t expected_m, int64_t n);

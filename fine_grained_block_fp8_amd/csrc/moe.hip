@@ -222,8 +222,8 @@ __global__ __launch_bounds__(256) void moe_quantize_kernel(const uint16_t* __res
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const float g0 = bf16_lo(gw[e]), g1 = bf16_hi(gw[e]);
-        const float a0 = g0 / (1.0f + expf(-g0)) * bf16_lo(uw[e]);
-        const float a1 = g1 / (1.0f + expf(-g1)) * bf16_hi(uw[e]);
+        const float a0 = silu_mul_f32(g0, bf16_lo(uw[e]));
+        const float a1 = silu_mul_f32(g1, bf16_hi(uw[e]));
         o[e] = pack_bf16x2(a0, a1);
       }
       v[i] = make_uint4(o[0], o[1], o[2], o[3]);

@@ -256,6 +256,7 @@ int fp8_gemm_nt_mx(const void* a_e4m3, const int32_t* sa, int64_t sa_ld, const v
  *   moe_gather_quantize    x [T][H] -> A1 (E4M3 [m_pad_max][H], scales)
  *   m_grouped_fp8_gemm_nt_contiguous  A1 x W1 [G][2I][H] -> h [m_pad_max][2I]
  *   silu_mul_quantize      h -> A2 = quantize(bf16(silu(h[:, :I]) * h[:, I:]))
+ *     (or both at once: moe_gate_up_silu_quantize  A1 x W1 -> A2, no h)
  *   m_grouped_fp8_gemm_nt_contiguous  A2 x W2 [G][H][I] -> y [m_pad_max][H]
  *   moe_combine            y -> out [T][H]
  * Every buffer is sized by m_pad_max = moe_max_padded_rows(T, topk, G), an
@@ -295,6 +296,23 @@ int moe_gather_quantize(const void* x_bf16, int64_t tokens, int64_t k, const int
  * m_indices entry is negative are zero rows.  h [m][2*inter] bf16. */
 int silu_mul_quantize(const void* h_bf16, int64_t m, int64_t inter, const int32_t* m_indices, void* q_e4m3, float* sa,
                       int64_t sa_ld, void* stream);
+
+/* The two steps above in one kernel (the gate_up product with SiLU-times-up
+ * and the activation quantizer in its epilogue; h never reaches memory):
+ * q [m][inter] and sq [inter/128][sq_ld] are exactly what
+ * m_grouped_fp8_gemm_nt_contiguous(a, sa, sa_ld, m_indices, w1, sb1,
+ * num_groups, h) followed by silu_mul_quantize(h, m, inter, m_indices, q, sq,
+ * sq_ld) write, bit for bit, on every 128-row block whose first row's group
+ * lies in [0, num_groups); a block whose first row is outside that range
+ * (padding) gets zero codes and scale 1, as silu_mul_quantize gives rows of
+ * group -1.  w1 [num_groups][2*inter][k] E4M3 (the gate rows, then the up
+ * rows) with sb1 [num_groups][2*inter/128][k/128] from the block quantizer;
+ * a [m][k], sa [k/128][sa_ld] as for the grouped product.  Requirements:
+ * m % 128 == 0, k % 128 == 0, inter % 128 == 0, (inter + 128) * k < 2^31,
+ * sa_ld and sq_ld multiples of 4 and >= m. */
+int moe_gate_up_silu_quantize(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* m_indices,
+                              const void* w1_e4m3, const float* sb1, int32_t num_groups, void* q_e4m3, float* sq,
+                              int64_t sq_ld, int64_t m, int64_t inter, int64_t k, void* stream);
 
 /* out[t][c] = bf16(sum_{j < topk} topk_weights[t][j] * y[row_of[t][j]][c]),
  * summed in FP32 in slot order; slots whose row lies outside [0, y_rows) are

@@ -47,6 +47,7 @@ def test_library_exports_every_declared_function():
         "moe_combine",
         "quantize_fp8_mx",
         "fp8_gemm_nt_mx",
+        "moe_gate_up_silu_quantize",
     }
     lib = fg.library()
     for n in names:
@@ -301,3 +302,22 @@ def test_describe_gemm_plans():
     assert _lib().fgfp8_describe_gemm(8192, 8192, 8192, buf, 4) == fg.FGFP8_OK
     assert len(buf.value) == 3  # truncated, NUL-terminated
     assert _lib().fgfp8_describe_gemm(8, 8, 100, buf, 4) == fg.FGFP8_EINVAL
+
+
+def test_fused_gate_up_rejects():
+    lib = _lib()
+
+    def call(a=P, m_indices=P, q=P, m=256, inter=256, k=512, groups=4, sa_ld=256, sq_ld=256):
+        return lib.moe_gate_up_silu_quantize(a, P, sa_ld, m_indices, P, P, groups, q, P, sq_ld, m, inter, k, None)
+
+    assert call(m=200) == fg.FGFP8_EINVAL  # m is a multiple of the 128-row blocks
+    assert call(inter=200) == fg.FGFP8_EINVAL
+    assert call(k=100) == fg.FGFP8_EINVAL
+    assert call(groups=0) == fg.FGFP8_EINVAL
+    assert call(sq_ld=6) == fg.FGFP8_EINVAL
+    assert call(sa_ld=128) == fg.FGFP8_EINVAL
+    assert call(inter=(1 << 20), k=(1 << 11)) == fg.FGFP8_EINVAL  # (inter + 128) * k beyond 2^31
+    assert "2^31" in fg.last_error()
+    assert call(m_indices=None) == fg.FGFP8_EINVAL
+    assert call(q=None) == fg.FGFP8_EINVAL
+    assert call(m=0, a=None, m_indices=None, q=None, sa_ld=0, sq_ld=0) == fg.FGFP8_OK  # empty: nothing to do

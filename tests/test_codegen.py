@@ -9,7 +9,9 @@ reads in every K block, which serialises the pipeline (a 1.5x slowdown of the
 grouped MoE product was traced to exactly this).  This test counts the full
 drains per kernel: one after the loop for the three-stage tiles, and one more
 for the two-stage tiles (256x256, 256x192: their wait at the top of each
-chunk is a full drain by design, since their copies are one chunk ahead).  The persistent walk of a
+chunk is a full drain by design, since their copies are one chunk ahead) and
+for the fused gate_up kernel (its epilogue waits once for its m_indices
+loads).  The persistent walk of a
 three-stage tile adds one drain, taken once per tile before its stores leave
 the counter.
 """
@@ -49,11 +51,12 @@ def test_gemm_loops_have_no_full_drain(tmp_path):
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     drains = kernel_drains(asm_path.read_text())
-    gemm = {k: v for k, v in drains.items() if "gemm_nt_kernel" in k or "gemm_nt_persistent_kernel" in k}
-    assert len(gemm) >= 15, sorted(drains)
+    gemm = {k: v for k, v in drains.items()
+            if "gemm_nt_kernel" in k or "gemm_nt_persistent_kernel" in k or "gemm_silu_kernel" in k}
+    assert len(gemm) >= 15 and any("gemm_silu_kernel" in k for k in gemm), sorted(drains)
     for name, n in gemm.items():
         tile = re.search(r"TileILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", name)
         assert tile, name
         two_stage = tile.group(5) == "2"
-        allowed = 2 if two_stage or "persistent" in name else 1
+        allowed = 2 if two_stage or "persistent" in name or "gemm_silu_kernel" in name else 1
         assert n <= allowed, f"{name}: {n} full vmcnt drains"

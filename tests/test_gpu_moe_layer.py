@@ -176,9 +176,21 @@ def run_layer_steps(c, w1, w2):
     fg.m_grouped_fp8_gemm_nt_contiguous(a2, w2, y, m_idx)
     out = fg.moe_combine(y, row_of, wts)
     fused = fg.moe_fp8_layer(x, idx, wts, w1, w2)
+    # the gate_up product fused with SiLU.mul + quantize, on poisoned outputs
+    qf = torch.full((m, c.inter), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sf = torch.full((c.inter // 128, fg.padded_rows(m)), float("nan"), dtype=torch.float32, device="cuda")
+    a2f = fg.moe_gate_up_silu_quantize(a1, w1, m_idx, out=(qf, sf))
     torch.cuda.synchronize()
     return dict(counts=counts, m_indices=m_idx, token_of_row=tok, row_of=row_of, a1=a1, h=h, a2=a2, y=y, out=out,
-                fused=fused)
+                fused=fused, a2f=a2f)
+
+
+def check_fused_gate_up(r, m):
+    """The fused kernel's activation codes and scales equal the two-step
+    path's (grouped product, then silu_mul_quantize) on every row, padding
+    blocks included."""
+    assert torch.equal(r["a2f"][0].view(torch.uint8), r["a2"][0].view(torch.uint8)), "fused act codes differ"
+    assert np.array_equal(bits32(r["a2f"][1][:, :m]), bits32(r["a2"][1][:, :m])), "fused act scales differ"
 
 
 @pytest.mark.parametrize(
@@ -226,6 +238,21 @@ def test_layer_parity(tokens, experts, topk, hidden, inter, seed):
     print(f"layer: h rounded differently {frac_h:.2e}; normwise act {rel_a:.2e}, y {rel_y:.2e}, out {rel:.2e}",
           flush=True)
     assert rel_a <= TOL_LAYER and rel_y <= TOL_LAYER and rel <= TOL_LAYER, (rel_a, rel_y, rel)
+    assert torch.equal(r["fused"].view(torch.int16), r["out"].view(torch.int16))
+    check_fused_gate_up(r, m)
+
+
+@pytest.mark.parametrize("tokens,experts,topk,hidden,inter,seed",
+                         [(64, 3, 2, 128, 128, 3), (500, 12, 4, 1024, 640, 4), (160, 4, 4, 7168, 2048, 5)])
+def test_fused_gate_up_bit_identical(tokens, experts, topk, hidden, inter, seed):
+    """moe_gate_up_silu_quantize against the grouped product followed by
+    silu_mul_quantize, bit for bit, over expert widths of one to sixteen
+    128-column blocks and K of one to 56 chunks."""
+    print(f"fused gate_up T={tokens} G={experts} top{topk} H={hidden} I={inter}", flush=True)
+    c = workloads.moe_layer(seed=200 + seed, experts=experts, tokens=tokens, topk=topk, hidden=hidden, inter=inter)
+    w1, w2 = device_weights(c)
+    r = run_layer_steps(c, w1, w2)
+    check_fused_gate_up(r, r["m_indices"].shape[0])
     assert torch.equal(r["fused"].view(torch.int16), r["out"].view(torch.int16))
 
 
@@ -281,6 +308,7 @@ def test_layer_full_size_sampled():
     counts, m_idx, tok, row_of = want
     m = m_idx.size
     assert torch.equal(r["fused"].view(torch.int16), r["out"].view(torch.int16))
+    check_fused_gate_up(r, m)
     rng = np.random.default_rng(0)
     # gathered operand on sampled rows (real and padding)
     rows = np.unique(np.concatenate([rng.choice(m, 64, replace=False), [0, m - 1]]))
