@@ -115,9 +115,10 @@ __device__ __forceinline__ int b_col_of_row(int rho) {
 // All waves cooperatively copy chunk kb of the A tile, the B tile and the
 // tile's scales into one LDS stage with direct global->LDS buffer loads (1 KB
 // = 8 LDS rows per wave instruction; rows past the matrix edge read as zero).
-// Wave w copies segments w, w + WAVES, ... of A and of B (both counts divide
-// evenly), wave 0 the activation scales and wave 1 the weight scales of the
-// tile's column blocks.  voff[] holds the per-lane byte offsets of those
+// Wave w copies segments w, w + WAVES, ... of A and of B (with 12 waves the
+// 32 A segments of a 256-row tile fall unevenly: waves 8-11 copy one fewer),
+// wave 0 the activation scales and wave 1 the weight scales of the tile's
+// column blocks.  voff[] holds the per-lane byte offsets of those
 // segments for chunk 0; the chunk's column offset is the scalar offset of
 // each load.  Staging the weight scales through LDS keeps scalar memory loads
 // out of the loop: their completion shares a counter with the LDS reads and
