@@ -13,14 +13,14 @@
 // zero accumulator and promotes it with sa * sb in FP32.  The KS partial
 // tiles are summed through LDS in wave order.
 //
-// The fused variant takes the bf16 activation (M <= 4) and quantizes it per
-// 1x128 group into LDS inside every workgroup, with exactly the arithmetic of
-// quantize_fp8_groups, while the weight loads are in flight: one launch per
-// decode linear instead of two (the pages' decode path spent its time in the
-// per-call activation-quantize chain until that was fused into one kernel:
-// AReno pull request, commit notes on fusing the activation quantize).
-// Both variants share the chunk order and the reduction order, so their
-// outputs are bit-identical.
+// The fused variant takes the bf16 activation (M <= 4; decode_xq_kernel below
+// covers M <= 16) and quantizes it per 1x128 group into LDS inside every
+// workgroup, with exactly the arithmetic of quantize_fp8_groups, while the
+// weight loads are in flight: one launch per decode linear instead of two (the
+// pages' decode path spent its time in the per-call activation-quantize chain
+// until that was fused into one kernel: AReno pull request, commit notes on
+// fusing the activation quantize).  All variants share the chunk order and the
+// reduction order, so their outputs are bit-identical.
 
 #include <cstdlib>
 
