@@ -32,10 +32,11 @@ namespace fgfp8 {
 // Chunks of one wave held in registers at a time.  With KS <= 4 (the split
 // of the wide shapes, N = 12288 at K = 4096: 768 slabs, three workgroups per
 // CU) a wave holds 8 chunks and stays within 168 VGPRs, so three waves fit
-// per SIMD; with KS = 8 (N = 4096, K = 12288: two waves per SIMD) it holds 12.
-// The A fragments of the non-fused form take registers too: it holds 8.
+// per SIMD; with KS = 8 (two waves per SIMD) it holds 12.  The A fragments of
+// the non-fused form take registers too: it holds 8.  KS = 16 (N = 4096 at
+// K = 12288: four waves per SIMD, 128 VGPRs) holds 6.
 template <int KS, bool FUSED>
-constexpr int decode_max_chunks() { return FUSED && KS >= 8 ? 12 : 8; }
+constexpr int decode_max_chunks() { return KS >= 16 ? 6 : (FUSED && KS >= 8 ? 12 : 8); }
 constexpr int kFusedMaxRows = (int)kFusedLdsMaxM;
 constexpr int64_t kFusedLdsMaxK = 32768;  // 4 x K bytes of LDS per workgroup
 
@@ -387,12 +388,17 @@ __global__ __launch_bounds__(KS * 64) void decode_xq_kernel(const uint16_t* __re
   }
 }
 
-// K split (1..8 waves per slab): enough waves in flight to cover HBM
-// latency, and at most 12 chunks per wave on the common shapes.
+// K split (1..16 waves per slab): enough waves in flight to cover HBM
+// latency, and at most 12 chunks per wave on the common shapes.  Where eight
+// waves would each take more than 8 chunks (K > 8192 on a narrow N), sixteen
+// waves of 128 VGPRs (four per SIMD) shorten every wave's serial tail:
+// measured at N = 4096, K = 12288, 13.6 -> 12.9 us at M = 1 and 17.3 -> 15.6
+// us at M = 4 (graph replay).
 int decode_split(int64_t n, int64_t k) {
   const int64_t slabs = (n + 15) / 16, kb = k / kGroup;
   int ks = 4;
   while (ks < 8 && (slabs * ks < 2048 || (kb + ks - 1) / ks > 12)) ks *= 2;
+  if (ks == 8 && (kb + 7) / 8 > 8) ks = 16;
   while (ks > 1 && (kb + ks - 1) / ks < 2) ks /= 2;
   return ks;
 }
@@ -432,7 +438,8 @@ static hipError_t launch_decode_t(int ks, const void* a, const float* sa, int64_
     case 1: return launch_decode_ks<1, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
     case 2: return launch_decode_ks<2, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
     case 4: return launch_decode_ks<4, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
-    default: return launch_decode_ks<8, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 8: return launch_decode_ks<8, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    default: return launch_decode_ks<16, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
   }
 }
 
@@ -451,9 +458,10 @@ static hipError_t launch_decode_xq_ks(const void* x, const void* b, const float*
   return hipGetLastError();
 }
 
-// Four chunks per request batch (140 VGPRs: three waves per SIMD).  Measured
-// against 6 and 8 chunks and other splits: four is fastest at both decode
-// shapes.  The split is decode_split's, so the result is bit-identical to the
+// Four chunks per request batch (140 VGPRs: three waves per SIMD; three
+// chunks at KS = 16, whose four waves per SIMD allow 128).  Measured against
+// 6 and 8 chunks and other splits: four is fastest at both decode shapes.
+// The split is decode_split's, so the result is bit-identical to the
 // two-launch path.
 static hipError_t launch_decode_xq(int ks, const void* x, const void* b, const float* sb, void* d, int64_t m,
                                    int64_t n, int64_t k, uint8_t* q_out, float* sa_out, int64_t sa_out_ld,
@@ -462,7 +470,8 @@ static hipError_t launch_decode_xq(int ks, const void* x, const void* b, const f
     case 1: return launch_decode_xq_ks<1, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
     case 2: return launch_decode_xq_ks<2, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
     case 4: return launch_decode_xq_ks<4, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
-    default: return launch_decode_xq_ks<8, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    case 8: return launch_decode_xq_ks<8, 4>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+    default: return launch_decode_xq_ks<16, 3>(x, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
   }
 }
 
