@@ -55,6 +55,12 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 STEPS_ARE = {
     "prefill": "act-quant (1x128) + block-scaled FP8 GEMM (bf16 out) for every linear; weights pre-quantized",
     "prefill_mx": "act-quant (1x32 E8M0) + MXFP8 GEMM (bf16 out) for every linear; weights pre-quantized (1x32 E8M0)",
+    "moe": "act-quant (1x128) of the padded expert layout + M-grouped contiguous block-scaled FP8 GEMM; "
+           "weights pre-quantized",
+    "moe_masked": "act-quant of the whole dispatch buffer (1x128) + masked grouped block-scaled FP8 GEMM; "
+                  "weights pre-quantized",
+    "decode": "act-quant (1x128) + decode-shaped FP8 GEMM (two launches) for M = 1 at both decode shapes; the "
+              "decode object times the fused single-launch form",
     "moe_layer": "route + gather/act-quant + grouped GEMM (gate_up) with SiLU*up/act-quant in its epilogue + "
                  "grouped GEMM (down) + weighted combine; expert weights pre-quantized; value counts routed rows only",
 }
