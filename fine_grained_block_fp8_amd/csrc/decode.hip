@@ -22,6 +22,7 @@
 // fusing the activation quantize).  All variants share the chunk order and the
 // reduction order, so their outputs are bit-identical.
 
+#include <atomic>
 #include <cstdlib>
 
 #include "common.hpp"
@@ -406,10 +407,17 @@ int decode_split(int64_t n, int64_t k) {
 template <int KS, bool FUSED, int XA>
 static hipError_t allow_lds() {
   // The fused variant holds the quantized activation (up to 4 x K bytes) in
-  // LDS; allow dynamic LDS beyond the 64 KB default, once per kernel.
-  static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED, XA>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  return once;
+  // LDS; allow dynamic LDS beyond the 64 KB default, once per kernel and
+  // device (devices beyond the table set it on every call).
+  static std::atomic<bool> done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED, XA>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_relaxed);
+  return e;
 }
 
 template <int KS, bool FUSED, int XA = 3>

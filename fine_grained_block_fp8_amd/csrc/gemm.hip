@@ -20,6 +20,7 @@
 // to match, so that every MFMA tile reads 16 consecutive LDS rows, exactly
 // like the A fragments.
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -1157,15 +1158,15 @@ bool use_persistent(int64_t k) {
 // Workgroups of a persistent launch: one per compute unit (the tiles' LDS
 // allows one per CU), a multiple of 8, at most the padded tile count.
 static int persistent_grid(int t_pad) {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];  // per device; 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kCUs;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  int g = cus[dev] / 8 * 8;
+  int g = n / 8 * 8;
   if (g < 8) g = 8;
   return g < t_pad ? g : t_pad;
 }
