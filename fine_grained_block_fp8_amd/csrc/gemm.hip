@@ -1222,6 +1222,11 @@ GemmKind plan_masked(int32_t num_groups, int64_t max_m, int64_t expected_m, int6
   // Tiles of 128 rows (the smallest that keeps two waves per SIMD); the
   // column width from the expected work: rounds of 256 CUs over
   // num_groups * ceil(expected_m / 128) row tiles, as in plan_gemm.
+  // Tuning and test override: FGFP8_MASKED_TILE=<tile name> (a 128-row tile).
+  if (const char* force = getenv("FGFP8_MASKED_TILE")) {
+    for (const Candidate& c : kCandidates)
+      if (c.bm == 128 && strcmp(force, gemm_kind_name(c.kind)) == 0) return c.kind;
+  }
   const int64_t em = expected_m > 0 && expected_m < max_m ? expected_m : max_m;
   const int64_t row_tiles = (int64_t)num_groups * ((em + 127) / 128);
   GemmKind best = kGemmTile128x256;

@@ -341,8 +341,11 @@ const char* fgfp8_last_error(void);
  * across tiles; same results bit for bit) for k >= 256; by default every
  * tile is a workgroup of its own, which measured faster.  FGFP8_DECODE_XQ
  * (any value) makes fp8_linear_nt's fused path use the register-quantizing
- * kernel at every m <= 16 (tests; same bits).  FGFP8_PRINT_CONFIG=1 prints
- * each call's kernel choice to stderr. */
+ * kernel at every m <= 16 (tests; same bits).  FGFP8_MASKED_TILE, set to
+ * tile128x256_w2x4 or tile128x128_w2x2, forces that tile in
+ * m_grouped_fp8_gemm_nt_masked in place of the one expected_m selects
+ * (tuning and tests; same values).  FGFP8_PRINT_CONFIG=1 prints each call's
+ * kernel choice to stderr. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
 
 #ifdef __cplusplus

@@ -84,6 +84,20 @@ def test_small_masked_cases(counts, max_m, n, k):
     check_masked(c, q, sa, qb, sb, d)
 
 
+@pytest.mark.parametrize("tile", ["tile128x256_w2x4", "tile128x128_w2x2"])
+@pytest.mark.parametrize("counts,max_m,n,k", [([0, 137, 200], 200, 264, 384), ([300, 129, 128, 256], 300, 520, 640)])
+def test_each_masked_tile(tile, counts, max_m, n, k, monkeypatch, capfd):
+    """Both 128-row tiles forced on ragged shapes (N not a multiple of the
+    tile width, counts that end inside a tile)."""
+    monkeypatch.setenv("FGFP8_MASKED_TILE", tile)
+    monkeypatch.setenv("FGFP8_PRINT_CONFIG", "1")
+    c = workloads.small_masked(counts, max_m, n, k, seed=sum(counts) + n + 3)
+    q, sa, qb, sb, d = gpu_masked(c)
+    lines = [ln for ln in capfd.readouterr().err.splitlines() if "m_grouped_fp8_gemm_nt_masked" in ln]
+    assert lines and lines[-1].endswith(tile), lines
+    check_masked(c, q, sa, qb, sb, d)
+
+
 def test_oracle_function_agrees_on_a_small_case():
     """The oracle's masked form itself (folded scale columns) on the GPU's
     quantized bytes."""
