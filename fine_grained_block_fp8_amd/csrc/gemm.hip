@@ -542,14 +542,23 @@ __device__ __forceinline__ void silu_epilogue(uint8_t* lds, v4f_t (&acc)[C::MT][
   }
 }
 
-template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false, bool SILU = false>
+// ROWSKIP (the masked product, whose tiles are often partly filled): a wave
+// whose rows all lie past M skips its fragment reads and MFMAs and only
+// issues its copies, and the waves are laid out row-half-major (wm = wave /
+// WAVES_N), so that waves w and w + 4 -- which share a SIMD -- belong to
+// different row halves and a skipping wave leaves its SIMD to the other.
+// The results are the same bits.
+template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false, bool SILU = false, bool ROWSKIP = false>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
                                           const float* sb_base, uint16_t* __restrict__ d, const TileOut& out,
                                           int64_t M, int64_t N, int K, int64_t sa_ld, int64_t m0, int64_t n0,
                                           int64_t sb_ld = 0, const GateUp& gu = GateUp{}) {
+  // the FP8-output and SiLU epilogues pair waves as wave = wm + WAVES_M * wn
+  static_assert(!ROWSKIP || (!FP8OUT && !UE8M0 && !MX && !SILU), "row skipping is for the bf16 FP32-scale tile");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
+  const int wm = ROWSKIP ? wave / C::WAVES_N : wave % C::WAVES_M;
+  const int wn = ROWSKIP ? wave % C::WAVES_N : wave / C::WAVES_M;
   const int KB = K / kGroup;
   const uint32_t a_rows = (uint32_t)(M - m0 < C::BM ? M - m0 : C::BM);
   const uint32_t b_rows = SILU ? gu.up_rows + (uint32_t)C::BN : (uint32_t)(N - n0 < C::BN ? N - n0 : C::BN);
@@ -628,6 +637,9 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
       int ea[C::MT], eb;
       read_a_ue8m0<C>(lds, aa, sa_addr, sb_addr, stage, af, ea, eb);
       mfma_tiles_ue8m0<C>(lds, ba, stage, load_stage, af, ea, eb, acc, loader, next);
+    } else if (ROWSKIP && (uint32_t)(wm * C::TM) >= a_rows) {  // uniform: this wave's rows are all past M
+#pragma unroll
+      for (int i = 0; i < StageLoader<C>::NSEG; i++) loader.issue(i, load_stage, next);
     } else {
       read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
       mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, load_stage, af, sc, nullptr, acc, loader, next);
@@ -1091,9 +1103,9 @@ __global__ __launch_bounds__(C::THREADS) void masked_gemm_nt_kernel(
   const int64_t base = (int64_t)g * max_m;
   const int64_t m0 = base + (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
   const int64_t KB = K / kGroup, NB = (N + kGroup - 1) / kGroup;
-  gemm_tile<C>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA, SB + (int64_t)g * NB * KB, D,
-               TileOut{D, nullptr, nullptr, 0}, base + rows, N, K,
-               sa_ld, m0, n0);
+  gemm_tile<C, false, false, false, false, true>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA,
+                                                SB + (int64_t)g * NB * KB, D, TileOut{D, nullptr, nullptr, 0},
+                                                base + rows, N, K, sa_ld, m0, n0);
 }
 
 // ------------------------------------------------------------ host side
