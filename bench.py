@@ -57,8 +57,8 @@ STEPS_ARE = {
     "prefill_mx": "act-quant (1x32 E8M0) + MXFP8 GEMM (bf16 out) for every linear; weights pre-quantized (1x32 E8M0)",
     "moe": "act-quant (1x128) of the padded expert layout + M-grouped contiguous block-scaled FP8 GEMM; "
            "weights pre-quantized",
-    "moe_masked": "act-quant of the whole dispatch buffer (1x128) + masked grouped block-scaled FP8 GEMM; "
-                  "weights pre-quantized",
+    "moe_masked": "act-quant (1x128) of the dispatch buffer's real rows (counts read on the device) + masked "
+                  "grouped block-scaled FP8 GEMM; weights pre-quantized",
     "decode": "act-quant (1x128) + decode-shaped FP8 GEMM (two launches) for M = 1 at both decode shapes; the "
               "decode object times the fused single-launch form",
     "moe_layer": "route + gather/act-quant + grouped GEMM (gate_up) with SiLU*up/act-quant in its epilogue + "
@@ -665,7 +665,8 @@ def bench_moe(args, fg, torch, workloads):
 def bench_masked(args, fg, torch, workloads):
     """Decode-time MoE: the masked grouped product over a dispatch buffer
     (32 experts, 1024 tokens routed top-4 by Zipf(1.1), K = 7168, N = 4096);
-    one step = quantize the buffer + the masked product."""
+    one step = quantize the buffer's real rows (the counts stay on the
+    device) + the masked product."""
     c = workloads.moe_masked()
     g, mm, n, k = c.num_groups, c.max_m, c.n, c.k
     x = dev_bf16(c.a.reshape(g * mm, k), torch)
@@ -676,12 +677,12 @@ def bench_masked(args, fg, torch, workloads):
     qb, sb = qb.view(g, n, k), sb.view(g, n // 128, k // 128)
     masked = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
     d = torch.empty((g, mm, n), dtype=torch.bfloat16, device="cuda")
-    qv = q.view(g, mm, k)
+    qv, xv = q.view(g, mm, k), x.view(g, mm, k)
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        fg.quantize_fp8_groups(x, out=(q, sa))
+        fg.quantize_fp8_groups_masked(xv, masked, out=(qv, sa))
         if ev:
             ev[1].record()
         fg.m_grouped_fp8_gemm_nt_masked((qv, sa), (qb, sb), d, masked, c.expected_m)

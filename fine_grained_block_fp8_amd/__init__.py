@@ -48,6 +48,7 @@ _lib.m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp,
 _lib.fp8_linear_nt.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _vp]
 _lib.fp8_gemm_nt_fp8_out.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _fp, _i64, _vp, _i64, _i64, _i64, _vp]
 _lib.m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _i64, _i64, _vp, _i64, _i64, _vp]
+_lib.quantize_fp8_groups_masked.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_groups_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_blocks_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt_ue8m0.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
@@ -69,7 +70,7 @@ for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_gr
               "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
-              "moe_gate_up_silu_quantize"):
+              "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -153,6 +154,33 @@ def quantize_fp8_groups(x: torch.Tensor, sa_ld: int | None = None, out=None, ue8
             raise ValueError("output shapes must be q [M, K] and sa [K/128, sa_ld]")
     fn = _lib.quantize_fp8_groups_ue8m0 if ue8m0 else _lib.quantize_fp8_groups
     _check(fn(_ptr(x), m, k, _ptr(q), _ptr(sa), sa_ld, _stream(x)))
+    return q, sa
+
+
+def quantize_fp8_groups_masked(x: torch.Tensor, masked_m: torch.Tensor, sa_ld: int | None = None, out=None):
+    """quantize_fp8_groups over a dispatch buffer x bf16 [G, max_m, K] whose
+    group g holds masked_m[g] real rows (int32 [G], on the device): only
+    those rows are quantized.  Returns (q float8_e4m3fn [G, max_m, K], sa
+    float32 [K/128, sa_ld]) with group g's row r in scale column g*max_m + r,
+    the operand the masked product takes; rows past a count keep whatever q
+    and sa held."""
+    _need(x, "x", (torch.bfloat16,), 3)
+    _need(masked_m, "masked_m", (torch.int32,), 1)
+    g, max_m, k = x.shape
+    if masked_m.shape[0] != g:
+        raise ValueError("masked_m must be [G]")
+    sa_ld = padded_rows(g * max_m) if sa_ld is None else int(sa_ld)
+    if out is None:
+        q = torch.empty((g, max_m, k), dtype=torch.float8_e4m3fn, device=x.device)
+        sa = torch.empty((k // GROUP if k % GROUP == 0 else 0, sa_ld), dtype=torch.float32, device=x.device)
+    else:
+        q, sa = out
+        _need(q, "q", _FP8, 3)
+        _need(sa, "sa", (torch.float32,), 2)
+        if tuple(q.shape) != (g, max_m, k) or tuple(sa.shape) != (k // GROUP, sa_ld):
+            raise ValueError("output shapes must be q [G, max_m, K] and sa [K/128, sa_ld]")
+    _check(_lib.quantize_fp8_groups_masked(_ptr(x), _ptr(masked_m), g, max_m, k, _ptr(q), _ptr(sa), sa_ld,
+                                           _stream(x)))
     return q, sa
 
 
@@ -583,6 +611,7 @@ __all__ = [
     "padded_rows",
     "quantize_fp8_blocks",
     "quantize_fp8_groups",
+    "quantize_fp8_groups_masked",
     "quantize_fp8_mx",
     "silu_mul_quantize",
 ]

@@ -110,6 +110,25 @@ int quantize_groups_impl(const char* who, bool ue8m0, const void* x_bf16, int64_
   return launched(fgfp8::launch_quantize_groups(x_bf16, m, k, q_e4m3, sa, sa_ld, (hipStream_t)stream, ue8m0), who);
 }
 
+int quantize_fp8_groups_masked(const void* x_bf16, const int32_t* masked_m, int32_t num_groups, int64_t max_m,
+                               int64_t k, void* q_e4m3, float* sa, int64_t sa_ld, void* stream) {
+  const char* who = "quantize_fp8_groups_masked";
+  if (num_groups < 1) return fail(FGFP8_EINVAL, "%s: num_groups=%d must be >= 1", who, (int)num_groups);
+  if (max_m < 0 || max_m % 4 != 0 || (int64_t)num_groups * max_m >= kMaxRows)
+    return fail(FGFP8_EINVAL, "%s: max_m=%lld must be a non-negative multiple of 4 (and num_groups * max_m < 2^31)",
+                who, (long long)max_m);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, (int64_t)num_groups * max_m, k, sa_ld)) return rc;
+  if (max_m == 0) return FGFP8_OK;
+  if (!x_bf16 || !masked_m || !q_e4m3 || !sa) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(masked_m) || !aligned16(q_e4m3) || !aligned16(sa))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_quantize_groups_masked(x_bf16, masked_m, num_groups, max_m, k, q_e4m3, sa, sa_ld,
+                                                       (hipStream_t)stream),
+                  who);
+}
+
 int quantize_blocks_impl(const char* who, bool ue8m0, const void* w_bf16, int64_t n, int64_t k, void* q_e4m3,
                          float* sb, void* stream) {
   if (n < 0 || (n + 127) / 128 > 65535) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);

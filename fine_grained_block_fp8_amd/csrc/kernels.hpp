@@ -11,6 +11,10 @@ hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, 
                                   hipStream_t stream, bool ue8m0 = false);
 // MX recipe: per-1x32 power-of-two scales, E8M0 codes packed four to an
 // int32, s int32 [k/128][s_ld].
+// The groups quantizer over a dispatch buffer [num_groups][max_m][k]: rows
+// r < masked_m[g] (clamped to [0, max_m]) of group g only; max_m % 4 == 0.
+hipError_t launch_quantize_groups_masked(const void* x, const int32_t* masked_m, int32_t num_groups, int64_t max_m,
+                                         int64_t k, void* q, float* sa, int64_t sa_ld, hipStream_t stream);
 hipError_t launch_quantize_mx(const void* x, int64_t m, int64_t k, void* q, int32_t* s, int64_t s_ld,
                               hipStream_t stream);
 hipError_t launch_quantize_blocks(const void* w, int64_t n, int64_t k, void* q, float* sb, hipStream_t stream,

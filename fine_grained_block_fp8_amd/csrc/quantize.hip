@@ -28,18 +28,32 @@ namespace fgfp8 {
 // numbered row-block-major so that neighbouring waves read neighbouring
 // kilobytes of the same rows.  The kernel is bound by HBM: 2 bytes in and 1
 // byte out per element.
+//
+// MASKED (a dispatch buffer of groups of max_m rows, max_m % 4 == 0): only
+// rows r < counts[group] of each group (clamped to [0, max_m]) count; m is
+// then the row of the group's end, so rows past the count are neither read
+// nor written, and a wave whose four rows are all past it exits at once.
 constexpr int kQgWaves = 4;
 
-template <bool UE8M0>
+template <bool UE8M0, bool MASKED = false>
 __global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const uint16_t* __restrict__ x,
                                                                          uint8_t* __restrict__ q,
                                                                          float* __restrict__ sa, int64_t m, int64_t k,
                                                                          int64_t sa_ld, int64_t group_quads,
-                                                                         int64_t total_blocks) {
+                                                                         int64_t total_blocks,
+                                                                         const int32_t* __restrict__ counts = nullptr,
+                                                                         int64_t max_m = 0) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * kQgWaves + (threadIdx.x >> 6);
   if (blk >= total_blocks) return;  // wave-uniform
   const int64_t r0 = (blk / group_quads) * 4;
+  if constexpr (MASKED) {
+    const int64_t grp = r0 / max_m;  // the block's four rows share a group
+    int c = __builtin_amdgcn_readfirstlane(counts[grp]);
+    c = c < 0 ? 0 : (c > max_m ? (int)max_m : c);
+    m = grp * max_m + c;
+    if (r0 >= m) return;  // wave-uniform
+  }
   const int64_t g = (blk % group_quads) * 4 + (lane >> 4);
   const bool g_ok = g < k / kGroup;
   const int64_t col = g * kGroup + (lane & 15) * 8;
@@ -80,6 +94,18 @@ hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, 
   else
     hipLaunchKernelGGL(quantize_groups_kernel<false>, dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
                        static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_groups_masked(const void* x, const int32_t* masked_m, int32_t num_groups, int64_t max_m,
+                                         int64_t k, void* q, float* sa, int64_t sa_ld, hipStream_t stream) {
+  const int64_t m = (int64_t)num_groups * max_m;
+  const int64_t group_quads = (k / kGroup + 3) / 4;
+  const int64_t total = m / 4 * group_quads;
+  const int64_t blocks = (total + kQgWaves - 1) / kQgWaves;
+  hipLaunchKernelGGL((quantize_groups_kernel<false, true>), dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total,
+                     masked_m, max_m);
   return hipGetLastError();
 }
 

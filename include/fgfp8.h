@@ -179,6 +179,26 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
                                  const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
                                  int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* stream);
 
+/* quantize_fp8_groups over the same dispatch buffer, reading the counts on
+ * the device: rows r < masked_m[g] of each group g (clamped to [0, max_m])
+ * are quantized exactly as quantize_fp8_groups quantizes them (codes and
+ * scales bit for bit), the other rows are neither read nor written.  The
+ * masked product never reads those rows, so the pair quantizes only what
+ * the dispatch delivered (deepgemm-rust README, "What's implemented",
+ * m_grouped_fp8_gemm_nt_masked row: a dispatch buffer whose per-group
+ * counts stay on the device, with no host synchronisation).
+ *
+ * x_bf16    [num_groups][max_m][k] bfloat16 (read).
+ * masked_m  [num_groups] int32 on the device.
+ * q_e4m3    [num_groups][max_m][k] E4M3; sa [k/128][sa_ld] float32 with
+ *           group g's row r in column g * max_m + r (the layout the masked
+ *           product takes).  Rows past a group's count keep their contents.
+ * Requirements: num_groups >= 1, max_m >= 0 and max_m % 4 == 0, k > 0 and
+ * k % 128 == 0, sa_ld % 4 == 0, sa_ld >= num_groups * max_m; pointers
+ * 16-byte aligned. */
+int quantize_fp8_groups_masked(const void* x_bf16, const int32_t* masked_m, int32_t num_groups, int64_t max_m,
+                               int64_t k, void* q_e4m3, float* sa, int64_t sa_ld, void* stream);
+
 /* The linear as the pages run it (Linnet "Backend plugins" page,
  * _BlockProduct.execute: round the bf16 input per 1x128 group, then
  * fp8_gemm_nt with the stored weight): D = quantize_groups(x) . B^T.

@@ -48,6 +48,7 @@ def test_library_exports_every_declared_function():
         "quantize_fp8_mx",
         "fp8_gemm_nt_mx",
         "moe_gate_up_silu_quantize",
+        "quantize_fp8_groups_masked",
     }
     lib = fg.library()
     for n in names:
@@ -160,6 +161,22 @@ def test_masked_rejects():
     assert call(k=200) == fg.FGFP8_EINVAL
     assert call(max_m=0, sa_ld=4) == fg.FGFP8_OK
     assert call(n=0) == fg.FGFP8_OK
+
+
+def test_masked_quantizer_rejects():
+    lib = _lib()
+
+    def call(g=4, max_m=64, k=256, sa_ld=256, mm=P, x=P):
+        return lib.quantize_fp8_groups_masked(x, mm, g, max_m, k, P, P, sa_ld, None)
+
+    assert call(max_m=62) == fg.FGFP8_EINVAL
+    assert "quantize_fp8_groups_masked" in fg.last_error() and "multiple of 4" in fg.last_error()
+    assert call(g=0) == fg.FGFP8_EINVAL
+    assert call(sa_ld=252) == fg.FGFP8_EINVAL  # sa_ld < num_groups * max_m
+    assert call(mm=None) == fg.FGFP8_EINVAL
+    assert call(x=P + 4) == fg.FGFP8_EINVAL  # misaligned
+    assert call(k=200) == fg.FGFP8_EINVAL
+    assert call(max_m=0, sa_ld=4, mm=None, x=None) == fg.FGFP8_OK
 
 
 def test_fp8_out_rejects():
@@ -285,6 +302,7 @@ def test_no_device_is_reported_not_crashed():
     assert lib.m_grouped_fp8_gemm_nt_contiguous(P, P, 128, P, P, P, 2, P, 128, 64, 128, None) == fg.FGFP8_ENODEV
     assert lib.fp8_linear_nt(P, 1, 256, P, P, 128, P, None, None, 0, None) == fg.FGFP8_ENODEV
     assert lib.m_grouped_fp8_gemm_nt_masked(P, P, 256, P, P, P, 4, 64, 32, P, 128, 256, None) == fg.FGFP8_ENODEV
+    assert lib.quantize_fp8_groups_masked(P, P, 4, 64, 256, P, P, 256, None) == fg.FGFP8_ENODEV
     assert lib.fp8_gemm_nt_fp8_out(P, P, 8, P, P, P, P, 8, None, 8, 256, 256, None) == fg.FGFP8_ENODEV
     mpm, ws = lib.moe_max_padded_rows(100, 4, 8), lib.moe_route_workspace_bytes(100, 8)
     assert lib.moe_route_contiguous(P, 100, 4, 8, P, P, P, P, mpm, P, ws, None) == fg.FGFP8_ENODEV

@@ -146,3 +146,50 @@ def test_decode_moe_dispatch_buffer_sampled():
     check_masked(c, q, sa, qb, sb, d, groups=[0, 1, 7, 20, 31], rows_per_group=6, cblocks=[0, 13, 31], rng=rng)
     for e in range(c.num_groups):
         assert torch.isfinite(d[e, : int(c.masked_m[e])].float()).all()
+
+
+# ------------------------------------------- quantizing the real rows only
+
+
+@pytest.mark.parametrize(
+    "counts,max_m,k",
+    [([0, 137, 200], 200, 384), ([64, 1, 17, 0, 33], 64, 256), ([-3, 40, 7, 32], 32, 640), ([5], 8, 128),
+     ([896, 0, 3, 894], 896, 7168)],
+)
+def test_masked_quantizer_bit_exact_and_leaves_other_rows(counts, max_m, k):
+    g = len(counts)
+    rng = np.random.default_rng(g + max_m + k)
+    x = workloads.activation_bf16(rng, g * max_m, k, outliers=True)
+    xd = to_dev_bf16(x).view(g, max_m, k)
+    mm = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    sa_ld = fg.padded_rows(g * max_m)
+    q = torch.full((g, max_m, k), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sa = torch.full((k // 128, sa_ld), float("nan"), dtype=torch.float32, device="cuda")
+    fg.quantize_fp8_groups_masked(xd, mm, out=(q, sa))
+    torch.cuda.synchronize()
+    qc, sc = codes(q).reshape(g, max_m, k), sa.cpu().numpy()
+    for e, c in enumerate(np.clip(counts, 0, max_m)):
+        if c:
+            oq, osa = oracle.quantize_groups(x[e * max_m : e * max_m + c])
+            assert np.array_equal(qc[e, :c], oq), f"group {e}"
+            assert np.array_equal(bits32(sc[:, e * max_m : e * max_m + c]), bits32(osa[:, :c])), f"group {e}"
+        assert np.all(qc[e, c:] == 0x7F), f"group {e}: rows past the count written"
+        assert np.all(np.isnan(sc[:, e * max_m + c : (e + 1) * max_m])), f"group {e}: scales past the count written"
+
+
+def test_masked_quantizer_then_product_equals_full_buffer_path():
+    """The decode dispatch buffer: quantizing only the real rows gives the
+    masked product the same bits as quantizing the whole buffer."""
+    c = workloads.moe_masked()
+    q, sa, qb, sb, d = gpu_masked(c)
+    g, mm, n, k = c.num_groups, c.max_m, c.n, c.k
+    masked_dev = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
+    x = to_dev_bf16(c.a.reshape(g * mm, k)).view(g, mm, k)
+    q2, sa2 = fg.quantize_fp8_groups_masked(x, masked_dev)
+    d2 = torch.full((g, mm, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.m_grouped_fp8_gemm_nt_masked((q2, sa2), (qb, sb), d2, masked_dev, c.expected_m)
+    torch.cuda.synchronize()
+    assert torch.equal(d2.view(torch.int16), d.view(torch.int16))
+    for e in (0, 9, 31):
+        r = int(c.masked_m[e])
+        assert torch.equal(q2[e, :r].view(torch.uint8), q.view(g, mm, k)[e, :r].view(torch.uint8))
