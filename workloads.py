@@ -307,3 +307,20 @@ def moe_layer(seed: int = 6, experts: int = 32, tokens: int = 8192, topk: int = 
             w2[g] = gaussian_bf16(r_w2, (hidden, inter), 0.02)
     return MoeLayer(f"moe_layer_{experts}e_top{topk}_{tokens}tok_h{hidden}_i{inter}", tokens, experts, topk, hidden,
                     inter, x, choice, weights, w1, w2)
+
+
+def device_fp8_operand(rows: int, k: int, seed: int, scale_shape, device: str = "cuda"):
+    """Random E4M3 codes [rows][k] drawn on the device (operands too large to
+    draw on the host: the largest K the library accepts), with float32 scales
+    of shape ``scale_shape`` drawn uniformly in [2^-9, 2^-7].  Codes are
+    uniform over the finite codes: magnitude code 0..0x7E with a random sign
+    bit (never 0x7F / 0xFF, the NaNs).  torch's seeded device generator; the
+    oracle sees the same bytes by copying the sampled rows back."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    q = torch.randint(0, 127, (rows, k), dtype=torch.uint8, device=device, generator=gen)
+    q |= torch.randint(0, 2, (rows, k), dtype=torch.uint8, device=device, generator=gen) << 7
+    s = torch.rand(scale_shape, dtype=torch.float32, device=device, generator=gen) * (2.0**-7 - 2.0**-9) + 2.0**-9
+    return q.view(torch.float8_e4m3fn), s
