@@ -777,7 +777,7 @@ def bench_moe_layer(args, fg, torch, workloads):
         mark()
         _counts, m_idx, tok, row_of = fg.moe_route_contiguous(idx, g, out=route)
         mark()
-        fg.moe_gather_quantize(x, tok, out=a1)
+        fg.moe_gather_quantize_tokens(x, row_of, tok, out=a1)
         mark()
         if fused:
             fg.moe_gate_up_silu_quantize(a1, (q1, s1), m_idx, out=a2)

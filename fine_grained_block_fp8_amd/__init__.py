@@ -61,6 +61,7 @@ _lib.moe_route_workspace_bytes.restype = ctypes.c_int64
 _lib.moe_route_contiguous.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]
 _lib.moe_gather_quantize.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _fp, _i64, _vp]
 _lib.silu_mul_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp, _fp, _i64, _vp]
+_lib.moe_gather_quantize_tokens.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _i64, _vp, _fp, _i64, _vp]
 _lib.moe_combine.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _i32, _vp, _vp]
 _lib.moe_gate_up_silu_quantize.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _vp, _fp, _i64, _i64, _i64, _i64, _vp]
 _lib.fgfp8_last_error.argtypes = []
@@ -70,7 +71,8 @@ for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_gr
               "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
-              "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked"):
+              "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked",
+              "moe_gather_quantize_tokens"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -473,6 +475,32 @@ def moe_gather_quantize(x: torch.Tensor, token_of_row: torch.Tensor, out=None):
     return q, sa
 
 
+def moe_gather_quantize_tokens(x: torch.Tensor, row_of: torch.Tensor, token_of_row: torch.Tensor, out=None):
+    """moe_gather_quantize for the routing layout (row_of int32 [T, topk] and
+    token_of_row int32 [m_pad_max] as moe_route_contiguous writes them): each
+    token's row is read and quantized once and written to its rows; rows no
+    token maps to get zero codes and scale 1.  Same bytes as
+    moe_gather_quantize."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(row_of, "row_of", (torch.int32,), 2)
+    _need(token_of_row, "token_of_row", (torch.int32,), 1)
+    tokens, k = x.shape
+    if row_of.shape[0] != tokens:
+        raise ValueError("row_of must be [T, topk]")
+    m = token_of_row.shape[0]
+    if out is None:
+        out = (torch.empty((m, k), dtype=torch.float8_e4m3fn, device=x.device),
+               torch.empty((k // GROUP, padded_rows(m)), dtype=torch.float32, device=x.device))
+    q, sa = out
+    _need(q, "q", _FP8, 2)
+    _need(sa, "sa", (torch.float32,), 2)
+    if tuple(q.shape) != (m, k):
+        raise ValueError("q must be [m_pad_max, K]")
+    _check(_lib.moe_gather_quantize_tokens(_ptr(x), tokens, k, row_of.shape[1], _ptr(row_of), _ptr(token_of_row), m,
+                                           _ptr(q), _ptr(sa), sa.shape[1], _stream(x)))
+    return q, sa
+
+
 def silu_mul_quantize(h: torch.Tensor, m_indices: torch.Tensor, out=None):
     """act = bf16(silu(h[:, :I]) * h[:, I:]) quantized per 1x128 group (rows
     with m_indices < 0 give zeros).  h: bf16 [M, 2I].  Returns (q [M, I], sa
@@ -567,7 +595,7 @@ def moe_fp8_layer(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.T
         raise ValueError("w1 must be [G, 2I, H] and w2 [G, H, I]")
     counts, m_indices, token_of_row, row_of = moe_route_contiguous(topk_idx, g)
     m = m_indices.shape[0]
-    a1 = moe_gather_quantize(x, token_of_row)
+    a1 = moe_gather_quantize_tokens(x, row_of, token_of_row)
     if fused:
         a2 = moe_gate_up_silu_quantize(a1, (q1, s1), m_indices)
     else:
@@ -605,6 +633,7 @@ __all__ = [
     "moe_fp8_layer",
     "moe_gate_up_silu_quantize",
     "moe_gather_quantize",
+    "moe_gather_quantize_tokens",
     "moe_max_padded_rows",
     "moe_route_contiguous",
     "moe_route_workspace_bytes",

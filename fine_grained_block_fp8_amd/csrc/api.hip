@@ -359,6 +359,26 @@ int moe_gather_quantize(const void* x_bf16, int64_t tokens, int64_t k, const int
                   who);
 }
 
+int moe_gather_quantize_tokens(const void* x_bf16, int64_t tokens, int64_t k, int32_t topk, const int32_t* row_of,
+                               const int32_t* token_of_row, int64_t m_pad_max, void* q_e4m3, float* sa, int64_t sa_ld,
+                               void* stream) {
+  const char* who = "moe_gather_quantize_tokens";
+  if (m_pad_max < 0 || m_pad_max >= kMaxRows) return fail(FGFP8_EINVAL, "%s: m_pad_max out of range", who);
+  if (tokens < 0 || tokens >= kMaxRows / 8) return fail(FGFP8_EINVAL, "%s: tokens out of range", who);
+  if (topk < 1 || topk > 8) return fail(FGFP8_EINVAL, "%s: topk=%d must be in [1, 8]", who, (int)topk);
+  if (int rc = check_k(who, k)) return rc;
+  if (int rc = check_sa(who, m_pad_max, k, sa_ld)) return rc;
+  if (m_pad_max == 0) return FGFP8_OK;
+  if ((tokens > 0 && (!x_bf16 || !row_of)) || !token_of_row || !q_e4m3 || !sa)
+    return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(sa))
+    return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_moe_gather_quantize_tokens(x_bf16, tokens, k, topk, row_of, token_of_row, m_pad_max,
+                                                           q_e4m3, sa, sa_ld, (hipStream_t)stream),
+                  who);
+}
+
 int silu_mul_quantize(const void* h_bf16, int64_t m, int64_t inter, const int32_t* m_indices, void* q_e4m3, float* sa,
                       int64_t sa_ld, void* stream) {
   const char* who = "silu_mul_quantize";

@@ -275,6 +275,94 @@ hipError_t launch_moe_silu_mul_quantize(const void* h, int64_t m, int64_t inter,
   return launch_moe_quantize(true, h, m, m_indices, m, inter, 2 * inter, q, sa, sa_ld, stream);
 }
 
+// ------------------------------------------- gather + quantize, by token
+// The same rows as the gather above when row_of and token_of_row are the
+// inverse maps the routing writes, but each token's row of x is read and
+// quantized once: a wave quantizes 4 tokens x 4 groups (as
+// quantize_groups_kernel) and writes every token's codes and scales to each
+// row row_of[t][j] it was routed to.  A row's codes depend on its values
+// only, so every copy holds the bytes the row-major gather writes.  The
+// rows no token maps to (padding, and the rows past the real count) are
+// written by moe_zero_rows_kernel below.
+__global__ __launch_bounds__(256) void moe_gather_tokens_kernel(const uint16_t* __restrict__ x, int64_t tokens,
+                                                                int64_t k, const int32_t* __restrict__ row_of,
+                                                                int topk, int64_t m_pad_max, uint8_t* __restrict__ q,
+                                                                float* __restrict__ sa, int64_t sa_ld,
+                                                                int64_t group_quads, int64_t total_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= total_blocks) return;  // wave-uniform
+  const int64_t t0 = (blk / group_quads) * 4;
+  const int64_t g = (blk % group_quads) * 4 + (lane >> 4);
+  const bool g_ok = g < k / kGroup;
+  const int64_t col = g * kGroup + (lane & 15) * 8;
+  // the rows of the wave's (up to) 4 tokens: lane i * topk + j holds row_of[t0 + i][j]
+  const int64_t nidx = (tokens - t0 < 4 ? tokens - t0 : 4) * topk;
+  const int32_t my_row = lane < nidx ? row_of[t0 * topk + lane] : -1;
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    v[i] = (g_ok && t0 + i < tokens) ? *reinterpret_cast<const uint4*>(x + (t0 + i) * k + col) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    if (t0 + i >= tokens) break;  // uniform
+    const uint32_t amax_bits = row16_max_u32(absmax8_bits(v[i]));
+    const float s = group_scale(__uint_as_float(amax_bits));
+    const double r = 1.0 / (double)s;
+    const uint2 o = quantize8(v[i], r);
+    for (int j = 0; j < topk; j++) {
+      const int32_t row = __builtin_amdgcn_readlane(my_row, i * topk + j);
+      if (row < 0 || row >= m_pad_max) continue;  // a dropped slot; uniform
+      if (g_ok) {
+        *reinterpret_cast<uint2*>(q + (int64_t)row * k + col) = o;
+        if ((lane & 15) == 0) sa[g * sa_ld + row] = s;
+      }
+    }
+  }
+}
+
+// Rows r < m_pad_max whose token_of_row entry lies outside [0, tokens): a
+// zero row quantized -- zero codes, scale 1 (the all-zero group's scale).
+// A wave takes 64 rows, finds its zero rows with one ballot and writes each
+// with all lanes (16 bytes per lane per store).
+__global__ __launch_bounds__(256) void moe_zero_rows_kernel(const int32_t* __restrict__ token_of_row, int64_t tokens,
+                                                            int64_t k, int64_t m_pad_max, uint8_t* __restrict__ q,
+                                                            float* __restrict__ sa, int64_t sa_ld) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const int64_t r = r0 + lane;
+  bool zero = false;
+  if (r < m_pad_max) {
+    const int32_t t = token_of_row[r];
+    zero = t < 0 || t >= tokens;
+  }
+  uint64_t mask = __ballot(zero);
+  const int64_t kb = k / kGroup;
+  while (mask != 0) {  // uniform
+    const int b = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const int64_t row = r0 + b;
+    uint4* dst = reinterpret_cast<uint4*>(q + row * k);
+    for (int64_t i = lane; i < k / 16; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
+    for (int64_t c = lane; c < kb; c += 64) sa[c * sa_ld + row] = 1.0f;
+  }
+}
+
+hipError_t launch_moe_gather_quantize_tokens(const void* x, int64_t tokens, int64_t k, int topk,
+                                             const int32_t* row_of, const int32_t* token_of_row, int64_t m_pad_max,
+                                             void* q, float* sa, int64_t sa_ld, hipStream_t stream) {
+  if (m_pad_max > 0)
+    hipLaunchKernelGGL(moe_zero_rows_kernel, dim3((uint32_t)((m_pad_max + 255) / 256)), dim3(256), 0, stream,
+                       token_of_row, tokens, k, m_pad_max, static_cast<uint8_t*>(q), sa, sa_ld);
+  const int64_t group_quads = (k / kGroup + 3) / 4;
+  const int64_t total = (tokens + 3) / 4 * group_quads;
+  if (total > 0)
+    hipLaunchKernelGGL(moe_gather_tokens_kernel, dim3((uint32_t)((total + 3) / 4)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), tokens, k, row_of, topk, m_pad_max,
+                       static_cast<uint8_t*>(q), sa, sa_ld, group_quads, total);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- combine
 // One workgroup per token; each thread sums 8 columns over the token's slots
 // in order (FP32), then rounds to bf16.  Slots whose row lies outside

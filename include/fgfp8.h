@@ -310,6 +310,21 @@ int moe_route_contiguous(const int32_t* topk_idx, int64_t tokens, int32_t topk, 
 int moe_gather_quantize(const void* x_bf16, int64_t tokens, int64_t k, const int32_t* token_of_row, int64_t m_pad_max,
                         void* q_e4m3, float* sa, int64_t sa_ld, void* stream);
 
+/* moe_gather_quantize for the layout moe_route_contiguous writes, by token:
+ * each token's row of x is read and quantized once and its codes and scales
+ * are written to every row row_of[t][j] (j < topk) it was routed to; rows
+ * r < m_pad_max whose token_of_row entry lies outside [0, tokens) get zero
+ * codes and scale 1 (a zero row, quantized).  With row_of and token_of_row
+ * the inverse maps the routing writes, q and sa equal what
+ * moe_gather_quantize writes, byte for byte: a row's codes depend on its
+ * values only.  It reads x once instead of once per routed slot.
+ * x [tokens][k] bf16; row_of [tokens][topk] int32; token_of_row [m_pad_max]
+ * int32; q [m_pad_max][k] E4M3; sa [k/128][sa_ld], sa_ld >= m_pad_max,
+ * sa_ld % 4 == 0.  Requirements: 1 <= topk <= 8, k % 128 == 0. */
+int moe_gather_quantize_tokens(const void* x_bf16, int64_t tokens, int64_t k, int32_t topk, const int32_t* row_of,
+                               const int32_t* token_of_row, int64_t m_pad_max, void* q_e4m3, float* sa, int64_t sa_ld,
+                               void* stream);
+
 /* act[r][c] = bf16(silu(h[r][c]) * h[r][inter + c]) in FP32 (silu(g) =
  * g / (1 + exp(-g)), the gate half first), quantized per 1x128 group as
  * quantize_fp8_groups: q [m][inter], sa [inter/128][sa_ld].  Rows whose

@@ -49,6 +49,7 @@ def test_library_exports_every_declared_function():
         "fp8_gemm_nt_mx",
         "moe_gate_up_silu_quantize",
         "quantize_fp8_groups_masked",
+        "moe_gather_quantize_tokens",
     }
     lib = fg.library()
     for n in names:
@@ -239,6 +240,14 @@ def test_moe_calls_reject():
     assert lib.moe_gather_quantize(P, 10, 128, None, 256, P, P, 256, None) == fg.FGFP8_EINVAL
     assert lib.moe_gather_quantize(P, -1, 128, P, 256, P, P, 256, None) == fg.FGFP8_EINVAL
     assert lib.moe_gather_quantize(P, 10, 128, P, 0, P, P, 4, None) == fg.FGFP8_OK
+    tok = lib.moe_gather_quantize_tokens
+    assert tok(P, 10, 128, 0, P, P, 256, P, P, 256, None) == fg.FGFP8_EINVAL  # topk
+    assert tok(P, 10, 128, 9, P, P, 256, P, P, 256, None) == fg.FGFP8_EINVAL
+    assert tok(P, 10, 100, 4, P, P, 256, P, P, 256, None) == fg.FGFP8_EINVAL  # k
+    assert tok(P, 10, 128, 4, P, P, 256, P, P, 252, None) == fg.FGFP8_EINVAL  # sa_ld
+    assert tok(P, 10, 128, 4, None, P, 256, P, P, 256, None) == fg.FGFP8_EINVAL  # row_of
+    assert tok(P, 10, 128, 4, P, None, 256, P, P, 256, None) == fg.FGFP8_EINVAL  # token_of_row
+    assert tok(P, 10, 128, 4, P, P, 0, P, P, 4, None) == fg.FGFP8_OK
     assert lib.silu_mul_quantize(P, 256, 64, P, P, P, 256, None) == fg.FGFP8_EINVAL
     assert lib.silu_mul_quantize(P + 2, 256, 128, P, P, P, 256, None) == fg.FGFP8_EINVAL
     assert lib.silu_mul_quantize(P, 0, 128, P, P, P, 4, None) == fg.FGFP8_OK
@@ -307,6 +316,7 @@ def test_no_device_is_reported_not_crashed():
     mpm, ws = lib.moe_max_padded_rows(100, 4, 8), lib.moe_route_workspace_bytes(100, 8)
     assert lib.moe_route_contiguous(P, 100, 4, 8, P, P, P, P, mpm, P, ws, None) == fg.FGFP8_ENODEV
     assert lib.moe_gather_quantize(P, 10, 128, P, 256, P, P, 256, None) == fg.FGFP8_ENODEV
+    assert lib.moe_gather_quantize_tokens(P, 10, 128, 4, P, P, 256, P, P, 256, None) == fg.FGFP8_ENODEV
     assert lib.silu_mul_quantize(P, 256, 128, P, P, P, 256, None) == fg.FGFP8_ENODEV
     assert lib.moe_combine(P, 64, 128, P, P, 8, 4, P, None) == fg.FGFP8_ENODEV
 

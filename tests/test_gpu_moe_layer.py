@@ -90,6 +90,34 @@ def test_gather_quantize_bit_exact(tokens, hidden, seed):
     assert np.array_equal(bits32(sa[:, :m]), bits32(osa[:, :m]))
 
 
+@pytest.mark.parametrize(
+    "tokens,hidden,experts,topk,seed",
+    [(0, 256, 4, 2, 0), (1, 128, 1, 1, 1), (100, 256, 8, 3, 2), (333, 640, 16, 8, 3), (257, 7168, 32, 4, 4)],
+)
+def test_gather_by_token_equals_gather_by_row(tokens, hidden, experts, topk, seed):
+    """The token-major gather (each token read and quantized once, written to
+    its rows; the other rows zero codes and scale 1) writes the bytes of the
+    row-major gather and of the oracle over every row of the buffer, with
+    dropped slots (expert ids outside the range) in the routing."""
+    rng = np.random.default_rng(seed)
+    x = workloads.activation_bf16(rng, max(tokens, 1), hidden, outliers=True)[:tokens]
+    idx = rng.integers(-1, experts + 1, size=(tokens, topk)).astype(np.int32)
+    print(f"gather by token: tokens={tokens} hidden={hidden} experts={experts} topk={topk}", flush=True)
+    _, _, tok, row_of = fg.moe_route_contiguous(dev_i32(idx), experts)
+    xd = to_dev_bf16(x)
+    m = tok.shape[0]
+    poison = lambda: (torch.full((m, hidden), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn),
+                      torch.full((hidden // 128, fg.padded_rows(m)), float("nan"), dtype=torch.float32, device="cuda"))
+    q1, s1 = fg.moe_gather_quantize(xd, tok, out=poison())
+    q2, s2 = fg.moe_gather_quantize_tokens(xd, row_of, tok, out=poison())
+    torch.cuda.synchronize()
+    assert torch.equal(q2.view(torch.uint8), q1.view(torch.uint8))
+    assert np.array_equal(bits32(s2[:, :m]), bits32(s1[:, :m]))
+    oq, osa = moe.gather_quantize(x, host(tok))
+    assert np.array_equal(codes(q2), oq)
+    assert np.array_equal(bits32(s2[:, :m]), bits32(osa[:, :m]))
+
+
 # ------------------------------------------------------------------ silu_mul
 def ordinal(c):
     c = c.astype(np.int32)
