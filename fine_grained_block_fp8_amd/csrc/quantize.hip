@@ -35,26 +35,12 @@ namespace fgfp8 {
 // nor written, and a wave whose four rows are all past it exits at once.
 constexpr int kQgWaves = 4;
 
-template <bool UE8M0, bool MASKED = false>
-__global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const uint16_t* __restrict__ x,
-                                                                         uint8_t* __restrict__ q,
-                                                                         float* __restrict__ sa, int64_t m, int64_t k,
-                                                                         int64_t sa_ld, int64_t group_quads,
-                                                                         int64_t total_blocks,
-                                                                         const int32_t* __restrict__ counts = nullptr,
-                                                                         int64_t max_m = 0) {
-  const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * kQgWaves + (threadIdx.x >> 6);
-  if (blk >= total_blocks) return;  // wave-uniform
-  const int64_t r0 = (blk / group_quads) * 4;
-  if constexpr (MASKED) {
-    const int64_t grp = r0 / max_m;  // the block's four rows share a group
-    int c = __builtin_amdgcn_readfirstlane(counts[grp]);
-    c = c < 0 ? 0 : (c > max_m ? (int)max_m : c);
-    m = grp * max_m + c;
-    if (r0 >= m) return;  // wave-uniform
-  }
-  const int64_t g = (blk % group_quads) * 4 + (lane >> 4);
+// Rows r0 .. r0 + 3 (those < m) and groups 4 gq .. 4 gq + 3 of x, one wave.
+template <bool UE8M0>
+__device__ __forceinline__ void quantize_block4(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+                                                float* __restrict__ sa, int64_t m, int64_t k, int64_t sa_ld,
+                                                int64_t r0, int64_t gq, int lane) {
+  const int64_t g = gq * 4 + (lane >> 4);
   const bool g_ok = g < k / kGroup;
   const int64_t col = g * kGroup + (lane & 15) * 8;
   uint4 v[4];
@@ -82,6 +68,28 @@ __global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const ui
   }
 }
 
+template <bool UE8M0, bool MASKED = false>
+__global__ __launch_bounds__(kQgWaves * 64) void quantize_groups_kernel(const uint16_t* __restrict__ x,
+                                                                         uint8_t* __restrict__ q,
+                                                                         float* __restrict__ sa, int64_t m, int64_t k,
+                                                                         int64_t sa_ld, int64_t group_quads,
+                                                                         int64_t total_blocks,
+                                                                         const int32_t* __restrict__ counts = nullptr,
+                                                                         int64_t max_m = 0) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * kQgWaves + (threadIdx.x >> 6);
+  if (blk >= total_blocks) return;  // wave-uniform
+  const int64_t r0 = (blk / group_quads) * 4;
+  if constexpr (MASKED) {
+    const int64_t grp = r0 / max_m;  // the block's four rows share a group
+    int c = __builtin_amdgcn_readfirstlane(counts[grp]);
+    c = c < 0 ? 0 : (c > max_m ? (int)max_m : c);
+    m = grp * max_m + c;
+    if (r0 >= m) return;  // wave-uniform
+  }
+  quantize_block4<UE8M0>(x, q, sa, m, k, sa_ld, r0, blk % group_quads, lane);
+}
+
 hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, float* sa, int64_t sa_ld,
                                   hipStream_t stream, bool ue8m0) {
   const int64_t row_blocks = (m + 3) / 4;
@@ -97,15 +105,82 @@ hipError_t launch_quantize_groups(const void* x, int64_t m, int64_t k, void* q, 
   return hipGetLastError();
 }
 
+// The masked form over a bounded grid: every workgroup forms the exclusive
+// prefix sums of the groups' live 4-row blocks (ceil(count / 4)) in LDS, and
+// its waves stride over the live (row block, group quad) tasks only, finding
+// a task's group by binary search.  Launching one wave per possible task
+// instead costs a count load per wave even where every row is past the
+// count (most of a dispatch buffer).  Up to kFlatMaxGroups groups.
+constexpr int kFlatMaxGroups = 1024;
+
+__global__ __launch_bounds__(256) void quantize_groups_masked_flat_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ sa, const int32_t* __restrict__ counts,
+    int num_groups, int64_t max_m, int64_t k, int64_t sa_ld, int64_t group_quads) {
+  __shared__ int64_t pre[kFlatMaxGroups + 1];
+  __shared__ int64_t wave_sum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // thread t owns groups 4t .. 4t + 3
+  int64_t mine[4], local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int g = 4 * tid + i;
+    int c = g < num_groups ? counts[g] : 0;
+    c = c < 0 ? 0 : (c > max_m ? (int)max_m : c);
+    mine[i] = (c + 3) / 4;
+    local += mine[i];
+  }
+  int64_t incl = local;  // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int64_t base = 0;
+  for (int w = 0; w < wave; w++) base += wave_sum[w];
+  int64_t run = base + incl - local;  // exclusive prefix of group 4t
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int g = 4 * tid + i;
+    if (g < num_groups) pre[g] = run;
+    run += mine[i];
+  }
+  if (tid == 255) pre[num_groups] = run;  // the total (groups past num_groups count zero)
+  __syncthreads();
+  const int64_t tasks = pre[num_groups] * group_quads;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < tasks; t += stride) {  // uniform per wave
+    const int64_t rb = t / group_quads, gq = t % group_quads;
+    int lo = 0, hi = num_groups - 1;  // the last group with pre[g] <= rb
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= rb) lo = mid;
+      else hi = mid - 1;
+    }
+    int c = counts[lo];
+    c = c < 0 ? 0 : (c > max_m ? (int)max_m : c);
+    const int64_t r0 = lo * max_m + 4 * (rb - pre[lo]);
+    quantize_block4<false>(x, q, sa, lo * max_m + c, k, sa_ld, r0, gq, lane);
+  }
+}
+
 hipError_t launch_quantize_groups_masked(const void* x, const int32_t* masked_m, int32_t num_groups, int64_t max_m,
                                          int64_t k, void* q, float* sa, int64_t sa_ld, hipStream_t stream) {
   const int64_t m = (int64_t)num_groups * max_m;
   const int64_t group_quads = (k / kGroup + 3) / 4;
   const int64_t total = m / 4 * group_quads;
   const int64_t blocks = (total + kQgWaves - 1) / kQgWaves;
-  hipLaunchKernelGGL((quantize_groups_kernel<false, true>), dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total,
-                     masked_m, max_m);
+  if (num_groups <= kFlatMaxGroups) {
+    const int64_t grid = blocks < 2048 ? blocks : 2048;
+    hipLaunchKernelGGL(quantize_groups_masked_flat_kernel, dim3((uint32_t)grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, masked_m, (int)num_groups,
+                       max_m, k, sa_ld, group_quads);
+  } else {
+    hipLaunchKernelGGL((quantize_groups_kernel<false, true>), dim3((uint32_t)blocks), dim3(kQgWaves * 64), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), sa, m, k, sa_ld, group_quads, total,
+                       masked_m, max_m);
+  }
   return hipGetLastError();
 }
 

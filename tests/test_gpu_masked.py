@@ -154,7 +154,10 @@ def test_decode_moe_dispatch_buffer_sampled():
 @pytest.mark.parametrize(
     "counts,max_m,k",
     [([0, 137, 200], 200, 384), ([64, 1, 17, 0, 33], 64, 256), ([-3, 40, 7, 32], 32, 640), ([5], 8, 128),
-     ([896, 0, 3, 894], 896, 7168)],
+     ([896, 0, 3, 894], 896, 7168),
+     # 1024 groups: the most the prefix-sum form takes; 1100: the one-wave-per-block form
+     (np.random.default_rng(6).integers(-2, 7, 1024).tolist(), 4, 128),
+     (np.random.default_rng(7).integers(-2, 11, 1100).tolist(), 8, 256)],
 )
 def test_masked_quantizer_bit_exact_and_leaves_other_rows(counts, max_m, k):
     g = len(counts)
