@@ -165,7 +165,8 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
  *            g * max_m + r.
  * sa         [k/128][sa_ld] float32: the MN-major scales of the buffer viewed
  *            as one (num_groups * max_m) x k matrix, i.e. the group folded
- *            into the scale column (what quantize_fp8_groups writes for it).
+ *            into the scale column (what quantize_fp8_groups writes for it,
+ *            and quantize_fp8_groups_masked for its real rows only).
  * masked_m   [num_groups] int32: rows of each group to compute (values
  *            outside [0, max_m] are clamped to it).
  * b_e4m3     [num_groups][n][k] E4M3; sb [num_groups][ceil(n/128)][k/128].
