@@ -50,14 +50,20 @@ __global__ __launch_bounds__(256) void moe_offsets_kernel(int32_t* __restrict__ 
                                                           int experts, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ starts) {
   // every thread owns experts e = threadIdx.x + 256 i; the exclusive scan of
-  // the padded totals runs over the experts in order in LDS
+  // the padded totals runs over the experts in order in LDS.  The block
+  // counts are read kBatch blocks at a time (independent loads), first to
+  // sum them, then again to write each block's offset, so a thread waits
+  // for memory once per batch rather than once per block.
+  constexpr int kBatch = 8;
   extern __shared__ int32_t padded[];
   for (int e = threadIdx.x; e < experts; e += blockDim.x) {
     int32_t run = 0;
-    for (int b = 0; b < nblocks; b++) {
-      const int32_t c = block_counts[(int64_t)b * experts + e];
-      block_counts[(int64_t)b * experts + e] = run;  // exclusive prefix within the expert
-      run += c;
+    for (int b0 = 0; b0 < nblocks; b0 += kBatch) {
+      int32_t c[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) c[i] = b0 + i < nblocks ? block_counts[(int64_t)(b0 + i) * experts + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) run += c[i];
     }
     counts[e] = run;
     padded[e] = (run + 127) / 128 * 128;
@@ -72,9 +78,21 @@ __global__ __launch_bounds__(256) void moe_offsets_kernel(int32_t* __restrict__ 
     }
   }
   __syncthreads();
+  // each block's first row for expert e: the expert's start plus the
+  // expert's pairs in the blocks before it
   for (int e = threadIdx.x; e < experts; e += blockDim.x) {
-    starts[e] = padded[e];
-    for (int b = 0; b < nblocks; b++) block_counts[(int64_t)b * experts + e] += padded[e];
+    int32_t run = padded[e];
+    starts[e] = run;
+    for (int b0 = 0; b0 < nblocks; b0 += kBatch) {
+      int32_t c[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) c[i] = b0 + i < nblocks ? block_counts[(int64_t)(b0 + i) * experts + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) {
+        if (b0 + i < nblocks) block_counts[(int64_t)(b0 + i) * experts + e] = run;
+        run += c[i];
+      }
+    }
   }
 }
 
