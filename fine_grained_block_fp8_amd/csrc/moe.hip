@@ -69,9 +69,28 @@ __global__ __launch_bounds__(256) void moe_offsets_kernel(int32_t* __restrict__ 
     padded[e] = (run + 127) / 128 * 128;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t off = 0;
-    for (int e = 0; e < experts; e++) {
+  {
+    // exclusive scan of padded[] over the experts: thread t takes the
+    // contiguous run e0 .. e1 - 1 (at most 8 experts for 2048), a wave
+    // shuffle scan and the four wave totals give the run's first offset
+    __shared__ int32_t wave_total[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int per = (experts + 255) / 256;
+    const int e0 = threadIdx.x * per < experts ? threadIdx.x * per : experts;
+    const int e1 = e0 + per < experts ? e0 + per : experts;
+    int32_t local = 0;
+    for (int e = e0; e < e1; e++) local += padded[e];
+    int32_t incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) wave_total[wave] = incl;
+    __syncthreads();
+    int32_t off = incl - local;
+    for (int w = 0; w < wave; w++) off += wave_total[w];
+    for (int e = e0; e < e1; e++) {
       const int32_t p = padded[e];
       padded[e] = off;
       off += p;
