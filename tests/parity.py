@@ -19,6 +19,8 @@ import numpy as np
 import torch
 
 import oracle
+from tests.oracle_workers import error_stats, magnitude_sum  # noqa: F401  (re-exported)
+from tests import oracle_workers
 
 TOL_NORMWISE = 2e-3
 
@@ -44,31 +46,19 @@ def d_to_f64(d: torch.Tensor) -> np.ndarray:
     return d.float().cpu().numpy().astype(np.float64)
 
 
-def magnitude_sum(qa, sa, qb, sb) -> np.ndarray:
-    """S[m, n] = sum_k |dequant(a)[m, k] * dequant(b)[n, k]| in FP64."""
-    t = np.abs(oracle.e4m3_table())
-    m, k = qa.shape
-    n = qb.shape[0]
-    fa = t[qa] * np.repeat(np.abs(sa[:, :m]).T.astype(np.float64), 128, axis=1)
-    sbe = np.repeat(np.repeat(np.abs(sb).astype(np.float64), 128, axis=0)[:n], 128, axis=1)
-    fb = t[qb] * sbe
-    return fa @ fb.T
-
-
 def check_gemm(got: np.ndarray, ref: np.ndarray, s: np.ndarray, k: int, label: str = "") -> dict:
     """Assert the normwise and elementwise criteria; return the metrics."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
-    assert np.all(np.isfinite(got)), f"{label}: non-finite outputs"
-    err = np.abs(got - ref)
-    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
-    bound = 2.0**-8 * np.abs(ref) + 2.0 * (k + k // 128) * 2.0**-24 * s
-    worst = float(np.max(err - bound)) if err.size else 0.0
-    bf16_ref = oracle.round_to_bf16(ref)
-    got_bits = (got.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
-    frac_diff = float(np.mean(got_bits != bf16_ref)) if err.size else 0.0
+    return assert_stats(error_stats(got, ref, s, k), label)
+
+
+def assert_stats(st: dict, label: str = "") -> dict:
+    """The two product criteria on (possibly merged) error statistics."""
+    assert st["finite"], f"{label}: non-finite outputs"
+    rel = float(np.sqrt(st["err2"]) / max(np.sqrt(st["ref2"]), 1e-300))
     assert rel <= TOL_NORMWISE, f"{label}: normwise relative error {rel:.3e} > {TOL_NORMWISE}"
-    assert worst <= 0.0, f"{label}: elementwise bound exceeded by {worst:.3e}"
-    return {"normwise": rel, "frac_not_bf16_rne": frac_diff}
+    assert st["worst"] <= 0.0, f"{label}: elementwise bound exceeded by {st['worst']:.3e}"
+    return {"normwise": rel, "frac_not_bf16_rne": st["ndiff"] / max(st["count"], 1)}
 
 
 # ----------------------------------------------------------------- GPU runs
@@ -127,3 +117,29 @@ def check_sampled(lin, q, sa, qb, sb, d, rows, cblocks, label="", quantizers=Non
     got = d_to_f64(d.index_select(0, ri).index_select(1, ci))
     s = magnitude_sum(oq, osa, oqb, osb)
     return check_gemm(got, ref, s, lin.k, label)
+
+
+def check_full(lin, q, sa, qb, sb, d, label=""):
+    """Every output of the product against the oracle: the oracle quantizes
+    all of A and B (compared bit for bit with the GPU's codes and scales),
+    then computes every output row (oracle.gemm_nt, in parallel row pieces)
+    and both product criteria are applied to the whole output."""
+    oqb, osb = oracle_workers.quantize_blocks(lin.b)
+    assert np.array_equal(codes(qb), oqb), f"{label}: weight codes differ"
+    assert np.array_equal(bits32(sb), bits32(osb)), f"{label}: weight scales differ"
+    oq, osa = oracle_workers.quantize_groups(lin.a)
+    assert np.array_equal(codes(q), oq), f"{label}: activation codes differ"
+    assert np.array_equal(bits32(sa[:, : lin.m]), bits32(osa[:, : lin.m])), f"{label}: activation scales differ"
+    got = d_to_f64(d)
+    return assert_stats(oracle_workers.product_stats(oq, osa, oqb, osb, got, lin.k), label)
+
+
+def one_row_per_band(rows: np.ndarray, band: int, rng) -> np.ndarray:
+    """One randomly chosen row from each band of `band` consecutive row
+    indices that contains any of `rows` (sorted)."""
+    out = []
+    bands = rows // band
+    for b in np.unique(bands):
+        cand = rows[bands == b]
+        out.append(int(cand[rng.integers(cand.size)]))
+    return np.array(out, dtype=np.int64)

@@ -12,7 +12,7 @@ import torch
 import fine_grained_block_fp8_amd as fg
 import oracle
 import workloads
-from tests.parity import bits32, check_sampled, codes, gpu_hot_path
+from tests.parity import bits32, check_full, check_sampled, codes, gpu_hot_path
 
 pytestmark = pytest.mark.gpu
 
@@ -62,11 +62,23 @@ def test_fp8_out_small_m(m):
 
 
 def test_fp8_out_prefill_o():
-    """The o projection's output shape (2048 x 4096) with outlier activations."""
+    """The o projection's output shape (2048 x 4096) with outlier activations:
+    the FP8 output equals the oracle's quantizer applied to the call's own
+    bf16 product (and the GPU quantizer's, bit for bit), and every output of
+    that product meets the product criteria against the oracle."""
     (lin,) = workloads.prefill_linears(names=["o"])
     q, sa, qb, sb, d = gpu_hot_path(lin)
-    q_out, sd = fg.fp8_gemm_nt_fp8_out((q, sa), (qb, sb))
-    q_ref, sd_ref = fg.quantize_fp8_groups(d)
+    m, n = lin.m, lin.n
+    q_out = torch.full((m, n), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sd = torch.full((n // 128, fg.padded_rows(m)), float("nan"), dtype=torch.float32, device="cuda")
+    d2 = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.fp8_gemm_nt_fp8_out((q, sa), (qb, sb), out=(q_out, sd), d=d2)
+    q_ref, sd_ref = fg.quantize_fp8_groups(d2)
     torch.cuda.synchronize()
     assert torch.equal(q_out.view(torch.uint8), q_ref.view(torch.uint8))
-    assert np.array_equal(bits32(sd[:, : lin.m]), bits32(sd_ref[:, : lin.m]))
+    assert np.array_equal(bits32(sd[:, :m]), bits32(sd_ref[:, :m]))
+    oq, osd = oracle.quantize_groups(d2.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(codes(q_out), oq), "FP8 output differs from the oracle quantizer"
+    assert np.array_equal(bits32(sd[:, :m]), bits32(osd[:, :m])), "output scales differ from the oracle's"
+    assert torch.equal(d2.view(torch.int16), d.view(torch.int16)), "bf16 output differs from fp8_gemm_nt"
+    check_full(lin, q, sa, qb, sb, d2, "fp8-out o")

@@ -10,13 +10,18 @@ import torch
 import fine_grained_block_fp8_amd as fg
 import oracle
 import workloads
+from tests import oracle_workers
 from tests.parity import (
+    assert_stats,
+    bits32,
+    check_full,
     check_gemm,
     check_sampled,
     codes,
     d_to_f64,
     gpu_hot_path,
     magnitude_sum,
+    one_row_per_band,
     sample_col_blocks,
     sample_rows,
     to_dev_bf16,
@@ -63,12 +68,14 @@ def test_odd_shapes(m, n, k):
 
 
 @pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
-def test_prefill_linears_sampled(name):
+def test_prefill_linears_full(name):
+    """Every output of each prefill linear against the oracle (all tiles of
+    the launch the bench times)."""
     (lin,) = workloads.prefill_linears(names=[name])
+    print(f"prefill {lin.name}: {fg.describe_gemm(lin.m, lin.n, lin.k)}", flush=True)
     q, sa, qb, sb, d = gpu_hot_path(lin)
-    assert torch.isfinite(d.float()).all(), "unwritten or non-finite outputs"
-    rng = np.random.default_rng(1)
-    check_sampled(lin, q, sa, qb, sb, d, sample_rows(lin.m, 48, rng), sample_col_blocks(lin.n, 12, rng), lin.name)
+    r = check_full(lin, q, sa, qb, sb, d, lin.name)
+    assert r["frac_not_bf16_rne"] < 0.05
 
 
 @pytest.mark.parametrize("m", [1, 4, 16])
@@ -76,17 +83,39 @@ def test_prefill_linears_sampled(name):
 def test_decode_linears_full(m, n, k):
     lin = workloads.decode_linear(m, n, k)
     q, sa, qb, sb, d = gpu_hot_path(lin)
-    rng = np.random.default_rng(2)
-    check_sampled(lin, q, sa, qb, sb, d, np.arange(m), sample_col_blocks(n, 40, rng), lin.name)
+    check_full(lin, q, sa, qb, sb, d, lin.name)
 
 
-@pytest.mark.parametrize("m,n,k", [(8192, 8192, 8192), (16384, 16384, 8192)])
-def test_square_sampled(m, n, k):
+def test_square_8192_full():
+    """Every output of the 8192^3 product against the oracle."""
+    lin = workloads.square_linear(8192, 8192, 8192)
+    print(f"square {lin.name}: {fg.describe_gemm(lin.m, lin.n, lin.k)}", flush=True)
+    q, sa, qb, sb, d = gpu_hot_path(lin)
+    check_full(lin, q, sa, qb, sb, d, lin.name)
+
+
+def test_square_16384_every_tile():
+    """M = N = 16384, K = 8192: every output column of one row from each
+    64-row band (the height of a wave's tile), so every output tile of the
+    launch -- every 256x256 workgroup tile and every 64-row wave tile in it --
+    is compared with the oracle; every output is checked to be written."""
+    m = n = 16384
+    k = 8192
     lin = workloads.square_linear(m, n, k)
+    print(f"square {lin.name}: {fg.describe_gemm(m, n, k)}", flush=True)
     q, sa, qb, sb, d = gpu_hot_path(lin)
     assert torch.isfinite(d.float()).all(), "unwritten or non-finite outputs"
-    rng = np.random.default_rng(3)
-    check_sampled(lin, q, sa, qb, sb, d, sample_rows(m, 24, rng), sample_col_blocks(n, 6, rng), lin.name)
+    rows = one_row_per_band(np.arange(m), 64, np.random.default_rng(3))
+    assert rows.size == m // 64
+    oqb, osb = oracle_workers.quantize_blocks(lin.b)
+    assert np.array_equal(codes(qb), oqb), "weight codes differ"
+    assert np.array_equal(bits32(sb), bits32(osb)), "weight scales differ"
+    oq, osa = oracle.quantize_groups(lin.a[rows])
+    ri = torch.as_tensor(rows, device=d.device)
+    assert np.array_equal(codes(q.view(torch.uint8).index_select(0, ri)), oq), "activation codes differ"
+    assert np.array_equal(bits32(sa[:, :m].index_select(1, ri)), bits32(osa[:, : rows.size])), "scales differ"
+    got = d_to_f64(d.index_select(0, ri))
+    assert_stats(oracle_workers.product_stats(oq, osa, oqb, osb, got, k, piece=32), lin.name)
 
 
 def test_constant_scales_closed_form():

@@ -7,7 +7,18 @@ import torch
 import fine_grained_block_fp8_amd as fg
 import oracle
 import workloads
-from tests.parity import block_rows, check_gemm, codes, bits32, d_to_f64, magnitude_sum, to_dev_bf16
+from tests import oracle_workers
+from tests.parity import (
+    assert_stats,
+    bits32,
+    block_rows,
+    check_gemm,
+    codes,
+    d_to_f64,
+    magnitude_sum,
+    one_row_per_band,
+    to_dev_bf16,
+)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,18 +102,40 @@ def test_one_group_equals_dense():
     assert torch.equal(dd.view(torch.int16), d.view(torch.int16))
 
 
-def test_moe_zipf_32_experts_sampled():
+def test_moe_zipf_32_experts_every_tile():
+    """The 32-expert Zipf case (K = 7168, N = 4096): every output column of
+    one real row from each 64-row band of the layout (the height of a wave's
+    tile) that holds real rows, so every 128x256 workgroup tile of every
+    expert -- and every 64-row wave tile with real rows -- is compared with
+    the oracle, with each expert's whole weight quantized by the oracle."""
     g = workloads.moe_grouped()
     assert g.num_groups == 32 and g.k == 7168 and g.n == 4096
     assert np.all(g.starts % 128 == 0) and g.m % 128 == 0
     assert int(g.sizes.sum()) == 8192 * 4
+    print(f"grouped {g.name}: m_pad={g.m}", flush=True)
     q, sa, qb, sb, d = gpu_grouped(g)
-    rng = np.random.default_rng(4)
-    groups = sorted(set([0, 31, int(np.argmax(g.sizes)), int(np.argmin(g.sizes))] + list(rng.choice(32, 4, replace=False))))
-    check_groups(g, q, sa, qb, sb, d, groups=groups, rows_per_group=24,
-                 cblocks=np.array([0, 7, 19, 31]), rng=rng)
     real = torch.from_numpy(g.m_indices >= 0).cuda()
     assert torch.isfinite(d[real].float()).all()
+    rows = one_row_per_band(np.nonzero(g.m_indices >= 0)[0], 64, np.random.default_rng(4))
+    assert set(g.m_indices[rows // 128 * 128]) == set(range(32)), "a sampled band in every expert"
+    oqb, osb = oracle_workers.quantize_blocks(g.b.reshape(g.num_groups * g.n, g.k))
+    assert np.array_equal(codes(qb.view(torch.uint8).reshape(-1, g.k)), oqb), "weight codes differ"
+    assert np.array_equal(bits32(sb.reshape(-1, g.k // 128)), bits32(osb)), "weight scales differ"
+    oqb = oqb.reshape(g.num_groups, g.n, g.k)
+    osb = osb.reshape(g.num_groups, g.n // 128, g.k // 128)
+    oq, osa = oracle.quantize_groups(g.a[rows])
+    ri = torch.as_tensor(rows, device="cuda")
+    assert np.array_equal(codes(q.view(torch.uint8).index_select(0, ri)), oq), "activation codes differ"
+    assert np.array_equal(bits32(sa[:, : g.m].index_select(1, ri)), bits32(osa[:, : rows.size])), "scales differ"
+    got = d_to_f64(d.index_select(0, ri))
+    parts = []
+    for e in range(g.num_groups):
+        sel = np.nonzero(g.m_indices[rows] == e)[0]
+        if sel.size == 0:
+            continue
+        parts.append(oracle_workers.product_stats(oq[sel], osa[:, sel], oqb[e], osb[e], got[sel], g.k, piece=64))
+        assert_stats(parts[-1], f"expert {e}")
+    assert_stats(oracle_workers.merge(parts), "all experts")
 
 
 def test_grouped_deterministic():
