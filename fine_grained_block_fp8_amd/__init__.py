@@ -59,6 +59,9 @@ _lib.moe_max_padded_rows.restype = ctypes.c_int64
 _lib.moe_route_workspace_bytes.argtypes = [_i64, _i32]
 _lib.moe_route_workspace_bytes.restype = ctypes.c_int64
 _lib.moe_route_contiguous.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]
+_lib.moe_route_contiguous_noalloc.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp]
+_lib.moe_route_noalloc_max_workspace_bytes.argtypes = []
+_lib.moe_route_noalloc_max_workspace_bytes.restype = ctypes.c_int64
 _lib.moe_gather_quantize.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _fp, _i64, _vp]
 _lib.silu_mul_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp, _fp, _i64, _vp]
 _lib.moe_gather_quantize_tokens.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _i64, _vp, _fp, _i64, _vp]
@@ -72,7 +75,7 @@ for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_gr
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
               "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked",
-              "moe_gather_quantize_tokens"):
+              "moe_gather_quantize_tokens", "moe_route_contiguous_noalloc"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -447,6 +450,33 @@ def moe_route_contiguous(topk_idx: torch.Tensor, num_experts: int, m_pad_max: in
     return counts, m_indices, token_of_row, row_of
 
 
+def moe_route_contiguous_noalloc(topk_idx: torch.Tensor, num_experts: int, out) -> tuple:
+    """moe_route_contiguous with the library's fixed routing workspace instead
+    of a caller's: nothing is allocated.  `out` = (counts [G], m_indices
+    [m_pad_max], token_of_row [m_pad_max], row_of [T, topk]), int32 device
+    tensors the caller owns.  Calls on one device share the workspace: calls
+    that overlap in time race."""
+    _need(topk_idx, "topk_idx", (torch.int32,), 2)
+    tokens, topk = topk_idx.shape
+    counts, m_indices, token_of_row, row_of = out
+    for t, name in ((counts, "counts"), (m_indices, "m_indices"), (token_of_row, "token_of_row")):
+        _need(t, name, (torch.int32,), 1)
+    _need(row_of, "row_of", (torch.int32,), 2)
+    if counts.shape[0] != num_experts or token_of_row.shape != m_indices.shape or tuple(row_of.shape) != (tokens, topk):
+        raise ValueError("routing buffers do not match (G, m_pad_max, [T, topk])")
+    _check(
+        _lib.moe_route_contiguous_noalloc(
+            _ptr(topk_idx), tokens, topk, num_experts, _ptr(counts), _ptr(m_indices), _ptr(token_of_row),
+            _ptr(row_of), m_indices.shape[0], _stream(topk_idx)
+        )
+    )
+    return counts, m_indices, token_of_row, row_of
+
+
+def moe_route_noalloc_max_workspace_bytes() -> int:
+    return int(_lib.moe_route_noalloc_max_workspace_bytes())
+
+
 def moe_route_workspace_bytes(tokens: int, num_experts: int) -> int:
     r = _lib.moe_route_workspace_bytes(tokens, num_experts)
     if r < 0:
@@ -636,6 +666,8 @@ __all__ = [
     "moe_gather_quantize_tokens",
     "moe_max_padded_rows",
     "moe_route_contiguous",
+    "moe_route_contiguous_noalloc",
+    "moe_route_noalloc_max_workspace_bytes",
     "moe_route_workspace_bytes",
     "padded_rows",
     "quantize_fp8_blocks",

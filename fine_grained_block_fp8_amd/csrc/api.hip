@@ -342,6 +342,38 @@ int moe_route_contiguous(const int32_t* topk_idx, int64_t tokens, int32_t topk, 
                   who);
 }
 
+int moe_route_contiguous_noalloc(const int32_t* topk_idx, int64_t tokens, int32_t topk, int32_t num_experts,
+                                 int32_t* counts, int32_t* m_indices, int32_t* token_of_row, int32_t* row_of,
+                                 int64_t m_pad_max, void* stream) {
+  const char* who = "moe_route_contiguous_noalloc";
+  if (tokens < 0 || tokens >= kMaxRows) return fail(FGFP8_EINVAL, "%s: tokens=%lld out of range", who, (long long)tokens);
+  if (topk < 1 || topk > 8) return fail(FGFP8_EINVAL, "%s: topk=%d must be 1..8", who, (int)topk);
+  if (num_experts < 1 || num_experts > 2048)
+    return fail(FGFP8_EINVAL, "%s: num_experts=%d must be 1..2048", who, (int)num_experts);
+  const int64_t need_rows = moe_max_padded_rows(tokens, topk, num_experts);
+  if (m_pad_max < need_rows || m_pad_max % 128 != 0 || m_pad_max >= kMaxRows)
+    return fail(FGFP8_EINVAL, "%s: m_pad_max=%lld must be a multiple of 128 and >= %lld", who, (long long)m_pad_max,
+                (long long)need_rows);
+  const int64_t need = fgfp8::moe_route_workspace_bytes(tokens, num_experts);
+  if (need > fgfp8::moe_route_scratch_bytes())
+    return fail(FGFP8_EINVAL,
+                "%s: tokens=%lld with num_experts=%d need %lld bytes of routing workspace, beyond the fixed %lld "
+                "(use moe_route_contiguous with a workspace of its own)",
+                who, (long long)tokens, (int)num_experts, (long long)need, (long long)fgfp8::moe_route_scratch_bytes());
+  if (!counts || !m_indices || !token_of_row || (tokens > 0 && (!topk_idx || !row_of)))
+    return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (int rc = check_device(who)) return rc;
+  void* ws = nullptr;
+  const hipError_t e = fgfp8::moe_route_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(FGFP8_ELAUNCH, "%s: cannot find the routing workspace on this device: %s", who, hipGetErrorString(e));
+  return launched(fgfp8::launch_moe_route(topk_idx, tokens, topk, num_experts, counts, m_indices, token_of_row, row_of,
+                                          m_pad_max, ws, (hipStream_t)stream),
+                  who);
+}
+
+int64_t moe_route_noalloc_max_workspace_bytes(void) { return fgfp8::moe_route_scratch_bytes(); }
+
 int moe_gather_quantize(const void* x_bf16, int64_t tokens, int64_t k, const int32_t* token_of_row, int64_t m_pad_max,
                         void* q_e4m3, float* sa, int64_t sa_ld, void* stream) {
   const char* who = "moe_gather_quantize";

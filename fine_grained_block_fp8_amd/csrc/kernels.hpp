@@ -98,6 +98,11 @@ int64_t moe_route_workspace_bytes(int64_t tokens, int experts);
 hipError_t launch_moe_route(const int32_t* topk_idx, int64_t tokens, int topk, int experts, int32_t* counts,
                             int32_t* m_indices, int32_t* token_of_row, int32_t* row_of, int64_t m_pad_max,
                             void* workspace, hipStream_t stream);
+// The fixed routing workspace of the allocation-free routing call: its size
+// in bytes, and its device address on the current device (looked up once per
+// device).  Every call on a device shares it.
+int64_t moe_route_scratch_bytes();
+hipError_t moe_route_scratch(void** out);
 // The same rows, each token's row read and quantized once and written to
 // the rows row_of[t][j]; rows no token maps to get zero codes and scale 1.
 hipError_t launch_moe_gather_quantize_tokens(const void* x, int64_t tokens, int64_t k, int topk,

@@ -18,6 +18,8 @@
 // real padded count carry group -1 and are skipped by the grouped product, so
 // no count ever has to reach the host.
 
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -199,6 +201,39 @@ __global__ __launch_bounds__(kRouteThreads) void moe_assign_kernel(const int32_t
 int64_t moe_route_workspace_bytes(int64_t tokens, int experts) {
   const int64_t nblocks = (tokens + kRouteThreads - 1) / kRouteThreads;
   return nblocks * experts * 4 + (int64_t)experts * 4;
+}
+
+// ------------------------------------------- routing without allocation
+// A fixed routing workspace for callers that cannot allocate device memory:
+// the per-256-token-block expert counts and the group starts of
+// launch_moe_route live in this array.  Each device that runs the library
+// holds its own copy (kRouteScratchInts int32, 4 MiB) until the process
+// ends.  Host code never passes the symbol itself to a kernel: its device
+// address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept in g_route_scratch.
+constexpr int64_t kRouteScratchInts = int64_t(1) << 20;
+static __device__ __align__(256) int32_t scratch[kRouteScratchInts];
+
+int64_t moe_route_scratch_bytes() { return kRouteScratchInts * 4; }
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_route_scratch[kScratchDevices];
+}  // namespace
+
+hipError_t moe_route_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_route_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_route_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_moe_route(const int32_t* topk_idx, int64_t tokens, int topk, int experts, int32_t* counts,

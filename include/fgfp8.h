@@ -18,7 +18,9 @@
  *  - Every pointer argument is a DEVICE pointer (memory of the current HIP
  *    device), owned by the caller.  The library never allocates, frees or
  *    synchronizes, never reads device data on the host, and keeps no device
- *    state between calls; every call is legal under HIP graph capture.
+ *    state between calls (the one exception is the fixed routing workspace
+ *    of moe_route_contiguous_noalloc, a device array inside the library);
+ *    every call is legal under HIP graph capture.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *    legacy default stream) and runs asynchronously: a return of FGFP8_OK
  *    means the work was enqueued, not that it finished.
@@ -303,6 +305,27 @@ int64_t moe_route_workspace_bytes(int64_t tokens, int32_t num_experts);
 int moe_route_contiguous(const int32_t* topk_idx, int64_t tokens, int32_t topk, int32_t num_experts, int32_t* counts,
                          int32_t* m_indices, int32_t* token_of_row, int32_t* row_of, int64_t m_pad_max,
                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* moe_route_contiguous without a workspace argument, for callers that
+ * cannot allocate device memory (code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments (minus
+ * workspace and workspace_bytes), same requirements and the same outputs,
+ * bit for bit.  The routing workspace is a fixed device array inside the
+ * library, one per device, of moe_route_noalloc_max_workspace_bytes() bytes
+ * (4 MiB), held from the first call on a device until the process ends; no
+ * call allocates or frees anything.  Problems whose
+ * moe_route_workspace_bytes(tokens, num_experts) exceeds that size are
+ * rejected with FGFP8_EINVAL (e.g. 256 experts allow up to ~1M tokens).
+ * Every call on one device shares the array and leaves its contents behind
+ * (nothing in it needs to start at zero: each call writes every entry it
+ * reads).  Calls that overlap in time on one device -- on different streams,
+ * or from different host threads -- therefore race and give undefined
+ * results: serialize them (one stream, or events). */
+int moe_route_contiguous_noalloc(const int32_t* topk_idx, int64_t tokens, int32_t topk, int32_t num_experts,
+                                 int32_t* counts, int32_t* m_indices, int32_t* token_of_row, int32_t* row_of,
+                                 int64_t m_pad_max, void* stream);
+/* The size of the fixed routing workspace above, in bytes.  Host-only. */
+int64_t moe_route_noalloc_max_workspace_bytes(void);
 
 /* Row r of the layout = x[token_of_row[r]] (a zero row for an index outside
  * [0, tokens)), quantized exactly as quantize_fp8_groups.  x [tokens][k] bf16;

@@ -50,6 +50,8 @@ def test_library_exports_every_declared_function():
         "moe_gate_up_silu_quantize",
         "quantize_fp8_groups_masked",
         "moe_gather_quantize_tokens",
+        "moe_route_contiguous_noalloc",
+        "moe_route_noalloc_max_workspace_bytes",
     }
     lib = fg.library()
     for n in names:
