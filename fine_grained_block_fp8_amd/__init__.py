@@ -52,6 +52,9 @@ _lib.quantize_fp8_groups_masked.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _fp
 _lib.quantize_fp8_groups_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_blocks_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt_ue8m0.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
+_lib.fp8_gemm_nt_ws.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
+_lib.fp8_gemm_nt_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.fp8_gemm_nt_workspace_bytes.restype = ctypes.c_int64
 _lib.quantize_fp8_mx.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp]
 _lib.fp8_gemm_nt_mx.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]
 _lib.moe_max_padded_rows.argtypes = [_i64, _i32, _i32]
@@ -75,7 +78,7 @@ for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_gr
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
               "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked",
-              "moe_gather_quantize_tokens", "moe_route_contiguous_noalloc"):
+              "moe_gather_quantize_tokens", "moe_route_contiguous_noalloc", "fp8_gemm_nt_ws"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -205,10 +208,13 @@ def quantize_fp8_blocks(w: torch.Tensor, out=None, ue8m0: bool = False):
     return q, sb
 
 
-def fp8_gemm_nt(a, b, d: torch.Tensor, ue8m0: bool = False) -> torch.Tensor:
+def fp8_gemm_nt(a, b, d: torch.Tensor, ue8m0: bool = False, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """d[M, N] (bf16, written in place) = A . B^T with A = (q [M, K], sa
     [K/128, sa_ld]) and B = (q [N, K], sb [ceil(N/128), K/128]).  ue8m0=True
-    runs fp8_gemm_nt_ue8m0 (every scale must be a power of two)."""
+    runs fp8_gemm_nt_ue8m0 (every scale must be a power of two).  With
+    `workspace` (a uint8 device tensor from gemm_workspace, zero-filled when
+    allocated) it runs fp8_gemm_nt_ws, which splits K over two workgroups per
+    tile on shapes whose tiles would leave compute units idle."""
     (qa, sa), (qb, sb) = a, b
     _need(qa, "a", _FP8, 2)
     _need(qb, "b", _FP8, 2)
@@ -223,9 +229,29 @@ def fp8_gemm_nt(a, b, d: torch.Tensor, ue8m0: bool = False) -> torch.Tensor:
         raise ValueError(f"d must be [{m}, {n}]")
     if k % GROUP == 0 and (sa.shape[0] != k // GROUP or tuple(sb.shape) != (-(-n // GROUP), k // GROUP)):
         raise ValueError("scale shapes must be sa [K/128, sa_ld] and sb [ceil(N/128), K/128]")
+    if workspace is not None:
+        if ue8m0:
+            raise ValueError("the workspace form is for FP32 scales")
+        _need(workspace, "workspace", (torch.uint8,), 1)
+        _check(_lib.fp8_gemm_nt_ws(_ptr(qa), _ptr(sa), sa.shape[1], _ptr(qb), _ptr(sb), _ptr(d), m, n, k,
+                                   _ptr(workspace), workspace.numel(), _stream(d)))
+        return d
     fn = _lib.fp8_gemm_nt_ue8m0 if ue8m0 else _lib.fp8_gemm_nt
     _check(fn(_ptr(qa), _ptr(sa), sa.shape[1], _ptr(qb), _ptr(sb), _ptr(d), m, n, k, _stream(d)))
     return d
+
+
+def fp8_gemm_nt_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Bytes of workspace fp8_gemm_nt_ws uses for this shape (0: none)."""
+    return int(_lib.fp8_gemm_nt_workspace_bytes(m, n, k))
+
+
+def gemm_workspace(m: int, n: int, k: int, device="cuda") -> torch.Tensor | None:
+    """A zero-filled workspace for fp8_gemm_nt(..., workspace=) at this
+    shape, or None when the shape's plan needs none.  Reusable by any later
+    call on the same stream (each call leaves it ready for the next)."""
+    nbytes = fp8_gemm_nt_workspace_bytes(m, n, k)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
 def fp8_gemm_nt_fp8_out(a, b, out=None, d: torch.Tensor | None = None):
@@ -656,6 +682,8 @@ __all__ = [
     "fp8_gemm_nt_mx",
     "fp8_linear",
     "fp8_linear_nt",
+    "fp8_gemm_nt_workspace_bytes",
+    "gemm_workspace",
     "last_error",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",

@@ -142,7 +142,8 @@ int quantize_blocks_impl(const char* who, bool ue8m0, const void* w_bf16, int64_
 }
 
 int gemm_impl(const char* who, bool ue8m0, const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3,
-              const float* sb, void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
+              const float* sb, void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream, void* workspace = nullptr,
+              int64_t workspace_bytes = 0) {
   if (m < 0 || m >= kMaxRows || n < 0 || n >= kMaxRows)
     return fail(FGFP8_EINVAL, "%s: m=%lld n=%lld out of range", who, (long long)m, (long long)n);
   if (int rc = check_k(who, k)) return rc;
@@ -151,12 +152,21 @@ int gemm_impl(const char* who, bool ue8m0, const void* a_e4m3, const float* sa, 
   if (!a_e4m3 || !sa || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(b_e4m3) || !aligned16(sb) || !aligned16(d_bf16))
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(FGFP8_EINVAL, "%s: workspace must be 256-byte aligned", who);
   if (int rc = check_device(who)) return rc;
-  const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
+  fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
+  if (workspace != nullptr && !ue8m0) {
+    const fgfp8::GemmPlan wp = fgfp8::plan_gemm_ws(m, n, k);
+    if (wp.kind == fgfp8::kGemmTile256x256SplitK2 && workspace_bytes >= fgfp8::gemm_splitk_workspace_bytes(m, n))
+      plan = wp;
+  }
   if (env_flag("FGFP8_PRINT_CONFIG"))
     fprintf(stderr, "[fgfp8] %s m=%lld n=%lld k=%lld: %s split=%d\n", who, (long long)m, (long long)n, (long long)k,
             fgfp8::gemm_kind_name(plan.kind), plan.split);
   const hipStream_t st = (hipStream_t)stream;
+  if (plan.kind == fgfp8::kGemmTile256x256SplitK2)
+    return launched(fgfp8::launch_gemm_splitk(a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, workspace, st), who);
   return launched(ue8m0 ? fgfp8::launch_gemm_ue8m0(plan, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, st)
                         : fgfp8::launch_gemm(plan, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, st),
                   who);
@@ -190,6 +200,20 @@ int fp8_gemm_nt_ue8m0(const void* a_e4m3, const float* sa, int64_t sa_ld, const 
 int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
                 void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream) {
   return gemm_impl("fp8_gemm_nt", false, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, stream);
+}
+
+int64_t fp8_gemm_nt_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0 || m >= kMaxRows || n >= kMaxRows || k > kMaxK) return 0;
+  const fgfp8::GemmPlan wp = fgfp8::plan_gemm_ws(m, n, k);
+  return wp.kind == fgfp8::kGemmTile256x256SplitK2 ? fgfp8::gemm_splitk_workspace_bytes(m, n) : 0;
+}
+
+int fp8_gemm_nt_ws(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                   void* d_bf16, int64_t m, int64_t n, int64_t k, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  if (workspace_bytes < 0) return fail(FGFP8_EINVAL, "fp8_gemm_nt_ws: negative workspace_bytes");
+  return gemm_impl("fp8_gemm_nt_ws", false, a_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, stream,
+                   workspace_bytes > 0 ? workspace : nullptr, workspace_bytes);
 }
 
 int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* m_indices,
@@ -508,7 +532,12 @@ int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len)
   if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: null or empty buffer");
   if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: bad shape");
   const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
-  snprintf(buf, (size_t)len, "%s split=%d", fgfp8::gemm_kind_name(plan.kind), plan.split);
+  const fgfp8::GemmPlan wp = fgfp8::plan_gemm_ws(m, n, k);
+  if (wp.kind != plan.kind)
+    snprintf(buf, (size_t)len, "%s split=%d; with workspace: %s", fgfp8::gemm_kind_name(plan.kind), plan.split,
+             fgfp8::gemm_kind_name(wp.kind));
+  else
+    snprintf(buf, (size_t)len, "%s split=%d", fgfp8::gemm_kind_name(plan.kind), plan.split);
   return FGFP8_OK;
 }
 

@@ -542,17 +542,149 @@ __device__ __forceinline__ void silu_epilogue(uint8_t* lds, v4f_t (&acc)[C::MT][
   }
 }
 
+// bf16 epilogue of a wave tile: lane (li, lg) owns rows m0 + wm*TM + 16*mt
+// + li; its values j = 8*s + e (s < NT/2, e < 8) go to column n0 + wn*TN +
+// 32*s + 8*lg + e, held in acc[mt][j % NT][j / NT], rounded to bf16 (RNE)
+// and stored as 16-byte words where the row is aligned and in range.
+template <class C, int MT0 = 0, int MT1 = C::MT>
+__device__ __forceinline__ void store_bf16(uint16_t* __restrict__ d, const v4f_t (&acc)[C::MT][C::NT], int64_t M,
+                                           int64_t N, int64_t m0, int64_t n0, int wm, int wn, int li, int lg) {
+  const bool vec = (N % 8) == 0;
+#pragma unroll
+  for (int mt = MT0; mt < MT1; mt++) {
+    const int64_t row = m0 + wm * C::TM + 16 * mt + li;
+    if (row >= M) continue;
+    uint16_t* drow = d + row * N;
+#pragma unroll
+    for (int s = 0; s < C::NT / 2; s++) {
+      const int64_t c0 = n0 + wn * C::TN + 32 * s + 8 * lg;
+      if (vec && c0 + 8 <= N) {
+        *reinterpret_cast<uint4*>(drow + c0) = pack8<C>(acc[mt], s);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int j = 8 * s + e;
+          if (c0 + e < N) drow[c0 + e] = (uint16_t)bf16_rne(acc[mt][j % C::NT][j / C::NT]);
+        }
+      }
+    }
+  }
+}
+
+// K split over two workgroups per output tile (fp8_gemm_nt with a
+// workspace, for shapes whose 256x256 tiles would leave half the compute
+// units idle).  Each workgroup sums the chunks kb0 .. kb1 - 1 of its tile in
+// FP32 as gemm_tile does; the two partial sums then meet through the
+// workspace: the first workgroup of the pair to finish (an atomic arrival
+// count) writes its partial and raises the tile's ready flag; the second
+// waits for the flag -- it only waits on a workgroup that has already
+// arrived, so the wait always ends -- adds the partial to its own
+// (acc0 + acc1, a single FP32 addition, the same bits whichever finished
+// first), rounds to bf16, stores, and sets the counter and the flag back
+// to zero for the next call.
+struct SplitK {
+  int kb0 = 0, kb1 = 0;     // chunk range; kb1 == 0: all of K
+  float* partial = nullptr;  // the tile's FP32 slot, BM * BN floats
+  int* arrive = nullptr;     // the tile's arrival count (0 between calls)
+  int* ready = nullptr;      // the tile's partial-ready flag (0 between calls)
+};
+
+// Longest wait for the partner's partial (s_sleep 2 units, ~128 cycles
+// each): far beyond the partner's few-microsecond store, a bound that turns
+// a broken invariant into an unwritten output tile instead of a hang.
+constexpr int kSplitSpinLimit = 1 << 24;
+
+// Cache policy of the partial's stores and loads: system scope (sc0 sc1),
+// so that they write through to and read from memory -- the two workgroups
+// of a tile may sit on different XCDs, whose L2 caches are not coherent with
+// each other -- without the whole-cache writeback and invalidation an
+// agent-scope fence costs.
+constexpr int kSysCoherent = 1 | 16;
+
+template <class C, int MT0>
+__device__ __forceinline__ void add_store_rows(rsrc_t rp, uint32_t base, v4f_t (&acc)[C::MT][C::NT],
+                                               uint16_t* __restrict__ d, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                               int wm, int wn, int li, int lg) {
+  constexpr int R = 2;  // rows of MFMA tiles per batch: 2 * NT loads in flight
+  if constexpr (MT0 < C::MT) {
+    v4f_t p[R][C::NT];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+      for (int t = 0; t < C::NT; t++)
+        p[r][t] = __builtin_bit_cast(v4f_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rp, base + (uint32_t)((MT0 + r) * C::NT + t) * 1024u, 0, kSysCoherent));
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+      for (int t = 0; t < C::NT; t++) acc[MT0 + r][t] += p[r][t];
+    store_bf16<C, MT0, MT0 + R>(d, acc, M, N, m0, n0, wm, wn, li, lg);
+    __builtin_amdgcn_sched_barrier(0);
+    add_store_rows<C, MT0 + R>(rp, base, acc, d, M, N, m0, n0, wm, wn, li, lg);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void split_fixup(uint8_t* lds, v4f_t (&acc)[C::MT][C::NT], const SplitK& sk,
+                                            uint16_t* __restrict__ d, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                            int wave, int wm, int wn, int lane) {
+  int* shared = reinterpret_cast<int*>(lds);
+  __syncthreads();  // every wave is past its last fragment read: LDS is free
+  if (threadIdx.x == 0)
+    shared[0] = __hip_atomic_fetch_add(sk.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  const bool first = shared[0] == 0;
+  // lane's j-th 4-float group at float4 index (wave * MT * NT + j) * 64 +
+  // lane of the tile's slot: each wave store or load moves 1 KB of
+  // consecutive bytes
+  const rsrc_t rp = make_rsrc(sk.partial, (uint32_t)(C::BM * C::BN * 4));
+  const uint32_t base = ((uint32_t)wave * (C::MT * C::NT) * 64u + (uint32_t)lane) * 16u;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  if (first) {
+#pragma unroll
+    for (int j = 0; j < C::MT * C::NT; j++)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[j / C::NT][j % C::NT]), rp,
+                                             base + (uint32_t)j * 1024u, 0, kSysCoherent);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial has reached memory
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(sk.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(sk.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == 0 && spins < kSplitSpinLimit) {
+      __builtin_amdgcn_s_sleep(2);
+      spins++;
+    }
+    shared[1] = spins < kSplitSpinLimit;
+  }
+  __syncthreads();
+  // No partial within the bound (a broken invariant): the tile is left
+  // unwritten rather than the workgroup hanging.
+  if (shared[1] == 0) return;  // uniform
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(sk.arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(sk.ready, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  // one row of MFMA tiles at a time: its partial is loaded, added and stored
+  // as bf16 before the next row's loads, so that the partial and all of acc
+  // are never live at once
+  const int li = lane & 15, lg = lane >> 4;
+  add_store_rows<C, 0>(rp, base, acc, d, M, N, m0, n0, wm, wn, li, lg);
+}
+
 // ROWSKIP (the masked product, whose tiles are often partly filled): a wave
 // whose rows all lie past M skips its fragment reads and MFMAs and only
 // issues its copies, and the waves are laid out row-half-major (wm = wave /
 // WAVES_N), so that waves w and w + 4 -- which share a SIMD -- belong to
 // different row halves and a skipping wave leaves its SIMD to the other.
 // The results are the same bits.
-template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false, bool SILU = false, bool ROWSKIP = false>
+template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false, bool SILU = false, bool ROWSKIP = false,
+          bool SPLIT = false>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
                                           const float* sb_base, uint16_t* __restrict__ d, const TileOut& out,
                                           int64_t M, int64_t N, int K, int64_t sa_ld, int64_t m0, int64_t n0,
-                                          int64_t sb_ld = 0, const GateUp& gu = GateUp{}) {
+                                          int64_t sb_ld = 0, const GateUp& gu = GateUp{}, const SplitK& sk = SplitK{}) {
   // the FP8-output and SiLU epilogues pair waves as wave = wm + WAVES_M * wn
   static_assert(!ROWSKIP || (!FP8OUT && !UE8M0 && !MX && !SILU), "row skipping is for the bf16 FP32-scale tile");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -614,12 +746,13 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   // most the copies of the chunks after it are outstanding": none with two
   // stages; with three, one chunk's NSEG segments plus the scale copy that
   // waves 0 and 1 issue.
-  loader.all(0, 0);
-  if (C::STAGES == 3) loader.all(1, KB > 1 ? 1 : 0);
+  const int kb0 = SPLIT ? sk.kb0 : 0, kb1 = SPLIT ? sk.kb1 : KB;
+  loader.all(0, kb0);
+  if (C::STAGES == 3) loader.all(1, kb0 + 1 < kb1 ? kb0 + 1 : kb0);
   int stage = 0;
-  for (int kb = 0; kb < KB; kb++) {
+  for (int kb = kb0; kb < kb1; kb++) {
     const int load_stage = stage == 0 ? C::STAGES - 1 : stage - 1;
-    const int next = kb + C::STAGES - 1 < KB ? kb + C::STAGES - 1 : KB - 1;
+    const int next = kb + C::STAGES - 1 < kb1 ? kb + C::STAGES - 1 : kb1 - 1;
     if (C::STAGES == 2) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     } else if (wave < 2) {
@@ -654,31 +787,14 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
     return;
   }
 
-  // Epilogue: lane (li, lg) owns row m0 + wm*TM + 16*mt + li; its values
-  // j = 8*s + e (s < NT/2, e < 8) go to column n0 + wn*TN + 32*s + 8*lg + e,
-  // held in acc[mt][j % NT][j / NT].  They are rounded to bf16 (RNE) and
-  // packed 8 to a 16-byte word, w[s].
+  if constexpr (SPLIT) {
+    split_fixup<C>(lds, acc, sk, d, M, N, m0, n0, wave, wm, wn, lane);
+    return;
+  }
+
+  // Epilogue: bf16 (store_bf16), or the FP8 output below.
   if constexpr (!FP8OUT) {
-    const bool vec = (N % 8) == 0;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; mt++) {
-      const int64_t row = m0 + wm * C::TM + 16 * mt + li;
-      if (row >= M) continue;
-      uint16_t* drow = d + row * N;
-#pragma unroll
-      for (int s = 0; s < C::NT / 2; s++) {
-        const int64_t c0 = n0 + wn * C::TN + 32 * s + 8 * lg;
-        if (vec && c0 + 8 <= N) {
-          *reinterpret_cast<uint4*>(drow + c0) = pack8<C>(acc[mt], s);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; e++) {
-            const int j = 8 * s + e;
-            if (c0 + e < N) drow[c0 + e] = (uint16_t)bf16_rne(acc[mt][j % C::NT][j / C::NT]);
-          }
-        }
-      }
-    }
+    store_bf16<C>(d, acc, M, N, m0, n0, wm, wn, li, lg);
     return;
   } else {
   // FP8 output (N % 128 == 0): the bf16 values above, quantized per 1x128
@@ -1021,6 +1137,33 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(const uint8_t* __re
   gemm_tile<C, FP8OUT, UE8M0, MX>(lds, A + m0 * K, B + n0 * K, SA, SB, out.d, out, M, N, K, sa_ld, m0, n0, sb_ld);
 }
 
+// K split in two (SplitK): workgroups b and b + tiles share output tile b
+// (the same XCD when tiles % 8 == 0), summing chunks [0, KB/2) and
+// [KB/2, KB).  ws_counters holds 2 * tiles ints (arrival counts, then
+// ready flags; zero between calls), ws_partials tiles * BM * BN floats.
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_nt_splitk_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ SA, const uint8_t* __restrict__ B,
+    const float* __restrict__ SB, uint16_t* __restrict__ D, int64_t M, int64_t N, int K, int64_t sa_ld, int tiles_m,
+    int tiles_n, int* __restrict__ ws_counters, float* __restrict__ ws_partials) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  const int tiles = tiles_m * tiles_n;
+  const int half = (int)blockIdx.x / tiles, t = (int)blockIdx.x - half * tiles;
+  int tm, tn;
+  tile_coords(t, tiles, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+  const int KB = K / kGroup, kbh = KB / 2;
+  SplitK sk;
+  sk.kb0 = half == 0 ? 0 : kbh;
+  sk.kb1 = half == 0 ? kbh : KB;
+  sk.partial = ws_partials + (size_t)t * (C::BM * C::BN);
+  sk.arrive = ws_counters + t;
+  sk.ready = ws_counters + tiles + t;
+  gemm_tile<C, false, false, false, false, false, true>(lds, A + m0 * K, B + n0 * K, SA, SB, D,
+                                                        TileOut{D, nullptr, nullptr, 0}, M, N, K, sa_ld, m0, n0, 0,
+                                                        GateUp{}, sk);
+}
+
 // Grouped: every BM-row block lies inside one group (groups start at
 // multiples of 128 rows and BM = 128); its group is m_indices of its first
 // row, and a block of padding (-1) is skipped.
@@ -1146,6 +1289,39 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
   return best;
 }
 
+// K split over two workgroups per 256x256 tile: where 256x256 tiles would
+// fill at most half the compute units (so both halves of every tile run in
+// one round) and each half keeps at least 32 chunks (measured on M = 2048,
+// N = 4096: 5% faster than 256x128 tiles at K = 12288, 17% slower at
+// K = 4096, where the exchange of the partial sums is not amortised).  Tuning and test
+// override: FGFP8_SPLITK=0|1 (1 forces it for k >= 256).
+GemmPlan plan_gemm_ws(int64_t m, int64_t n, int64_t k) {
+  const GemmPlan base = plan_gemm(m, n, k);
+  if (base.kind == kGemmDecode) return base;
+  const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  bool split = 2 * tiles <= kCUs && k >= 64 * kGroup;
+  if (const char* force = getenv("FGFP8_SPLITK")) split = strcmp(force, "0") != 0 && k >= 2 * kGroup;
+  return split ? GemmPlan{kGemmTile256x256SplitK2, 2} : base;
+}
+
+int64_t gemm_splitk_workspace_bytes(int64_t m, int64_t n) {
+  const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  return (2 * tiles * 4 + 255) / 256 * 256 + tiles * 256 * 256 * 4;
+}
+
+hipError_t launch_gemm_splitk(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb, void* d,
+                              int64_t m, int64_t n, int64_t k, void* workspace, hipStream_t stream) {
+  using C = Tile256x256;
+  const int tiles_m = (int)((m + C::BM - 1) / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
+  const int tiles = tiles_m * tiles_n;
+  int* counters = static_cast<int*>(workspace);
+  float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + (2 * (int64_t)tiles * 4 + 255) / 256 * 256);
+  hipLaunchKernelGGL(gemm_nt_splitk_kernel<C>, dim3(2u * (uint32_t)tiles), dim3(C::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(a), sa, static_cast<const uint8_t*>(b), sb, static_cast<uint16_t*>(d), m,
+                     n, (int)k, sa_ld, tiles_m, tiles_n, counters, partials);
+  return hipGetLastError();
+}
+
 const char* gemm_kind_name(GemmKind kind) {
   switch (kind) {
     case kGemmTile256x256: return "tile256x256_w4x2";
@@ -1154,6 +1330,7 @@ const char* gemm_kind_name(GemmKind kind) {
     case kGemmTile256x128: return "tile256x128_w4x2";
     case kGemmTile128x128: return "tile128x128_w2x2";
     case kGemmDecode: return "decode_splitk_slab16";
+    case kGemmTile256x256SplitK2: return "tile256x256_w4x2_splitk2";
   }
   return "?";
 }
@@ -1220,6 +1397,7 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int
                        const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const TileOut out{static_cast<uint16_t*>(d), nullptr, nullptr, 0};
   switch (plan.kind) {
+    case kGemmTile256x256SplitK2:  // without a workspace: whole tiles
     case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile256x192: return launch_tile<Tile256x192>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
@@ -1297,6 +1475,7 @@ hipError_t launch_gemm_ue8m0(const GemmPlan& plan, const void* a, const float* s
                              const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const TileOut out{static_cast<uint16_t*>(d), nullptr, nullptr, 0};
   switch (plan.kind) {
+    case kGemmTile256x256SplitK2:
     case kGemmTile256x256: return launch_tile<Tile256x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
     case kGemmTile256x192: return launch_tile<Tile256x192>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
     case kGemmTile128x256: return launch_tile<Tile128x256>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);

@@ -28,6 +28,7 @@ enum GemmKind : int {
   kGemmTile128x128 = 3,  // 128x128, 4 waves of 64x64
   kGemmDecode = 4,       // M <= 16: 16-column slabs, K split across waves
   kGemmTile256x192 = 5,  // 256x192, 12 waves of 64x64
+  kGemmTile256x256SplitK2 = 6,  // 256x256 tiles, K split over two workgroups (needs a workspace)
 };
 
 struct GemmPlan {
@@ -37,6 +38,15 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k);
 const char* gemm_kind_name(GemmKind kind);
+// The plan when a workspace may be used: plan_gemm's, or the K-split 256x256
+// tiles where those fill the compute units and whole tiles would not.
+GemmPlan plan_gemm_ws(int64_t m, int64_t n, int64_t k);
+// Workspace bytes of the K-split plan for (m, n, k) (0 for other plans):
+// 2 ints per 256x256 tile (zero between calls), padded to 256 bytes, then
+// one 256x256 FP32 partial per tile.
+int64_t gemm_splitk_workspace_bytes(int64_t m, int64_t n);
+hipError_t launch_gemm_splitk(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb, void* d,
+                              int64_t m, int64_t n, int64_t k, void* workspace, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int64_t sa_ld, const void* b,
                        const float* sb, void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);

@@ -114,6 +114,32 @@ int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, 
 int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
                 void* d_bf16, int64_t m, int64_t n, int64_t k, void* stream);
 
+/* fp8_gemm_nt with a caller workspace.  On shapes whose 256x256 output
+ * tiles would fill at most half of the compute units (few rows against a
+ * modest N, e.g. M = 2048 with N = 4096), the 128-wide K chunks of every tile
+ * are split over two workgroups: each accumulates its half exactly as
+ * fp8_gemm_nt accumulates all of K (a fresh FP32 partial per chunk, promoted
+ * with sa * sb), and the two FP32 sums meet through the workspace and are
+ * added once before the bf16 rounding.  The result is deterministic; it
+ * differs from fp8_gemm_nt's only in the FP32 summation order (the two
+ * products differ only in the order they sum, which the recipe allows).
+ * Other shapes run exactly as fp8_gemm_nt.
+ *
+ * workspace        device memory, 256-byte aligned, of workspace_bytes >=
+ *                  fp8_gemm_nt_workspace_bytes(m, n, k); it must be filled
+ *                  with zeros before its first use, and every call leaves it
+ *                  ready for the next one when it completes.  Calls that may
+ *                  overlap in time (different streams) must not share it.
+ *                  A smaller workspace (or NULL with 0 bytes) runs the
+ *                  fp8_gemm_nt plan.
+ * Other arguments and requirements: as fp8_gemm_nt. */
+int fp8_gemm_nt_ws(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* b_e4m3, const float* sb,
+                   void* d_bf16, int64_t m, int64_t n, int64_t k, void* workspace, int64_t workspace_bytes,
+                   void* stream);
+/* Bytes of workspace fp8_gemm_nt_ws uses for (m, n, k): 0 when its plan for
+ * the shape does not split K (or the shape is invalid).  Host-only. */
+int64_t fp8_gemm_nt_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
 /* Block-scaled product with an FP8 output for the next layer: the bf16
  * result of fp8_gemm_nt, quantized per 1x128 group of each row exactly as
  * quantize_fp8_groups quantizes a bf16 input, inside the product's epilogue
@@ -394,7 +420,8 @@ const char* fgfp8_last_error(void);
  * (tile256x256_w4x2, tile256x192_w4x3, tile256x128_w4x2, tile128x256_w2x4,
  * tile128x128_w2x2), forces that tile in fp8_gemm_nt (tuning and tests; the
  * FP8-output call takes tile256x256_w4x2 for tile256x192_w4x3); other values
- * are ignored.  FGFP8_PERSISTENT=1 makes fp8_gemm_nt (bf16 output, FP32
+ * are ignored.  FGFP8_SPLITK=1 (0) forces (forbids) the K-split plan of
+ * fp8_gemm_nt_ws for k >= 256.  FGFP8_PERSISTENT=1 makes fp8_gemm_nt (bf16 output, FP32
  * scales) and m_grouped_fp8_gemm_nt_contiguous walk their tiles
  * persistently (one workgroup per compute unit, the K pipeline continuing
  * across tiles; same results bit for bit) for k >= 256; by default every

@@ -52,6 +52,8 @@ def test_library_exports_every_declared_function():
         "moe_gather_quantize_tokens",
         "moe_route_contiguous_noalloc",
         "moe_route_noalloc_max_workspace_bytes",
+        "fp8_gemm_nt_ws",
+        "fp8_gemm_nt_workspace_bytes",
     }
     lib = fg.library()
     for n in names:
@@ -351,3 +353,24 @@ def test_fused_gate_up_rejects():
     assert call(m_indices=None) == fg.FGFP8_EINVAL
     assert call(q=None) == fg.FGFP8_EINVAL
     assert call(m=0, a=None, m_indices=None, q=None, sa_ld=0, sq_ld=0) == fg.FGFP8_OK  # empty: nothing to do
+
+
+def test_gemm_workspace_sizes_and_rejects():
+    """fp8_gemm_nt_ws: the workspace query (K split where 256x256 tiles fill
+    at most half the compute units and K has at least 64 chunks), and the
+    argument checks that come before any device work."""
+    lib = fg.library()
+    tiles = 8 * 16  # 2048 x 4096 in 256x256 tiles
+    assert lib.fp8_gemm_nt_workspace_bytes(2048, 4096, 12288) == (2 * tiles * 4 + 255) // 256 * 256 + tiles * 256 * 256 * 4
+    assert lib.fp8_gemm_nt_workspace_bytes(2048, 4096, 4096) == 0  # too few chunks per half
+    assert lib.fp8_gemm_nt_workspace_bytes(2048, 24576, 4096) == 0  # whole tiles fill the CUs
+    assert lib.fp8_gemm_nt_workspace_bytes(16, 4096, 12288) == 0  # decode shapes
+    assert lib.fp8_gemm_nt_workspace_bytes(2048, 4096, 100) == 0  # invalid K
+    assert lib.fp8_gemm_nt_workspace_bytes(-1, 4096, 12288) == 0
+    # a workspace that is not 256-byte aligned
+    assert lib.fp8_gemm_nt_ws(P, P, 2048, P, P, P, 2048, 4096, 12288, P + 16, 1 << 26, None) == fg.FGFP8_EINVAL
+    assert "256-byte" in fg.last_error()
+    assert lib.fp8_gemm_nt_ws(P, P, 2048, P, P, P, 2048, 4096, 12288, P, -1, None) == fg.FGFP8_EINVAL
+    # the fp8_gemm_nt checks apply
+    assert lib.fp8_gemm_nt_ws(P, P, 2048, P, P, P, 2048, 4096, 100, P, 1 << 26, None) == fg.FGFP8_EINVAL
+    assert lib.fp8_gemm_nt_ws(None, None, 0, None, None, None, 0, 4096, 12288, None, 0, None) == fg.FGFP8_OK

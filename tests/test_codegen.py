@@ -60,3 +60,48 @@ def test_gemm_loops_have_no_full_drain(tmp_path):
         two_stage = tile.group(5) == "2"
         allowed = 2 if two_stage or "persistent" in name or "gemm_silu_kernel" in name else 1
         assert n <= allowed, f"{name}: {n} full vmcnt drains"
+
+
+def mfma_loop_drains(asm: str, kernel_prefix: str) -> list[int]:
+    """Full drains inside each loop that contains MFMAs, for the kernels
+    whose symbol starts with kernel_prefix.  A loop is its header block (the
+    label the compiler marks "Loop Header") and every block it annotates as
+    "in Loop: Header=<that block>" (the compiler may place them before the
+    header)."""
+    out = []
+    cur = None
+    blocks: list[tuple[str, list[str]]] = []
+    for line in asm.splitlines() + ["_Zend:"]:
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            if cur is not None and cur.startswith(kernel_prefix):
+                headers = [lab for lab, body in blocks if body and "Loop Header" in body[0]]
+                for h in headers:
+                    key = h.lstrip(".L")  # BB0_11
+                    loop = [l for lab, body in blocks
+                            if lab == h or (body and f"in Loop: Header={key}" in body[0]) for l in body]
+                    if any("v_mfma" in l for l in loop):
+                        out.append(sum("s_waitcnt vmcnt(0)" in l for l in loop))
+            cur, blocks = m.group(1), [("", [])]
+            continue
+        b = re.match(r"^(\.LBB\w+):|^; %(bb\.\w+):", line)
+        if b:
+            blocks.append((b.group(1) or b.group(2), [line]))
+        elif blocks:
+            blocks[-1][1].append(line)
+    return out
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="HIP toolchain not installed")
+def test_split_k_loop_has_one_full_drain(tmp_path):
+    """The K-split kernel's K loop (the two-stage 256x256 tile) keeps its one
+    full drain per chunk; the waits of its partial-sum exchange come after
+    the loop."""
+    asm_path = tmp_path / "gemm.s"
+    cmd = [fgbuild.hipcc(), *[a for a in fgbuild.COMMON if a != "-fPIC"], "--cuda-device-only", "-S", GEMM_SRC,
+           "-o", str(asm_path)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    loops = mfma_loop_drains(asm_path.read_text(), "_ZN5fgfp821gemm_nt_splitk_kernel")
+    assert loops == [1], loops

@@ -376,3 +376,64 @@ def test_empty_problems_through_the_binding():
     out = fg.moe_fp8_layer(torch.empty((0, 256), dtype=torch.bfloat16, device=dev), idx, wts, w1, w2)
     torch.cuda.synchronize()
     assert out.shape == (0, 256)
+
+
+# ------------------------------------------------ K split (fp8_gemm_nt_ws)
+def _split_run(q, sa, qb, sb, m, n, ws):
+    d = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.fp8_gemm_nt((q, sa), (qb, sb), d, workspace=ws)
+    return d
+
+
+def _counters_zero(ws, m, n):
+    tiles = -(-m // 256) * -(-n // 256)
+    return bool((ws[: 8 * tiles].view(torch.int32) == 0).all())
+
+
+def test_split_k_down_projection_full():
+    """The down projection (2048 x 4096 x 12288) through fp8_gemm_nt_ws, whose
+    plan splits K over two workgroups per 256x256 tile: every output against
+    the oracle, the same bits on a second call, and the workspace's counters
+    back to zero after each call."""
+    (lin,) = workloads.prefill_linears(names=["down"])
+    assert "splitk2" in fg.describe_gemm(lin.m, lin.n, lin.k)
+    x = to_dev_bf16(lin.a)
+    w = to_dev_bf16(lin.b)
+    q, sa = fg.quantize_fp8_groups(x)
+    qb, sb = fg.quantize_fp8_blocks(w)
+    ws = fg.gemm_workspace(lin.m, lin.n, lin.k)
+    assert ws is not None
+    d1 = _split_run(q, sa, qb, sb, lin.m, lin.n, ws)
+    torch.cuda.synchronize()
+    assert _counters_zero(ws, lin.m, lin.n)
+    d2 = _split_run(q, sa, qb, sb, lin.m, lin.n, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16)), "two calls differ"
+    assert _counters_zero(ws, lin.m, lin.n)
+    check_full(lin, q, sa, qb, sb, d1, "down, K split")
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 520, 768), (256, 256, 256), (513, 1000, 1408), (17, 384, 640),
+                                   (1000, 136, 2304)])
+def test_split_k_forced_ragged_shapes(m, n, k, monkeypatch):
+    """The K split forced (FGFP8_SPLITK=1) on ragged M, N and on K of two
+    chunks (one per half): every output against the oracle, twice, with the
+    counters back to zero; a workspace below the required size runs the
+    unsplit plan, bit for bit."""
+    monkeypatch.setenv("FGFP8_SPLITK", "1")
+    lin = workloads.random_linear(m, n, k, seed=m * 3 + n + k)
+    print(f"split {m}x{n}x{k}: {fg.describe_gemm(m, n, k)}", flush=True)
+    q, sa, qb, sb, d0 = gpu_hot_path(lin)
+    nbytes = fg.fp8_gemm_nt_workspace_bytes(m, n, k)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    d1 = _split_run(q, sa, qb, sb, m, n, ws)
+    d2 = _split_run(q, sa, qb, sb, m, n, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+    assert _counters_zero(ws, m, n)
+    check_sampled(lin, q, sa, qb, sb, d1, np.arange(m), np.arange(-(-n // 128)), f"split {m}x{n}x{k}")
+    small = torch.zeros(nbytes - 256, dtype=torch.uint8, device="cuda")
+    d3 = _split_run(q, sa, qb, sb, m, n, small)
+    torch.cuda.synchronize()
+    assert torch.equal(d3.view(torch.int16), d0.view(torch.int16)), "an undersized workspace must run fp8_gemm_nt"
