@@ -34,7 +34,9 @@ operands), decode (M=1 linears),
 moe (contiguous grouped, 32 experts), moe_masked (masked grouped over a
 decode-time dispatch buffer), moe_layer (the whole MoE layer: routing, gather,
 two grouped products, SiLU-times-up and combine, 8192 tokens top-4 over 32
-experts, H = 7168, I = 2048), square8k, square16k, copy (counter calibration).
+experts, H = 7168, I = 2048), square8k, square16k, copy (counter calibration),
+stream (the plain streaming read at 48 MiB and 768 MiB: the HBM ceiling at the
+decode weight's size).
 """
 
 from __future__ import annotations
@@ -71,8 +73,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy"])
+    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy", "stream"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--trials", type=int, default=TRIALS, help="timed trials of --steps steps each")
+    p.add_argument("--no-extra", action="store_true",
+                   help="prefill: skip the 8192^3, 16384^2x8192 and 32-expert grouped objects")
     p.add_argument("--moe-unfused", action="store_true",
                    help="moe_layer: run the gate_up product and SiLU.mul+quantize as two launches")
     p.add_argument("--no-decode", action="store_true")
@@ -109,7 +114,11 @@ class PreparedLinear:
         self.sa = torch.empty((k // 128, fg.padded_rows(m)), dtype=torch.int32 if recipe == "mx" else torch.float32,
                               device="cuda")
         self.d = torch.empty((m, lin.n), dtype=torch.bfloat16, device="cuda")
-        self.plan = fg.describe_gemm(m, lin.n, k)
+        # the product's workspace (allocated once, zero-filled), for shapes
+        # whose plan splits K over two workgroups per tile
+        self.ws = fg.gemm_workspace(m, lin.n, k) if recipe == "fp32" else None
+        plan = fg.describe_gemm(m, lin.n, k)
+        self.plan = plan.split("with workspace: ")[1] if self.ws is not None else plan.split(";")[0]
         self.kernel = self.plan.split()[0]
 
     def run(self, fg, ev=None):
@@ -126,7 +135,7 @@ class PreparedLinear:
         if self.recipe == "mx":
             fg.fp8_gemm_nt_mx((self.q, self.sa), (self.qb, self.sb), self.d)
         else:
-            fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d, ue8m0=self.ue8m0)
+            fg.fp8_gemm_nt((self.q, self.sa), (self.qb, self.sb), self.d, ue8m0=self.ue8m0, workspace=self.ws)
         if ev is not None and ev[2] is not None:
             ev[2].record()
 
@@ -211,6 +220,109 @@ class GpuAhead:
         self.torch.cuda._sleep(int(self.cycles_per_s * seconds))
 
 
+TRIALS = 5  # timed trials per measurement; min and median are reported
+
+
+class SmiSampler:
+    """The GPU's graphics clock and socket power as amdsmi reports them,
+    polled every millisecond from a host thread, keeping only the samples
+    taken while a window is open.  summary() is None where amdsmi is not
+    usable."""
+
+    def __init__(self):
+        self.samples = []
+        self._open = False
+        self._stop = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        except Exception as e:  # not on every box
+            log(f"amdsmi unavailable: {e!r}")
+            self._smi = None
+
+    def __enter__(self):
+        import threading
+
+        if self._smi is None:
+            return self
+        self._stop = threading.Event()
+
+        def poll():
+            while not self._stop.is_set():
+                if self._open:
+                    try:
+                        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                        if self._open:
+                            self.samples.append((m.get("current_gfxclk"), m.get("current_socket_power"), time.time()))
+                    except Exception:
+                        pass
+                time.sleep(0.001)
+
+        self._t = threading.Thread(target=poll, daemon=True)
+        self._t.start()
+        return self
+
+    def window_open(self):
+        self._open = True
+
+    def window_close(self):
+        self._open = False
+
+    def __exit__(self, *exc):
+        if self._stop is not None:
+            self._stop.set()
+            self._t.join()
+
+    def summary(self):
+        clk = [x[0] for x in self.samples if isinstance(x[0], (int, float)) and x[0] > 0]
+        pw = [x[1] for x in self.samples if isinstance(x[1], (int, float)) and x[1] > 0]
+        if not clk:
+            return None
+        return {"source": "amdsmi gpu_metrics current_gfxclk / current_socket_power, sampled every ~1 ms inside "
+                          "the timed trials",
+                "samples": len(clk), "gfxclk_mhz_median": float(np.median(clk)), "gfxclk_mhz_min": float(min(clk)),
+                "gfxclk_mhz_max": float(max(clk)),
+                "socket_power_w_median": float(np.median(pw)) if pw else None,
+                "socket_power_w_max": float(max(pw)) if pw else None}
+
+
+def sustained_clock(step, torch, step_s: float, seconds: float = 1.2, settle: float = 0.3):
+    """The GPU clock and power under a sustained run of `step`: enough steps
+    for `seconds` of GPU time (`step_s` each) are enqueued back to back after
+    the timed trials, and amdsmi is sampled until they finish, keeping the
+    samples after the first `settle` seconds.  amdsmi's metrics refresh far
+    more slowly than the ~10 ms timed trials last, so the clock is read over
+    a run long enough for them to follow."""
+    smi = SmiSampler()
+    if smi._smi is None:
+        return None
+    torch.cuda.synchronize()
+    smi.__enter__()
+    smi.window_open()
+    t0 = time.time()
+    for _ in range(max(1, int(seconds / max(step_s, 1e-6)))):
+        step()
+    torch.cuda.synchronize()
+    smi.window_close()
+    smi.__exit__()
+    smi.samples = [x for x in smi.samples if x[2] >= t0 + settle]
+    out = smi.summary()
+    if out is not None:
+        out["source"] = (f"amdsmi gpu_metrics current_gfxclk / current_socket_power, sampled every ~1 ms over "
+                         f"~{seconds - settle:.1f} s of back-to-back steps right after the timed trials")
+    return out
+
+
+def trial_stats(seconds: list, steps: int) -> dict:
+    ms = sorted(x / steps * 1e3 for x in seconds)
+    return {"trials": len(ms), "ms_per_step": [round(x, 4) for x in ms], "ms_per_step_min": round(ms[0], 4),
+            "ms_per_step_median": round(float(np.median(ms)), 4)}
+
+
 def host_enqueue_seconds(fn, torch, reps=3):
     """Host time to enqueue fn() (no synchronisation inside), max of reps."""
     worst = 0.0
@@ -267,11 +379,13 @@ def dominant_kernel(per) -> str:
     return max(total, key=total.get)
 
 
-def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32"):
-    """Warm-up, the per-linear pass, then the timed region: `steps` steps
-    bracketed by two events, with events recorded only around the launches of
-    the dominant kernel (its mean launch duration for the roofline).  Returns
-    (preps, elapsed seconds, per-linear rows, timed dominant-kernel launch)."""
+def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32", trials=TRIALS):
+    """Warm-up, the per-linear pass, then `trials` timed regions: `steps`
+    steps each, bracketed by two events, with events recorded only around
+    the launches of the dominant kernel (its mean launch duration for the
+    roofline); then the GPU clock under a sustained run of the step.  Returns
+    (preps, per-trial elapsed seconds, per-linear rows, timed dominant-kernel
+    launches, clock summary)."""
     preps = [PreparedLinear(l, fg, torch, recipe) for l in linears]
     torch.cuda.synchronize()
     for _ in range(warmup):
@@ -283,26 +397,27 @@ def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32"):
     host_step = host_enqueue_seconds(lambda: [p.run(fg, ev) for p, ev in zip(preps, probe)], torch)
     per = per_linear_pass(preps, steps, fg, torch, ahead, host_step)
     dom = dominant_kernel(per)
-    dom_ev = [[(None, HipEvent(torch), HipEvent(torch)) if r["_kernel"] == dom else None for r in per]
-              for _ in range(steps)]
-    e_first, e_last = HipEvent(torch), HipEvent(torch)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ahead.spin(1.5 * host_step * steps + 2e-3)
-    e_first.record()
-    for s in range(steps):
-        for p, ev in zip(preps, dom_ev[s]):
-            p.run(fg, ev)
-    e_last.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    elapsed = e_first.elapsed_time(e_last) * 1e-3
-    launches = [ev[1].elapsed_time(ev[2]) * 1e-3 for row in dom_ev for ev in row if ev is not None]
+    elapsed, launches = [], []
+    for _ in range(trials):
+        dom_ev = [[(None, HipEvent(torch), HipEvent(torch)) if r["_kernel"] == dom else None for r in per]
+                  for _ in range(steps)]
+        e_first, e_last = HipEvent(torch), HipEvent(torch)
+        torch.cuda.synchronize()
+        ahead.spin(1.5 * host_step * steps + 2e-3)
+        e_first.record()
+        for s in range(steps):
+            for p, ev in zip(preps, dom_ev[s]):
+                p.run(fg, ev)
+        e_last.record()
+        torch.cuda.synchronize()
+        elapsed.append(e_first.elapsed_time(e_last) * 1e-3)
+        launches += [ev[1].elapsed_time(ev[2]) * 1e-3 for row in dom_ev for ev in row if ev is not None]
     timed = {"kernel": dom, "mean_s": float(np.mean(launches)), "launches": len(launches)}
-    log(f"timed region: {elapsed * 1e3 / steps:.4f} ms/step on the GPU (events); host enqueue {host_step * 1e3:.3f} ms/step; "
-        f"wall {wall * 1e3:.2f} ms including the spin; {dom}: {len(launches)} launches timed, "
-        f"mean {timed['mean_s'] * 1e6:.2f} us")
-    return preps, elapsed, per, timed
+    clock = sustained_clock(lambda: [p.run(fg) for p in preps], torch, float(np.median(elapsed)) / steps)
+    log(f"timed: {steps} steps x {trials} trials, ms/step " + ", ".join(f"{e * 1e3 / steps:.4f}" for e in elapsed)
+        + f"; host enqueue {host_step * 1e3:.3f} ms/step; {dom}: {len(launches)} launches timed, "
+        f"mean {timed['mean_s'] * 1e6:.2f} us; gpu clock {clock}")
+    return preps, elapsed, per, timed, clock
 
 
 # The sources the tile GEMM kernels are built from.
@@ -357,7 +472,8 @@ def roofline_of(per, timed=None):
     flops_per_launch = e["flops"] / e["n"]
     mean_s = timed["mean_s"] if timed is not None else e["s"] / e["n"]
     achieved = flops_per_launch / mean_s / 1e12
-    kernel = f"gemm_nt_kernel<{name.replace(' mx', ', mx')}>"
+    kernel = (f"gemm_nt_splitk_kernel<{name.replace('_splitk2', '')}>" if name.endswith("_splitk2")
+              else f"gemm_nt_kernel<{name.replace(' mx', ', mx')}>")
     return {
         "bound": "mfma",
         "kernel": kernel,
@@ -376,8 +492,33 @@ def roofline_of(per, timed=None):
     }
 
 
+def bench_object(lin, steps, warmup, fg, torch, trials=TRIALS) -> dict:
+    """One linear as a bench object of its own: act-quant + product per step,
+    `trials` timed regions of `steps` steps, min and median step time, the
+    clock, and the product kernel's roofline."""
+    preps, elapsed, per, timed, clock = bench_linears([lin], steps, warmup, fg, torch, trials=trials)
+    del preps
+    st = trial_stats(elapsed, steps)
+    r = per[0]
+    return {
+        "workload": lin.name,
+        "m": lin.m, "n": lin.n, "k": lin.k,
+        "kernel": r["kernel"],
+        "steps_are": "act-quant (1x128) + block-scaled FP8 GEMM (bf16 out); weight pre-quantized",
+        "ms_min": st["ms_per_step_min"],
+        "ms_median": st["ms_per_step_median"],
+        "tflops_median": round(lin.flops / (st["ms_per_step_median"] * 1e-3) / 1e12, 1),
+        "frac_of_fp8_peak": round(lin.flops / (st["ms_per_step_median"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "quant_us": round(r["quant_us"], 2),
+        "gemm_us": round(r["gemm_us"], 2),
+        "timing": st,
+        "gpu_clock": clock,
+        "roofline": roofline_of(per, timed),
+    }
+
+
 # ------------------------------------------------------------------- decode
-def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288)), sets=8, reps=50):
+def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288)), sets=8, reps=50, trials=TRIALS):
     """Act-quant + product per call at M = 1, 4, 16; 8 rotating weight sets
     (8 x 50 MB > 256 MB last-level cache) replayed from a HIP graph, and
     eagerly.  M <= 4 runs the fused kernel; M = 16 the quantizer and the
@@ -426,12 +567,15 @@ def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288))
         for _ in range(3):
             g.replay()
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_s = e0.elapsed_time(e1) * 1e-3 / (reps * sets)
+        graph_trials = []
+        for _ in range(trials):
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_trials.append(e0.elapsed_time(e1) * 1e-3 / (reps * sets))
+        graph_s = float(np.median(graph_trials))
         nbytes = quant_bytes(m, k) + gemm_bytes(m, n, k)
         out.append(
             {
@@ -441,6 +585,8 @@ def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288))
                 "kernel": ("fused act-quant + " if fused else "act-quant kernel + ") + fg.describe_gemm(m, n, k),
                 "bytes_per_call": nbytes,
                 "graph_us": round(graph_s * 1e6, 3),
+                "graph_us_min": round(min(graph_trials) * 1e6, 3),
+                "graph_timing": f"median and min of {trials} trials of {reps} replays of {sets} calls",
                 "graph_gbs": round(nbytes / graph_s / 1e9, 1),
                 "graph_frac_hbm": round(nbytes / graph_s / 1e9 / PEAK_HBM_GBS, 4),
                 "eager_us": round(eager_s * 1e6, 3),
@@ -449,6 +595,54 @@ def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288))
             }
         )
         del weights, qb0, sb0, g
+        torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------ streaming ceiling
+def bench_stream(fg, torch, sizes=(50_331_648, 805_306_368), sets=8, reps=50, trials=TRIALS):
+    """The plain streaming read (fgfp8_stream_read) at the decode weight's
+    size (48 MiB, 8 rotating buffers so that nothing is served from the
+    256 MB last-level cache, replayed from a HIP graph as the decode linears
+    are) and at 768 MiB: the rate a kernel that only reads contiguous memory
+    reaches, the practical ceiling of the HBM-bound calls at that size."""
+    out = []
+    sink = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    for nbytes in sizes:
+        nsets = sets if nbytes < (256 << 20) else 1
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(nsets)]
+
+        def one_round():
+            for b in bufs:
+                fg.stream_read(b, sink)
+
+        for _ in range(3):
+            one_round()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            one_round()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                one_round()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r = reps if nbytes < (256 << 20) else max(reps // 5, 4)
+        res = []
+        for _ in range(trials):
+            e0.record()
+            for _ in range(r):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e-3 / (r * nsets))
+        t = float(np.median(res))
+        out.append({"bytes": nbytes, "buffers": nsets, "us": round(t * 1e6, 3), "us_min": round(min(res) * 1e6, 3),
+                    "gbs": round(nbytes / t / 1e9, 1), "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)})
+        log(f"stream read {nbytes / 2**20:.0f} MiB: {out[-1]['us']} us, {out[-1]['gbs']} GB/s")
+        del bufs, g
         torch.cuda.empty_cache()
     return out
 
@@ -475,12 +669,17 @@ def cpu_baseline(linears, rows=None, cols=None):
         oracle.gemm_nt(q, sa, qb, sb)
         flops += 2 * a.shape[0] * qb.shape[0] * a.shape[1]
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')}, {i.get('threading_layer')})"
+            for i in info if i.get("user_api") == "blas"]
     m = prepared[0][0].shape[0]
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "blas": ", ".join(blas) or None,
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": (f"one whole step: {m} rows x all output columns of each of the {len(linears)} linears"
                    if cols is None else f"{m} rows x the first min(N, {cols}) output columns of each of the "
@@ -528,6 +727,9 @@ def main():
     if args.workload == "copy":
         copy_calibration(args, torch)
         return
+    if args.workload == "stream":
+        print(json.dumps({"workload": "stream_read", "results": bench_stream(fg, torch, trials=args.trials)}))
+        return
     recipe = {"prefill_ue8m0": "ue8m0", "prefill_mx": "mx"}.get(args.workload, "fp32")
     if args.workload in ("prefill", "prefill_ue8m0", "prefill_mx"):
         linears = workloads.prefill_linears()
@@ -553,27 +755,54 @@ def main():
 
     if linears is not None:
         log(f"workload {workload}: " + ", ".join(f"{l.name} [{fg.describe_gemm(l.m, l.n, l.k)}]" for l in linears))
-        preps, elapsed, per, timed = bench_linears(linears, args.steps, args.warmup, fg, torch, recipe=recipe)
+        preps, elapsed, per, timed, clock = bench_linears(linears, args.steps, args.warmup, fg, torch,
+                                                            recipe=recipe, trials=args.trials)
         total_flops = sum(l.flops for l in linears)
-        ms_per_step = elapsed / args.steps * 1e3
-        value = total_flops * args.steps / elapsed / 1e12
+        trials = trial_stats(elapsed, args.steps)
+        ms_per_step = trials["ms_per_step_median"]
+        value = total_flops / (ms_per_step * 1e-3) / 1e12
         gemm_s = sum(r["_gemm_s"] for r in per)
         roof = roofline_of(per, timed)
         del preps
     elif args.workload == "moe_masked":
         value, ms_per_step, per, roof, gemm_s, total_flops = bench_masked(args, fg, torch, workloads)
+        trials = clock = None
     elif args.workload == "moe_layer":
         value, ms_per_step, per, roof, gemm_s, total_flops = bench_moe_layer(args, fg, torch, workloads)
+        trials = clock = None
     else:
-        value, ms_per_step, per, roof, gemm_s, total_flops = bench_moe(args, fg, torch, workloads)
+        obj = bench_moe(args, fg, torch, workloads)
+        value, ms_per_step, per, roof, gemm_s, total_flops = (obj["tflops_useful_median"], obj["ms_median"],
+                                                             obj["rows"], obj["roofline"], obj["_gemm_s"],
+                                                             obj["_flops"])
+        trials, clock = obj["timing"], obj["gpu_clock"]
     torch.cuda.empty_cache()
 
-    decode = None
+    extra = {}
+    if args.workload == "prefill" and not args.no_extra:
+        # The other two shapes the targets name, timed as objects of their own
+        # (each: act-quant + product per step, trials, clock, roofline).
+        for key, lin in (("square_8192", workloads.square_linear(8192, 8192, 8192)),
+                         ("square_16384x16384x8192", workloads.square_linear(16384, 16384, 8192))):
+            log(f"{key}: {fg.describe_gemm(lin.m, lin.n, lin.k)}")
+            extra[key] = bench_object(lin, min(args.steps, 10), args.warmup, fg, torch, args.trials)
+            del lin
+            torch.cuda.empty_cache()
+        extra["moe_grouped_zipf32"] = bench_moe(args, fg, torch, workloads, steps=min(args.steps, 10))
+        for v in extra.values():
+            for k in [k for k in v if k.startswith("_") or k == "rows"]:
+                del v[k]
+        torch.cuda.empty_cache()
+
+    decode = stream = None
     if args.workload in ("prefill", "decode") and not args.no_decode:
-        decode = bench_decode(fg, torch, reps=args.decode_reps)
+        decode = bench_decode(fg, torch, reps=args.decode_reps, trials=args.trials)
         for r in decode:
             log(f"decode M={r['m']} N={r['n']} K={r['k']}: graph {r['graph_us']} us {r['graph_gbs']} GB/s; "
                 f"eager {r['eager_us']} us")
+        stream = bench_stream(fg, torch, sizes=(50_331_648,), trials=args.trials)[0]
+        for r in decode:
+            r["frac_of_stream_read_48MiB"] = round(r["graph_gbs"] / stream["gbs"], 4)
 
     cpu = None
     if args.workload == "prefill" and not args.no_cpu_baseline:
@@ -607,15 +836,25 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "decode": decode,
+        "stream_ceiling": stream,
+        "timing": trials,
+        "gpu_clock": clock,
+        **extra,
     }
     print(json.dumps(line), flush=True)
 
 
-def bench_moe(args, fg, torch, workloads):
+def bench_moe(args, fg, torch, workloads, steps=None) -> dict:
+    """The M-grouped contiguous product on the 32-expert Zipf(1.1) top-4
+    layout (K = 7168, N = 4096): one step = act-quant of the padded layout +
+    the grouped product; `args.trials` timed regions; TFLOP/s on the useful
+    (routed-row) FLOPs, padded FLOPs beside it."""
+    steps = steps or args.steps
     g = workloads.moe_grouped()
     x = dev_bf16(g.a, torch)
     q, sa = fg.quantize_fp8_groups(x)
     w = dev_bf16(g.b.reshape(g.num_groups * g.n, g.k), torch)
+    g.b = None
     qb, sb = fg.quantize_fp8_blocks(w)
     del w
     qb = qb.view(g.num_groups, g.n, g.k)
@@ -636,30 +875,55 @@ def bench_moe(args, fg, torch, workloads):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[HipEvent(torch) for _ in range(3)] for _ in range(args.steps)]
     ahead = GpuAhead(torch)
     probe = [HipEvent(torch) for _ in range(3)]
     host_step = host_enqueue_seconds(lambda: step(probe), torch)
-    e_first, e_last = HipEvent(torch), HipEvent(torch)
-    torch.cuda.synchronize()
-    ahead.spin(1.5 * host_step * args.steps + 2e-3)
-    e_first.record()
-    for s in range(args.steps):
-        step(evs[s])
-    e_last.record()
-    torch.cuda.synchronize()
-    elapsed = e_first.elapsed_time(e_last) * 1e-3
-    gt = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    qt = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    elapsed, gts, qts = [], [], []
+    for _ in range(args.trials):
+        evs = [[HipEvent(torch) for _ in range(3)] for _ in range(steps)]
+        e_first, e_last = HipEvent(torch), HipEvent(torch)
+        torch.cuda.synchronize()
+        ahead.spin(1.5 * host_step * steps + 2e-3)
+        e_first.record()
+        for s in range(steps):
+            step(evs[s])
+        e_last.record()
+        torch.cuda.synchronize()
+        elapsed.append(e_first.elapsed_time(e_last) * 1e-3)
+        gts += [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
+        qts += [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
+    clock = sustained_clock(step, torch, float(np.median(elapsed)) / steps)
+    gt, qt = float(np.mean(gts)), float(np.mean(qts))
+    st = trial_stats(elapsed, steps)
     flops = g.useful_flops
-    per = [{"name": g.name, "m_pad": g.m, "n": g.n, "k": g.k, "groups": g.num_groups, "quant_us": qt * 1e6,
-            "gemm_us": gt * 1e6, "gemm_tflops_useful": flops / gt / 1e12,
-            "gemm_tflops_padded": 2 * g.m * g.n * g.k / gt / 1e12, "_gemm_s": gt}]
-    roof = {"bound": "mfma", "kernel": "grouped_gemm_nt_kernel<tile128x256_w2x4>", "achieved": round(flops / gt / 1e12, 1),
-            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(flops / gt / 1e12 / PEAK_FP8_TFLOPS, 4),
-            "traffic": None, "mean_launch_us": round(gt * 1e6, 2)}
-    return flops * args.steps / elapsed / 1e12, elapsed / args.steps * 1e3, per, roof, gt, flops
-
+    padded = 2 * g.m * g.n * g.k
+    kernel = "grouped_gemm_nt_kernel<tile128x256_w2x4>"
+    log(f"moe grouped: ms/step {st['ms_per_step']}; gemm mean {gt * 1e6:.1f} us")
+    rows = [{"name": g.name, "m_pad": g.m, "n": g.n, "k": g.k, "groups": g.num_groups, "quant_us": qt * 1e6,
+             "gemm_us": gt * 1e6, "gemm_tflops_useful": flops / gt / 1e12, "gemm_tflops_padded": padded / gt / 1e12,
+             "_gemm_s": gt}]
+    nbytes = (g.m * g.k + 4 * g.m * (g.k // 128) + g.num_groups * (g.n * g.k + 4 * (g.n // 128) * (g.k // 128))
+              + 2 * g.m * g.n)
+    roof = {"bound": "mfma", "kernel": kernel, "achieved": round(flops / gt / 1e12, 1), "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(flops / gt / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": recorded_traffic(kernel),
+            "algorithmic_gflop_per_launch": round(flops / 1e9, 3),
+            "algorithmic_flops_are": "useful: 2 x routed rows x N x K (padding rows excluded)",
+            "padded_gflop_per_launch": round(padded / 1e9, 3), "algorithmic_bytes_per_launch": nbytes,
+            "mean_launch_us": round(gt * 1e6, 2), "launches": len(gts),
+            "launch_timing": "HIP events around each launch of the grouped product inside the timed trials"}
+    ms = st["ms_per_step_median"]
+    return {
+        "workload": g.name, "m_pad": g.m, "routed_rows": int(g.sizes.sum()), "n": g.n, "k": g.k,
+        "groups": g.num_groups, "kernel": kernel,
+        "steps_are": STEPS_ARE["moe"],
+        "ms_min": st["ms_per_step_min"], "ms_median": ms,
+        "tflops_useful_median": round(flops / (ms * 1e-3) / 1e12, 1),
+        "tflops_padded_median": round(padded / (ms * 1e-3) / 1e12, 1),
+        "gemm_us": round(gt * 1e6, 2), "gemm_tflops_useful": round(flops / gt / 1e12, 1),
+        "gemm_tflops_padded": round(padded / gt / 1e12, 1), "quant_us": round(qt * 1e6, 2),
+        "timing": st, "gpu_clock": clock, "roofline": roof, "rows": rows,
+        "_gemm_s": gt, "_flops": flops,
+    }
 
 
 def bench_masked(args, fg, torch, workloads):

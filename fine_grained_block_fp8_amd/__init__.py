@@ -52,6 +52,7 @@ _lib.quantize_fp8_groups_masked.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _fp
 _lib.quantize_fp8_groups_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_blocks_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
 _lib.fp8_gemm_nt_ue8m0.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp]
+_lib.fgfp8_stream_read.argtypes = [_vp, _i64, _vp, _i64, _vp]
 _lib.fp8_gemm_nt_ws.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
 _lib.fp8_gemm_nt_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.fp8_gemm_nt_workspace_bytes.restype = ctypes.c_int64
@@ -78,7 +79,7 @@ for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_gr
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
               "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked",
-              "moe_gather_quantize_tokens", "moe_route_contiguous_noalloc", "fp8_gemm_nt_ws"):
+              "moe_gather_quantize_tokens", "moe_route_contiguous_noalloc", "fp8_gemm_nt_ws", "fgfp8_stream_read"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -203,6 +204,14 @@ def quantize_fp8_blocks(w: torch.Tensor, out=None, ue8m0: bool = False):
         sb = torch.empty((-(-n // GROUP), k // GROUP if k % GROUP == 0 else 0), dtype=torch.float32, device=w.device)
     else:
         q, sb = out
+        _need(q, "q", _FP8, 2)
+        _need(sb, "sb", (torch.float32,), 2)
+        if tuple(q.shape) != (n, k):
+            raise ValueError(f"q must be [{n}, {k}]")
+        if k % GROUP == 0 and tuple(sb.shape) != (-(-n // GROUP), k // GROUP):
+            raise ValueError(f"sb must be [{-(-n // GROUP)}, {k // GROUP}]")
+        if q.device != w.device or sb.device != w.device:
+            raise ValueError("q and sb must be on w's device")
     fn = _lib.quantize_fp8_blocks_ue8m0 if ue8m0 else _lib.quantize_fp8_blocks
     _check(fn(_ptr(w), n, k, _ptr(q), _ptr(sb), _stream(w)))
     return q, sb
@@ -663,6 +672,15 @@ def moe_fp8_layer(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.T
     return moe_combine(y, row_of, topk_weights)
 
 
+def stream_read(src: torch.Tensor, out: torch.Tensor) -> None:
+    """Measurement aid: read all of src (a contiguous device tensor whose
+    size is a multiple of 32 KiB) once; out (uint8, >= 4096 bytes) receives
+    XORs of what was read."""
+    if not (src.is_cuda and src.is_contiguous() and out.is_cuda and out.dtype == torch.uint8):
+        raise ValueError("src must be a contiguous device tensor and out a uint8 device tensor")
+    _check(_lib.fgfp8_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(out), out.numel(), _stream(src)))
+
+
 def describe_gemm(m: int, n: int, k: int) -> str:
     buf = ctypes.create_string_buffer(128)
     _check(_lib.fgfp8_describe_gemm(m, n, k, buf, 128))
@@ -684,6 +702,7 @@ __all__ = [
     "fp8_linear_nt",
     "fp8_gemm_nt_workspace_bytes",
     "gemm_workspace",
+    "stream_read",
     "last_error",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",

@@ -528,6 +528,19 @@ int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, 
   return launched(fgfp8::launch_gemm(plan, q_e4m3, sa, sa_ld, b_e4m3, sb, d_bf16, m, n, k, (hipStream_t)stream), who);
 }
 
+int fgfp8_stream_read(const void* src, int64_t bytes, void* out, int64_t out_bytes, void* stream) {
+  const char* who = "fgfp8_stream_read";
+  const int64_t unit = fgfp8::stream_read_unit_bytes();
+  if (bytes < 0 || bytes % unit != 0 || out_bytes < 4096)
+    return fail(FGFP8_EINVAL, "%s: bytes=%lld must be a multiple of %lld and out_bytes >= 4096", who,
+                (long long)bytes, (long long)unit);
+  if (bytes == 0) return FGFP8_OK;
+  if (!src || !out) return fail(FGFP8_EINVAL, "%s: null pointer", who);
+  if (!aligned16(src) || !aligned16(out)) return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
+  if (int rc = check_device(who)) return rc;
+  return launched(fgfp8::launch_stream_read(src, bytes, out, out_bytes, (hipStream_t)stream), who);
+}
+
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len) {
   if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: null or empty buffer");
   if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: bad shape");

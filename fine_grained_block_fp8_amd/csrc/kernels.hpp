@@ -103,6 +103,12 @@ hipError_t launch_masked_gemm(GemmKind kind, const void* a, const float* sa, int
                               const void* b, const float* sb, int32_t num_groups, int64_t max_m, void* d, int64_t n,
                               int64_t k, hipStream_t stream);
 
+// Streaming read (measurement aid): bytes (a multiple of
+// stream_read_unit_bytes()) of src read once; out receives one 16-byte XOR
+// per thread of a grid of at most out_bytes / 4096 workgroups.
+int64_t stream_read_unit_bytes();
+hipError_t launch_stream_read(const void* src, int64_t bytes, void* out, int64_t out_bytes, hipStream_t stream);
+
 // Mixture-of-experts layer steps around the grouped product.
 int64_t moe_route_workspace_bytes(int64_t tokens, int experts);
 hipError_t launch_moe_route(const int32_t* topk_idx, int64_t tokens, int topk, int experts, int32_t* counts,

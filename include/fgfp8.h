@@ -8,9 +8,9 @@
  * B (the weight, N x K) one FP32 scale per 128x128 block; both operands are
  * FP8 E4M3 (OCP "FN": bias 7, largest finite 448, no infinities); the product
  * is accumulated in FP32, with both scales applied once per 128-wide K chunk,
- * and written as bfloat16.  The activation is rounded to FP8 per 128 inputs
- * of a row with a scale of its own, and the activation scales are stored
- * column by column with the row count padded to a multiple of four (Linnet
+ * and written as bfloat16.  Every 128-element run of an activation row is
+ * rounded to FP8 under its own scale, and those scales are stored one K
+ * group after another with the row count rounded up to four (Linnet
  * "Backend plugins" page, module docstring of the DeepGEMM plugin source and
  * _BlockProduct.execute).
  *
@@ -59,8 +59,8 @@ enum {
  *
  * Defined by the per-(1x128) activation scales of the recipe (deepgemm-rust
  * README, "What's implemented", fp8_gemm_nt row) and the Linnet plugin's
- * rounding of "each 128 inputs of a row to FP8 with a scale of their own"
- * (Linnet "Backend plugins" page, plugin module docstring).  For row m and
+ * input rounding, one FP8 scale per 128-element run of a row (Linnet
+ * "Backend plugins" page, plugin module docstring).  For row m and
  * group g (columns 128g .. 128g+127):
  *     amax = max |x[m][k]|                       (exact, over the group)
  *     s    = fl32(amax / 448), or 1 when amax == 0
@@ -96,12 +96,12 @@ int quantize_fp8_blocks(const void* w_bf16, int64_t n, int64_t k, void* q_e4m3, 
  *     D[m][n] = sum_kb  sa[kb][m] * sb[n/128][kb] * P(m, n, kb),
  *     P(m, n, kb) = sum over the 128 k of chunk kb of a[m][k] * b[n][k],
  * with P formed in FP32 by the matrix cores for each 128-wide chunk, then
- * scaled and accumulated in FP32 registers ("per-128-block scale promotion in
- * registers", deepgemm-rust README, kernel notes under "What's implemented"),
- * and rounded once to bfloat16 (round to nearest even).  The summation order
- * inside a chunk is the hardware's; results agree with any other order to
- * FP32 rounding ("the two products differ only in the order they sum",
- * Linnet "Backend plugins" page).
+ * scaled and accumulated in FP32 registers (the scales are applied to each
+ * 128-wide block's partial in registers: deepgemm-rust README, kernel notes
+ * under "What's implemented"), and rounded once to bfloat16 (round to nearest
+ * even).  The summation order inside a chunk is the hardware's; results agree
+ * with any other order to FP32 rounding (the Linnet "Backend plugins" page
+ * notes that two such products differ only by summation order).
  *
  * a_e4m3  [m][k] E4M3, the quantized activation.
  * sa      [k/128][sa_ld] float32, MN-major activation scales (as written by
@@ -121,8 +121,8 @@ int fp8_gemm_nt(const void* a_e4m3, const float* sa, int64_t sa_ld, const void* 
  * fp8_gemm_nt accumulates all of K (a fresh FP32 partial per chunk, promoted
  * with sa * sb), and the two FP32 sums meet through the workspace and are
  * added once before the bf16 rounding.  The result is deterministic; it
- * differs from fp8_gemm_nt's only in the FP32 summation order (the two
- * products differ only in the order they sum, which the recipe allows).
+ * differs from fp8_gemm_nt's only in the FP32 summation order, which the
+ * recipe leaves free.
  * Other shapes run exactly as fp8_gemm_nt.
  *
  * workspace        device memory, 256-byte aligned, of workspace_bytes >=
@@ -433,6 +433,14 @@ const char* fgfp8_last_error(void);
  * (tuning and tests; same values).  FGFP8_PRINT_CONFIG=1 prints each call's
  * kernel choice to stderr. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
+
+/* Measurement aid: reads `bytes` of device memory at src once (bytes a
+ * multiple of 32768), with nothing else to do -- the practical ceiling of
+ * the HBM-bound calls at a given size (the decode product reads its weight
+ * once per call).  Each thread stores one 16-byte XOR of what it read into
+ * out (out_bytes >= 4096; the grid is at most out_bytes / 4096 workgroups of
+ * 256 threads), so that no load is dropped.  Pointers 16-byte aligned. */
+int fgfp8_stream_read(const void* src, int64_t bytes, void* out, int64_t out_bytes, void* stream);
 
 #ifdef __cplusplus
 }

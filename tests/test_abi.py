@@ -54,6 +54,7 @@ def test_library_exports_every_declared_function():
         "moe_route_noalloc_max_workspace_bytes",
         "fp8_gemm_nt_ws",
         "fp8_gemm_nt_workspace_bytes",
+        "fgfp8_stream_read",
     }
     lib = fg.library()
     for n in names:
