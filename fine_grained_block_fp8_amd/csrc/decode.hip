@@ -3,8 +3,8 @@
 // Same definition as the dense product (deepgemm-rust README, "What's
 // implemented" table, fp8_gemm_nt row; per-128-block scale promotion), but
 // with at most 16 activation rows the work is bound by reading B (N*K bytes)
-// from HBM: decode "re-reads the full weight tensor from HBM every generated
-// token" (AReno FP8 decode pull request, Summary).  A workgroup owns 16 output
+// from HBM: every decoded token streams the whole weight from memory again
+// (AReno FP8 decode pull request, Summary).  A workgroup owns 16 output
 // columns -- one 16-row slab of B, contiguous in memory -- and its KS waves
 // split K into contiguous chunk ranges.  Each wave issues the loads of all
 // its chunks (two 16-byte loads per lane per chunk, straight into MFMA
@@ -103,40 +103,35 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
   float sav[FUSED ? 1 : MAXC];
   float sbv = 0.0f;
   const rsrc_t rsb = make_rsrc(sbw, (uint32_t)KB * 4u);
+  // the non-fused form's activation and its scales (M rows; scale column li
+  // of chunk kb at kb * sa_ld + li)
+  const rsrc_t ra = make_rsrc(FUSED ? nullptr : Ain, FUSED ? 0u : (uint32_t)M * (uint32_t)K);
+  const rsrc_t rsa = make_rsrc(FUSED ? nullptr : SA, FUSED ? 0u : (uint32_t)((int64_t)KB * sa_ld * 4));
   // Small operands first: requests queue in order behind the weight stream,
   // so anything issued after it would arrive only when the stream has.
   auto issue = [&](int cb, int nc) {
     sbv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
         rsb, lane < nc ? (uint32_t)(cb + lane) * 4u : kOob, 0, 0));
     if (!FUSED) {
-      // A fragments and scales: only lanes of rows < M load (the texture
-      // unit then handles M lanes of each request, not 64).  The branches
-      // make the compiler wait for all of a batch's loads before its first
-      // MFMA, which costs less here than 64-lane requests would.
+      // A fragments and scales, every load issued (rows >= M and chunks past
+      // the batch get out-of-range offsets and read zeros), so that the
+      // compiler waits for each chunk's own loads rather than for the whole
+      // batch before the first MFMA.
 #pragma unroll
       for (int u = 0; u < MAXC; u++) {
-        if (u < nc) {
-          const int kb = cb + u;
-          if (row_ok) {
-            const uint8_t* p = static_cast<const uint8_t*>(Ain) + (int64_t)li * K + kb * kGroup + lg * 32;
-            a0[u] = *reinterpret_cast<const uint4*>(p);
-            a1[u] = *reinterpret_cast<const uint4*>(p + 16);
-            sav[u] = SA[(int64_t)kb * sa_ld + li];
-          } else {
-            a0[u] = make_uint4(0, 0, 0, 0);
-            a1[u] = make_uint4(0, 0, 0, 0);
-            sav[u] = 0.0f;
-          }
-        }
+        const bool ok = row_ok && u < nc;
+        const uint32_t o = ok ? (uint32_t)li * (uint32_t)K + (uint32_t)(cb + u) * 128u + (uint32_t)lg * 32u : kOob;
+        a0[u] = load_rsrc16(ra, o);
+        a1[u] = load_rsrc16(ra, ok ? o + 16u : kOob);
+        sav[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rsa, ok ? ((uint32_t)(cb + u) * (uint32_t)sa_ld + (uint32_t)li) * 4u : kOob, 0, 0));
       }
     }
 #pragma unroll
     for (int u = 0; u < MAXC; u++) {
-      if (FUSED || u < nc) {  // (the non-fused form waits for all loads anyway)
-        const uint32_t o = u < nc ? off + (uint32_t)(cb + u) * 128u : kOob;
-        b0[u] = load_rsrc16(rb, o);
-        b1[u] = load_rsrc16(rb, u < nc ? o + 16u : kOob);
-      }
+      const uint32_t o = u < nc ? off + (uint32_t)(cb + u) * 128u : kOob;
+      b0[u] = load_rsrc16(rb, o);
+      b1[u] = load_rsrc16(rb, u < nc ? o + 16u : kOob);
     }
   };
   // One MFMA per chunk into alternating partial registers, each promoted

@@ -2,10 +2,10 @@
 // with FP32 scales, for gfx950.
 //
 // Recipe: per-(1x128) activation scales and per-(128x128) weight scales
-// (deepgemm-rust README, "What's implemented" table, fp8_gemm_nt row); each
-// 128 inputs of a row rounded to FP8 with a scale of their own, the scales
-// stored column by column with rows padded to a multiple of four (Linnet
-// "Backend plugins" page, plugin module docstring).  Scale s = fl32(amax/448),
+// (deepgemm-rust README, "What's implemented" table, fp8_gemm_nt row); every
+// 128-element run of a row gets its own FP8 scale, and the scales are laid
+// out one K group after another with the row count rounded up to four
+// (Linnet "Backend plugins" page, plugin module docstring).  Scale s = fl32(amax/448),
 // 1 for an all-zero group; element code = E4M3_RNE(fl32(x / s)).  The UE8M0
 // variants round s up to a power of two (the Blackwell path's UE8M0 scale
 // factors, deepgemm-rust README key techniques) and are otherwise the same;

@@ -3,9 +3,10 @@ masked), in FP64.
 
 Test infrastructure (see the package docstring): not part of the product path.
 
-Definition (deepgemm-rust README, "What's implemented" table, fp8_gemm_nt row,
-"per-(1x128) activation scales x per-(128x128) weight scales, FP32 promotion,
-BF16 out", and the kernel notes on per-128-block scale promotion): for every
+Definition (deepgemm-rust README, "What's implemented" table, fp8_gemm_nt row:
+activation scales per 1x128 group, weight scales per 128x128 block, partials
+promoted to FP32, bfloat16 output; and the kernel notes on applying the scales
+per 128-wide block): for every
 128-wide chunk kb of K, the FP8 operands give a partial product
 
     P[m, n, kb] = sum_{k in chunk kb} dec(qa[m, k]) * dec(qb[n, k])
@@ -17,12 +18,12 @@ which is then scaled by sa[kb][m] * sb[n // 128][kb] and accumulated:
 In FP64 the partial products are exact (every E4M3 product is a multiple of
 2^-18 and |P| < 128 * 448^2 < 2^25, well inside 53 bits) and so is each scale
 product (float32 x float32), so the only roundings are one per accumulated
-term.  The pages note that two such block-scaled products "differ only in the
-order they sum" (Linnet "Backend plugins" page, module docstring of the plugin
-source): ``gemm_nt_dequantized`` is that other order (dequantize both operands,
+term.  The pages note that two such block-scaled products differ only by the
+order of their sums (Linnet "Backend plugins" page, module docstring of the
+plugin source): ``gemm_nt_dequantized`` is that other order (dequantize both operands,
 then one FP64 matrix product) and the tests check the two agree.
 
-Output rounding ("BF16 out"): ``round_to_bf16`` rounds the FP64 result once,
+Output rounding (bfloat16 output): ``round_to_bf16`` rounds the FP64 result once,
 to nearest-even, to a bfloat16 bit pattern.  It is used only for diagnostics;
 parity is judged against the FP64 result.
 """

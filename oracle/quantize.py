@@ -2,9 +2,10 @@
 
 Test infrastructure (see the package docstring): not part of the product path.
 
-The recipe ("DeepSeek recipe: per-(1x128) activation scales x per-(128x128)
-weight scales", deepgemm-rust README, "What's implemented" table, fp8_gemm_nt
-row): each 128 inputs of a row get an FP8 rounding with a scale of their own
+The recipe (the DeepSeek one the deepgemm-rust README names in its "What's
+implemented" table, fp8_gemm_nt row: activation scales per 1x128 group,
+weight scales per 128x128 block): every 128-element run of a row is rounded
+to FP8 under its own scale
 (Linnet "Backend plugins" page, module docstring of the DeepGEMM plugin
 source), and the weight has one scale per 128x128 block.  Scales are FP32, not
 powers of two: the Hopper kernels take f32 scales and the plugin asks for no
@@ -16,7 +17,7 @@ Readings where the pages are silent (each listed in the design notes):
 * an all-zero group gets s = 1;
 * the element is y = fl32(x / s), a correctly rounded float32 division (not a
   multiplication by a reciprocal), then rounded to E4M3 (``e4m3_encode``);
-* activation scales are stored "column by column" with the rows padded to a
+* activation scales are stored one K group after another (MN-major), the rows padded to a
   multiple of four (Linnet page, module docstring and the `padded` row count
   in _BlockProduct.execute): SA is float32 [K/128][sa_ld], sa_ld = roundup(M, 4),
   entry [g][m] the scale of row m's group g; entries of rows >= M unspecified

@@ -1,7 +1,8 @@
 """Comparison helpers for the GPU-vs-oracle parity tests.
 
-The GEMM result is not unique (block-scaled products "differ only in the order
-they sum", Linnet "Backend plugins" page), so it is judged by:
+The GEMM result is not unique (two block-scaled products may sum in different
+orders, which the Linnet "Backend plugins" page notes is their only
+difference), so it is judged by:
 
 * normwise relative error ||D_gpu - D64||_F / ||D64||_F <= 2e-3 (the reading
   of the 2e-3 target chosen in the design notes: a perfect bf16 rounding of

@@ -55,7 +55,10 @@ def host(t):
 @pytest.mark.parametrize(
     "tokens,topk,experts,seed",
     [(0, 4, 8, 0), (1, 1, 1, 1), (255, 2, 3, 2), (256, 8, 16, 3), (257, 4, 32, 4), (1000, 6, 256, 5),
-     (700, 8, 2048, 6), (3000, 4, 32, 7)],
+     (700, 8, 2048, 6), (3000, 4, 32, 7),
+     # expert counts that split unevenly over the offsets scan's 256 threads
+     # (runs of ceil(E/256) experts, the last threads' runs short or empty)
+     (900, 4, 257, 8), (1200, 6, 300, 9), (2500, 8, 1000, 10), (4000, 3, 2047, 11)],
 )
 def test_route_bit_exact(tokens, topk, experts, seed):
     rng = np.random.default_rng(seed)

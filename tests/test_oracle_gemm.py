@@ -1,8 +1,8 @@
 """Pins for the oracle's block-scaled product and its grouped variant.
 
 Anchors: exact rational brute force (fractions.Fraction), exact integer
-arithmetic for the FP8 partial products, the invariant the pages state ("the
-two products differ only in the order they sum", Linnet "Backend plugins"
+arithmetic for the FP8 partial products, the invariant the pages state (two
+such products differ only by summation order: Linnet "Backend plugins"
 page, module docstring of the DeepGEMM plugin source), the constant-scale
 quick start of the deepgemm-rust README (a closed form), and reductions to a
 plain matrix product.
@@ -171,6 +171,38 @@ def test_grouped_reduces_to_dense_per_group():
     # the flat (num_groups * n, k) weight form of the quick start gives the same result
     d_flat = oracle.grouped_gemm_nt(qa, sa, m_idx, qb.reshape(G * n, k), sb.reshape(G * 2, 2), G)
     assert np.array_equal(np.nan_to_num(d_flat, nan=7.0), np.nan_to_num(d, nan=7.0))
+
+
+def test_grouped_layout_matches_the_quickstart_fixture():
+    """The grouped layout and operand shapes against the deepgemm-rust
+    "Quick start" grouped example (tests/golden/grouped_quickstart_layout.json):
+    every group starts at a multiple of the fixture's alignment, b is
+    (num_groups * n, k) and sfb (num_groups * ceil(n/128), ceil(k/128));
+    the oracle accepts exactly those flat forms, and refuses a weight whose
+    rows are not a multiple of num_groups."""
+    with open(os.path.join(GOLDEN, "grouped_quickstart_layout.json")) as f:
+        fx = json.load(f)
+    align = fx["alignment"]
+    assert align == 128 and fx["b_shape"] == ["num_groups * n", "k"]
+    assert fx["sfb_shape"] == ["num_groups * ceil(n/128)", "ceil(k/128)"]
+    sizes = [3, 0, 200, 128, 1]
+    starts, padded, m_idx = workloads.grouped_layout(sizes)
+    assert np.all(starts % align == 0) and np.all(padded % align == 0)
+    assert starts.tolist() == [0, 128, 128, 384, 512] and m_idx.shape[0] == 640
+    G, n, k = len(sizes), 136, 256  # n not a multiple of 128: ceil(n/128) = 2 blocks per group
+    rng = np.random.default_rng(43)
+    qa, sa, _, _ = random_operands(rng, m_idx.shape[0], n, k)
+    qb = rng.choice(FINITE, size=(G * n, k)).astype(np.uint8)  # (num_groups * n, k)
+    sb = (rng.random((G * -(-n // 128), -(-k // 128))) + 0.5).astype(np.float32)
+    d = oracle.grouped_gemm_nt(qa, sa, m_idx, qb, sb, G)
+    for g in range(G):
+        rows = np.nonzero(m_idx == g)[0]
+        if rows.size:
+            nb = -(-n // 128)
+            ref = oracle.gemm_nt(qa[rows], sa[:, rows], qb[g * n:(g + 1) * n], sb[g * nb:(g + 1) * nb])
+            assert np.array_equal(d[rows], ref)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm_nt(qa, sa, m_idx, qb[:-1], sb, G)
 
 
 def test_grouped_with_one_group_equals_dense():
