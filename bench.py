@@ -76,6 +76,8 @@ def parse():
     p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy", "stream"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--trials", type=int, default=TRIALS, help="timed trials of --steps steps each")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the sustained run that reads the GPU clock (profiling runs)")
     p.add_argument("--no-extra", action="store_true",
                    help="prefill: skip the 8192^3, 16384^2x8192 and 32-expert grouped objects")
     p.add_argument("--moe-unfused", action="store_true",
@@ -221,6 +223,7 @@ class GpuAhead:
 
 
 TRIALS = 5  # timed trials per measurement; min and median are reported
+NO_CLOCK = False  # --no-clock
 
 
 class SmiSampler:
@@ -297,6 +300,8 @@ def sustained_clock(step, torch, step_s: float, seconds: float = 1.2, settle: fl
     samples after the first `settle` seconds.  amdsmi's metrics refresh far
     more slowly than the ~10 ms timed trials last, so the clock is read over
     a run long enough for them to follow."""
+    if NO_CLOCK:
+        return None
     smi = SmiSampler()
     if smi._smi is None:
         return None
@@ -437,10 +442,11 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the FETCH_SIZE / WRITE_SIZE
-    counter runs summarised in profiles/ (scaled by a plain-copy
-    calibration), or None when no record matches the current sources."""
+def recorded_traffic(kernel: str, shape=None):
+    """HBM bytes per launch of `kernel` (at `shape` = [m, n, k] when given)
+    from the FETCH_SIZE / WRITE_SIZE counter runs summarised in profiles/
+    (scaled by a plain-copy calibration), or None when no record matches the
+    current sources."""
     import glob
 
     want = kernel_sources_hash()
@@ -449,7 +455,8 @@ def recorded_traffic(kernel: str):
             for line in f:
                 if line.startswith("traffic-record:"):
                     rec = json.loads(line.split(":", 1)[1])
-                    if rec.get("kernel") == kernel and rec.get("sources") == want:
+                    if (rec.get("kernel") == kernel and rec.get("sources") == want
+                            and (shape is None or rec.get("shape") == list(shape))):
                         return rec["bytes_per_launch"]
     return None
 
@@ -471,6 +478,8 @@ def roofline_of(per, timed=None):
         name, e = timed["kernel"], by[timed["kernel"]]
     flops_per_launch = e["flops"] / e["n"]
     mean_s = timed["mean_s"] if timed is not None else e["s"] / e["n"]
+    shapes = {(r["m"], r["n"], r["k"]) for r in per if r["_kernel"] == name}
+    shape = next(iter(shapes)) if len(shapes) == 1 else None
     achieved = flops_per_launch / mean_s / 1e12
     kernel = (f"gemm_nt_splitk_kernel<{name.replace('_splitk2', '')}>" if name.endswith("_splitk2")
               else f"gemm_nt_kernel<{name.replace(' mx', ', mx')}>")
@@ -481,7 +490,7 @@ def roofline_of(per, timed=None):
         "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-        "traffic": recorded_traffic(kernel),
+        "traffic": recorded_traffic(kernel, shape),
         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "algorithmic_bytes_per_launch": round(e["bytes"] / e["n"]),
         "launches_per_step": e["n"],
@@ -706,7 +715,9 @@ def copy_calibration(args, torch):
 
 # --------------------------------------------------------------------- main
 def main():
+    global NO_CLOCK
     args = parse()
+    NO_CLOCK = args.no_clock
     if args.gpus != 1:
         print(
             json.dumps(
@@ -905,7 +916,8 @@ def bench_moe(args, fg, torch, workloads, steps=None) -> dict:
     nbytes = (g.m * g.k + 4 * g.m * (g.k // 128) + g.num_groups * (g.n * g.k + 4 * (g.n // 128) * (g.k // 128))
               + 2 * g.m * g.n)
     roof = {"bound": "mfma", "kernel": kernel, "achieved": round(flops / gt / 1e12, 1), "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(flops / gt / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": recorded_traffic(kernel),
+            "unit": "TFLOP/s", "frac": round(flops / gt / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "traffic": recorded_traffic(kernel, (g.m, g.n, g.k)),
             "algorithmic_gflop_per_launch": round(flops / 1e9, 3),
             "algorithmic_flops_are": "useful: 2 x routed rows x N x K (padding rows excluded)",
             "padded_gflop_per_launch": round(padded / 1e9, 3), "algorithmic_bytes_per_launch": nbytes,
