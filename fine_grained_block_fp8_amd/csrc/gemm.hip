@@ -39,6 +39,12 @@ struct Tile {
   static constexpr int STAGES = STAGES_;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
+  // Waves that copy the K chunks into LDS (the first COPY_WAVES).  In the
+  // 256x256 tile only waves 0-3 copy: waves w and w + 4 share a SIMD, and the
+  // SIMD's arbiter favours the older wave, which reaches the barrier ~30%
+  // sooner; giving it all the copy issue shortens the younger wave's chunk
+  // (measured: +2-3% on the 256x256 shapes, bit-identical results).
+  static constexpr int COPY_WAVES = (BM_ == 256 && BN_ == 256) ? 4 : WAVES;
   static constexpr int TM = BM / WAVES_M;  // wave tile rows
   static constexpr int TN = BN / WAVES_N;  // wave tile columns (inside one 128-column scale block)
   static constexpr int MT = TM / 16;
@@ -59,10 +65,11 @@ struct Tile {
   static constexpr int LDS = EPI_OFF + WAVES * TM * 4;
   static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-  // The copies of a chunk are 8-row segments dealt to the waves in turn; an
-  // uneven deal (some waves copy one segment fewer) needs the vmcnt(0) wait
-  // of the two-stage loop, which does not count copies.
-  static_assert(((BM / 8) % WAVES == 0 && (BN / 8) % WAVES == 0) || STAGES == 2, "segments divide evenly among waves");
+  // The copies of a chunk are 8-row segments dealt to the copying waves in
+  // turn; an uneven deal (some waves copy one segment fewer) needs the
+  // vmcnt(0) wait of the two-stage loop, which does not count copies.
+  static_assert(((BM / 8) % COPY_WAVES == 0 && (BN / 8) % COPY_WAVES == 0) || STAGES == 2,
+                "segments divide evenly among waves");
   static_assert(BM * 4 <= SB_IN_S, "one wave loads a stage's activation scales");
   static_assert(BN * 4 <= S_BYTES - SB_IN_S, "one wave loads a stage's MX weight scales");
   static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
@@ -113,13 +120,13 @@ __device__ __forceinline__ int b_col_of_row(int rho) {
   return w * C::TN + wave_col<C>(rl & 15, rl >> 4);
 }
 
-// All waves cooperatively copy chunk kb of the A tile, the B tile and the
-// tile's scales into one LDS stage with direct global->LDS buffer loads (1 KB
-// = 8 LDS rows per wave instruction; rows past the matrix edge read as zero).
-// Wave w copies segments w, w + WAVES, ... of A and of B (with 12 waves the
-// 32 A segments of a 256-row tile fall unevenly: waves 8-11 copy one fewer),
-// wave 0 the activation scales and wave 1 the weight scales of the tile's
-// column blocks.  voff[] holds the per-lane byte offsets of those
+// The copying waves (Tile::COPY_WAVES of them) copy chunk kb of the A tile
+// and the B tile into one LDS stage with direct global->LDS buffer loads (1
+// KB = 8 LDS rows per wave instruction; rows past the matrix edge read as
+// zero): wave w copies segments w, w + COPY_WAVES, ... of A and of B (with 12
+// waves the 32 A segments of a 256-row tile fall unevenly: waves 8-11 copy
+// one fewer).  Wave 0 copies the activation scales and wave 1 the weight
+// scales of the tile's column blocks.  voff[] holds the per-lane byte offsets of those
 // segments for chunk 0; the chunk's column offset is the scalar offset of
 // each load.  Staging the weight scales through LDS keeps scalar memory loads
 // out of the loop: their completion shares a counter with the LDS reads and
@@ -127,11 +134,19 @@ __device__ __forceinline__ int b_col_of_row(int rho) {
 // MFMA.
 template <class C>
 struct StageLoader {
+  static constexpr int CW = C::COPY_WAVES;
   static constexpr int A_SEGS = C::BM / 8, B_SEGS = C::BN / 8;
-  static constexpr int AN = (A_SEGS + C::WAVES - 1) / C::WAVES, BN_ = (B_SEGS + C::WAVES - 1) / C::WAVES,
-                       NSEG = AN + BN_;
-  static constexpr bool EVEN = A_SEGS % C::WAVES == 0 && B_SEGS % C::WAVES == 0;
-  static_assert(NSEG + 1 < 16, "a chunk's copies must fit the 4-bit vmcnt field used by the waits");
+  static constexpr int AN = (A_SEGS + CW - 1) / CW, BN_ = (B_SEGS + CW - 1) / CW, NSEG = AN + BN_;
+  static constexpr bool EVEN = A_SEGS % CW == 0 && B_SEGS % CW == 0;
+  static_assert(NSEG + 1 < 16 || C::STAGES == 2, "a chunk's copies must fit the 4-bit vmcnt field used by the waits");
+  // 256x256: segment i of a wave lies a multiple of K bytes past its first A
+  // (or B) segment, with the same swizzle, so one vector offset per operand
+  // serves all of them and the difference goes in the scalar offset.  In A,
+  // segment i is 8 * CW * i rows further; in B (LDS rows permuted as
+  // b_col_of_row: within a 128-column wave region, row 16 t + c holds column
+  // 32 (c & 3) + 8 (c >> 2) + t) it is col_delta(i) columns further.
+  static constexpr bool SOFF = C::BM == 256 && C::BN == 256 && C::TN == 128 && C::NT == 8 && 128 % (8 * CW) == 0;
+  static constexpr int col_delta(int i) { return 128 * ((8 * CW * i) / 128) + ((8 * CW * i) % 128) / 16; }
   uint8_t* lds;
   rsrc_t ra, rb, rs, rsb;
   const uint32_t* voff;
@@ -140,20 +155,22 @@ struct StageLoader {
   // 0: the weight-scale copy is one 4-byte block scale per lane; else the MX
   // recipe's packed words, 16 bytes per lane, rows sb_row_bytes apart per chunk.
   uint32_t sb_row_bytes = 0;
-  // Segment i (< NSEG) of chunk kb into `stage`; segment NSEG is the scales
-  // (wave 0 only).
+  uint32_t kdim = 0;  // K (bytes per operand row)
+  __device__ __forceinline__ bool copier() const { return wave < CW; }
+  // Segment i (< NSEG; copying waves only) of chunk kb into `stage`; segment
+  // NSEG is the scales (waves 0 and 1).
   __device__ __forceinline__ void issue(int i, int stage, int kb) const {
     const uint32_t koff = (uint32_t)kb * 128u;
     if (i < AN) {
-      if (EVEN || wave + C::WAVES * i < A_SEGS)  // wave-uniform
+      if (EVEN || wave + CW * i < A_SEGS)  // wave-uniform
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (lds_void_t*)(lds + C::A_OFF + stage * C::A_BYTES + (wave + C::WAVES * i) * 1024), 16, voff[i], koff,
-            0, 0);
+            ra, (lds_void_t*)(lds + C::A_OFF + stage * C::A_BYTES + (wave + CW * i) * 1024), 16,
+            SOFF ? voff[0] : voff[i], SOFF ? koff + (uint32_t)(8 * CW * i) * kdim : koff, 0, 0);
     } else if (i < NSEG) {
-      if (EVEN || wave + C::WAVES * (i - AN) < B_SEGS)
+      if (EVEN || wave + CW * (i - AN) < B_SEGS)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (lds_void_t*)(lds + C::B_OFF + stage * C::B_BYTES + (wave + C::WAVES * (i - AN)) * 1024), 16,
-            voff[i], koff, 0, 0);
+            rb, (lds_void_t*)(lds + C::B_OFF + stage * C::B_BYTES + (wave + CW * (i - AN)) * 1024), 16,
+            SOFF ? voff[AN] : voff[i], SOFF ? koff + (uint32_t)col_delta(i - AN) * kdim : koff, 0, 0);
     } else if (wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + C::S_OFF + stage * C::S_BYTES), 16,
                                                (uint32_t)lane * 16u, (uint32_t)kb * sa_ld_bytes, 0, 0);
@@ -165,8 +182,11 @@ struct StageLoader {
                                                16, vsb, (uint32_t)kb * sb_row_bytes, 0, 0);
   }
   __device__ __forceinline__ void all(int stage, int kb) const {
+    if (copier()) {  // wave-uniform
 #pragma unroll
-    for (int i = 0; i <= NSEG; i++) issue(i, stage, kb);
+      for (int i = 0; i < NSEG; i++) issue(i, stage, kb);
+    }
+    issue(NSEG, stage, kb);
   }
 };
 
@@ -202,12 +222,12 @@ __device__ __forceinline__ void stage_offsets(uint32_t* voff, uint32_t K, int wa
   const int r8 = lane >> 3, cs = lane & 7;
 #pragma unroll
   for (int i = 0; i < AN; i++) {
-    const int rho = (wave + C::WAVES * i) * 8 + r8;
+    const int rho = (wave + C::COPY_WAVES * i) * 8 + r8;
     voff[i] = (uint32_t)rho * K + (k_segment(cs ^ swz(rho)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < BN_; i++) {
-    const int rho = (wave + C::WAVES * i) * 8 + r8;
+    const int rho = (wave + C::COPY_WAVES * i) * 8 + r8;
     const uint32_t col = (uint32_t)b_col_of_row<C>(rho);
     voff[AN + i] = (col + (col >= (uint32_t)kGroup ? up_rows : 0u)) * K + (k_segment(cs ^ swz(rho)) << 4);
   }
@@ -270,23 +290,27 @@ __device__ __forceinline__ void read_a(const uint8_t* lds, const FragAddr& aa, u
   }
 }
 
-// Column tiles [T0, T1) of a chunk, software-pipelined one MFMA deep: MFMA i
-// is issued, then the FP32 promotion of MFMA i-1's partial runs on the VALU
-// (independent of MFMA i, so the two overlap), and the B fragment of the next
-// column tile is read one tile ahead (from LDS, or from registers when PRE).
+// Column tiles [T0, T1) of a chunk, software-pipelined two MFMAs deep: MFMA i
+// is issued, then the FP32 promotion of MFMA i-2's partial runs on the VALU
+// (independent of MFMAs i-1 and i, so they overlap), and the B fragment of
+// the next column tile is read one tile ahead (from LDS, or from registers
+// when PRE).  Each accumulator still takes its chunks' promotions in chunk
+// order, so the schedule does not change a bit of the result.
 template <class C, int T0, int T1, bool PRE, bool LD>
 __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& ba, int stage, int load_stage,
                                            const v8i_t (&af)[C::MT], const float (&sc)[C::MT], const v8i_t* pre,
                                            v4f_t (&acc)[C::MT][C::NT], const StageLoader<C>& ld, int next_kb) {
-  // With LD, the next chunk's global->LDS copies (NSEG instructions per
-  // wave) are spread over the first half of the column tiles, so that no
-  // wave stalls for long on a full vector-memory queue, and they still land
-  // well before the next barrier.
-  constexpr int NL = StageLoader<C>::NSEG, HALF = (T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1;
+  // With LD (copying waves), the next chunk's global->LDS copies (NSEG
+  // instructions per wave) are spread over the first half of the column
+  // tiles -- over all of them where only some waves copy -- so that no wave
+  // stalls for long on a full vector-memory queue, and they still land well
+  // before the next barrier.
+  constexpr int NL = StageLoader<C>::NSEG;
+  constexpr int HALF = C::COPY_WAVES < C::WAVES ? T1 - T0 : ((T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1);
   constexpr int PER = (NL + HALF - 1) / HALF;
   constexpr int N_MFMA = (T1 - T0) * C::MT;
   v8i_t bfr[2];
-  v4f_t part[2];
+  v4f_t part[3];
   bfr[0] = PRE ? pre[0] : read_b<C>(lds, ba, stage, T0);
 #pragma unroll
   for (int i = 0; i < N_MFMA; i++) {
@@ -297,20 +321,23 @@ __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& b
         if (u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
     }
     if (mt == 0 && t + 1 < T1) bfr[(u + 1) & 1] = PRE ? pre[u + 1] : read_b<C>(lds, ba, stage, t + 1);
-    part[i & 1] = mfma_fp8(bfr[u & 1], af[mt]);
-    if (i > 0) {
-      const int pu = (i - 1) / C::MT, pm = (i - 1) % C::MT;
-      promote(acc[pm][T0 + pu], part[(i - 1) & 1], sc[pm]);
+    part[i % 3] = mfma_fp8(bfr[u & 1], af[mt]);
+    if (i > 1) {
+      const int pu = (i - 2) / C::MT, pm = (i - 2) % C::MT;
+      promote(acc[pm][T0 + pu], part[(i - 2) % 3], sc[pm]);
     }
     // Keep the written order: MFMA i is issued before the promotion of
-    // partial i-1, so one wave alone issues MFMAs back to back (the VALU work
-    // of the previous partial fills the gap) instead of stalling on the
-    // result of the MFMA it just issued.
+    // partial i-2, whose MFMA has finished by then, so the promotion needs
+    // no wait states and the wave issues MFMAs back to back (promoting i-1
+    // instead costs ~100 cycles of hazard waits per chunk; measured +1-2% on
+    // the 256x256 shapes).
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    if (i > 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  promote(acc[C::MT - 1][T1 - 1], part[(N_MFMA - 1) & 1], sc[C::MT - 1]);
+  if constexpr (N_MFMA > 1)
+    promote(acc[(N_MFMA - 2) % C::MT][T0 + (N_MFMA - 2) / C::MT], part[(N_MFMA - 2) % 3], sc[(N_MFMA - 2) % C::MT]);
+  promote(acc[C::MT - 1][T1 - 1], part[(N_MFMA - 1) % 3], sc[C::MT - 1]);
 }
 
 // UE8M0 recipe: with power-of-two scales the scaling is exact, so the
@@ -332,11 +359,12 @@ __device__ __forceinline__ void read_a_ue8m0(const uint8_t* lds, const FragAddr&
   }
 }
 
-template <class C>
+template <class C, bool LD>
 __device__ __forceinline__ void mfma_tiles_ue8m0(const uint8_t* lds, const FragAddr& ba, int stage, int load_stage,
                                                  const v8i_t (&af)[C::MT], const int (&ea)[C::MT], int eb,
                                                  v4f_t (&acc)[C::MT][C::NT], const StageLoader<C>& ld, int next_kb) {
-  constexpr int NL = StageLoader<C>::NSEG, HALF = C::NT / 2 > 0 ? C::NT / 2 : 1;
+  constexpr int NL = StageLoader<C>::NSEG;
+  constexpr int HALF = C::COPY_WAVES < C::WAVES ? C::NT : (C::NT / 2 > 0 ? C::NT / 2 : 1);
   constexpr int PER = (NL + HALF - 1) / HALF;
   constexpr int N_MFMA = C::NT * C::MT;
   v8i_t bfr[2];
@@ -347,7 +375,7 @@ __device__ __forceinline__ void mfma_tiles_ue8m0(const uint8_t* lds, const FragA
     if (mt == 0) {
 #pragma unroll
       for (int q = 0; q < PER; q++)
-        if (u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
+        if (LD && u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
       if (u + 1 < C::NT) bfr[(u + 1) & 1] = read_b<C>(lds, ba, stage, u + 1);
     }
     acc[mt][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[u & 1], af[mt], acc[mt][u], 0, 0, 0, eb, 0,
@@ -380,12 +408,13 @@ __device__ __forceinline__ int read_eb_mx(const uint8_t* lds, const uint32_t (&e
   return (int)((w >> (8 * lg)) & 0xffu);
 }
 
-template <class C>
+template <class C, bool LD>
 __device__ __forceinline__ void mfma_tiles_mx(const uint8_t* lds, const FragAddr& ba, const uint32_t (&ebo)[C::NT],
                                               int stage, int load_stage, int lg, const v8i_t (&af)[C::MT],
                                               const int (&ea)[C::MT], v4f_t (&acc)[C::MT][C::NT],
                                               const StageLoader<C>& ld, int next_kb) {
-  constexpr int NL = StageLoader<C>::NSEG, HALF = C::NT / 2 > 0 ? C::NT / 2 : 1;
+  constexpr int NL = StageLoader<C>::NSEG;
+  constexpr int HALF = C::COPY_WAVES < C::WAVES ? C::NT : (C::NT / 2 > 0 ? C::NT / 2 : 1);
   constexpr int PER = (NL + HALF - 1) / HALF;
   constexpr int N_MFMA = C::NT * C::MT;
   v8i_t bfr[2];
@@ -398,7 +427,7 @@ __device__ __forceinline__ void mfma_tiles_mx(const uint8_t* lds, const FragAddr
     if (mt == 0) {
 #pragma unroll
       for (int q = 0; q < PER; q++)
-        if (u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
+        if (LD && u * PER + q < NL) ld.issue(u * PER + q, load_stage, next_kb);
       if (u + 1 < C::NT) {
         bfr[(u + 1) & 1] = read_b<C>(lds, ba, stage, u + 1);
         ebr[(u + 1) & 1] = read_eb_mx<C>(lds, ebo, stage, u + 1, lg);
@@ -722,7 +751,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   uint32_t voff[StageLoader<C>::NSEG];
   stage_offsets<C>(voff, (uint32_t)K, wave, lane, SILU ? gu.up_rows : 0u);
   const StageLoader<C> loader{lds, ra, rb, rs, rsb, voff, (uint32_t)(sa_ld * 4), vsb, wave, lane,
-                              MX ? (uint32_t)(sb_ld * 4) : 0u};
+                              MX ? (uint32_t)(sb_ld * 4) : 0u, (uint32_t)K};
   // MX: byte offsets of the packed weight-scale word each lane's B fragment
   // row refers to, per column tile.
   uint32_t ebo[C::NT];
@@ -746,9 +775,14 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   // most the copies of the chunks after it are outstanding": none with two
   // stages; with three, one chunk's NSEG segments plus the scale copy that
   // waves 0 and 1 issue.
+  // The loop is written once per copying role (CP: this wave issues
+  // segment copies), chosen once per wave, so that the loop itself has no
+  // branch around the copies.
   const int kb0 = SPLIT ? sk.kb0 : 0, kb1 = SPLIT ? sk.kb1 : KB;
   loader.all(0, kb0);
   if (C::STAGES == 3) loader.all(1, kb0 + 1 < kb1 ? kb0 + 1 : kb0);
+  auto k_loop = [&](auto cp) {
+  constexpr bool CP = decltype(cp)::value;
   int stage = 0;
   for (int kb = kb0; kb < kb1; kb++) {
     const int load_stage = stage == 0 ? C::STAGES - 1 : stage - 1;
@@ -765,19 +799,28 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
     if constexpr (MX) {
       int ea[C::MT];
       read_a_mx<C>(lds, aa, sa_addr, stage, lg, af, ea);
-      mfma_tiles_mx<C>(lds, ba, ebo, stage, load_stage, lg, af, ea, acc, loader, next);
+      mfma_tiles_mx<C, CP>(lds, ba, ebo, stage, load_stage, lg, af, ea, acc, loader, next);
     } else if constexpr (UE8M0) {
       int ea[C::MT], eb;
       read_a_ue8m0<C>(lds, aa, sa_addr, sb_addr, stage, af, ea, eb);
-      mfma_tiles_ue8m0<C>(lds, ba, stage, load_stage, af, ea, eb, acc, loader, next);
+      mfma_tiles_ue8m0<C, CP>(lds, ba, stage, load_stage, af, ea, eb, acc, loader, next);
     } else if (ROWSKIP && (uint32_t)(wm * C::TM) >= a_rows) {  // uniform: this wave's rows are all past M
+      if (CP) {
 #pragma unroll
-      for (int i = 0; i < StageLoader<C>::NSEG; i++) loader.issue(i, load_stage, next);
+        for (int i = 0; i < StageLoader<C>::NSEG; i++) loader.issue(i, load_stage, next);
+      }
     } else {
       read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
-      mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, load_stage, af, sc, nullptr, acc, loader, next);
+      mfma_tiles<C, 0, C::NT, false, CP>(lds, ba, stage, load_stage, af, sc, nullptr, acc, loader, next);
     }
     stage = stage + 1 == C::STAGES ? 0 : stage + 1;
+  }
+  };
+  if constexpr (C::COPY_WAVES == C::WAVES) {
+    k_loop(std::true_type{});
+  } else {
+    if (loader.copier()) k_loop(std::true_type{});  // wave-uniform
+    else k_loop(std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
 
@@ -959,7 +1002,9 @@ __device__ __forceinline__ StageLoader<C> tile_loader(uint8_t* lds, const TileRe
                         (uint32_t)(sa_ld * 4),
                         (uint32_t)(nb_lane * KB * 4),
                         wave,
-                        lane};
+                        lane,
+                        0u,
+                        (uint32_t)K};
 }
 
 __device__ __forceinline__ TileRef select_tile(bool first, const TileRef& x, const TileRef& y) {
@@ -1048,6 +1093,9 @@ __device__ __forceinline__ void gemm_persistent(uint8_t* lds, const Src& src, co
   }
   int pending = 0;  // three stages: 1 = packed results to store, 2 = their stores in flight
   int stage = 0, kb = 0;
+  // written once per copying role, as gemm_tile's loop
+  auto walk = [&](auto cp) {
+  constexpr bool CP = decltype(cp)::value;
   while (true) {
     const int load_stage = stage == 0 ? C::STAGES - 1 : stage - 1;
     // The chunk this iteration copies: STAGES - 1 ahead, in this tile or the
@@ -1072,7 +1120,7 @@ __device__ __forceinline__ void gemm_persistent(uint8_t* lds, const Src& src, co
     }
     if (wave < 2) ld.issue(StageLoader<C>::NSEG, load_stage, next_kb);  // scales
     read_a<C>(lds, aa, sa_addr, sb_addr, stage, af, sc);
-    mfma_tiles<C, 0, C::NT, false, true>(lds, ba, stage, load_stage, af, sc, nullptr, acc, ld, next_kb);
+    mfma_tiles<C, 0, C::NT, false, CP>(lds, ba, stage, load_stage, af, sc, nullptr, acc, ld, next_kb);
     stage = stage + 1 == C::STAGES ? 0 : stage + 1;
     if (kb + 1 < KB) {
       kb++;
@@ -1101,6 +1149,13 @@ __device__ __forceinline__ void gemm_persistent(uint8_t* lds, const Src& src, co
     has_next = tn_ < src.t_pad;
     if (!has_next) nxt = cur;
     kb = 0;
+  }
+  };
+  if constexpr (C::COPY_WAVES == C::WAVES) {
+    walk(std::true_type{});
+  } else {
+    if (wave < C::COPY_WAVES) walk(std::true_type{});  // wave-uniform
+    else walk(std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into LDS outlives the loop
   if constexpr (C::STAGES == 3) store_packed<C>(d, pend, M, N, pend_m0, pend_n0, wm, wn, li, lg);
