@@ -39,12 +39,13 @@ struct Tile {
   static constexpr int STAGES = STAGES_;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
-  // Waves that copy the K chunks into LDS (the first COPY_WAVES).  In the
-  // 256x256 tile only waves 0-3 copy: waves w and w + 4 share a SIMD, and the
-  // SIMD's arbiter favours the older wave, which reaches the barrier ~30%
-  // sooner; giving it all the copy issue shortens the younger wave's chunk
-  // (measured: +2-3% on the 256x256 shapes, bit-identical results).
-  static constexpr int COPY_WAVES = (BM_ == 256 && BN_ == 256) ? 4 : WAVES;
+  // Waves that copy the K chunks into LDS (the first COPY_WAVES).  With 8 or
+  // 12 waves only waves 0-3, one per SIMD, copy: waves w, w + 4 (and w + 8)
+  // share a SIMD, and its arbiter favours the older wave, which reaches the
+  // barrier ~30% sooner; giving it all the copy issue shortens the others'
+  // chunk (measured, bit-identical results: +2-3% on the 256x256 shapes, +2%
+  // on 256x128 and 256x192, +4% on the grouped 128x256 product).
+  static constexpr int COPY_WAVES = WAVES >= 8 ? 4 : WAVES;
   static constexpr int TM = BM / WAVES_M;  // wave tile rows
   static constexpr int TN = BN / WAVES_N;  // wave tile columns (inside one 128-column scale block)
   static constexpr int MT = TM / 16;
