@@ -36,7 +36,8 @@ decode-time dispatch buffer), moe_layer (the whole MoE layer: routing, gather,
 two grouped products, SiLU-times-up and combine, 8192 tokens top-4 over 32
 experts, H = 7168, I = 2048), square8k, square16k, copy (counter calibration),
 stream (the plain streaming read at 48 MiB and 768 MiB: the HBM ceiling at the
-decode weight's size).
+decode weight's size), quantize (the activation quantizer at the prefill shapes
+beside torch's bf16 -> FP8 cast of the same tensor, which moves the same bytes).
 """
 
 from __future__ import annotations
@@ -73,7 +74,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy", "stream"])
+    p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy", "stream", "quantize"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--trials", type=int, default=TRIALS, help="timed trials of --steps steps each")
     p.add_argument("--no-clock", action="store_true",
@@ -608,6 +609,58 @@ def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288))
     return out
 
 
+# ------------------------------------------------------ quantizer ceiling
+def bench_quantize(fg, torch, shapes=((2048, 4096), (2048, 12288), (8192, 8192)), reps=50, trials=TRIALS):
+    """quantize_fp8_groups at the prefill activation shapes, beside torch's
+    bf16 -> float8_e4m3fn cast of the same tensor (a vendor elementwise kernel
+    that moves the same 2 bytes in and 1 byte out per element, without the
+    group amax): the rate a read-plus-write stream of that size reaches.
+    Inputs rotate over enough buffers (>= 600 MB) that no launch is served
+    from the 256 MB last-level cache."""
+    out = []
+    for m, k in shapes:
+        sets = max(2, int(600e6 // (3 * m * k)))
+        g = torch.Generator(device="cuda")
+        g.manual_seed(m + k)
+        xs = [torch.randn((m, k), device="cuda", generator=g).to(torch.bfloat16) for _ in range(sets)]
+        qs = [fg.quantize_fp8_groups(x) for x in xs]
+        casts = [torch.empty((m, k), dtype=torch.float8_e4m3fn, device="cuda") for _ in range(sets)]
+
+        def quant():
+            for x, o in zip(xs, qs):
+                fg.quantize_fp8_groups(x, out=o)
+
+        def cast():
+            for x, c in zip(xs, casts):
+                c.copy_(x)
+
+        res = {}
+        for name, fn in (("quantize_fp8_groups", quant), ("torch_cast_to_fp8", cast)):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(trials):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(max(1, reps // sets)):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3 / (max(1, reps // sets) * sets))
+            res[name] = ts
+        qb = quant_bytes(m, k)
+        row = {"m": m, "k": k, "bytes": qb, "sets": sets}
+        for name, ts in res.items():
+            t = float(np.median(ts))
+            row[name] = {"us": round(t * 1e6, 3), "us_min": round(min(ts) * 1e6, 3), "gbs": round(qb / t / 1e9, 1),
+                         "frac_hbm": round(qb / t / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"quantize {m}x{k}: {row['quantize_fp8_groups']['us']} us; torch cast {row['torch_cast_to_fp8']['us']} us")
+        out.append(row)
+        del xs, qs, casts
+        torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------ streaming ceiling
 def bench_stream(fg, torch, sizes=(50_331_648, 805_306_368), sets=8, reps=50, trials=TRIALS):
     """The plain streaming read (fgfp8_stream_read) at the decode weight's
@@ -740,6 +793,11 @@ def main():
         return
     if args.workload == "stream":
         print(json.dumps({"workload": "stream_read", "results": bench_stream(fg, torch, trials=args.trials)}))
+        return
+    if args.workload == "quantize":
+        print(json.dumps({"workload": "activation_quantize_vs_cast", "timing": "median and min of the trials; "
+                          "launches back to back over rotating inputs, event time per launch",
+                          "results": bench_quantize(fg, torch, trials=args.trials)}))
         return
     recipe = {"prefill_ue8m0": "ue8m0", "prefill_mx": "mx"}.get(args.workload, "fp32")
     if args.workload in ("prefill", "prefill_ue8m0", "prefill_mx"):
