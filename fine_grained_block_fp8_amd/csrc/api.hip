@@ -517,7 +517,7 @@ int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, 
   if (fused) {
     if (env_flag("FGFP8_PRINT_CONFIG"))
       fprintf(stderr, "[fgfp8] fp8_linear_nt m=%lld n=%lld k=%lld: fused decode split=%d\n", (long long)m,
-              (long long)n, (long long)k, fgfp8::decode_split(n, k));
+              (long long)n, (long long)k, fgfp8::decode_split(m, n, k));
     return launched(fgfp8::launch_decode_fused(x_bf16, b_e4m3, sb, d_bf16, m, n, k, q_e4m3, sa, sa_ld,
                                                (hipStream_t)stream),
                     who);
@@ -549,6 +549,9 @@ int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len)
   if (wp.kind != plan.kind)
     snprintf(buf, (size_t)len, "%s split=%d; with workspace: %s", fgfp8::gemm_kind_name(plan.kind), plan.split,
              fgfp8::gemm_kind_name(wp.kind));
+  else if (plan.kind == fgfp8::kGemmDecode && fgfp8::decode_plan(m, n, k).slabs > 1)
+    snprintf(buf, (size_t)len, "%s split=%d slabs=%d", fgfp8::gemm_kind_name(plan.kind), plan.split,
+             fgfp8::decode_plan(m, n, k).slabs);
   else
     snprintf(buf, (size_t)len, "%s split=%d", fgfp8::gemm_kind_name(plan.kind), plan.split);
   return FGFP8_OK;

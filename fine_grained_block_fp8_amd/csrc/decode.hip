@@ -24,6 +24,7 @@
 
 #include <atomic>
 #include <cstdlib>
+#include <cstring>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -36,8 +37,10 @@ namespace fgfp8 {
 // per SIMD; with KS = 8 (two waves per SIMD) it holds 12.  The A fragments of
 // the non-fused form take registers too: it holds 8.  KS = 16 (N = 4096 at
 // K = 12288: four waves per SIMD, 128 VGPRs) holds 6.
-template <int KS, bool FUSED>
-constexpr int decode_max_chunks() { return KS >= 16 ? 6 : (FUSED && KS >= 8 ? 12 : 8); }
+// With S = 3 slabs per workgroup a chunk brings three slabs' weight
+// fragments: 4 chunks at a time (<= 8 waves, two per SIMD).
+template <int KS, bool FUSED, int S = 1>
+constexpr int decode_max_chunks() { return S > 1 ? 4 : (KS >= 16 ? 6 : (FUSED && KS >= 8 ? 12 : 8)); }
 constexpr int kFusedMaxRows = (int)kFusedLdsMaxM;
 constexpr int64_t kFusedLdsMaxK = 32768;  // 4 x K bytes of LDS per workgroup
 
@@ -53,6 +56,12 @@ __device__ __forceinline__ v4f_t mfma_fp8_dec(const v8i_t& x, const v8i_t& y) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// S slabs per workgroup (1 or 3): the workgroup owns 16 S consecutive output
+// columns, and each wave's activation fragments of a chunk serve all S
+// slabs' MFMAs, so the activation is read (or, fused, quantized) once per
+// S slabs.  Every output takes the same chunks, promotions and wave-order
+// reduction whatever S is, so the result does not depend on S.
+//
 // FUSED = false: A is E4M3 [M][K] with scales sa [K/128][sa_ld] in global
 // memory.  FUSED = true: X is bf16 [M][K] (M <= 4), quantized here; if q_out
 // is non-null, workgroup 0 also writes the quantized activation and its
@@ -60,7 +69,7 @@ __device__ __forceinline__ v4f_t mfma_fp8_dec(const v8i_t& x, const v8i_t& y) {
 // lane issued ahead of the weight stream (loads complete in issue order, so
 // one issued after the stream can only be used once the whole stream has
 // arrived): 3 covers M = 1; 12 covers M <= 4 at the common K.
-template <int KS, bool FUSED, int XA = 3>
+template <int KS, bool FUSED, int XA = 3, int S = 1>
 __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict__ Ain, const float* __restrict__ SA,
                                                          int64_t sa_ld, const uint8_t* __restrict__ B,
                                                          const float* __restrict__ SB, uint16_t* __restrict__ D,
@@ -69,20 +78,25 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t nw = (int64_t)blockIdx.x * 16 * S;  // the workgroup's first column
   const int KB = K / kGroup;
   const int per = (KB + KS - 1) / KS;
   const int c_begin = wave * per;
   const int c_end = c_begin + per < KB ? c_begin + per : KB;
-  const uint32_t b_rows = (uint32_t)(N - n0 < 16 ? N - n0 : 16);
-  const rsrc_t rb = make_rsrc(B + n0 * K, b_rows * (uint32_t)K);
+  rsrc_t rb[S], rsb[S];
+#pragma unroll
+  for (int sl = 0; sl < S; sl++) {
+    const int64_t n0 = nw + 16 * sl;  // slabs past N get empty resources: every load reads zeros
+    const uint32_t b_rows = (uint32_t)(N - n0 <= 0 ? 0 : (N - n0 < 16 ? N - n0 : 16));
+    rb[sl] = make_rsrc(B + (b_rows ? n0 : 0) * K, b_rows * (uint32_t)K);
+    rsb[sl] = make_rsrc(SB + (b_rows ? n0 / kGroup : 0) * KB, b_rows ? (uint32_t)KB * 4u : 0u);
+  }
   const uint32_t off = (uint32_t)li * (uint32_t)K + (uint32_t)lg * 32u;
-  const float* sbw = SB + (n0 / kGroup) * KB;
   const bool row_ok = li < M;
 
-  // LDS: [red: KS x 64 x 16 B][FUSED: qa 4 x K bytes][FUSED: scales KB x 4 floats]
+  // LDS: [red: S x KS x 64 x 16 B][FUSED: qa 4 x K bytes][FUSED: scales KB x 4 floats]
   v4f_t* red = reinterpret_cast<v4f_t*>(smem);
-  uint8_t* qa = smem + KS * 64 * 16;
+  uint8_t* qa = smem + S * KS * 64 * 16;
   float* qs = reinterpret_cast<float*>(qa + kFusedMaxRows * K);
 
   // Every operand of a batch of chunks is requested before any is used, so
@@ -97,12 +111,13 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
   // around a load would make it wait for all of them (the whole weight
   // stream) before the first use.
   constexpr uint32_t kOob = 0x80000000u;
-  constexpr int MAXC = decode_max_chunks<KS, FUSED>();
-  v4f_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 b0[MAXC], b1[MAXC], a0[FUSED ? 1 : MAXC], a1[FUSED ? 1 : MAXC];
+  constexpr int MAXC = decode_max_chunks<KS, FUSED, S>();
+  v4f_t acc[S];
+#pragma unroll
+  for (int sl = 0; sl < S; sl++) acc[sl] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 b0[MAXC][S], b1[MAXC][S], a0[FUSED ? 1 : MAXC], a1[FUSED ? 1 : MAXC];
   float sav[FUSED ? 1 : MAXC];
-  float sbv = 0.0f;
-  const rsrc_t rsb = make_rsrc(sbw, (uint32_t)KB * 4u);
+  float sbv[S];
   // the non-fused form's activation and its scales (M rows; scale column li
   // of chunk kb at kb * sa_ld + li)
   const rsrc_t ra = make_rsrc(FUSED ? nullptr : Ain, FUSED ? 0u : (uint32_t)M * (uint32_t)K);
@@ -110,8 +125,10 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
   // Small operands first: requests queue in order behind the weight stream,
   // so anything issued after it would arrive only when the stream has.
   auto issue = [&](int cb, int nc) {
-    sbv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-        rsb, lane < nc ? (uint32_t)(cb + lane) * 4u : kOob, 0, 0));
+#pragma unroll
+    for (int sl = 0; sl < S; sl++)
+      sbv[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rsb[sl], lane < nc ? (uint32_t)(cb + lane) * 4u : kOob, 0, 0));
     if (!FUSED) {
       // A fragments and scales, every load issued (rows >= M and chunks past
       // the batch get out-of-range offsets and read zeros), so that the
@@ -130,16 +147,19 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
 #pragma unroll
     for (int u = 0; u < MAXC; u++) {
       const uint32_t o = u < nc ? off + (uint32_t)(cb + u) * 128u : kOob;
-      b0[u] = load_rsrc16(rb, o);
-      b1[u] = load_rsrc16(rb, u < nc ? o + 16u : kOob);
+#pragma unroll
+      for (int sl = 0; sl < S; sl++) {
+        b0[u][sl] = load_rsrc16(rb[sl], o);
+        b1[u][sl] = load_rsrc16(rb[sl], u < nc ? o + 16u : kOob);
+      }
     }
   };
   // One MFMA per chunk into alternating partial registers, each promoted
   // after the next MFMA is issued (so the MFMAs do not wait on each other);
   // chunks are added to acc in order.
   auto compute = [&](int cb, int nc) {
-    v4f_t part[2];
-    float scl[2];
+    v4f_t part[2][S];
+    float scl[2][S];
 #pragma unroll
     for (int u = 0; u <= MAXC; u++) {
       if (u < nc) {
@@ -159,24 +179,34 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
           af = frag_of(a0[u], a1[u]);
           sa_u = sav[u];
         }
-        part[u & 1] = mfma_fp8_dec(frag_of(b0[u], b1[u]), af);
-        scl[u & 1] = sa_u * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sbv), u));
+#pragma unroll
+        for (int sl = 0; sl < S; sl++) {
+          part[u & 1][sl] = mfma_fp8_dec(frag_of(b0[u][sl], b1[u][sl]), af);
+          scl[u & 1][sl] =
+              sa_u * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sbv[sl]), u));
+        }
         if (!FUSED) {  // registers are scarcer here: promote at once
-          const v4f_t& p = part[u & 1];
-          const float sc = scl[u & 1];
-          acc[0] = __builtin_fmaf(p[0], sc, acc[0]);
-          acc[1] = __builtin_fmaf(p[1], sc, acc[1]);
-          acc[2] = __builtin_fmaf(p[2], sc, acc[2]);
-          acc[3] = __builtin_fmaf(p[3], sc, acc[3]);
+#pragma unroll
+          for (int sl = 0; sl < S; sl++) {
+            const v4f_t& p = part[u & 1][sl];
+            const float sc = scl[u & 1][sl];
+            acc[sl][0] = __builtin_fmaf(p[0], sc, acc[sl][0]);
+            acc[sl][1] = __builtin_fmaf(p[1], sc, acc[sl][1]);
+            acc[sl][2] = __builtin_fmaf(p[2], sc, acc[sl][2]);
+            acc[sl][3] = __builtin_fmaf(p[3], sc, acc[sl][3]);
+          }
         }
       }
       if (FUSED && u > 0 && u - 1 < nc) {
-        const v4f_t& p = part[(u - 1) & 1];
-        const float sc = scl[(u - 1) & 1];
-        acc[0] = __builtin_fmaf(p[0], sc, acc[0]);
-        acc[1] = __builtin_fmaf(p[1], sc, acc[1]);
-        acc[2] = __builtin_fmaf(p[2], sc, acc[2]);
-        acc[3] = __builtin_fmaf(p[3], sc, acc[3]);
+#pragma unroll
+        for (int sl = 0; sl < S; sl++) {
+          const v4f_t& p = part[(u - 1) & 1][sl];
+          const float sc = scl[(u - 1) & 1][sl];
+          acc[sl][0] = __builtin_fmaf(p[0], sc, acc[sl][0]);
+          acc[sl][1] = __builtin_fmaf(p[1], sc, acc[sl][1]);
+          acc[sl][2] = __builtin_fmaf(p[2], sc, acc[sl][2]);
+          acc[sl][3] = __builtin_fmaf(p[3], sc, acc[sl][3]);
+        }
       }
     }
   };
@@ -232,17 +262,22 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
     nc = c_end - cb < MAXC ? c_end - cb : MAXC;
     if (nc > 0) issue(cb, nc);
   }
-  red[wave * 64 + lane] = acc;
+#pragma unroll
+  for (int sl = 0; sl < S; sl++) red[(sl * KS + wave) * 64 + lane] = acc[sl];
   __syncthreads();
-  if (wave == 0) {
-    v4f_t s = red[lane];
+  // wave sl % KS sums slab sl's KS partials in wave order
+#pragma unroll
+  for (int sl = 0; sl < S; sl++) {
+    if (wave != sl % KS) continue;  // wave-uniform
+    v4f_t s = red[(sl * KS) * 64 + lane];
 #pragma unroll
     for (int w = 1; w < KS; w++) {
-      const v4f_t o = red[w * 64 + lane];
+      const v4f_t o = red[(sl * KS + w) * 64 + lane];
       s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
     }
     // lane (li, lg): output row li, columns n0 + 4*lg .. n0 + 4*lg + 3
-    if (row_ok) {
+    const int64_t n0 = nw + 16 * sl;
+    if (row_ok && n0 < N) {
       const int64_t c0 = n0 + 4 * lg;
       uint16_t* drow = D + (int64_t)li * N;
       if ((N % 4) == 0 && c0 + 4 <= N) {
@@ -390,16 +425,41 @@ __global__ __launch_bounds__(KS * 64) void decode_xq_kernel(const uint16_t* __re
 // waves of 128 VGPRs (four per SIMD) shorten every wave's serial tail:
 // measured at N = 4096, K = 12288, 13.6 -> 12.9 us at M = 1 and 17.3 -> 15.6
 // us at M = 4 (graph replay).
-int decode_split(int64_t n, int64_t k) {
-  const int64_t slabs = (n + 15) / 16, kb = k / kGroup;
+//
+// Slabs per workgroup: 3 where more than 4 activation rows make the
+// activation's fragments as costly as the weight's (each slab workgroup
+// re-reads all M rows from L2) and the shape allows -- K <= 16384, so that
+// three slabs' reduction space (and the fused form's activation) fits in
+// LDS, and a split of 8 waves, since with 16 three slabs' fragments do not
+// fit the 128 VGPRs of four waves per SIMD -- else 1.  The split is then
+// planned over the workgroups instead of the slabs.  Measured (graph replay
+// over 8 weight sets, N = 12288, K = 4096): M = 16 19.5 -> 18.4 us per call;
+// at M = 1 and 4 three slabs lose (11.4 -> 14.6 and 14.4 -> 16.0 us).
+// FGFP8_DECODE_SLABS=1|3 forces the choice (tests, tuning).  The fused
+// forms and the two-launch path take the same plan for the same M, so they
+// stay bit-identical.
+static int split_for(int64_t units, int64_t kb) {
   int ks = 4;
-  while (ks < 8 && (slabs * ks < 2048 || (kb + ks - 1) / ks > 12)) ks *= 2;
+  while (ks < 8 && (units * ks < 2048 || (kb + ks - 1) / ks > 12)) ks *= 2;
   if (ks == 8 && (kb + 7) / 8 > 8) ks = 16;
   while (ks > 1 && (kb + ks - 1) / ks < 2) ks /= 2;
   return ks;
 }
 
-template <int KS, bool FUSED, int XA>
+DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
+  const int64_t slabs = (n + 15) / 16, kb = k / kGroup;
+  const char* force = getenv("FGFP8_DECODE_SLABS");
+  const bool three = force != nullptr ? strcmp(force, "3") == 0 : m > kFusedLdsMaxM;
+  if (three && k <= 16384) {
+    const int ks = split_for((slabs + 2) / 3, kb);
+    if (ks == 8) return {ks, 3};
+  }
+  return {split_for(slabs, kb), 1};
+}
+
+int decode_split(int64_t m, int64_t n, int64_t k) { return decode_plan(m, n, k).ks; }
+
+template <int KS, bool FUSED, int XA, int S>
 static hipError_t allow_lds() {
   // The fused variant holds the quantized activation (up to 4 x K bytes) in
   // LDS; allow dynamic LDS beyond the 64 KB default, once per kernel and
@@ -409,27 +469,26 @@ static hipError_t allow_lds() {
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   const bool cached = dev >= 0 && dev < 64;
   if (cached && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED, XA>),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED, XA, S>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_relaxed);
   return e;
 }
 
-template <int KS, bool FUSED, int XA = 3>
+template <int KS, bool FUSED, int XA = 3, int S = 1>
 static hipError_t launch_decode_ks(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
                                    void* d, int64_t m, int64_t n, int64_t k, uint8_t* q_out, float* sa_out,
                                    int64_t sa_out_ld, hipStream_t stream) {
-  size_t lds = (size_t)KS * 64 * 16;
-  if (FUSED) {
-    lds += (size_t)kFusedMaxRows * k + (size_t)(k / kGroup) * kFusedMaxRows * 4;
-    if (lds > 64 * 1024) {
-      const hipError_t e = allow_lds<KS, FUSED, XA>();
-      if (e != hipSuccess) return e;
-    }
+  size_t lds = (size_t)S * KS * 64 * 16;
+  if (FUSED) lds += (size_t)kFusedMaxRows * k + (size_t)(k / kGroup) * kFusedMaxRows * 4;
+  if (lds > 64 * 1024) {
+    const hipError_t e = allow_lds<KS, FUSED, XA, S>();
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_kernel<KS, FUSED, XA>), dim3((uint32_t)((n + 15) / 16)), dim3(KS * 64), lds, stream, a, sa,
-                     sa_ld, static_cast<const uint8_t*>(b), sb, static_cast<uint16_t*>(d), (int)m, n, (int)k, q_out,
-                     sa_out, sa_out_ld);
+  const int64_t wgs = ((n + 15) / 16 + S - 1) / S;
+  hipLaunchKernelGGL((decode_kernel<KS, FUSED, XA, S>), dim3((uint32_t)wgs), dim3(KS * 64), lds, stream, a, sa, sa_ld,
+                     static_cast<const uint8_t*>(b), sb, static_cast<uint16_t*>(d), (int)m, n, (int)k, q_out, sa_out,
+                     sa_out_ld);
   return hipGetLastError();
 }
 
@@ -437,6 +496,9 @@ template <bool FUSED, int XA = 3>
 static hipError_t launch_decode_t(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b,
                                   const float* sb, void* d, int64_t m, int64_t n, int64_t k, uint8_t* q_out,
                                   float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
+  if (decode_plan(m, n, k).slabs == 3) {
+    if (ks == 8) return launch_decode_ks<8, FUSED, XA, 3>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
+  }
   switch (ks) {
     case 1: return launch_decode_ks<1, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
     case 2: return launch_decode_ks<2, FUSED, XA>(a, sa, sa_ld, b, sb, d, m, n, k, q_out, sa_out, sa_out_ld, stream);
@@ -480,7 +542,7 @@ static hipError_t launch_decode_xq(int ks, const void* x, const void* b, const f
 
 hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
                                int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
-  const int ks = decode_split(n, k);
+  const int ks = decode_split(m, n, k);
   // Test override: FGFP8_DECODE_XQ forces the register form at any M.
   if (m > kFusedMaxRows || k > kFusedLdsMaxK || getenv("FGFP8_DECODE_XQ") != nullptr)
     return launch_decode_xq(ks, x, b, sb, d, m, n, k, static_cast<uint8_t*>(q_out), sa_out, sa_out_ld, stream);

@@ -1325,7 +1325,7 @@ constexpr int kCUs = 256;
 }  // namespace
 
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
-  if (m <= 16) return {kGemmDecode, decode_split(n, k)};
+  if (m <= 16) return {kGemmDecode, decode_split(m, n, k)};
   // Tuning and test override: FGFP8_GEMM_TILE=<tile name> forces a tile.
   if (const char* force = getenv("FGFP8_GEMM_TILE")) {
     for (const Candidate& c : kCandidates)

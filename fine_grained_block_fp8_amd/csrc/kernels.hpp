@@ -71,7 +71,12 @@ hipError_t launch_gemm_fp8out(GemmKind kind, const void* a, const float* sa, int
                               int64_t k, hipStream_t stream);
 
 // Decode-shaped products (M <= 16): K split over ks waves per 16-column slab.
-int decode_split(int64_t n, int64_t k);
+// Decode plan: waves per slab (the K split) and slabs per workgroup.
+struct DecodePlan {
+  int ks, slabs;
+};
+DecodePlan decode_plan(int64_t m, int64_t n, int64_t k);
+int decode_split(int64_t m, int64_t n, int64_t k);
 hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
                          void* d, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 // Fused activation quantization + product: one kernel for M <= kFusedMaxM

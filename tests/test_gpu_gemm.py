@@ -233,6 +233,35 @@ def test_register_quantizing_kernel_at_small_m(m, n, k, monkeypatch):
     assert torch.equal(d.view(torch.int16), d_two.view(torch.int16))
 
 
+@pytest.mark.parametrize("m", [1, 4, 13, 16])
+@pytest.mark.parametrize("n,k", [(12288, 4096), (1040, 4096)])
+def test_decode_three_slabs_per_workgroup(m, n, k, monkeypatch):
+    """Three 16-column slabs per workgroup (FGFP8_DECODE_SLABS=3; 1040
+    columns leave the last workgroup one slab past N): every output against
+    the oracle, and the fused forms (LDS form for m <= 4, register form
+    without the activation outputs) give the two-call path's bits."""
+    monkeypatch.setenv("FGFP8_DECODE_SLABS", "3")
+    desc = fg.describe_gemm(m, n, k)
+    print(f"decode {m}x{n}x{k}: {desc}", flush=True)
+    assert "slabs=3" in desc
+    lin = workloads.decode_linear(m, n, k) if (n, k) in workloads.DECODE_SHAPES else workloads.random_linear(m, n, k, seed=m + n)
+    q, sa, qb, sb, d_two = gpu_hot_path(lin)
+    check_full(lin, q, sa, qb, sb, d_two, f"slabs3 {m}x{n}x{k}")
+    x = to_dev_bf16(lin.a)
+    if m <= 4:
+        d = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+        q2 = torch.full((m, k), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+        sa2 = torch.full((k // 128, fg.padded_rows(m)), float("nan"), dtype=torch.float32, device="cuda")
+        fg.fp8_linear_nt(x, (qb, sb), d, (q2, sa2))
+        torch.cuda.synchronize()
+        assert np.array_equal(codes(q2), codes(q))
+        assert torch.equal(d.view(torch.int16), d_two.view(torch.int16))
+    d3 = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fg.fp8_linear_nt(x, (qb, sb), d3)
+    torch.cuda.synchronize()
+    assert torch.equal(d3.view(torch.int16), d_two.view(torch.int16))
+
+
 TILES = ["tile256x256_w4x2", "tile256x192_w4x3", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
 # the persistent walk takes tiles of whole 128-column blocks
 PERSISTENT_TILES = [t for t in TILES if t != "tile256x192_w4x3"]
