@@ -427,7 +427,10 @@ const char* fgfp8_last_error(void);
  * across tiles; same results bit for bit) for k >= 256; by default every
  * tile is a workgroup of its own, which measured faster.  FGFP8_DECODE_XQ
  * (any value) makes fp8_linear_nt's fused path use the register-quantizing
- * kernel at every m <= 16 (tests; same bits).  FGFP8_MASKED_TILE, set to
+ * kernel at every m <= 16 (tests; same bits).  FGFP8_DECODE_SLABS=1|3 sets
+ * the 16-column weight slabs per workgroup of the m <= 16 product (by
+ * default 3 for m > 4 where the shape allows, else 1; the description then
+ * ends in "slabs=3"; same values either way).  FGFP8_MASKED_TILE, set to
  * tile128x256_w2x4 or tile128x128_w2x2, forces that tile in
  * m_grouped_fp8_gemm_nt_masked in place of the one expected_m selects
  * (tuning and tests; same values).  FGFP8_PRINT_CONFIG=1 prints each call's
