@@ -303,11 +303,14 @@ __device__ __forceinline__ void mfma_tiles(const uint8_t* lds, const FragAddr& b
                                            v4f_t (&acc)[C::MT][C::NT], const StageLoader<C>& ld, int next_kb) {
   // With LD (copying waves), the next chunk's global->LDS copies (NSEG
   // instructions per wave) are spread over the first half of the column
-  // tiles -- over all of them where only some waves copy -- so that no wave
-  // stalls for long on a full vector-memory queue, and they still land well
-  // before the next barrier.
+  // tiles, so that no wave stalls for long on a full vector-memory queue,
+  // and they land well before the next barrier even when the weight streams
+  // from HBM: spread over all the tiles, the copying waves of gate_up waited
+  // ~880 ticks per chunk for their last copies with the weights rotating
+  // through more than the last-level cache (183.6 us), against ~470 over the
+  // first half (177.9 us; the same 170-171 us with the weight cache-resident).
   constexpr int NL = StageLoader<C>::NSEG;
-  constexpr int HALF = C::COPY_WAVES < C::WAVES ? T1 - T0 : ((T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1);
+  constexpr int HALF = (T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1;
   constexpr int PER = (NL + HALF - 1) / HALF;
   constexpr int N_MFMA = (T1 - T0) * C::MT;
   v8i_t bfr[2];
@@ -365,7 +368,7 @@ __device__ __forceinline__ void mfma_tiles_ue8m0(const uint8_t* lds, const FragA
                                                  const v8i_t (&af)[C::MT], const int (&ea)[C::MT], int eb,
                                                  v4f_t (&acc)[C::MT][C::NT], const StageLoader<C>& ld, int next_kb) {
   constexpr int NL = StageLoader<C>::NSEG;
-  constexpr int HALF = C::COPY_WAVES < C::WAVES ? C::NT : (C::NT / 2 > 0 ? C::NT / 2 : 1);
+  constexpr int HALF = C::NT / 2 > 0 ? C::NT / 2 : 1;
   constexpr int PER = (NL + HALF - 1) / HALF;
   constexpr int N_MFMA = C::NT * C::MT;
   v8i_t bfr[2];
@@ -415,7 +418,7 @@ __device__ __forceinline__ void mfma_tiles_mx(const uint8_t* lds, const FragAddr
                                               const int (&ea)[C::MT], v4f_t (&acc)[C::MT][C::NT],
                                               const StageLoader<C>& ld, int next_kb) {
   constexpr int NL = StageLoader<C>::NSEG;
-  constexpr int HALF = C::COPY_WAVES < C::WAVES ? C::NT : (C::NT / 2 > 0 ? C::NT / 2 : 1);
+  constexpr int HALF = C::NT / 2 > 0 ? C::NT / 2 : 1;
   constexpr int PER = (NL + HALF - 1) / HALF;
   constexpr int N_MFMA = C::NT * C::MT;
   v8i_t bfr[2];
