@@ -337,6 +337,26 @@ def test_describe_gemm_plans():
     assert _lib().fgfp8_describe_gemm(8, 8, 100, buf, 4) == fg.FGFP8_EINVAL
 
 
+def test_decode_slab_plan(monkeypatch):
+    """The m <= 16 product's plan (host-only): three slabs per workgroup
+    (with a split of 8 waves) for m > 4 where K <= 16384 and the split comes
+    to 8, else one; FGFP8_DECODE_SLABS forces it where the shape allows."""
+    monkeypatch.delenv("FGFP8_DECODE_SLABS", raising=False)
+    assert fg.describe_gemm(16, 12288, 4096) == "decode_splitk_slab16 split=8 slabs=3"
+    assert fg.describe_gemm(5, 12288, 4096) == "decode_splitk_slab16 split=8 slabs=3"
+    assert fg.describe_gemm(4, 12288, 4096) == "decode_splitk_slab16 split=4"
+    assert fg.describe_gemm(1, 12288, 4096) == "decode_splitk_slab16 split=4"
+    # 256 slabs at K = 12288: sixteen waves per slab, no room for three slabs
+    assert fg.describe_gemm(16, 4096, 12288) == "decode_splitk_slab16 split=16"
+    # K past 16384: the fused form's activation and three slabs' sums exceed LDS
+    assert "slabs" not in fg.describe_gemm(16, 12288, 32768)
+    monkeypatch.setenv("FGFP8_DECODE_SLABS", "1")
+    assert fg.describe_gemm(16, 12288, 4096) == "decode_splitk_slab16 split=4"
+    monkeypatch.setenv("FGFP8_DECODE_SLABS", "3")
+    assert fg.describe_gemm(1, 12288, 4096) == "decode_splitk_slab16 split=8 slabs=3"
+    assert fg.describe_gemm(1, 1040, 4096) == "decode_splitk_slab16 split=8 slabs=3"
+
+
 def test_fused_gate_up_rejects():
     lib = _lib()
 
