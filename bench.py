@@ -10,15 +10,19 @@ offline step, as the pages' plugin keeps weights and scales as persistent
 parameters).  Inputs are seeded synthetic data resident in HBM before the
 timed region.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--workload prefill]
 
 Prints ONE JSON line: value = TFLOP/s over the step (2*M*N*K summed over the
-four linears, divided by the time of quantize + product).  The K timed steps
-are enqueued while a bounded spin kernel holds the GPU, so they run back to
-back on the device; the step time is the HIP-event time from the first timed
-launch to the end of the last (the host-side Python launch path, ~10-30 us per
-call, is not part of the device's work; callers that launch from C++ or a HIP
-graph see the same device time).  Also reported:
+four linears, divided by the time of quantize + product), the median of 5
+trials of K steps.  The step time is the HIP-event time from the first timed
+launch to the end of the last.  The host enqueues a prefill step in about a
+third of its device time, so the launches run back to back on the device by
+themselves; where the host would fall behind (small kernels), the steps are
+enqueued while a bounded spin kernel holds the GPU (the host-side Python
+launch path, ~10-30 us per call, is not part of the device's work; callers
+that launch from C++ or a HIP graph see the same device time).  Trials of
+100 steps measure the sustained rate: the GPU's power management takes tens
+of milliseconds to settle after an idle or sleeping gap.  Also reported:
 * roofline: the dominant kernel's algorithmic TFLOP/s from HIP events on the
   launch stream, recorded around that kernel's launches only (created without
   the system-scope fence, so that recording them barely disturbs the step),
@@ -72,8 +76,8 @@ STEPS_ARE = {
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="prefill", choices=["prefill", "prefill_ue8m0", "prefill_mx", "decode", "moe", "moe_masked", "moe_layer", "square8k", "square16k", "copy", "stream", "quantize"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--trials", type=int, default=TRIALS, help="timed trials of --steps steps each")
@@ -222,6 +226,18 @@ class GpuAhead:
     def spin(self, seconds: float) -> None:
         self.torch.cuda._sleep(int(self.cycles_per_s * seconds))
 
+    def lead_in(self, host_s: float, gpu_s: float) -> None:
+        """Before a timed region of steps that take `gpu_s` on the device and
+        `host_s` to enqueue: spin only where the host would fall behind the
+        device.  Where it keeps ahead by itself the first launch starts at
+        once and no spin is run, because a few milliseconds of a sleeping GPU
+        let its power management drop the clock, and the steps that follow
+        then run during the climb back (measured on the prefill step: 20-step
+        trials after a 6 ms spin 0.459 ms per step, 100-step trials with no
+        spin 0.410, the same as a long back-to-back run)."""
+        if host_s > 0.5 * gpu_s:
+            self.spin(1.5 * host_s + 2e-3)
+
 
 TRIALS = 5  # timed trials per measurement; min and median are reported
 NO_CLOCK = False  # --no-clock
@@ -229,12 +245,14 @@ NO_CLOCK = False  # --no-clock
 
 class SmiSampler:
     """The GPU's graphics clock and socket power as amdsmi reports them,
-    polled every millisecond from a host thread, keeping only the samples
-    taken while a window is open.  summary() is None where amdsmi is not
-    usable."""
+    polled from a host thread, keeping only the samples taken while a window
+    is open.  The firmware refreshes these metrics about once a second, so a
+    reading describes the run only once the run has lasted well over a
+    second.  summary() is None where amdsmi is not usable."""
 
-    def __init__(self):
+    def __init__(self, period: float = 0.01):
         self.samples = []
+        self.period = period
         self._open = False
         self._stop = None
         try:
@@ -260,11 +278,13 @@ class SmiSampler:
                 if self._open:
                     try:
                         m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                        xcc = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and 0 < v < 65535]
                         if self._open:
-                            self.samples.append((m.get("current_gfxclk"), m.get("current_socket_power"), time.time()))
+                            self.samples.append((m.get("current_gfxclk"), m.get("current_socket_power"), time.time(),
+                                                 float(np.median(xcc)) if xcc else None))
                     except Exception:
                         pass
-                time.sleep(0.001)
+                time.sleep(self.period)
 
         self._t = threading.Thread(target=poll, daemon=True)
         self._t.start()
@@ -282,44 +302,57 @@ class SmiSampler:
             self._t.join()
 
     def summary(self):
-        clk = [x[0] for x in self.samples if isinstance(x[0], (int, float)) and x[0] > 0]
-        pw = [x[1] for x in self.samples if isinstance(x[1], (int, float)) and x[1] > 0]
+        ok = lambda v: isinstance(v, (int, float)) and 0 < v < 65535
+        clk = [x[0] for x in self.samples if ok(x[0])]
+        pw = [x[1] for x in self.samples if ok(x[1])]
+        xcc = [x[3] for x in self.samples if ok(x[3])]
         if not clk:
             return None
-        return {"source": "amdsmi gpu_metrics current_gfxclk / current_socket_power, sampled every ~1 ms inside "
-                          "the timed trials",
-                "samples": len(clk), "gfxclk_mhz_median": float(np.median(clk)), "gfxclk_mhz_min": float(min(clk)),
+        readings = len({(x[0], x[1]) for x in self.samples})
+        return {"source": "amdsmi gpu_metrics current_gfxclk / current_socket_power",
+                "samples": len(clk), "distinct_readings": readings,
+                "gfxclk_mhz_median": float(np.median(clk)), "gfxclk_mhz_min": float(min(clk)),
                 "gfxclk_mhz_max": float(max(clk)),
+                "xcd_gfxclk_mhz_median": float(np.median(xcc)) if xcc else None,
                 "socket_power_w_median": float(np.median(pw)) if pw else None,
                 "socket_power_w_max": float(max(pw)) if pw else None}
 
 
-def sustained_clock(step, torch, step_s: float, seconds: float = 1.2, settle: float = 0.3):
+def sustained_clock(step, torch, step_s: float, seconds: float = 3.0, settle: float = 1.5):
     """The GPU clock and power under a sustained run of `step`: enough steps
     for `seconds` of GPU time (`step_s` each) are enqueued back to back after
     the timed trials, and amdsmi is sampled until they finish, keeping the
-    samples after the first `settle` seconds.  amdsmi's metrics refresh far
-    more slowly than the ~10 ms timed trials last, so the clock is read over
-    a run long enough for them to follow."""
+    samples after the first `settle` seconds.  The metrics refresh about once
+    a second, so the first readings of a run still describe what came before
+    it; the settle skips them.  The run's own device time per step (events
+    around it) is reported beside the clock, so that the reading can be
+    matched with the trials."""
     if NO_CLOCK:
         return None
     smi = SmiSampler()
     if smi._smi is None:
         return None
+    n = max(1, int(seconds / max(step_s, 1e-6)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     smi.__enter__()
     smi.window_open()
     t0 = time.time()
-    for _ in range(max(1, int(seconds / max(step_s, 1e-6)))):
+    e0.record()
+    for _ in range(n):
         step()
+    e1.record()
     torch.cuda.synchronize()
     smi.window_close()
     smi.__exit__()
     smi.samples = [x for x in smi.samples if x[2] >= t0 + settle]
     out = smi.summary()
     if out is not None:
-        out["source"] = (f"amdsmi gpu_metrics current_gfxclk / current_socket_power, sampled every ~1 ms over "
-                         f"~{seconds - settle:.1f} s of back-to-back steps right after the timed trials")
+        out["source"] = (f"amdsmi gpu_metrics current_gfxclk (and the median over the XCDs' current_gfxclks) / "
+                         f"current_socket_power, polled every ~10 ms over the last ~{seconds - settle:.1f} s of "
+                         f"{n} back-to-back steps right after the timed trials (the firmware refreshes them about "
+                         f"once a second)")
+        out["sustained_ms_per_step"] = round(e0.elapsed_time(e1) / n, 4)
     return out
 
 
@@ -341,13 +374,26 @@ def host_enqueue_seconds(fn, torch, reps=3):
     return worst
 
 
-def per_linear_pass(preps, steps, fg, torch, ahead, host_step):
+def gpu_step_seconds(fn, torch, reps=10):
+    """Device time per call of fn() over `reps` calls enqueued back to back
+    (an upper bound where the host is the slower side)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def per_linear_pass(preps, steps, fg, torch, ahead, host_step, gpu_step):
     """Per-linear breakdown: `steps` steps with three events per linear
     (before the act-quant, between, after the product).  Runs before the
     timed region, so its event records do not weigh on the step time."""
     events = [[[HipEvent(torch) for _ in range(3)] for _ in preps] for _ in range(steps)]
     torch.cuda.synchronize()
-    ahead.spin(1.5 * host_step * steps + 2e-3)
+    ahead.lead_in(host_step * steps, gpu_step * steps)
     for s in range(steps):
         for p, ev in zip(preps, events[s]):
             p.run(fg, ev)
@@ -401,7 +447,8 @@ def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32", trials=TRIAL
     ahead = GpuAhead(torch)
     probe = [[HipEvent(torch) for _ in range(3)] for _ in preps]
     host_step = host_enqueue_seconds(lambda: [p.run(fg, ev) for p, ev in zip(preps, probe)], torch)
-    per = per_linear_pass(preps, steps, fg, torch, ahead, host_step)
+    gpu_step = gpu_step_seconds(lambda: [p.run(fg) for p in preps], torch)
+    per = per_linear_pass(preps, steps, fg, torch, ahead, host_step, gpu_step)
     dom = dominant_kernel(per)
     elapsed, launches = [], []
     for _ in range(trials):
@@ -409,7 +456,7 @@ def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32", trials=TRIAL
                   for _ in range(steps)]
         e_first, e_last = HipEvent(torch), HipEvent(torch)
         torch.cuda.synchronize()
-        ahead.spin(1.5 * host_step * steps + 2e-3)
+        ahead.lead_in(host_step * steps, gpu_step * steps)
         e_first.record()
         for s in range(steps):
             for p, ev in zip(preps, dom_ev[s]):
@@ -421,7 +468,7 @@ def bench_linears(linears, steps, warmup, fg, torch, recipe="fp32", trials=TRIAL
     timed = {"kernel": dom, "mean_s": float(np.mean(launches)), "launches": len(launches)}
     clock = sustained_clock(lambda: [p.run(fg) for p in preps], torch, float(np.median(elapsed)) / steps)
     log(f"timed: {steps} steps x {trials} trials, ms/step " + ", ".join(f"{e * 1e3 / steps:.4f}" for e in elapsed)
-        + f"; host enqueue {host_step * 1e3:.3f} ms/step; {dom}: {len(launches)} launches timed, "
+        + f"; host enqueue {host_step * 1e3:.3f} ms/step (device {gpu_step * 1e3:.3f}); {dom}: {len(launches)} launches timed, "
         f"mean {timed['mean_s'] * 1e6:.2f} us; gpu clock {clock}")
     return preps, elapsed, per, timed, clock
 
@@ -854,10 +901,10 @@ def main():
         for key, lin in (("square_8192", workloads.square_linear(8192, 8192, 8192)),
                          ("square_16384x16384x8192", workloads.square_linear(16384, 16384, 8192))):
             log(f"{key}: {fg.describe_gemm(lin.m, lin.n, lin.k)}")
-            extra[key] = bench_object(lin, min(args.steps, 10), args.warmup, fg, torch, args.trials)
+            extra[key] = bench_object(lin, args.steps, args.warmup, fg, torch, args.trials)
             del lin
             torch.cuda.empty_cache()
-        extra["moe_grouped_zipf32"] = bench_moe(args, fg, torch, workloads, steps=min(args.steps, 10))
+        extra["moe_grouped_zipf32"] = bench_moe(args, fg, torch, workloads)
         for v in extra.values():
             for k in [k for k in v if k.startswith("_") or k == "rows"]:
                 del v[k]
@@ -947,12 +994,13 @@ def bench_moe(args, fg, torch, workloads, steps=None) -> dict:
     ahead = GpuAhead(torch)
     probe = [HipEvent(torch) for _ in range(3)]
     host_step = host_enqueue_seconds(lambda: step(probe), torch)
+    gpu_step = gpu_step_seconds(step, torch)
     elapsed, gts, qts = [], [], []
     for _ in range(args.trials):
         evs = [[HipEvent(torch) for _ in range(3)] for _ in range(steps)]
         e_first, e_last = HipEvent(torch), HipEvent(torch)
         torch.cuda.synchronize()
-        ahead.spin(1.5 * host_step * steps + 2e-3)
+        ahead.lead_in(host_step * steps, gpu_step * steps)
         e_first.record()
         for s in range(steps):
             step(evs[s])
@@ -1030,9 +1078,10 @@ def bench_masked(args, fg, torch, workloads):
     ahead = GpuAhead(torch)
     probe = [HipEvent(torch) for _ in range(3)]
     host_step = host_enqueue_seconds(lambda: step(probe), torch)
+    gpu_step = gpu_step_seconds(step, torch)
     e_first, e_last = HipEvent(torch), HipEvent(torch)
     torch.cuda.synchronize()
-    ahead.spin(1.5 * host_step * args.steps + 2e-3)
+    ahead.lead_in(host_step * args.steps, gpu_step * args.steps)
     e_first.record()
     for s in range(args.steps):
         step(evs[s])
@@ -1132,9 +1181,10 @@ def bench_moe_layer(args, fg, torch, workloads):
     ahead = GpuAhead(torch)
     probe = [HipEvent(torch) for _ in range(len(names) + 1)]
     host_step = host_enqueue_seconds(lambda: step(probe), torch)
+    gpu_step = gpu_step_seconds(step, torch)
     e_first, e_last = HipEvent(torch), HipEvent(torch)
     torch.cuda.synchronize()
-    ahead.spin(1.5 * host_step * args.steps + 2e-3)
+    ahead.lead_in(host_step * args.steps, gpu_step * args.steps)
     e_first.record()
     for s_ in range(args.steps):
         step(evs[s_])
