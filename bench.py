@@ -578,8 +578,9 @@ def bench_object(lin, steps, warmup, fg, torch, trials=TRIALS) -> dict:
 def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288)), sets=8, reps=50, trials=TRIALS):
     """Act-quant + product per call at M = 1, 4, 16; 8 rotating weight sets
     (8 x 50 MB > 256 MB last-level cache) replayed from a HIP graph, and
-    eagerly.  M <= 4 runs the fused kernel; M = 16 the quantizer and the
-    decode product (two launches)."""
+    eagerly.  M <= 4 runs the fused kernel; M = 16 passes the activation
+    workspace, with which the library runs the quantizer and the decode
+    product (two launches) at these shapes."""
     import workloads
 
     out = []
@@ -639,7 +640,7 @@ def bench_decode(fg, torch, ms=(1, 4, 16), shapes=((12288, 4096), (4096, 12288))
                 "m": m,
                 "n": n,
                 "k": k,
-                "kernel": ("fused act-quant + " if fused else "act-quant kernel + ") + fg.describe_gemm(m, n, k),
+                "kernel": fg.describe_linear(m, n, k, act is not None),
                 "bytes_per_call": nbytes,
                 "graph_us": round(graph_s * 1e6, 3),
                 "graph_us_min": round(min(graph_trials) * 1e6, 3),

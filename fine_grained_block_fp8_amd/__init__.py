@@ -74,8 +74,10 @@ _lib.moe_gate_up_silu_quantize.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, 
 _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
+_lib.fgfp8_describe_linear.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
               "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
+              "fgfp8_describe_linear",
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
               "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked",
@@ -356,8 +358,10 @@ def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor, 
 
 
 # fp8_linear_nt: one fused kernel up to FUSED_MAX_M rows when no workspace is
-# given; up to FUSED_FAST_MAX_M rows that kernel is also the fastest path
-# (above it, quantize + product with a workspace is faster).
+# given; up to FUSED_FAST_MAX_M rows that kernel is the fastest path.  Above
+# it, passing the workspace is never slower: the library then runs the fused
+# three-slab kernel where it wins, else quantize + product
+# (describe_linear names the choice).
 FUSED_MAX_M, FUSED_FAST_MAX_M = 16, 4
 
 
@@ -365,9 +369,9 @@ def fp8_linear_nt(x: torch.Tensor, weight, d: torch.Tensor, act_out=None) -> tor
     """d[M, N] = quantize_groups(x) . B^T for bf16 x [M, K] and the stored
     weight (q [N, K], sb).  `act_out` = (q [M, K], sa [K/128, sa_ld])
     optionally receives the quantized activation.  One fused kernel for
-    M <= 4; for 4 < M <= 16 a fused kernel without `act_out`, the quantizer
-    and the product with it; above 16 rows `act_out` is required.  Every
-    path gives the same bits."""
+    M <= 4; for 4 < M <= 16 a fused kernel, or with `act_out` the quantizer
+    and the product where they are faster (describe_linear says which);
+    above 16 rows `act_out` is required.  Every path gives the same bits."""
     qb, sb = weight
     _need(x, "x", (torch.bfloat16,), 2)
     _need(qb, "b", _FP8, 2)
@@ -687,6 +691,14 @@ def describe_gemm(m: int, n: int, k: int) -> str:
     return buf.value.decode()
 
 
+def describe_linear(m: int, n: int, k: int, act_out: bool) -> str:
+    """The path fp8_linear_nt takes (act_out: whether the quantized
+    activation is passed too)."""
+    buf = ctypes.create_string_buffer(256)
+    _check(_lib.fgfp8_describe_linear(m, n, k, int(bool(act_out)), buf, 256))
+    return buf.value.decode()
+
+
 __all__ = [
     "FGFP8_EINVAL",
     "FGFP8_ELAUNCH",
@@ -695,6 +707,7 @@ __all__ = [
     "Fgfp8Error",
     "declared_functions",
     "describe_gemm",
+    "describe_linear",
     "fp8_gemm_nt",
     "fp8_gemm_nt_fp8_out",
     "fp8_gemm_nt_mx",

@@ -494,6 +494,19 @@ int moe_combine(const void* y_bf16, int64_t y_rows, int64_t hdim, const int32_t*
                   who);
 }
 
+// The kernel form fp8_linear_nt runs for m rows (act_out: the quantized
+// activation is wanted too): "lds4" (m <= 4: the activation quantized into
+// LDS by every workgroup), "lds16" (the three-slab form, the same up to 16
+// rows), "registers" (each wave quantizes its K range in registers), or
+// nullptr for quantize_fp8_groups followed by fp8_gemm_nt.
+static const char* linear_form(int64_t m, int64_t n, int64_t k, bool act_out) {
+  if (fgfp8::decode_fused_wide(m, n, k, act_out)) return "lds16";
+  if (m <= fgfp8::kFusedLdsMaxM)
+    return k <= fgfp8::kFusedLdsMaxK && getenv("FGFP8_DECODE_XQ") == nullptr ? "lds4" : "registers";
+  if (m <= fgfp8::kFusedMaxM && !act_out) return "registers";
+  return nullptr;
+}
+
 int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, const float* sb, int64_t n,
                   void* d_bf16, void* q_e4m3, float* sa, int64_t sa_ld, void* stream) {
   const char* who = "fp8_linear_nt";
@@ -504,7 +517,8 @@ int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, 
   if (!x_bf16 || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if ((q_e4m3 == nullptr) != (sa == nullptr))
     return fail(FGFP8_EINVAL, "%s: q_e4m3 and sa must be given together", who);
-  const bool fused = m <= fgfp8::kFusedLdsMaxM || (m <= fgfp8::kFusedMaxM && q_e4m3 == nullptr);
+  const char* form = linear_form(m, n, k, q_e4m3 != nullptr);
+  const bool fused = form != nullptr;
   if (!fused && q_e4m3 == nullptr)
     return fail(FGFP8_EINVAL, "%s: m=%lld k=%lld needs the q_e4m3/sa workspace", who, (long long)m, (long long)k);
   if (q_e4m3 != nullptr) {
@@ -516,8 +530,8 @@ int fp8_linear_nt(const void* x_bf16, int64_t m, int64_t k, const void* b_e4m3, 
   if (int rc = check_device(who)) return rc;
   if (fused) {
     if (env_flag("FGFP8_PRINT_CONFIG"))
-      fprintf(stderr, "[fgfp8] fp8_linear_nt m=%lld n=%lld k=%lld: fused decode split=%d\n", (long long)m,
-              (long long)n, (long long)k, fgfp8::decode_split(m, n, k));
+      fprintf(stderr, "[fgfp8] fp8_linear_nt m=%lld n=%lld k=%lld: fused decode split=%d form=%s\n", (long long)m,
+              (long long)n, (long long)k, fgfp8::decode_split(m, n, k), form);
     return launched(fgfp8::launch_decode_fused(x_bf16, b_e4m3, sb, d_bf16, m, n, k, q_e4m3, sa, sa_ld,
                                                (hipStream_t)stream),
                     who);
@@ -541,9 +555,7 @@ int fgfp8_stream_read(const void* src, int64_t bytes, void* out, int64_t out_byt
   return launched(fgfp8::launch_stream_read(src, bytes, out, out_bytes, (hipStream_t)stream), who);
 }
 
-int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len) {
-  if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: null or empty buffer");
-  if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: bad shape");
+static void describe_plan(int64_t m, int64_t n, int64_t k, char* buf, size_t len) {
   const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
   const fgfp8::GemmPlan wp = fgfp8::plan_gemm_ws(m, n, k);
   if (wp.kind != plan.kind)
@@ -554,6 +566,30 @@ int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len)
              fgfp8::decode_plan(m, n, k).slabs);
   else
     snprintf(buf, (size_t)len, "%s split=%d", fgfp8::gemm_kind_name(plan.kind), plan.split);
+}
+
+int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len) {
+  if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: null or empty buffer");
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: bad shape");
+  describe_plan(m, n, k, buf, (size_t)len);
+  return FGFP8_OK;
+}
+
+int fgfp8_describe_linear(int64_t m, int64_t n, int64_t k, int act_out, char* buf, int64_t len) {
+  if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_linear: null or empty buffer");
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_linear: bad shape");
+  const char* form = linear_form(m, n, k, act_out != 0);
+  if (form != nullptr) {
+    const fgfp8::DecodePlan p = fgfp8::decode_plan(m, n, k);
+    snprintf(buf, (size_t)len, "fused act-quant + decode_splitk_slab16 split=%d slabs=%d form=%s", p.ks,
+             strcmp(form, "lds16") == 0 ? 3 : (strcmp(form, "registers") == 0 ? 1 : p.slabs), form);
+    return FGFP8_OK;
+  }
+  if (act_out == 0)
+    return fail(FGFP8_EINVAL, "fgfp8_describe_linear: m=%lld needs the q_e4m3/sa workspace", (long long)m);
+  char plan[160];
+  describe_plan(m, n, k, plan, sizeof plan);
+  snprintf(buf, (size_t)len, "quantize_fp8_groups + %s", plan);
   return FGFP8_OK;
 }
 

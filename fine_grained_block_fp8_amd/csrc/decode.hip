@@ -42,7 +42,6 @@ namespace fgfp8 {
 template <int KS, bool FUSED, int S = 1>
 constexpr int decode_max_chunks() { return S > 1 ? 4 : (KS >= 16 ? 6 : (FUSED && KS >= 8 ? 12 : 8)); }
 constexpr int kFusedMaxRows = (int)kFusedLdsMaxM;
-constexpr int64_t kFusedLdsMaxK = 32768;  // 4 x K bytes of LDS per workgroup
 
 __device__ __forceinline__ v8i_t frag_of(uint4 lo, uint4 hi) {
   v8i_t f;
@@ -63,13 +62,19 @@ __device__ __forceinline__ v4f_t mfma_fp8_dec(const v8i_t& x, const v8i_t& y) {
 // reduction whatever S is, so the result does not depend on S.
 //
 // FUSED = false: A is E4M3 [M][K] with scales sa [K/128][sa_ld] in global
-// memory.  FUSED = true: X is bf16 [M][K] (M <= 4), quantized here; if q_out
-// is non-null, workgroup 0 also writes the quantized activation and its
-// scales (q_out [M][K], sa_out [K/128][sa_out_ld]).  XA: activation loads per
-// lane issued ahead of the weight stream (loads complete in issue order, so
-// one issued after the stream can only be used once the whole stream has
-// arrived): 3 covers M = 1; 12 covers M <= 4 at the common K.
-template <int KS, bool FUSED, int XA = 3, int S = 1>
+// memory.  FUSED = true: X is bf16 [M][K] (M <= MR), quantized here; if q_out
+// is non-null, the quantized activation and its scales are written out too
+// (q_out [M][K], sa_out [K/128][sa_out_ld]), each (row, group) task by
+// workgroup task % gridDim.x, so that no workgroup carries all the writes
+// (one writer made it the launch's last workgroup: +1.5 us at M = 16).  XA:
+// activation loads per lane issued ahead of the weight stream (loads complete
+// in issue order, so one issued after the stream can only be used once the
+// whole stream has arrived): 3 covers M = 1; 12 covers M <= 4 at the common
+// K; 16 covers the three-slab form's M * K/128 <= 512.
+//
+// MR: the activation rows the fused form's LDS holds (4, or 16 for the
+// three-slab form at 4 < M <= 16; see launch_decode_fused).
+template <int KS, bool FUSED, int XA = 3, int S = 1, int MR = kFusedMaxRows>
 __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict__ Ain, const float* __restrict__ SA,
                                                          int64_t sa_ld, const uint8_t* __restrict__ B,
                                                          const float* __restrict__ SB, uint16_t* __restrict__ D,
@@ -94,10 +99,10 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
   const uint32_t off = (uint32_t)li * (uint32_t)K + (uint32_t)lg * 32u;
   const bool row_ok = li < M;
 
-  // LDS: [red: S x KS x 64 x 16 B][FUSED: qa 4 x K bytes][FUSED: scales KB x 4 floats]
+  // LDS: [red: S x KS x 64 x 16 B][FUSED: qa MR x K bytes][FUSED: scales KB x MR floats]
   v4f_t* red = reinterpret_cast<v4f_t*>(smem);
   uint8_t* qa = smem + S * KS * 64 * 16;
-  float* qs = reinterpret_cast<float*>(qa + kFusedMaxRows * K);
+  float* qs = reinterpret_cast<float*>(qa + MR * K);
 
   // Every operand of a batch of chunks is requested before any is used, so
   // a wave waits for memory once per batch, not once per chunk: the B
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
           if (row_ok) {
             const uint8_t* p = qa + li * K + kb * kGroup + lg * 32;
             af = frag_of(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 16));
-            sa_u = qs[kb * kFusedMaxRows + li];
+            sa_u = qs[kb * MR + li];
           } else {
             af = frag_of(make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0));
             sa_u = 0.0f;
@@ -237,8 +242,8 @@ __global__ __launch_bounds__(KS * 64) void decode_kernel(const void* __restrict_
       const double r = 1.0 / (double)s;
       const uint2 o = quantize8(v, r);
       *reinterpret_cast<uint2*>(qa + m * K + g * kGroup + part * 8) = o;
-      if (part == 0) qs[g * kFusedMaxRows + m] = s;
-      if (q_out != nullptr && blockIdx.x == 0) {
+      if (part == 0) qs[g * MR + m] = s;
+      if (q_out != nullptr && (uint32_t)task % gridDim.x == blockIdx.x) {
         *reinterpret_cast<uint2*>(q_out + (int64_t)m * K + g * kGroup + part * 8) = o;
         if (part == 0) sa_out[(int64_t)g * sa_out_ld + m] = s;
       }
@@ -435,9 +440,13 @@ __global__ __launch_bounds__(KS * 64) void decode_xq_kernel(const uint16_t* __re
 // planned over the workgroups instead of the slabs.  Measured (graph replay
 // over 8 weight sets, N = 12288, K = 4096): M = 16 19.5 -> 18.4 us per call;
 // at M = 1 and 4 three slabs lose (11.4 -> 14.6 and 14.4 -> 16.0 us).
+// Three slabs also need a workgroup for every CU: at N = 2048, K = 4096, M =
+// 16 the 43 three-slab workgroups took 13.7 us against 10.4 for 128 of one.
 // FGFP8_DECODE_SLABS=1|3 forces the choice (tests, tuning).  The fused
 // forms and the two-launch path take the same plan for the same M, so they
 // stay bit-identical.
+constexpr int64_t kDecodeCUs = 256;
+
 static int split_for(int64_t units, int64_t kb) {
   int ks = 4;
   while (ks < 8 && (units * ks < 2048 || (kb + ks - 1) / ks > 12)) ks *= 2;
@@ -449,7 +458,7 @@ static int split_for(int64_t units, int64_t kb) {
 DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t slabs = (n + 15) / 16, kb = k / kGroup;
   const char* force = getenv("FGFP8_DECODE_SLABS");
-  const bool three = force != nullptr ? strcmp(force, "3") == 0 : m > kFusedLdsMaxM;
+  const bool three = force != nullptr ? strcmp(force, "3") == 0 : m > kFusedLdsMaxM && (slabs + 2) / 3 >= kDecodeCUs;
   if (three && k <= 16384) {
     const int ks = split_for((slabs + 2) / 3, kb);
     if (ks == 8) return {ks, 3};
@@ -459,7 +468,7 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k) {
 
 int decode_split(int64_t m, int64_t n, int64_t k) { return decode_plan(m, n, k).ks; }
 
-template <int KS, bool FUSED, int XA, int S>
+template <int KS, bool FUSED, int XA, int S, int MR>
 static hipError_t allow_lds() {
   // The fused variant holds the quantized activation (up to 4 x K bytes) in
   // LDS; allow dynamic LDS beyond the 64 KB default, once per kernel and
@@ -469,24 +478,24 @@ static hipError_t allow_lds() {
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   const bool cached = dev >= 0 && dev < 64;
   if (cached && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED, XA, S>),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KS, FUSED, XA, S, MR>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_relaxed);
   return e;
 }
 
-template <int KS, bool FUSED, int XA = 3, int S = 1>
+template <int KS, bool FUSED, int XA = 3, int S = 1, int MR = kFusedMaxRows>
 static hipError_t launch_decode_ks(const void* a, const float* sa, int64_t sa_ld, const void* b, const float* sb,
                                    void* d, int64_t m, int64_t n, int64_t k, uint8_t* q_out, float* sa_out,
                                    int64_t sa_out_ld, hipStream_t stream) {
   size_t lds = (size_t)S * KS * 64 * 16;
-  if (FUSED) lds += (size_t)kFusedMaxRows * k + (size_t)(k / kGroup) * kFusedMaxRows * 4;
+  if (FUSED) lds += (size_t)MR * k + (size_t)(k / kGroup) * MR * 4;
   if (lds > 64 * 1024) {
-    const hipError_t e = allow_lds<KS, FUSED, XA, S>();
+    const hipError_t e = allow_lds<KS, FUSED, XA, S, MR>();
     if (e != hipSuccess) return e;
   }
   const int64_t wgs = ((n + 15) / 16 + S - 1) / S;
-  hipLaunchKernelGGL((decode_kernel<KS, FUSED, XA, S>), dim3((uint32_t)wgs), dim3(KS * 64), lds, stream, a, sa, sa_ld,
+  hipLaunchKernelGGL((decode_kernel<KS, FUSED, XA, S, MR>), dim3((uint32_t)wgs), dim3(KS * 64), lds, stream, a, sa, sa_ld,
                      static_cast<const uint8_t*>(b), sb, static_cast<uint16_t*>(d), (int)m, n, (int)k, q_out, sa_out,
                      sa_out_ld);
   return hipGetLastError();
@@ -540,9 +549,38 @@ static hipError_t launch_decode_xq(int ks, const void* x, const void* b, const f
   }
 }
 
+// The three-slab form with all M <= 16 rows quantized into LDS: each
+// workgroup's 32 lanes-of-16 take the M * K/128 quantize tasks, and every
+// lane's share must go out in one batch of kWideAhead loads ahead of the
+// weight stream (a load issued after the stream would arrive only with it).
+// Every workgroup redoes the whole quantization, and that costs more than
+// the separate quantize launch once a lane has more than 8 tasks: measured
+// (graph replay over 8 weight sets, N = 12288, K = 4096), the two-launch path
+// against this form took 17.9 / 16.4 us at M = 5, 18.3 / 17.2 at M = 6,
+// 18.1 / 17.8 at M = 8, 18.4 / 19.8 at M = 12 and 18.6 / 22.0 at M = 16.
+// Without a workspace for the two-launch path it is compared with the
+// register form instead, which it beats at every such M (20.5 against 30.8
+// us at M = 16).
+constexpr int kWideRows = 16, kWideAhead = 16;
+
+bool decode_fused_wide(int64_t m, int64_t n, int64_t k, bool act_out) {
+  if (m <= kFusedMaxRows || m > kWideRows || getenv("FGFP8_DECODE_XQ") != nullptr) return false;
+  // LDS: three slabs' sums (24 KB), 16 x K activation bytes and their
+  // scales; K <= 8192 keeps them within 160 KB (the 8-wave split of three
+  // slabs implies it too: more than 64 chunks take 16 waves)
+  if (k > 8192) return false;
+  const DecodePlan p = decode_plan(m, n, k);
+  const int64_t per_lane = (m * (k / kGroup) + 8 * 4 - 1) / (8 * 4);
+  return p.slabs == 3 && p.ks == 8 && per_lane <= (act_out ? 8 : kWideAhead);
+}
+
 hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
                                int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream) {
   const int ks = decode_split(m, n, k);
+  if (decode_fused_wide(m, n, k, q_out != nullptr))
+    return launch_decode_ks<8, true, kWideAhead, 3, kWideRows>(x, nullptr, 0, b, sb, d, m, n, k,
+                                                               static_cast<uint8_t*>(q_out), sa_out, sa_out_ld,
+                                                               stream);
   // Test override: FGFP8_DECODE_XQ forces the register form at any M.
   if (m > kFusedMaxRows || k > kFusedLdsMaxK || getenv("FGFP8_DECODE_XQ") != nullptr)
     return launch_decode_xq(ks, x, b, sb, d, m, n, k, static_cast<uint8_t*>(q_out), sa_out, sa_out_ld, stream);

@@ -85,6 +85,12 @@ hipError_t launch_decode(int ks, const void* a, const float* sa, int64_t sa_ld, 
 // only when the caller gives no workspace for the two-launch path.
 constexpr int64_t kFusedMaxM = 16;
 constexpr int64_t kFusedLdsMaxM = 4;
+constexpr int64_t kFusedLdsMaxK = 32768;  // 4 x K bytes of LDS per workgroup
+// Whether the fused call at 4 < M <= 16 quantizes into LDS too (three slabs
+// per workgroup and few enough quantize tasks per lane; act_out: the caller
+// also wants the quantized activation, so the two-launch path is the
+// alternative).
+bool decode_fused_wide(int64_t m, int64_t n, int64_t k, bool act_out);
 hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, void* d, int64_t m, int64_t n,
                                int64_t k, void* q_out, float* sa_out, int64_t sa_out_ld, hipStream_t stream);
 

@@ -236,12 +236,17 @@ int quantize_fp8_groups_masked(const void* x_bf16, const int32_t* masked_m, int3
  * inside every workgroup while the weight stream is in flight (decode: the
  * activation-quantize step must not cost a launch of its own; the AReno FP8
  * decode pull request measured the separate quantize chain holding a decode
- * linear at ~1.2x until it was fused).  For 4 < m <= 16 (or k > 32768) with
+ * linear at ~1.2x until it was fused).  For 4 < m <= 16 on wide weights
+ * (n of about 12288 and more, so that workgroups of three 16-column slabs
+ * still cover every CU) it is one kernel that quantizes all m rows into LDS,
+ * where m * k/128 <= 512 with q_e4m3/sa NULL and <= 256 with them given (past
+ * that the separate quantize launch is cheaper than every workgroup redoing
+ * the quantization).  Otherwise, for 4 < m <= 16 (or k > 32768), with
  * q_e4m3/sa NULL it is a single kernel that quantizes x in registers, each
  * wave its own K range; with q_e4m3/sa given it runs quantize_fp8_groups and
- * fp8_gemm_nt, which is faster at those m.  Every path is bit-identical to
- * quantize_fp8_groups followed by fp8_gemm_nt.  Above 16 rows it runs those
- * two calls.
+ * fp8_gemm_nt.  fgfp8_describe_linear names the path.  Every path is
+ * bit-identical to quantize_fp8_groups followed by fp8_gemm_nt.  Above 16
+ * rows it runs those two calls.
  *
  * x_bf16  [m][k] bfloat16, input.
  * b_e4m3  [n][k] E4M3 and sb [ceil(n/128)][k/128] float32: the stored weight
@@ -436,6 +441,15 @@ const char* fgfp8_last_error(void);
  * (tuning and tests; same values).  FGFP8_PRINT_CONFIG=1 prints each call's
  * kernel choice to stderr. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
+
+/* The path fp8_linear_nt takes for an m x n x k call, act_out non-zero when
+ * the caller passes q_e4m3/sa: "fused act-quant + decode_splitk_slab16
+ * split=S slabs=L form=F" (F = lds4, lds16 or registers, as described at
+ * fp8_linear_nt) or "quantize_fp8_groups + " and fgfp8_describe_gemm's text.
+ * Writes a NUL-terminated string of at most len bytes into buf.  Host-only.
+ * FGFP8_EINVAL for a null buffer, a bad shape, or m > 16 with act_out == 0
+ * (fp8_linear_nt needs the workspace there). */
+int fgfp8_describe_linear(int64_t m, int64_t n, int64_t k, int act_out, char* buf, int64_t len);
 
 /* Measurement aid: reads `bytes` of device memory at src once (bytes a
  * multiple of 32768), with nothing else to do -- the practical ceiling of

@@ -33,6 +33,7 @@ def test_library_exports_every_declared_function():
         "m_grouped_fp8_gemm_nt_contiguous",
         "fgfp8_last_error",
         "fgfp8_describe_gemm",
+        "fgfp8_describe_linear",
         "fp8_linear_nt",
         "m_grouped_fp8_gemm_nt_masked",
         "fp8_gemm_nt_fp8_out",
@@ -339,13 +340,17 @@ def test_describe_gemm_plans():
 
 def test_decode_slab_plan(monkeypatch):
     """The m <= 16 product's plan (host-only): three slabs per workgroup
-    (with a split of 8 waves) for m > 4 where K <= 16384 and the split comes
-    to 8, else one; FGFP8_DECODE_SLABS forces it where the shape allows."""
+    (with a split of 8 waves) for m > 4 where K <= 16384, the split comes to
+    8 and the three-slab workgroups still number at least the 256 CUs, else
+    one; FGFP8_DECODE_SLABS forces it where the shape allows."""
     monkeypatch.delenv("FGFP8_DECODE_SLABS", raising=False)
     assert fg.describe_gemm(16, 12288, 4096) == "decode_splitk_slab16 split=8 slabs=3"
     assert fg.describe_gemm(5, 12288, 4096) == "decode_splitk_slab16 split=8 slabs=3"
     assert fg.describe_gemm(4, 12288, 4096) == "decode_splitk_slab16 split=4"
     assert fg.describe_gemm(1, 12288, 4096) == "decode_splitk_slab16 split=4"
+    # fewer three-slab workgroups than CUs: one slab per workgroup
+    assert fg.describe_gemm(16, 8192, 4096) == "decode_splitk_slab16 split=4"
+    assert fg.describe_gemm(16, 2048, 4096) == "decode_splitk_slab16 split=8"
     # 256 slabs at K = 12288: sixteen waves per slab, no room for three slabs
     assert fg.describe_gemm(16, 4096, 12288) == "decode_splitk_slab16 split=16"
     # K past 16384: the fused form's activation and three slabs' sums exceed LDS
@@ -355,6 +360,33 @@ def test_decode_slab_plan(monkeypatch):
     monkeypatch.setenv("FGFP8_DECODE_SLABS", "3")
     assert fg.describe_gemm(1, 12288, 4096) == "decode_splitk_slab16 split=8 slabs=3"
     assert fg.describe_gemm(1, 1040, 4096) == "decode_splitk_slab16 split=8 slabs=3"
+
+
+def test_describe_linear_paths(monkeypatch):
+    """fp8_linear_nt's path (host-only): the LDS fused form up to 4 rows, the
+    three-slab LDS form above that on wide weights while the quantize tasks
+    per lane fit (8 with the activation outputs, 16 without), the register
+    form without a workspace elsewhere, quantize + product with one."""
+    for v in ("FGFP8_DECODE_SLABS", "FGFP8_DECODE_XQ"):
+        monkeypatch.delenv(v, raising=False)
+    d = fg.describe_linear
+    assert d(1, 12288, 4096, False) == "fused act-quant + decode_splitk_slab16 split=4 slabs=1 form=lds4"
+    assert d(4, 12288, 4096, True) == "fused act-quant + decode_splitk_slab16 split=4 slabs=1 form=lds4"
+    assert d(8, 12288, 4096, True) == "fused act-quant + decode_splitk_slab16 split=8 slabs=3 form=lds16"
+    assert d(16, 12288, 4096, False) == "fused act-quant + decode_splitk_slab16 split=8 slabs=3 form=lds16"
+    assert d(16, 12288, 4096, True) == "quantize_fp8_groups + decode_splitk_slab16 split=8 slabs=3"
+    assert d(16, 4096, 12288, False) == "fused act-quant + decode_splitk_slab16 split=16 slabs=1 form=registers"
+    assert d(16, 4096, 12288, True) == "quantize_fp8_groups + decode_splitk_slab16 split=16"
+    # too few slabs for three per workgroup on every CU
+    assert d(16, 2048, 4096, False).endswith("slabs=1 form=registers")
+    assert d(2048, 4096, 4096, True).startswith("quantize_fp8_groups + tile")
+    buf = ctypes.create_string_buffer(64)
+    assert _lib().fgfp8_describe_linear(2048, 4096, 4096, 0, buf, 64) == fg.FGFP8_EINVAL  # needs the workspace
+    assert _lib().fgfp8_describe_linear(8, 8, 100, 1, buf, 64) == fg.FGFP8_EINVAL
+    assert _lib().fgfp8_describe_linear(8, 8, 128, 1, None, 64) == fg.FGFP8_EINVAL
+    monkeypatch.setenv("FGFP8_DECODE_XQ", "1")
+    assert d(8, 12288, 4096, False).endswith("slabs=1 form=registers")
+    assert d(4, 12288, 4096, True).endswith("form=registers")
 
 
 def test_fused_gate_up_rejects():

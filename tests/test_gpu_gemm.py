@@ -211,7 +211,7 @@ def test_fused_linear_matches_two_calls_and_oracle(m, n, k):
     check_sampled(lin, q, sa, qb, sb, d, np.arange(m), sample_col_blocks(n, 8, rng), f"fused {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m", [1, 3, 4])
+@pytest.mark.parametrize("m", [1, 3, 4, 8, 16])
 @pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288), (1000, 384)])
 def test_register_quantizing_kernel_at_small_m(m, n, k, monkeypatch):
     """The register-quantizing fused kernel forced at m <= 4 (where the LDS
@@ -260,6 +260,48 @@ def test_decode_three_slabs_per_workgroup(m, n, k, monkeypatch):
     fg.fp8_linear_nt(x, (qb, sb), d3)
     torch.cuda.synchronize()
     assert torch.equal(d3.view(torch.int16), d_two.view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,k,force3", [(5, 12288, 4096, False), (8, 12288, 4096, False), (16, 12288, 4096, False),
+                                           (13, 1040, 4096, True), (16, 1040, 2048, True), (6, 1040, 8192, True),
+                                           (16, 2048, 4096, False), (16, 4096, 12288, False)])
+def test_fused_three_slab_lds_form(m, n, k, force3, monkeypatch, capfd):
+    """fp8_linear_nt at 4 < m <= 16, with and without the activation
+    outputs: the path it takes is the one describe_linear names (the
+    three-slab kernel that quantizes all rows into LDS where it applies,
+    FGFP8_DECODE_SLABS=3 forcing three slabs on the ragged 1040-column
+    weights), its output is the oracle's element by element and the two-call
+    path's bit for bit, and the activation outputs (each (row, group) written
+    by one workgroup) are the oracle's quantizer's."""
+    monkeypatch.setenv("FGFP8_PRINT_CONFIG", "1")
+    if force3:
+        monkeypatch.setenv("FGFP8_DECODE_SLABS", "3")
+    lin = workloads.decode_linear(m, n, k) if (n, k) in workloads.DECODE_SHAPES else workloads.random_linear(m, n, k, seed=m + n + k)
+    q, sa, qb, sb, d_two = gpu_hot_path(lin)
+    x = to_dev_bf16(lin.a)
+    oq, osa = oracle.quantize_groups(lin.a)
+    for act in (True, False):
+        form = fg.describe_linear(m, n, k, act)
+        d = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out = None
+        if act:
+            out = (torch.full((m, k), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn),
+                   torch.full((k // 128, fg.padded_rows(m)), float("nan"), dtype=torch.float32, device="cuda"))
+        capfd.readouterr()
+        fg.fp8_linear_nt(x, (qb, sb), d, out)
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err
+        print(f"fused {m}x{n}x{k} act={act}: {form} | {err.strip()}", flush=True)
+        if form.startswith("fused"):
+            assert form.split("form=")[1] in err, (form, err)
+        wide = "form=lds16" in form
+        assert wide == ("slabs=3" in fg.describe_gemm(m, n, k) and m * k // 128 <= (256 if act else 512)), form
+        if act:
+            assert np.array_equal(codes(out[0]), oq)
+            assert np.array_equal(out[1][:, :m].cpu().numpy().view(np.uint32), osa[:, :m].view(np.uint32))
+        assert torch.equal(d.view(torch.int16), d_two.view(torch.int16)), f"{form}: output differs from the two-call path"
+        if wide and act:
+            check_full(lin, q, sa, qb, sb, d, f"fused lds16 {m}x{n}x{k}")
 
 
 TILES = ["tile256x256_w4x2", "tile256x192_w4x3", "tile256x128_w4x2", "tile128x256_w2x4", "tile128x128_w2x2"]
