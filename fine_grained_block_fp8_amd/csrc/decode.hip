@@ -441,7 +441,7 @@ __global__ __launch_bounds__(KS * 64) void decode_xq_kernel(const uint16_t* __re
 // over 8 weight sets, N = 12288, K = 4096): M = 16 19.5 -> 18.4 us per call;
 // at M = 1 and 4 three slabs lose (11.4 -> 14.6 and 14.4 -> 16.0 us).
 // Three slabs also need a workgroup for every CU: at N = 2048, K = 4096, M =
-// 16 the 43 three-slab workgroups took 13.7 us against 10.4 for 128 of one.
+// 16 the 43 three-slab workgroups took 13.7 us against 10.8 for 128 of one.
 // FGFP8_DECODE_SLABS=1|3 forces the choice (tests, tuning).  The fused
 // forms and the two-launch path take the same plan for the same M, so they
 // stay bit-identical.
@@ -470,7 +470,7 @@ int decode_split(int64_t m, int64_t n, int64_t k) { return decode_plan(m, n, k).
 
 template <int KS, bool FUSED, int XA, int S, int MR>
 static hipError_t allow_lds() {
-  // The fused variant holds the quantized activation (up to 4 x K bytes) in
+  // The fused variant holds the quantized activation (MR x K bytes) in
   // LDS; allow dynamic LDS beyond the 64 KB default, once per kernel and
   // device (devices beyond the table set it on every call).
   static std::atomic<bool> done[64];
