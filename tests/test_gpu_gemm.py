@@ -234,12 +234,13 @@ def test_register_quantizing_kernel_at_small_m(m, n, k, monkeypatch):
 
 
 @pytest.mark.parametrize("m", [1, 4, 13, 16])
-@pytest.mark.parametrize("n,k", [(12288, 4096), (1040, 4096)])
+@pytest.mark.parametrize("n,k", [(12288, 4096), (1040, 4096), (1000, 2048)])
 def test_decode_three_slabs_per_workgroup(m, n, k, monkeypatch):
     """Three 16-column slabs per workgroup (FGFP8_DECODE_SLABS=3; 1040
-    columns leave the last workgroup one slab past N): every output against
-    the oracle, and the fused forms (LDS form for m <= 4, register form
-    without the activation outputs) give the two-call path's bits."""
+    columns leave the last workgroup one slab past N, 1000 end in a slab of
+    8 columns): every output against the oracle, and the fused forms (with
+    the activation outputs for m <= 4, and the fused kernel fp8_linear_nt
+    picks without them) give the two-call path's bits."""
     monkeypatch.setenv("FGFP8_DECODE_SLABS", "3")
     desc = fg.describe_gemm(m, n, k)
     print(f"decode {m}x{n}x{k}: {desc}", flush=True)
@@ -264,6 +265,7 @@ def test_decode_three_slabs_per_workgroup(m, n, k, monkeypatch):
 
 @pytest.mark.parametrize("m,n,k,force3", [(5, 12288, 4096, False), (8, 12288, 4096, False), (16, 12288, 4096, False),
                                            (13, 1040, 4096, True), (16, 1040, 2048, True), (6, 1040, 8192, True),
+                                           (11, 1000, 2048, True),
                                            (16, 2048, 4096, False), (16, 4096, 12288, False)])
 def test_fused_three_slab_lds_form(m, n, k, force3, monkeypatch, capfd):
     """fp8_linear_nt at 4 < m <= 16, with and without the activation
