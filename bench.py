@@ -308,7 +308,7 @@ class SmiSampler:
         xcc = [x[3] for x in self.samples if ok(x[3])]
         if not clk:
             return None
-        readings = len({(x[0], x[1]) for x in self.samples})
+        readings = len({(x[0], x[1]) for x in self.samples if ok(x[0])})
         return {"source": "amdsmi gpu_metrics current_gfxclk / current_socket_power",
                 "samples": len(clk), "distinct_readings": readings,
                 "gfxclk_mhz_median": float(np.median(clk)), "gfxclk_mhz_min": float(min(clk)),

@@ -84,3 +84,31 @@ def test_recorded_traffic_is_gated_by_the_sources_hash(tmp_path, monkeypatch):
     assert bench.recorded_traffic("gemm_nt_kernel<tile256x256_w4x2>") == 123
     assert bench.recorded_traffic("gemm_nt_kernel<tile256x128_w4x2>") is None  # recorded for other sources
     assert bench.recorded_traffic("gemm_nt_kernel<tile128x128_w2x2>") is None
+
+
+def test_lead_in_spins_only_where_the_host_falls_behind():
+    """The timed region's lead-in: no spin kernel where the host enqueues the
+    steps in under half their device time (a sleeping GPU lowers its clock),
+    a spin of 1.5x the host time + 2 ms otherwise."""
+    spins = []
+    ahead = object.__new__(bench.GpuAhead)
+    ahead.spin = spins.append
+    ahead.lead_in(host_s=100 * 0.15e-3, gpu_s=100 * 0.41e-3)  # the prefill step
+    assert spins == []
+    ahead.lead_in(host_s=100 * 0.05e-3, gpu_s=100 * 0.02e-3)  # small kernels
+    assert spins == [pytest.approx(1.5 * 100 * 0.05e-3 + 2e-3)]
+
+
+def test_clock_summary_counts_refreshes():
+    """The clock record: medians over the valid samples (65535 marks a
+    metric the firmware does not report), the XCDs' median, and how many
+    distinct metric refreshes the samples hold."""
+    s = bench.SmiSampler.__new__(bench.SmiSampler)
+    s.samples = [(2000, 1400, 0.0, 1990.0)] * 50 + [(2040, 1398, 1.0, 2010.0)] * 60 + [(65535, None, 2.0, None)]
+    out = s.summary()
+    assert out["samples"] == 110 and out["distinct_readings"] == 2
+    assert out["gfxclk_mhz_median"] == 2040.0 and out["gfxclk_mhz_min"] == 2000.0
+    assert out["xcd_gfxclk_mhz_median"] == 2010.0
+    assert out["socket_power_w_median"] == 1398.0 and out["socket_power_w_max"] == 1400.0
+    s.samples = []
+    assert s.summary() is None
