@@ -1,6 +1,7 @@
 """Host-side logic of bench.py (no GPU): the one-GPU contract, the
 algorithmic byte counts, the dominant-kernel choice and roofline arithmetic,
-and the gating of recorded HBM traffic by the GEMM sources' hash."""
+the gating of recorded HBM traffic by the GEMM sources' hash, the timed
+region's lead-in and the clock record's summary."""
 
 import json
 import os
