@@ -332,6 +332,13 @@ def test_describe_gemm_plans():
     assert fg.describe_gemm(16, 4096, 12288).startswith("decode")
     assert fg.describe_gemm(8192, 8192, 8192).startswith("tile256x256")
     assert fg.describe_gemm(2048, 4096, 4096) == fg.describe_gemm(2048, 4096, 4096)
+    # the calibrated planner: fewest rounds of tiles weighted by each tile's
+    # measured rate (shapes where the fastest forced tile was the one named)
+    for (m, n, k), tile in [((2048, 6144, 4096), "tile256x192_w4x3"), ((4096, 6144, 4096), "tile256x192_w4x3"),
+                            ((2048, 12288, 4096), "tile256x192_w4x3"), ((2048, 24576, 4096), "tile256x256_w4x2"),
+                            ((2048, 3072, 4096), "tile128x256_w2x4"), ((8192, 7168, 2048), "tile256x256_w4x2"),
+                            ((512, 4096, 4096), "tile128x128_w2x2")]:
+        assert fg.describe_gemm(m, n, k).split()[0] == tile, (m, n, k)
     buf = ctypes.create_string_buffer(4)
     assert _lib().fgfp8_describe_gemm(8192, 8192, 8192, buf, 4) == fg.FGFP8_OK
     assert len(buf.value) == 3  # truncated, NUL-terminated
