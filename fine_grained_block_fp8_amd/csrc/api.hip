@@ -557,15 +557,16 @@ int fgfp8_stream_read(const void* src, int64_t bytes, void* out, int64_t out_byt
 
 static void describe_plan(int64_t m, int64_t n, int64_t k, char* buf, size_t len) {
   const fgfp8::GemmPlan plan = fgfp8::plan_gemm(m, n, k);
+  const char* walk = fgfp8::plan_persistent(plan, m, n, k) ? " persistent" : "";
   const fgfp8::GemmPlan wp = fgfp8::plan_gemm_ws(m, n, k);
   if (wp.kind != plan.kind)
-    snprintf(buf, (size_t)len, "%s split=%d; with workspace: %s", fgfp8::gemm_kind_name(plan.kind), plan.split,
-             fgfp8::gemm_kind_name(wp.kind));
+    snprintf(buf, (size_t)len, "%s split=%d%s; with workspace: %s", fgfp8::gemm_kind_name(plan.kind), plan.split,
+             walk, fgfp8::gemm_kind_name(wp.kind));
   else if (plan.kind == fgfp8::kGemmDecode && fgfp8::decode_plan(m, n, k).slabs > 1)
     snprintf(buf, (size_t)len, "%s split=%d slabs=%d", fgfp8::gemm_kind_name(plan.kind), plan.split,
              fgfp8::decode_plan(m, n, k).slabs);
   else
-    snprintf(buf, (size_t)len, "%s split=%d", fgfp8::gemm_kind_name(plan.kind), plan.split);
+    snprintf(buf, (size_t)len, "%s split=%d%s", fgfp8::gemm_kind_name(plan.kind), plan.split, walk);
 }
 
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len) {

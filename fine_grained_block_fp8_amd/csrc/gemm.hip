@@ -1400,13 +1400,36 @@ const char* gemm_kind_name(GemmKind kind) {
   return "?";
 }
 
-// Persistent walk (gemm_persistent) or one workgroup per tile.  Tuning and
-// test override: FGFP8_PERSISTENT=0|1.  The walk needs K >= 256 (two chunks
-// per tile keep a finished tile's stores ahead of the next pack).
-bool use_persistent(int64_t k) {
+// Persistent walk (gemm_persistent) or one workgroup per tile.  The walk
+// runs the K pipeline on from one tile into the next, which pays where a
+// launch takes two or more rounds of tiles: measured with identical bits
+// (A/B interleaved on one box), 256x256 tiles 1-6% faster (2048 x 24576 x
+// 4096 169.1 against 172.7 us, 8192^3 425.8 against 433.2, 16384^2 x 8192
+// 1725 against 1747, most at short K: 8192 x 8192 x 1024 71.5 against 75.8),
+// the grouped product 7% faster at K = 2048 (627 against 674 us) and 3% at
+// K = 1024, but 1% slower at K = 7168, and one round of tiles 5% slower (o
+// at M = 2048).  So: two or more rounds, the 256x256 tile for the dense
+// product (the only one measured there) and K <= 4096 for the grouped one.
+// Tuning and test override: FGFP8_PERSISTENT=0|1.  The walk needs K >= 256
+// (two chunks per tile keep a finished tile's stores ahead of the next pack).
+bool use_persistent(int64_t tiles, int64_t k, bool grouped, bool measured_tile) {
   if (k < 2 * kGroup) return false;
   if (const char* force = getenv("FGFP8_PERSISTENT")) return strcmp(force, "0") != 0;
-  return false;
+  return tiles >= 2 * kCUs && measured_tile && (!grouped || k <= 4096);
+}
+
+bool plan_persistent(const GemmPlan& plan, int64_t m, int64_t n, int64_t k) {
+  // launch_tile's rule: tiles of whole 128-column blocks only
+  int bm = 0, bn = 0;
+  switch (plan.kind) {
+    case kGemmTile256x256: bm = 256, bn = 256; break;
+    case kGemmTile256x128: bm = 256, bn = 128; break;
+    case kGemmTile128x256: bm = 128, bn = 256; break;
+    case kGemmTile128x128: bm = 128, bn = 128; break;
+    default: return false;
+  }
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+  return use_persistent(tiles, k, false, bm == 256 && bn == 256);
 }
 
 // Workgroups of a persistent launch: one per compute unit (the tiles' LDS
@@ -1436,7 +1459,8 @@ static hipError_t launch_tile(const void* a, const float* sa, int64_t sa_ld, con
   // column blocks align with 128 (the epilogue pairs waves wn, wn ^ 1).
   constexpr bool kAligned = C::BN % kGroup == 0;
   if constexpr (kAligned) {
-    if (!ue8m0 && out.q == nullptr && use_persistent(k)) {
+    if (!ue8m0 && out.q == nullptr &&
+        use_persistent((int64_t)tiles_m * tiles_n, k, false, C::BM == 256 && C::BN == 256)) {
       const int t_pad = (tiles_m * tiles_n + 7) / 8 * 8;
       const DenseTiles src{pa, pb, sb, k, tiles_m, tiles_n, t_pad, C::BM, C::BN};
       hipLaunchKernelGGL(gemm_nt_persistent_kernel<C>, dim3((uint32_t)persistent_grid(t_pad)), block, 0, stream, src,
@@ -1600,7 +1624,7 @@ hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, co
                                int64_t k, hipStream_t stream) {
   using C = Tile128x256;
   const int tiles_m = (int)(m / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
-  if (use_persistent(k)) {
+  if (use_persistent((int64_t)tiles_m * tiles_n, k, true, true)) {
     const int t_pad = (tiles_m * tiles_n + 7) / 8 * 8;
     const GroupedTiles src{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), sb, m_indices, m, n, k,
                            (int)num_groups, tiles_m, tiles_n, t_pad};

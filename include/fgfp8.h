@@ -426,11 +426,14 @@ const char* fgfp8_last_error(void);
  * tile128x128_w2x2), forces that tile in fp8_gemm_nt (tuning and tests; the
  * FP8-output call takes tile256x256_w4x2 for tile256x192_w4x3); other values
  * are ignored.  FGFP8_SPLITK=1 (0) forces (forbids) the K-split plan of
- * fp8_gemm_nt_ws for k >= 256.  FGFP8_PERSISTENT=1 makes fp8_gemm_nt (bf16 output, FP32
- * scales) and m_grouped_fp8_gemm_nt_contiguous walk their tiles
- * persistently (one workgroup per compute unit, the K pipeline continuing
- * across tiles; same results bit for bit) for k >= 256; by default every
- * tile is a workgroup of its own, which measured faster.  FGFP8_DECODE_XQ
+ * fp8_gemm_nt_ws for k >= 256.  FGFP8_PERSISTENT=1 (0) forces (forbids)
+ * the persistent tile walk of fp8_gemm_nt (bf16 output, FP32 scales) and
+ * m_grouped_fp8_gemm_nt_contiguous for k >= 256: one workgroup per compute
+ * unit, the K pipeline continuing across tiles, same results bit for bit.
+ * By default it is taken where it measured faster: two or more rounds of
+ * 256x256 tiles in fp8_gemm_nt, and two or more rounds of tiles at
+ * k <= 4096 in the grouped call (the description then ends in
+ * "persistent"); every other tile is a workgroup of its own.  FGFP8_DECODE_XQ
  * (any value) makes fp8_linear_nt's fused path use the register-quantizing
  * kernel at every m <= 16 (tests; same bits).  FGFP8_DECODE_SLABS=1|3 sets
  * the 16-column weight slabs per workgroup of the m <= 16 product (by

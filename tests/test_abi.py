@@ -345,6 +345,24 @@ def test_describe_gemm_plans():
     assert _lib().fgfp8_describe_gemm(8, 8, 100, buf, 4) == fg.FGFP8_EINVAL
 
 
+def test_persistent_walk_plan(monkeypatch):
+    """The persistent walk is the default for two or more rounds of 256x256
+    tiles (host-only); FGFP8_PERSISTENT forces or forbids it."""
+    monkeypatch.delenv("FGFP8_PERSISTENT", raising=False)
+    monkeypatch.delenv("FGFP8_GEMM_TILE", raising=False)
+    assert fg.describe_gemm(2048, 24576, 4096) == "tile256x256_w4x2 split=0 persistent"  # 768 tiles
+    assert fg.describe_gemm(8192, 8192, 8192).endswith(" persistent")
+    assert fg.describe_gemm(4096, 4096, 4096) == "tile256x256_w4x2 split=0"  # one round
+    assert fg.describe_gemm(2048, 4096, 4096) == "tile128x256_w2x4 split=0"
+    assert fg.describe_gemm(2048, 6144, 4096) == "tile256x192_w4x3 split=0"  # not whole 128-column blocks
+    assert fg.describe_gemm(8192, 8192, 128) == "tile256x256_w4x2 split=0"  # one chunk: no walk
+    monkeypatch.setenv("FGFP8_PERSISTENT", "0")
+    assert fg.describe_gemm(2048, 24576, 4096) == "tile256x256_w4x2 split=0"
+    monkeypatch.setenv("FGFP8_PERSISTENT", "1")
+    assert fg.describe_gemm(4096, 4096, 4096) == "tile256x256_w4x2 split=0 persistent"
+    assert fg.describe_gemm(2048, 4096, 4096) == "tile128x256_w2x4 split=0 persistent"
+
+
 def test_decode_slab_plan(monkeypatch):
     """The m <= 16 product's plan (host-only): three slabs per workgroup
     (with a split of 8 waves) for m > 4 where K <= 16384, the split comes to

@@ -71,6 +71,12 @@ def test_dominant_kernel_and_roofline():
     assert two["algorithmic_gflop_per_launch"] == pytest.approx(2 * 2048 * 4096 * (4096 + 12288) / 2 / 1e9, abs=1e-3)
 
 
+def test_persistent_kernel_name():
+    """A plan that walks its tiles persistently names that kernel."""
+    roof = bench.roofline_of([_row("gate_up", 2048, 24576, 4096, "tile256x256_w4x2 persistent", 170e-6)])
+    assert roof["kernel"] == "gemm_nt_persistent_kernel<tile256x256_w4x2>"
+
+
 def test_recorded_traffic_is_gated_by_the_sources_hash(tmp_path, monkeypatch):
     h = bench.kernel_sources_hash()
     assert len(h) == 16 and h == bench.kernel_sources_hash()
