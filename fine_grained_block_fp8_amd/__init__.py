@@ -48,6 +48,10 @@ _lib.m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp,
 _lib.fp8_linear_nt.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _vp]
 _lib.fp8_gemm_nt_fp8_out.argtypes = [_vp, _fp, _i64, _vp, _fp, _vp, _fp, _i64, _vp, _i64, _i64, _i64, _vp]
 _lib.m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _i64, _i64, _vp, _i64, _i64, _vp]
+_lib.m_grouped_fp8_gemm_nt_masked_ws.argtypes = [_vp, _fp, _i64, _vp, _vp, _fp, _i32, _i64, _i64, _vp, _i64, _i64, _vp,
+                                                 _i64, _vp]
+_lib.m_grouped_fp8_gemm_nt_masked_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64]
+_lib.m_grouped_fp8_gemm_nt_masked_workspace_bytes.restype = ctypes.c_int64
 _lib.quantize_fp8_groups_masked.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_groups_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _i64, _vp]
 _lib.quantize_fp8_blocks_ue8m0.argtypes = [_vp, _i64, _i64, _vp, _fp, _vp]
@@ -76,7 +80,7 @@ _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 _lib.fgfp8_describe_linear.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
-              "m_grouped_fp8_gemm_nt_masked", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
+              "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_ws", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
               "fgfp8_describe_linear",
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
@@ -327,12 +331,16 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, d: torch.Tensor, m_indices: torch.Ten
     return d
 
 
-def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor, expected_m: int | None = None):
+def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor, expected_m: int | None = None,
+                                 workspace: torch.Tensor | None = None):
     """Masked grouped product: A = (q [G, max_m, K], sa [K/128, sa_ld]) with the
     group folded into the scale column (row g*max_m + r), B = (q [G, N, K], sb
     [G, ceil(N/128), K/128]), masked_m int32 [G] on the device, d bf16
     [G, max_m, N] (rows past masked_m[g] are not written).  expected_m is a
-    host-side hint for the tile choice."""
+    host-side hint for the tile choice.  workspace (masked_workspace()): one
+    workgroup per CU walks the live tiles and splits the last round's tiles
+    along K where that round would leave CUs idle (deterministic; split tiles
+    round differently from the plain call, within the same bounds)."""
     (qa, sa), (qb, sb) = a, b
     _need(qa, "a", _FP8, 3)
     _need(qb, "b", _FP8, 3)
@@ -349,12 +357,35 @@ def m_grouped_fp8_gemm_nt_masked(a, b, d: torch.Tensor, masked_m: torch.Tensor, 
     if k % GROUP == 0 and sa.shape[0] != k // GROUP:
         raise ValueError("sa must be [K/128, sa_ld]")
     em = 0 if expected_m is None else int(expected_m)
+    if workspace is None:
+        _check(
+            _lib.m_grouped_fp8_gemm_nt_masked(
+                _ptr(qa), _ptr(sa), sa.shape[1], _ptr(masked_m), _ptr(qb), _ptr(sb), g, max_m, em, _ptr(d), n, k,
+                _stream(d)
+            )
+        )
+        return d
+    _need(workspace, "workspace", (torch.uint8,), 1)
     _check(
-        _lib.m_grouped_fp8_gemm_nt_masked(
-            _ptr(qa), _ptr(sa), sa.shape[1], _ptr(masked_m), _ptr(qb), _ptr(sb), g, max_m, em, _ptr(d), n, k, _stream(d)
+        _lib.m_grouped_fp8_gemm_nt_masked_ws(
+            _ptr(qa), _ptr(sa), sa.shape[1], _ptr(masked_m), _ptr(qb), _ptr(sb), g, max_m, em, _ptr(d), n, k,
+            _ptr(workspace), workspace.numel(), _stream(d)
         )
     )
     return d
+
+
+def m_grouped_fp8_gemm_nt_masked_workspace_bytes(num_groups: int, max_m: int, n: int, k: int) -> int:
+    """Bytes of workspace the masked product's workspace form uses (0: invalid arguments)."""
+    return int(_lib.m_grouped_fp8_gemm_nt_masked_workspace_bytes(num_groups, max_m, n, k))
+
+
+def masked_workspace(num_groups: int, max_m: int, n: int, k: int, device="cuda") -> torch.Tensor | None:
+    """A zero-filled workspace for m_grouped_fp8_gemm_nt_masked(..., workspace=),
+    reusable by every later call on the same stream (each call leaves it ready
+    for the next)."""
+    nbytes = m_grouped_fp8_gemm_nt_masked_workspace_bytes(num_groups, max_m, n, k)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
 # fp8_linear_nt: one fused kernel up to FUSED_MAX_M rows when no workspace is
@@ -719,6 +750,8 @@ __all__ = [
     "last_error",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
+    "m_grouped_fp8_gemm_nt_masked_workspace_bytes",
+    "masked_workspace",
     "moe_combine",
     "moe_fp8_layer",
     "moe_gate_up_silu_quantize",

@@ -268,10 +268,9 @@ int fp8_gemm_nt_fp8_out(const void* a_e4m3, const float* sa, int64_t sa_ld, cons
                   who);
 }
 
-int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
-                                 const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
-                                 int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* stream) {
-  const char* who = "m_grouped_fp8_gemm_nt_masked";
+static int masked_impl(const char* who, const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                       const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m, int64_t expected_m,
+                       void* d_bf16, int64_t n, int64_t k, void* stream, void* workspace, int64_t workspace_bytes) {
   if (num_groups < 1) return fail(FGFP8_EINVAL, "%s: num_groups=%d must be >= 1", who, (int)num_groups);
   if (max_m < 0 || max_m % 4 != 0 || (int64_t)num_groups * max_m >= kMaxRows)
     return fail(FGFP8_EINVAL, "%s: max_m=%lld must be a non-negative multiple of 4 (and num_groups * max_m < 2^31)",
@@ -279,6 +278,9 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
   if (n < 0 || n >= kMaxRows) return fail(FGFP8_EINVAL, "%s: n=%lld out of range", who, (long long)n);
   if (int rc = check_k(who, k)) return rc;
   if (int rc = check_sa(who, (int64_t)num_groups * max_m, k, sa_ld)) return rc;
+  if (workspace_bytes < 0) return fail(FGFP8_EINVAL, "%s: negative workspace_bytes", who);
+  if (workspace_bytes > 0 && (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return fail(FGFP8_EINVAL, "%s: the workspace must be a non-null, 256-byte aligned pointer", who);
   if (max_m == 0 || n == 0) return FGFP8_OK;
   if (!a_e4m3 || !sa || !masked_m || !b_e4m3 || !sb || !d_bf16) return fail(FGFP8_EINVAL, "%s: null pointer", who);
   if (!aligned16(a_e4m3) || !aligned16(sa) || !aligned16(masked_m) || !aligned16(b_e4m3) || !aligned16(sb) ||
@@ -286,13 +288,39 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
     return fail(FGFP8_EINVAL, "%s: base pointers must be 16-byte aligned", who);
   if (int rc = check_device(who)) return rc;
   const fgfp8::GemmKind kind = fgfp8::plan_masked(num_groups, max_m, expected_m, n);
+  const bool split = workspace_bytes >= fgfp8::masked_split_workspace_bytes() &&
+                     fgfp8::masked_split_walk(kind, num_groups, max_m, expected_m, n);
   if (env_flag("FGFP8_PRINT_CONFIG"))
-    fprintf(stderr, "[fgfp8] m_grouped_fp8_gemm_nt_masked groups=%d max_m=%lld expected_m=%lld n=%lld k=%lld: %s\n",
-            (int)num_groups, (long long)max_m, (long long)expected_m, (long long)n, (long long)k,
-            fgfp8::gemm_kind_name(kind));
+    fprintf(stderr, "[fgfp8] %s groups=%d max_m=%lld expected_m=%lld n=%lld k=%lld: %s%s\n", who, (int)num_groups,
+            (long long)max_m, (long long)expected_m, (long long)n, (long long)k,
+            split ? "tail-split " : "", fgfp8::gemm_kind_name(kind));
+  if (split)
+    return launched(fgfp8::launch_masked_gemm_split(kind, a_e4m3, sa, sa_ld, masked_m, b_e4m3, sb, num_groups, max_m,
+                                                    d_bf16, n, k, workspace, (hipStream_t)stream),
+                    who);
   return launched(fgfp8::launch_masked_gemm(kind, a_e4m3, sa, sa_ld, masked_m, b_e4m3, sb, num_groups, max_m, d_bf16,
                                             n, k, (hipStream_t)stream),
                   who);
+}
+
+int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                                 const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
+                                 int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* stream) {
+  return masked_impl("m_grouped_fp8_gemm_nt_masked", a_e4m3, sa, sa_ld, masked_m, b_e4m3, sb, num_groups, max_m,
+                     expected_m, d_bf16, n, k, stream, nullptr, 0);
+}
+
+int64_t m_grouped_fp8_gemm_nt_masked_workspace_bytes(int32_t num_groups, int64_t max_m, int64_t n, int64_t k) {
+  if (num_groups < 1 || max_m <= 0 || n <= 0 || k <= 0 || k % 128 != 0 || k > kMaxK) return 0;
+  return fgfp8::masked_split_workspace_bytes();
+}
+
+int m_grouped_fp8_gemm_nt_masked_ws(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                                    const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
+                                    int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* workspace,
+                                    int64_t workspace_bytes, void* stream) {
+  return masked_impl("m_grouped_fp8_gemm_nt_masked_ws", a_e4m3, sa, sa_ld, masked_m, b_e4m3, sb, num_groups, max_m,
+                     expected_m, d_bf16, n, k, stream, workspace, workspace_bytes);
 }
 
 int quantize_fp8_mx(const void* x_bf16, int64_t m, int64_t k, void* q_e4m3, int32_t* s, int64_t s_ld,

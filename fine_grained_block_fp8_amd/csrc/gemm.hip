@@ -617,9 +617,10 @@ __device__ __forceinline__ void store_bf16(uint16_t* __restrict__ d, const v4f_t
 // to zero for the next call.
 struct SplitK {
   int kb0 = 0, kb1 = 0;     // chunk range; kb1 == 0: all of K
-  float* partial = nullptr;  // the tile's FP32 slot, BM * BN floats
+  float* partial = nullptr;  // the tile's FP32 slot, BM * BN floats (n-way: parts consecutive slots)
   int* arrive = nullptr;     // the tile's arrival count (0 between calls)
-  int* ready = nullptr;      // the tile's partial-ready flag (0 between calls)
+  int* ready = nullptr;      // the tile's partial-ready flag (0 between calls; pair form only)
+  int parts = 1, part = 0;   // n-way form: this workgroup sums part `part` of `parts`
 };
 
 // Longest wait for the partner's partial (s_sleep 2 units, ~128 cycles
@@ -706,6 +707,91 @@ __device__ __forceinline__ void split_fixup(uint8_t* lds, v4f_t (&acc)[C::MT][C:
   add_store_rows<C, 0>(rp, base, acc, d, M, N, m0, n0, wm, wn, li, lg);
 }
 
+// n-way form: the tile's parts summed in a fixed order, p_0 + p_1 + ... +
+// p_{parts-1}, one row of MFMA tiles at a time, this workgroup's own part
+// (index own) taken from its registers and every other part loaded from its
+// slot; the bits do not depend on which part arrived last.
+template <class C, int MT0>
+__device__ __forceinline__ void load_part_rows(rsrc_t rp, uint32_t off, const v4f_t (&acc)[C::MT][C::NT], bool own,
+                                               v4f_t (&p)[2][C::NT]) {
+  if (own) {  // uniform
+#pragma unroll
+    for (int r = 0; r < 2; r++)
+#pragma unroll
+      for (int t = 0; t < C::NT; t++) p[r][t] = acc[MT0 + r][t];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 2; r++)
+#pragma unroll
+      for (int t = 0; t < C::NT; t++)
+        p[r][t] = __builtin_bit_cast(v4f_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rp, off + (uint32_t)((MT0 + r) * C::NT + t) * 1024u, 0, kSysCoherent));
+  }
+}
+
+template <class C, int MT0>
+__device__ __forceinline__ void sum_store_rows(rsrc_t rp, uint32_t base, int parts, int own,
+                                               v4f_t (&acc)[C::MT][C::NT], uint16_t* __restrict__ d, int64_t M,
+                                               int64_t N, int64_t m0, int64_t n0, int wm, int wn, int li, int lg) {
+  constexpr uint32_t kSlot = (uint32_t)(C::BM * C::BN * 4);
+  if constexpr (MT0 < C::MT) {
+    static_assert(C::MT % 2 == 0, "rows of MFMA tiles go in pairs");
+    v4f_t sum[2][C::NT];
+    load_part_rows<C, MT0>(rp, base, acc, own == 0, sum);
+    for (int i = 1; i < parts; i++) {
+      v4f_t p[2][C::NT];
+      load_part_rows<C, MT0>(rp, (uint32_t)i * kSlot + base, acc, own == i, p);
+#pragma unroll
+      for (int r = 0; r < 2; r++)
+#pragma unroll
+        for (int t = 0; t < C::NT; t++) sum[r][t] += p[r][t];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; r++)
+#pragma unroll
+      for (int t = 0; t < C::NT; t++) acc[MT0 + r][t] = sum[r][t];
+    store_bf16<C, MT0, MT0 + 2>(d, acc, M, N, m0, n0, wm, wn, li, lg);
+    __builtin_amdgcn_sched_barrier(0);
+    sum_store_rows<C, MT0 + 2>(rp, base, parts, own, acc, d, M, N, m0, n0, wm, wn, li, lg);
+  }
+}
+
+// n-way K split without waiting: every part stores its FP32 partial to its
+// own slot (system scope, written through to memory), and only then counts
+// its arrival; the part that arrives last -- every other part's slot already
+// in memory -- sums the parts in index order, rounds and stores the tile,
+// and resets the count for the next call.  No workgroup ever waits on
+// another, so the protocol cannot hang whatever the residency.  parts == 1:
+// the plain bf16 store.
+template <class C>
+__device__ __forceinline__ void split_fixup_n(uint8_t* lds, v4f_t (&acc)[C::MT][C::NT], const SplitK& sk,
+                                              uint16_t* __restrict__ d, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                              int wave, int wm, int wn, int lane) {
+  const int li = lane & 15, lg = lane >> 4;
+  if (sk.parts <= 1) {
+    store_bf16<C>(d, acc, M, N, m0, n0, wm, wn, li, lg);
+    return;
+  }
+  constexpr uint32_t kSlot = (uint32_t)(C::BM * C::BN * 4);
+  const rsrc_t rp = make_rsrc(sk.partial, (uint32_t)sk.parts * kSlot);
+  // the slot layout of split_fixup: 1 KB of consecutive bytes per wave store
+  const uint32_t base = ((uint32_t)wave * (C::MT * C::NT) * 64u + (uint32_t)lane) * 16u;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int j = 0; j < C::MT * C::NT; j++)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[j / C::NT][j % C::NT]), rp,
+                                           (uint32_t)sk.part * kSlot + base + (uint32_t)j * 1024u, 0, kSysCoherent);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of the part has reached memory
+  int* shared = reinterpret_cast<int*>(lds);
+  __syncthreads();  // every wave's share stored; every wave past its last fragment read (LDS free)
+  if (threadIdx.x == 0)
+    shared[0] = __hip_atomic_fetch_add(sk.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  if (shared[0] != sk.parts - 1) return;  // uniform: another part finishes the tile
+  if (threadIdx.x == 0) __hip_atomic_store(sk.arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  sum_store_rows<C, 0>(rp, base, sk.parts, sk.part, acc, d, M, N, m0, n0, wm, wn, li, lg);
+}
+
 // ROWSKIP (the masked product, whose tiles are often partly filled): a wave
 // whose rows all lie past M skips its fragment reads and MFMAs and only
 // issues its copies, and the waves are laid out row-half-major (wm = wave /
@@ -713,7 +799,7 @@ __device__ __forceinline__ void split_fixup(uint8_t* lds, v4f_t (&acc)[C::MT][C:
 // different row halves and a skipping wave leaves its SIMD to the other.
 // The results are the same bits.
 template <class C, bool FP8OUT = false, bool UE8M0 = false, bool MX = false, bool SILU = false, bool ROWSKIP = false,
-          bool SPLIT = false>
+          int SPLIT = 0>
 __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const uint8_t* b, const float* sa,
                                           const float* sb_base, uint16_t* __restrict__ d, const TileOut& out,
                                           int64_t M, int64_t N, int K, int64_t sa_ld, int64_t m0, int64_t n0,
@@ -834,8 +920,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
     return;
   }
 
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT == 1) {
     split_fixup<C>(lds, acc, sk, d, M, N, m0, n0, wave, wm, wn, lane);
+    return;
+  } else if constexpr (SPLIT == 2) {
+    split_fixup_n<C>(lds, acc, sk, d, M, N, m0, n0, wave, wm, wn, lane);
     return;
   }
 
@@ -1218,7 +1307,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_splitk_kernel(
   sk.partial = ws_partials + (size_t)t * (C::BM * C::BN);
   sk.arrive = ws_counters + t;
   sk.ready = ws_counters + tiles + t;
-  gemm_tile<C, false, false, false, false, false, true>(lds, A + m0 * K, B + n0 * K, SA, SB, D,
+  gemm_tile<C, false, false, false, false, false, 1>(lds, A + m0 * K, B + n0 * K, SA, SB, D,
                                                         TileOut{D, nullptr, nullptr, 0}, M, N, K, sa_ld, m0, n0, 0,
                                                         GateUp{}, sk);
 }
@@ -1308,6 +1397,109 @@ __global__ __launch_bounds__(C::THREADS) void masked_gemm_nt_kernel(
   gemm_tile<C, false, false, false, false, true>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA,
                                                 SB + (int64_t)g * NB * KB, D, TileOut{D, nullptr, nullptr, 0},
                                                 base + rows, N, K, sa_ld, m0, n0);
+}
+
+// The masked product over a workspace.  Its live tiles -- row tiles below
+// each group's count, in group order, column tile fastest -- are dealt
+// round-robin to one workgroup per compute unit (G of them).  When the last
+// round would hold r < G tiles, those r tiles are split along K into s =
+// min(G / r, kMaskedMaxParts, K / 128) parts each, so that the last round
+// spreads over r * s workgroups instead of leaving G - r CUs idle; their
+// parts meet through split_fixup_n (slots: s per split tile, at most G;
+// counters: one per split tile).  The counts stay on the device: every
+// workgroup derives the tile list from them.
+constexpr int kMaskedMaxParts = 8;
+constexpr int kMaskedMaxGrid = 256;  // slots and counters the workspace holds
+
+__device__ __forceinline__ int masked_rows(const int32_t* masked_m, int g, int64_t max_m) {
+  const int rows = masked_m[g];
+  return rows < 0 ? 0 : (rows > max_m ? (int)max_m : rows);
+}
+
+// Live tiles of the first g groups for every g at once: lane l of the
+// returned chunk scan holds the live tiles of groups g0 .. g0 + l.
+__device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void masked_gemm_nt_split_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ SA, const int32_t* __restrict__ masked_m,
+    const uint8_t* __restrict__ B, const float* __restrict__ SB, uint16_t* __restrict__ D, int64_t max_m, int64_t N,
+    int K, int64_t sa_ld, int num_groups, int tiles_n, int* __restrict__ counters, float* __restrict__ partials) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+  const int lane = threadIdx.x & 63;
+  const int G = (int)gridDim.x;
+  const int KB = K / kGroup;
+  const int64_t NB = (N + kGroup - 1) / kGroup;
+  // the first 64 groups' live tiles stay in registers (lane = group); more
+  // groups are rescanned from memory
+  const int rows0 = lane < num_groups ? masked_rows(masked_m, lane, max_m) : 0;
+  const int lt0 = (rows0 + C::BM - 1) / C::BM * tiles_n;
+  const int incl0 = wave_inclusive_sum(lt0, lane);
+  int live = __shfl(incl0, 63, 64);
+  for (int g0 = 64; g0 < num_groups; g0 += 64) {
+    const int g = g0 + lane;
+    const int lt = g < num_groups ? (masked_rows(masked_m, g, max_m) + C::BM - 1) / C::BM * tiles_n : 0;
+    live += __shfl(wave_inclusive_sum(lt, lane), 63, 64);
+  }
+  const int rem = live % G;
+  int parts = rem ? G / rem : 1;
+  parts = parts < kMaskedMaxParts ? parts : kMaskedMaxParts;
+  parts = parts < KB ? parts : KB;
+  if (parts < 2) parts = 1;
+  const int full = parts > 1 ? live - rem : live;
+  const int items = full + (parts > 1 ? rem * parts : 0);
+  for (int it = (int)blockIdx.x; it < items; it += G) {  // uniform
+    int tile = it, part = 0;
+    if (it >= full) {
+      tile = full + (it - full) / parts;
+      part = (it - full) % parts;
+    }
+    // the tile's group: the first whose inclusive live count passes it
+    int g = 0, local = 0, before = 0;
+    for (int g0 = 0; g0 < num_groups; g0 += 64) {
+      const int gl = g0 + lane;
+      const int lt =
+          g0 == 0 ? lt0 : (gl < num_groups ? (masked_rows(masked_m, gl, max_m) + C::BM - 1) / C::BM * tiles_n : 0);
+      const int incl = g0 == 0 ? incl0 : wave_inclusive_sum(lt, lane);
+      const uint64_t hit = __ballot(before + incl > tile);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        g = g0 + l;
+        local = tile - before - (__shfl(incl, l, 64) - __shfl(lt, l, 64));
+        break;
+      }
+      before += __shfl(incl, 63, 64);
+    }
+    g = __builtin_amdgcn_readfirstlane(g);
+    const int rows = __builtin_amdgcn_readfirstlane(g < 64 ? __shfl(rows0, g, 64) : masked_rows(masked_m, g, max_m));
+    local = __builtin_amdgcn_readfirstlane(local);
+    const int tm = local / tiles_n, tn = local - (local / tiles_n) * tiles_n;
+    const int64_t base = (int64_t)g * max_m;
+    const int64_t m0 = base + (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    SplitK sk;
+    sk.kb0 = 0;
+    sk.kb1 = KB;
+    if (it >= full) {
+      const int q = tile - full;
+      sk.parts = parts;
+      sk.part = part;
+      sk.kb0 = part * KB / parts;
+      sk.kb1 = (part + 1) * KB / parts;
+      sk.partial = partials + (size_t)q * parts * (C::BM * C::BN);
+      sk.arrive = counters + q;
+    }
+    __syncthreads();  // every wave is past the previous tile's last LDS read
+    gemm_tile<C, false, false, false, false, true, 2>(lds, A + m0 * K, B + (int64_t)g * N * K + n0 * K, SA,
+                                                      SB + (int64_t)g * NB * KB, D, TileOut{D, nullptr, nullptr, 0},
+                                                      base + rows, N, K, sa_ld, m0, n0, 0, GateUp{}, sk);
+  }
 }
 
 // ------------------------------------------------------------ host side
@@ -1432,9 +1624,8 @@ bool plan_persistent(const GemmPlan& plan, int64_t m, int64_t n, int64_t k) {
   return use_persistent(tiles, k, false, bm == 256 && bn == 256);
 }
 
-// Workgroups of a persistent launch: one per compute unit (the tiles' LDS
-// allows one per CU), a multiple of 8, at most the padded tile count.
-static int persistent_grid(int t_pad) {
+// Compute units of the current device (queried once per device).
+static int device_cus() {
   static std::atomic<int> cus[64];  // per device; 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -1443,6 +1634,13 @@ static int persistent_grid(int t_pad) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kCUs;
     cus[dev].store(n, std::memory_order_relaxed);
   }
+  return n;
+}
+
+// Workgroups of a persistent launch: one per compute unit (the tiles' LDS
+// allows one per CU), a multiple of 8, at most the padded tile count.
+static int persistent_grid(int t_pad) {
+  const int n = device_cus();
   int g = n / 8 * 8;
   if (g < 8) g = 8;
   return g < t_pad ? g : t_pad;
@@ -1531,6 +1729,63 @@ static hipError_t launch_masked_tile(const void* a, const float* sa, int64_t sa_
                      stream, static_cast<const uint8_t*>(a), sa, masked_m, static_cast<const uint8_t*>(b), sb,
                      static_cast<uint16_t*>(d), max_m, n, (int)k, sa_ld, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+// Whether the workspace form walks the tiles with the last round split: only
+// where the expected live tiles (num_groups * ceil(expected_m / 128) column
+// tiles of the plan) fill at most a quarter of the CUs.  Measured (N = 4096,
+// K = 7168, A/B on one box): 32 live tiles 26.4 against 45.8 us, 64 tiles
+// 38.2 against 46.2, but 128 tiles 65.3 against 47.6 -- from about half the
+// CUs on, the plain launch already streams the weights at the HBM rate, and
+// the split's partial round trips only add bytes -- and from 256 tiles on
+// within -4% .. +12% of the plain launch (1024 tokens top-4 over 32 experts,
+// Zipf: 271 against 266 us).  Tuning and test override:
+// FGFP8_MASKED_SPLIT=0|1.
+bool masked_split_walk(GemmKind kind, int32_t num_groups, int64_t max_m, int64_t expected_m, int64_t n) {
+  if (const char* force = getenv("FGFP8_MASKED_SPLIT")) return strcmp(force, "0") != 0;
+  const int64_t bn = kind == kGemmTile128x128 ? 128 : 256;
+  const int64_t em = expected_m > 0 && expected_m < max_m ? expected_m : max_m;
+  const int64_t tiles = (int64_t)num_groups * ((em + 127) / 128) * ((n + bn - 1) / bn);
+  int cus = device_cus();
+  cus = cus < kMaskedMaxGrid ? cus : kMaskedMaxGrid;
+  return tiles * 4 <= cus;
+}
+
+int64_t masked_split_workspace_bytes() {
+  // counters, then kMaskedMaxGrid slots of the widest 128-row tile
+  return (int64_t)kMaskedMaxGrid * 4 + (int64_t)kMaskedMaxGrid * 128 * 256 * 4;
+}
+
+template <class C>
+static hipError_t launch_masked_split_tile(const void* a, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                                           const void* b, const float* sb, int32_t num_groups, int64_t max_m, void* d,
+                                           int64_t n, int64_t k, void* workspace, hipStream_t stream) {
+  static_assert(C::BM * C::BN <= 128 * 256, "a slot holds one 128x256 tile");
+  const int tiles_n = (int)((n + C::BN - 1) / C::BN);
+  int grid = device_cus();
+  grid = grid < kMaskedMaxGrid ? grid : kMaskedMaxGrid;
+  int* counters = static_cast<int*>(workspace);
+  float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + (int64_t)kMaskedMaxGrid * 4);
+  hipLaunchKernelGGL(masked_gemm_nt_split_kernel<C>, dim3((uint32_t)grid), dim3(C::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(a), sa, masked_m, static_cast<const uint8_t*>(b), sb,
+                     static_cast<uint16_t*>(d), max_m, n, (int)k, sa_ld, (int)num_groups, tiles_n, counters, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_masked_gemm_split(GemmKind kind, const void* a, const float* sa, int64_t sa_ld,
+                                    const int32_t* masked_m, const void* b, const float* sb, int32_t num_groups,
+                                    int64_t max_m, void* d, int64_t n, int64_t k, void* workspace,
+                                    hipStream_t stream) {
+  switch (kind) {
+    case kGemmTile128x256:
+      return launch_masked_split_tile<Tile128x256>(a, sa, sa_ld, masked_m, b, sb, num_groups, max_m, d, n, k,
+                                                   workspace, stream);
+    case kGemmTile128x128:
+      return launch_masked_split_tile<Tile128x128>(a, sa, sa_ld, masked_m, b, sb, num_groups, max_m, d, n, k,
+                                                   workspace, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_masked_gemm(GemmKind kind, const void* a, const float* sa, int64_t sa_ld, const int32_t* masked_m,

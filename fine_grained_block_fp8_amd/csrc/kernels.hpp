@@ -115,6 +115,16 @@ GemmKind plan_masked(int32_t num_groups, int64_t max_m, int64_t expected_m, int6
 hipError_t launch_masked_gemm(GemmKind kind, const void* a, const float* sa, int64_t sa_ld, const int32_t* masked_m,
                               const void* b, const float* sb, int32_t num_groups, int64_t max_m, void* d, int64_t n,
                               int64_t k, hipStream_t stream);
+// The masked product over a workspace of masked_split_workspace_bytes():
+// one workgroup per CU walks the live tiles, the last round's tiles split
+// along K when it would leave CUs idle.  The workspace is zero before the
+// first call; each call leaves it so.
+int64_t masked_split_workspace_bytes();
+// Whether that form pays for this call (from the expected rows per group).
+bool masked_split_walk(GemmKind kind, int32_t num_groups, int64_t max_m, int64_t expected_m, int64_t n);
+hipError_t launch_masked_gemm_split(GemmKind kind, const void* a, const float* sa, int64_t sa_ld,
+                                    const int32_t* masked_m, const void* b, const float* sb, int32_t num_groups,
+                                    int64_t max_m, void* d, int64_t n, int64_t k, void* workspace, hipStream_t stream);
 
 // Streaming read (measurement aid): bytes (a multiple of
 // stream_read_unit_bytes()) of src read once; out receives one 16-byte XOR

@@ -208,6 +208,39 @@ int m_grouped_fp8_gemm_nt_masked(const void* a_e4m3, const float* sa, int64_t sa
                                  const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
                                  int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* stream);
 
+/* The masked product with a workspace (the same row of the deepgemm-rust
+ * README; its kernel notes name persistent tile scheduling and a tile order
+ * for the SM count), for dispatches too small to fill the GPU.  Where the
+ * expected live tiles -- num_groups * ceil(expected_m / 128) tiles of 128
+ * rows, times the plan's column tiles -- fill at most a quarter of the
+ * compute units, one workgroup per compute unit walks the live tiles (those
+ * whose rows lie below their group's count, in group order), and when the
+ * last round of tiles would leave compute units idle, each of that round's
+ * tiles is split along K into up to 8 parts whose FP32 partials meet in the
+ * workspace; otherwise the call runs m_grouped_fp8_gemm_nt_masked.  The
+ * parts are summed in a fixed order by whichever arrives last, so the
+ * results are deterministic; a split tile's sum of parts rounds differently
+ * from the unsplit form (within the same parity bar), and which tiles split
+ * depends on the live tile count and the device's compute units.  No
+ * workgroup waits on another.  FGFP8_MASKED_SPLIT=1 (0) forces (forbids)
+ * the walk whatever expected_m says.
+ *
+ * workspace  device memory, 256-byte aligned, of workspace_bytes >=
+ *            m_grouped_fp8_gemm_nt_masked_workspace_bytes(...); zero-filled
+ *            before its first use, and every call leaves it so when it
+ *            completes.  Calls that may overlap in time must not share it.  A
+ *            smaller workspace (or NULL with 0 bytes) runs
+ *            m_grouped_fp8_gemm_nt_masked.
+ * Other arguments and requirements: as m_grouped_fp8_gemm_nt_masked. */
+int m_grouped_fp8_gemm_nt_masked_ws(const void* a_e4m3, const float* sa, int64_t sa_ld, const int32_t* masked_m,
+                                    const void* b_e4m3, const float* sb, int32_t num_groups, int64_t max_m,
+                                    int64_t expected_m, void* d_bf16, int64_t n, int64_t k, void* workspace,
+                                    int64_t workspace_bytes, void* stream);
+/* Bytes of workspace m_grouped_fp8_gemm_nt_masked_ws uses: 1 KB of counters
+ * and 256 FP32 slots of one 128 x 256 tile (32 MiB + 1 KB); 0 for invalid
+ * arguments.  Host-only. */
+int64_t m_grouped_fp8_gemm_nt_masked_workspace_bytes(int32_t num_groups, int64_t max_m, int64_t n, int64_t k);
+
 /* quantize_fp8_groups over the same dispatch buffer, reading the counts on
  * the device: rows r < masked_m[g] of each group g (clamped to [0, max_m])
  * are quantized exactly as quantize_fp8_groups quantizes them (codes and

@@ -55,6 +55,8 @@ def test_library_exports_every_declared_function():
         "moe_route_noalloc_max_workspace_bytes",
         "fp8_gemm_nt_ws",
         "fp8_gemm_nt_workspace_bytes",
+        "m_grouped_fp8_gemm_nt_masked_ws",
+        "m_grouped_fp8_gemm_nt_masked_workspace_bytes",
         "fgfp8_stream_read",
     }
     lib = fg.library()
@@ -168,6 +170,31 @@ def test_masked_rejects():
     assert call(k=200) == fg.FGFP8_EINVAL
     assert call(max_m=0, sa_ld=4) == fg.FGFP8_OK
     assert call(n=0) == fg.FGFP8_OK
+
+
+def test_masked_workspace_size_and_rejects():
+    """m_grouped_fp8_gemm_nt_masked_ws: the workspace query (1 KB of counters
+    and 256 slots of one 128 x 256 FP32 tile) and the checks that come before
+    any device work."""
+    lib = fg.library()
+    want = 256 * 4 + 256 * 128 * 256 * 4
+    assert lib.m_grouped_fp8_gemm_nt_masked_workspace_bytes(32, 128, 4096, 7168) == want
+    assert fg.m_grouped_fp8_gemm_nt_masked_workspace_bytes(1, 4, 16, 128) == want
+    assert lib.m_grouped_fp8_gemm_nt_masked_workspace_bytes(0, 128, 4096, 7168) == 0
+    assert lib.m_grouped_fp8_gemm_nt_masked_workspace_bytes(4, 128, 4096, 100) == 0
+    assert lib.m_grouped_fp8_gemm_nt_masked_workspace_bytes(4, -4, 4096, 256) == 0
+
+    def call(ws=P, nbytes=want, g=4, max_m=64, k=256):
+        return lib.m_grouped_fp8_gemm_nt_masked_ws(P, P, 256, P, P, P, g, max_m, 32, P, 128, k, ws, nbytes, None)
+
+    assert call(ws=P + 16) == fg.FGFP8_EINVAL
+    assert "256-byte" in fg.last_error()
+    assert call(ws=None) == fg.FGFP8_EINVAL
+    assert call(nbytes=-1) == fg.FGFP8_EINVAL
+    assert call(max_m=62) == fg.FGFP8_EINVAL  # the masked call's own checks apply
+    assert "m_grouped_fp8_gemm_nt_masked_ws" in fg.last_error()
+    assert call(k=200) == fg.FGFP8_EINVAL
+    assert call(max_m=0) == fg.FGFP8_OK
 
 
 def test_masked_quantizer_rejects():
@@ -317,6 +344,8 @@ def test_no_device_is_reported_not_crashed():
     assert lib.m_grouped_fp8_gemm_nt_contiguous(P, P, 128, P, P, P, 2, P, 128, 64, 128, None) == fg.FGFP8_ENODEV
     assert lib.fp8_linear_nt(P, 1, 256, P, P, 128, P, None, None, 0, None) == fg.FGFP8_ENODEV
     assert lib.m_grouped_fp8_gemm_nt_masked(P, P, 256, P, P, P, 4, 64, 32, P, 128, 256, None) == fg.FGFP8_ENODEV
+    assert lib.m_grouped_fp8_gemm_nt_masked_ws(P, P, 256, P, P, P, 4, 64, 32, P, 128, 256, P, 1 << 26,
+                                               None) == fg.FGFP8_ENODEV
     assert lib.quantize_fp8_groups_masked(P, P, 4, 64, 256, P, P, 256, None) == fg.FGFP8_ENODEV
     assert lib.fp8_gemm_nt_fp8_out(P, P, 8, P, P, P, P, 8, None, 8, 256, 256, None) == fg.FGFP8_ENODEV
     mpm, ws = lib.moe_max_padded_rows(100, 4, 8), lib.moe_route_workspace_bytes(100, 8)

@@ -19,7 +19,7 @@ from tests.parity import bits32, check_gemm, codes, d_to_f64, magnitude_sum, to_
 pytestmark = pytest.mark.gpu
 
 
-def gpu_masked(c: workloads.Masked, masked_dev=None, expected_m=None):
+def gpu_masked(c: workloads.Masked, masked_dev=None, expected_m=None, workspace=None):
     g, mm, n, k = c.num_groups, c.max_m, c.n, c.k
     x = to_dev_bf16(c.a.reshape(g * mm, k))
     q, sa = fg.quantize_fp8_groups(x)
@@ -38,7 +38,7 @@ def gpu_masked(c: workloads.Masked, masked_dev=None, expected_m=None):
         masked_dev = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
     d = torch.full((g, mm, n), float("nan"), dtype=torch.bfloat16, device="cuda")
     fg.m_grouped_fp8_gemm_nt_masked((q.view(g, mm, k), sa), (qb, sb), d, masked_dev,
-                                    c.expected_m if expected_m is None else expected_m)
+                                    c.expected_m if expected_m is None else expected_m, workspace=workspace)
     torch.cuda.synchronize()
     return q, sa, qb, sb, d
 
@@ -146,6 +146,131 @@ def test_decode_moe_dispatch_buffer_sampled():
     check_masked(c, q, sa, qb, sb, d, groups=[0, 1, 7, 20, 31], rows_per_group=6, cblocks=[0, 13, 31], rng=rng)
     for e in range(c.num_groups):
         assert torch.isfinite(d[e, : int(c.masked_m[e])].float()).all()
+
+
+# ------------------------------------------------ the workspace (tail-split) form
+
+
+def tail_split_tiles(counts, max_m, n, k, bn, grid):
+    """The tiles the workspace form splits along K, by the rule its header
+    states: live tiles (128-row tiles below each count, group order, column
+    tile fastest) dealt to `grid` workgroups; the last round's r tiles split
+    into min(grid // r, 8, K/128) parts when that is at least 2."""
+    tiles_n = -(-n // bn)
+    rows = np.clip(np.asarray(counts), 0, max_m)
+    order = [(g, tm, tn) for g in range(len(rows)) for tm in range(-(-int(rows[g]) // 128)) for tn in range(tiles_n)]
+    rem = len(order) % grid
+    parts = min(grid // rem if rem else 1, 8, k // 128)
+    return (set(order[len(order) - rem:]) if parts >= 2 else set()), parts
+
+
+def masked_grid():
+    return min(torch.cuda.get_device_properties(0).multi_processor_count, 256)
+
+
+@pytest.mark.parametrize(
+    "counts,max_m,n,k",
+    [
+        ([0, 137, 200], 200, 264, 384),
+        ([64, 1, 17, 0, 33], 64, 128, 256),
+        ([300, 129, 128, 256], 300, 512, 640),
+        ([5], 8, 16, 128),
+        ([900, 0, 3, 894, 260], 900, 4096, 1024),  # several whole rounds before the split one
+        (np.random.default_rng(5).integers(-3, 200, 70).tolist(), 196, 384, 512),
+    ],
+)
+def test_tail_split_matches_oracle_and_is_deterministic(counts, max_m, n, k, capfd, monkeypatch):
+    """The split walk (forced) against the oracle on ragged cases (few live
+    tiles, so the whole launch is one split round; several whole rounds
+    before the split one; 70 groups, past the 64 held in registers), twice
+    in a row on one workspace: the same bits both times, and every tile the
+    rule does not split equal to the plain call bit for bit."""
+    monkeypatch.setenv("FGFP8_PRINT_CONFIG", "1")
+    monkeypatch.setenv("FGFP8_MASKED_SPLIT", "1")
+    c = workloads.small_masked(counts, max_m, n, k, seed=sum(counts) + max_m + n + k + 1)
+    ws = fg.masked_workspace(c.num_groups, c.max_m, c.n, c.k)
+    q, sa, qb, sb, d = gpu_masked(c, workspace=ws)
+    line = [ln for ln in capfd.readouterr().err.splitlines() if "m_grouped_fp8_gemm_nt_masked_ws" in ln][-1]
+    assert "tail-split" in line, line
+    check_masked(c, q, sa, qb, sb, d)
+    masked_dev = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
+    d2 = torch.full_like(d, float("nan"))
+    fg.m_grouped_fp8_gemm_nt_masked((q.view(c.num_groups, c.max_m, c.k), sa), (qb, sb), d2, masked_dev, c.expected_m,
+                                    workspace=ws)
+    d3 = torch.full_like(d, float("nan"))
+    fg.m_grouped_fp8_gemm_nt_masked((q.view(c.num_groups, c.max_m, c.k), sa), (qb, sb), d3, masked_dev, c.expected_m)
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.int16), d2.view(torch.int16)), "the workspace form is not deterministic"
+    bn = 256 if line.endswith("tile128x256_w2x4") else 128
+    split, parts = tail_split_tiles(c.masked_m, c.max_m, c.n, c.k, bn, masked_grid())
+    same = torch.ones(d.shape, dtype=torch.bool, device="cuda")
+    for g, tm, tn in split:
+        same[g, tm * 128 : tm * 128 + 128, tn * bn : tn * bn + bn] = False
+    a, b = d.view(torch.int16), d3.view(torch.int16)
+    assert torch.equal(a[same], b[same]), "a tile that is not split differs from the plain call"
+
+
+def test_tail_split_zipf_dispatch_buffer(monkeypatch):
+    """The split walk (forced) on the 32-expert, K = 7168, N = 4096 decode
+    dispatch buffer (1024 tokens, Zipf(1.1) top-4): 800 live tiles, so three
+    whole rounds and 32 tiles split in 8.  Every split tile against the
+    oracle (all its columns, sampled rows), sampled rows of other groups, the
+    untouched rows past the counts, and the tiles that are not split equal to
+    the plain call bit for bit."""
+    monkeypatch.setenv("FGFP8_MASKED_SPLIT", "1")
+    c = workloads.moe_masked()
+    ws = fg.masked_workspace(c.num_groups, c.max_m, c.n, c.k)
+    q, sa, qb, sb, d = gpu_masked(c, workspace=ws)
+    split, parts = tail_split_tiles(c.masked_m, c.max_m, c.n, c.k, 256, masked_grid())
+    if masked_grid() == 256:
+        assert len(split) == 32 and parts == 8
+    groups = sorted({g for g, _, _ in split} | {0, 7})
+    rng = np.random.default_rng(13)
+    check_masked(c, q, sa, qb, sb, d, groups=groups, rows_per_group=8, rng=rng)
+    d3 = torch.full_like(d, float("nan"))
+    masked_dev = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
+    fg.m_grouped_fp8_gemm_nt_masked((q.view(c.num_groups, c.max_m, c.k), sa), (qb, sb), d3, masked_dev, c.expected_m)
+    torch.cuda.synchronize()
+    same = torch.ones(d.shape, dtype=torch.bool, device="cuda")
+    for g, tm, tn in split:
+        same[g, tm * 128 : tm * 128 + 128, tn * 256 : tn * 256 + 256] = False
+    assert torch.equal(d.view(torch.int16)[same], d3.view(torch.int16)[same])
+    for e in range(c.num_groups):
+        assert torch.isfinite(d[e, : int(c.masked_m[e])].float()).all()
+
+
+def test_tail_split_workspace_reused_by_a_smaller_call(monkeypatch):
+    """One workspace for two different calls in a row (the second smaller):
+    each call leaves the counters at zero for the next."""
+    monkeypatch.setenv("FGFP8_MASKED_SPLIT", "1")
+    ws = fg.masked_workspace(4, 300, 512, 640)
+    for counts, max_m, n, k in (([300, 129, 128, 256], 300, 512, 640), ([0, 37, 5], 40, 136, 256)):
+        c = workloads.small_masked(counts, max_m, n, k, seed=max_m + n)
+        q, sa, qb, sb, d = gpu_masked(c, workspace=ws)
+        check_masked(c, q, sa, qb, sb, d)
+    assert int(ws[:1024].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_workspace_form_walks_only_small_dispatches(capfd, monkeypatch):
+    """By default the workspace form walks and splits only where the expected
+    live tiles fill at most a quarter of the CUs: 2 groups of 16 expected rows
+    at N = 4096 (32 tiles) walk, 32 groups of 128 (512 tiles) run the plain
+    kernel -- with the plain call's bits."""
+    monkeypatch.setenv("FGFP8_PRINT_CONFIG", "1")
+    for groups, em, walk in ((2, 16, True), (32, 128, False)):
+        c = workloads.small_masked([em] * groups, 128, 4096, 256, seed=groups)
+        c = workloads.Masked(c.name, c.num_groups, c.max_m, c.n, c.k, c.masked_m, em, c.a, c.b)
+        ws = fg.masked_workspace(c.num_groups, c.max_m, c.n, c.k)
+        q, sa, qb, sb, d = gpu_masked(c, workspace=ws)
+        line = [ln for ln in capfd.readouterr().err.splitlines() if "m_grouped_fp8_gemm_nt_masked_ws" in ln][-1]
+        assert ("tail-split" in line) == walk, line
+        check_masked(c, q, sa, qb, sb, d, rows_per_group=6, cblocks=[0, 17, 31])
+        if not walk:
+            d3 = torch.full_like(d, float("nan"))
+            fg.m_grouped_fp8_gemm_nt_masked((q.view(c.num_groups, c.max_m, c.k), sa), (qb, sb), d3,
+                                            torch.from_numpy(c.masked_m.astype(np.int32)).cuda(), em)
+            torch.cuda.synchronize()
+            assert torch.equal(d.view(torch.int16), d3.view(torch.int16))
 
 
 # ------------------------------------------- quantizing the real rows only
