@@ -474,8 +474,9 @@ const char* fgfp8_last_error(void);
  * ends in "slabs=3"; same values either way).  FGFP8_MASKED_TILE, set to
  * tile128x256_w2x4 or tile128x128_w2x2, forces that tile in
  * m_grouped_fp8_gemm_nt_masked in place of the one expected_m selects
- * (tuning and tests; same values).  FGFP8_PRINT_CONFIG=1 prints each call's
- * kernel choice to stderr. */
+ * (tuning and tests; same values).  FGFP8_MASKED_SPLIT=1 (0) forces (forbids)
+ * the split walk of m_grouped_fp8_gemm_nt_masked_ws.  FGFP8_PRINT_CONFIG=1
+ * prints each call's kernel choice to stderr. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
 
 /* The path fp8_linear_nt takes for an m x n x k call, act_out non-zero when
