@@ -510,3 +510,58 @@ def test_split_k_forced_ragged_shapes(m, n, k, monkeypatch):
     d3 = _split_run(q, sa, qb, sb, m, n, small)
     torch.cuda.synchronize()
     assert torch.equal(d3.view(torch.int16), d0.view(torch.int16)), "an undersized workspace must run fp8_gemm_nt"
+
+
+def test_workspace_forms_replay_in_graphs(monkeypatch):
+    """The two workspace protocols under HIP graph capture: the K-split dense
+    product (pairs meeting through arrival counts and ready flags) and the
+    masked product's split walk (forced; parts counted in, the last one sums)
+    each reset their counters inside the kernel and record no memset, so
+    every replay -- with eager calls on the same workspaces in between --
+    gives the eager result bit for bit."""
+    monkeypatch.setenv("FGFP8_MASKED_SPLIT", "1")
+    lin = workloads.random_linear(512, 1024, 8192, seed=321)
+    x = torch.from_numpy(lin.a.view(np.int16)).view(torch.bfloat16).cuda()
+    w = torch.from_numpy(lin.b.view(np.int16)).view(torch.bfloat16).cuda()
+    qa, sa = fg.quantize_fp8_groups(x)
+    qb, sb = fg.quantize_fp8_blocks(w)
+    ws_dense = fg.gemm_workspace(lin.m, lin.n, lin.k)
+    assert ws_dense is not None, fg.describe_gemm(lin.m, lin.n, lin.k)
+    d_dense = torch.empty((lin.m, lin.n), dtype=torch.bfloat16, device="cuda")
+    c = workloads.small_masked([300, 129, 128, 256], 300, 512, 640, seed=99)
+    g_, mm, n, k = c.num_groups, c.max_m, c.n, c.k
+    mq, msa = fg.quantize_fp8_groups(torch.from_numpy(c.a.reshape(g_ * mm, k).view(np.int16)).view(torch.bfloat16).cuda())
+    mqb, msb = fg.quantize_fp8_blocks(torch.from_numpy(c.b.reshape(g_ * n, k).view(np.int16)).view(torch.bfloat16).cuda())
+    mqb, msb = mqb.view(g_, n, k), msb.view(g_, n // 128, k // 128)
+    counts = torch.from_numpy(c.masked_m.astype(np.int32)).cuda()
+    ws_masked = fg.masked_workspace(g_, mm, n, k)
+    d_masked = torch.full((g_, mm, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+
+    def work():
+        fg.fp8_gemm_nt((qa, sa), (qb, sb), d_dense, workspace=ws_dense)
+        fg.m_grouped_fp8_gemm_nt_masked((mq.view(g_, mm, k), msa), (mqb, msb), d_masked, counts, c.expected_m,
+                                        workspace=ws_masked)
+
+    work()
+    torch.cuda.synchronize()
+    ref_dense, ref_masked = d_dense.clone(), d_masked.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        work()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            work()
+    torch.cuda.synchronize()
+    for i in range(4):
+        d_dense.fill_(float("nan"))
+        d_masked.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d_dense.view(torch.int16), ref_dense.view(torch.int16)), f"replay {i}: K-split product differs"
+        assert torch.equal(d_masked.view(torch.int16), ref_masked.view(torch.int16)), f"replay {i}: masked differs"
+        work()  # eager calls on the same workspaces between replays
+        torch.cuda.synchronize()
+    assert int(ws_masked[:1024].view(torch.int32).abs().sum().item()) == 0
