@@ -1021,7 +1021,9 @@ def bench_moe(args, fg, torch, workloads, steps=None) -> dict:
     st = trial_stats(elapsed, steps)
     flops = g.useful_flops
     padded = 2 * g.m * g.n * g.k
-    kernel = "grouped_gemm_nt_kernel<tile128x256_w2x4>"
+    plan = fg.describe_grouped(g.m, g.n, g.k)
+    kernel = ("grouped_gemm_nt_persistent_kernel<" if plan.endswith(" persistent") else "grouped_gemm_nt_kernel<") + \
+        plan.split()[0] + ">"
     log(f"moe grouped: ms/step {st['ms_per_step']}; gemm mean {gt * 1e6:.1f} us")
     rows = [{"name": g.name, "m_pad": g.m, "n": g.n, "k": g.k, "groups": g.num_groups, "quant_us": qt * 1e6,
              "gemm_us": gt * 1e6, "gemm_tflops_useful": flops / gt / 1e12, "gemm_tflops_padded": padded / gt / 1e12,

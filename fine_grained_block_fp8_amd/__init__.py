@@ -79,9 +79,10 @@ _lib.fgfp8_last_error.argtypes = []
 _lib.fgfp8_last_error.restype = ctypes.c_char_p
 _lib.fgfp8_describe_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 _lib.fgfp8_describe_linear.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_char_p, _i64]
+_lib.fgfp8_describe_grouped.argtypes = [_i64, _i64, _i64, ctypes.c_char_p, _i64]
 for _name in ("quantize_fp8_groups", "quantize_fp8_blocks", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
               "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_ws", "fp8_gemm_nt_fp8_out", "fp8_linear_nt", "fgfp8_describe_gemm",
-              "fgfp8_describe_linear",
+              "fgfp8_describe_linear", "fgfp8_describe_grouped",
               "quantize_fp8_groups_ue8m0", "quantize_fp8_blocks_ue8m0", "fp8_gemm_nt_ue8m0", "moe_route_contiguous",
               "moe_gather_quantize", "silu_mul_quantize", "moe_combine", "quantize_fp8_mx", "fp8_gemm_nt_mx",
               "moe_gate_up_silu_quantize", "quantize_fp8_groups_masked",
@@ -719,6 +720,13 @@ def stream_read(src: torch.Tensor, out: torch.Tensor) -> None:
 def describe_gemm(m: int, n: int, k: int) -> str:
     buf = ctypes.create_string_buffer(128)
     _check(_lib.fgfp8_describe_gemm(m, n, k, buf, 128))
+    return buf.value.decode()
+
+
+def describe_grouped(m: int, n: int, k: int) -> str:
+    """The kernel m_grouped_fp8_gemm_nt_contiguous runs for m padded rows."""
+    buf = ctypes.create_string_buffer(128)
+    _check(_lib.fgfp8_describe_grouped(m, n, k, buf, 128))
     return buf.value.decode()
 
 

@@ -234,7 +234,7 @@ int m_grouped_fp8_gemm_nt_contiguous(const void* a_e4m3, const float* sa, int64_
   if (int rc = check_device(who)) return rc;
   if (env_flag("FGFP8_PRINT_CONFIG"))
     fprintf(stderr, "[fgfp8] m_grouped_fp8_gemm_nt_contiguous m=%lld n=%lld k=%lld groups=%d: %s\n", (long long)m,
-            (long long)n, (long long)k, (int)num_groups, fgfp8::gemm_kind_name(fgfp8::kGemmTile128x256));
+            (long long)n, (long long)k, (int)num_groups, fgfp8::gemm_kind_name(fgfp8::plan_grouped_gemm(m, n, k)));
   return launched(fgfp8::launch_grouped_gemm(a_e4m3, sa, sa_ld, m_indices, b_e4m3, sb, num_groups, d_bf16, m, n, k,
                                              (hipStream_t)stream),
                   who);
@@ -601,6 +601,14 @@ int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len)
   if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: null or empty buffer");
   if (m <= 0 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_gemm: bad shape");
   describe_plan(m, n, k, buf, (size_t)len);
+  return FGFP8_OK;
+}
+
+int fgfp8_describe_grouped(int64_t m, int64_t n, int64_t k, char* buf, int64_t len) {
+  if (!buf || len <= 0) return fail(FGFP8_EINVAL, "fgfp8_describe_grouped: null or empty buffer");
+  if (m <= 0 || m % 128 || n <= 0 || k <= 0 || k % 128) return fail(FGFP8_EINVAL, "fgfp8_describe_grouped: bad shape");
+  snprintf(buf, (size_t)len, "%s%s", fgfp8::gemm_kind_name(fgfp8::plan_grouped_gemm(m, n, k)),
+           fgfp8::plan_grouped_walk(m, n, k) ? " persistent" : "");
   return FGFP8_OK;
 }
 

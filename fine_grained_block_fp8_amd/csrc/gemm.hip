@@ -55,7 +55,13 @@ struct Tile {
   // packed E8M0 words of the MX recipe) at +0, and at +1024 the weight
   // scales: one 4-byte slot per lane of the copy, slot j holding the scale
   // of the tile's column block j, or (MX) the tile's BN packed E8M0 words.
-  static constexpr int S_BYTES = 1024 + 1024;
+  // Tiles whose stages leave no room for the scale area (128x512: two
+  // stages of 80 KB fill the 160 KB) keep their scales in registers: each
+  // wave loads the activation scales of its rows and the weight scale of its
+  // column block for the next chunk with vector loads (gemm_tile), and the
+  // LDS holds operand stages only.
+  static constexpr bool REG_SCALES = STAGES * (A_BYTES + B_BYTES) + STAGES * 2048 + WAVES * TM * 4 > 160 * 1024;
+  static constexpr int S_BYTES = REG_SCALES ? 0 : 1024 + 1024;
   static constexpr int SB_IN_S = 1024;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = STAGES * A_BYTES;
@@ -63,7 +69,7 @@ struct Tile {
   // FP8-output epilogue: one float per (wave, row) for the partner-wave amax
   // exchange of 64-column wave tiles.
   static constexpr int EPI_OFF = S_OFF + STAGES * S_BYTES;
-  static constexpr int LDS = EPI_OFF + WAVES * TM * 4;
+  static constexpr int LDS = EPI_OFF + (REG_SCALES ? 0 : WAVES * TM * 4);
   static_assert(TN == 64 || TN == 128, "a wave tile spans 64 or 128 columns of one scale block");
   static_assert(TM % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
   // The copies of a chunk are 8-row segments dealt to the copying waves in
@@ -71,8 +77,8 @@ struct Tile {
   // vmcnt(0) wait of the two-stage loop, which does not count copies.
   static_assert(((BM / 8) % COPY_WAVES == 0 && (BN / 8) % COPY_WAVES == 0) || STAGES == 2,
                 "segments divide evenly among waves");
-  static_assert(BM * 4 <= SB_IN_S, "one wave loads a stage's activation scales");
-  static_assert(BN * 4 <= S_BYTES - SB_IN_S, "one wave loads a stage's MX weight scales");
+  static_assert(REG_SCALES || BM * 4 <= SB_IN_S, "one wave loads a stage's activation scales");
+  static_assert(REG_SCALES || BN * 4 <= S_BYTES - SB_IN_S, "one wave loads a stage's MX weight scales");
   static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -91,6 +97,15 @@ using Tile256x192 = Tile<256, 192, 4, 3, 2>;
 using Tile128x256 = Tile<128, 256, 2, 4, 3>;
 using Tile256x128 = Tile<256, 128, 4, 2, 3>;
 using Tile128x128 = Tile<128, 128, 2, 2, 3>;
+// The grouped product's wide tile: 128 rows (the experts' alignment unit, so
+// no tile straddles two experts) by 512 columns, 8 waves of 64x128 -- the
+// 256x256 tile's wave tiles, LDS fragment bytes per FLOP and stage size
+// (plus 16 KB), where 128x256 tiles need 64x64 wave tiles.
+using Tile128x512 = Tile<128, 512, 2, 4, 2>;
+static_assert(Tile128x512::REG_SCALES && Tile128x512::LDS == 160 * 1024, "two 80 KB stages, scales in registers");
+static_assert(!Tile256x256::REG_SCALES && !Tile256x192::REG_SCALES && !Tile128x256::REG_SCALES &&
+                  !Tile256x128::REG_SCALES && !Tile128x128::REG_SCALES,
+              "the other tiles stage their scales through LDS");
 
 // LDS layout of a K chunk: row r of a tile is 128 bytes (8 slots of 16
 // bytes); logical slot c of row r is stored at slot c ^ swz(r).  Fragment
@@ -187,7 +202,7 @@ struct StageLoader {
 #pragma unroll
       for (int i = 0; i < NSEG; i++) issue(i, stage, kb);
     }
-    issue(NSEG, stage, kb);
+    if constexpr (!C::REG_SCALES) issue(NSEG, stage, kb);
   }
 };
 
@@ -806,6 +821,8 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
                                           int64_t sb_ld = 0, const GateUp& gu = GateUp{}, const SplitK& sk = SplitK{}) {
   // the FP8-output and SiLU epilogues pair waves as wave = wm + WAVES_M * wn
   static_assert(!ROWSKIP || (!FP8OUT && !UE8M0 && !MX && !SILU), "row skipping is for the bf16 FP32-scale tile");
+  static_assert(!C::REG_SCALES || (C::STAGES == 2 && !FP8OUT && !UE8M0 && !MX && !SILU && !ROWSKIP && SPLIT == 0),
+                "register scales: the two-stage bf16 FP32-scale tile");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = ROWSKIP ? wave / C::WAVES_N : wave % C::WAVES_M;
@@ -869,7 +886,25 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
   // segment copies), chosen once per wave, so that the loop itself has no
   // branch around the copies.
   const int kb0 = SPLIT ? sk.kb0 : 0, kb1 = SPLIT ? sk.kb1 : KB;
+  // REG_SCALES: this wave's scales of the next chunk -- its rows' activation
+  // scales (row wm*TM + 16 mt + li: the rows of its promotions) and its
+  // column block's weight scale -- loaded one chunk ahead; the two-stage
+  // loop's vmcnt(0) at the top of a chunk covers them.  Rows past M read
+  // whatever the scale buffer holds there, as the LDS copy does; their
+  // outputs are never stored.
+  float sa_nx[C::MT], sb_nx = 0.0f;
+  const int64_t nb_wave = (n0 + wn * C::TN) / kGroup < nblocks ? (n0 + wn * C::TN) / kGroup : nblocks - 1;
+  auto load_scales = [&](int kb) {
+    if constexpr (C::REG_SCALES) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; mt++)
+        sa_nx[mt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, (uint32_t)(wm * C::TM + 16 * mt + li) * 4u, (uint32_t)kb * (uint32_t)(sa_ld * 4), 0));
+      sb_nx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, (uint32_t)(nb_wave * KB + kb) * 4u, 0, 0));
+    }
+  };
   loader.all(0, kb0);
+  load_scales(kb0);
   if (C::STAGES == 3) loader.all(1, kb0 + 1 < kb1 ? kb0 + 1 : kb0);
   auto k_loop = [&](auto cp) {
   constexpr bool CP = decltype(cp)::value;
@@ -885,6 +920,18 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* a, const 
       __builtin_amdgcn_s_waitcnt(0x0F70 | StageLoader<C>::NSEG);  // vmcnt(NSEG)
     }
     barrier_no_fence();
+    if constexpr (C::REG_SCALES) {
+      // the products first, so that the next chunk's loads reuse the same
+      // registers (no loop-carried copies, whose waits would drain the copies)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; mt++) sc[mt] = sa_nx[mt] * sb_nx;
+      load_scales(next);
+#pragma unroll
+      for (int mt = 0; mt < C::MT; mt++) af[mt] = read_frag(lds, aa, (uint32_t)(stage * C::A_BYTES + 2048 * mt));
+      mfma_tiles<C, 0, C::NT, false, CP>(lds, ba, stage, load_stage, af, sc, nullptr, acc, loader, next);
+      stage = stage + 1 == C::STAGES ? 0 : stage + 1;
+      continue;
+    }
     if (wave < 2) loader.issue(StageLoader<C>::NSEG, load_stage, next);  // scales
     if constexpr (MX) {
       int ea[C::MT];
@@ -1154,6 +1201,7 @@ __device__ __forceinline__ void gemm_persistent(uint8_t* lds, const Src& src, co
   const int KB = K / kGroup;
   const int G = (int)gridDim.x;
 
+  static_assert(!C::REG_SCALES, "the walk stages its scales through LDS");
   TileRef cur, nxt;
   int t = next_tile(src, (int)blockIdx.x, cur);
   if (t >= src.t_pad) return;  // uniform, before any barrier
@@ -1588,6 +1636,7 @@ const char* gemm_kind_name(GemmKind kind) {
     case kGemmTile128x128: return "tile128x128_w2x2";
     case kGemmDecode: return "decode_splitk_slab16";
     case kGemmTile256x256SplitK2: return "tile256x256_w4x2_splitk2";
+    case kGemmTile128x512: return "tile128x512_w2x4";
   }
   return "?";
 }
@@ -1691,6 +1740,7 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* a, const float* sa, int
     case kGemmTile256x128: return launch_tile<Tile256x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream);
     case kGemmDecode: return launch_decode(plan.split, a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmTile128x512: break;  // the grouped product's tile only
   }
   return hipErrorInvalidValue;
 }
@@ -1827,6 +1877,7 @@ hipError_t launch_gemm_ue8m0(const GemmPlan& plan, const void* a, const float* s
     case kGemmTile128x128: return launch_tile<Tile128x128>(a, sa, sa_ld, b, sb, out, m, n, k, stream, true);
     // decode shapes: the promote path is exact for power-of-two scales
     case kGemmDecode: return launch_decode(plan.split, a, sa, sa_ld, b, sb, d, m, n, k, stream);
+    case kGemmTile128x512: break;
   }
   return hipErrorInvalidValue;
 }
@@ -1874,12 +1925,52 @@ hipError_t launch_grouped_gemm_silu(const void* a, const float* sa, int64_t sa_l
   return hipGetLastError();
 }
 
+// The grouped product's tile: 128x512 or 128x256, whichever costs fewer
+// rounds of 256 CUs times tile area over its measured efficiency (outputs per
+// CU per unit time, relative to the dense 256x256 tile).  The wide tile
+// reads a chunk's fragments with the 256x256 tile's LDS bytes per FLOP, but
+// here the experts' weights stream from HBM, and a 128-row block reads its
+// expert's whole weight whatever the tile width, so both tiles move the same
+// weight bytes per FLOP.  Measured (interleaved A/B, one box): the 32-expert
+// product at K = 7168, N = 4096 1107.9-1109.2 us against 1106.2-1108.5 us for
+// 128x256; the MoE layer's down product (K = 2048, N = 7168) 630.1-630.6 us
+// against 645.0-645.5 for 128x256 in the persistent walk, hence 0.84.
+// Tuning and test override: FGFP8_GROUPED_TILE=<tile name>.
+constexpr double kEff128x512 = 0.84;
+GemmKind plan_grouped_gemm(int64_t m, int64_t n, int64_t k) {
+  (void)k;
+  if (const char* force = getenv("FGFP8_GROUPED_TILE")) {
+    if (strcmp(force, gemm_kind_name(kGemmTile128x512)) == 0) return kGemmTile128x512;
+    if (strcmp(force, gemm_kind_name(kGemmTile128x256)) == 0) return kGemmTile128x256;
+  }
+  const int64_t blocks = m / 128;
+  auto cost = [&](int64_t bn, double eff) {
+    const int64_t tiles = blocks * ((n + bn - 1) / bn);
+    return (double)((tiles + kCUs - 1) / kCUs) * (double)(128 * bn) / eff;
+  };
+  return cost(512, kEff128x512) < cost(256, 0.82) ? kGemmTile128x512 : kGemmTile128x256;
+}
+
+// Whether the grouped product runs the persistent walk (128x256 tiles only).
+bool plan_grouped_walk(int64_t m, int64_t n, int64_t k) {
+  if (plan_grouped_gemm(m, n, k) != kGemmTile128x256) return false;
+  return use_persistent((m / 128) * ((n + 255) / 256), k, true, true);
+}
+
 hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
                                const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream) {
+  if (plan_grouped_gemm(m, n, k) == kGemmTile128x512) {
+    using W = Tile128x512;
+    const int tiles_m = (int)(m / W::BM), tiles_n = (int)((n + W::BN - 1) / W::BN);
+    hipLaunchKernelGGL(grouped_gemm_nt_kernel<W>, dim3((uint32_t)tiles_m * tiles_n), dim3(W::THREADS), 0, stream,
+                       static_cast<const uint8_t*>(a), sa, m_indices, static_cast<const uint8_t*>(b), sb,
+                       static_cast<uint16_t*>(d), m, n, (int)k, sa_ld, (int)num_groups, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
   using C = Tile128x256;
   const int tiles_m = (int)(m / C::BM), tiles_n = (int)((n + C::BN - 1) / C::BN);
-  if (use_persistent((int64_t)tiles_m * tiles_n, k, true, true)) {
+  if (plan_grouped_walk(m, n, k)) {
     const int t_pad = (tiles_m * tiles_n + 7) / 8 * 8;
     const GroupedTiles src{static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), sb, m_indices, m, n, k,
                            (int)num_groups, tiles_m, tiles_n, t_pad};

@@ -29,6 +29,7 @@ enum GemmKind : int {
   kGemmDecode = 4,       // M <= 16: 16-column slabs, K split across waves
   kGemmTile256x192 = 5,  // 256x192, 12 waves of 64x64
   kGemmTile256x256SplitK2 = 6,  // 256x256 tiles, K split over two workgroups (needs a workspace)
+  kGemmTile128x512 = 7,  // 128x512, 8 waves of 64x128, scales in registers (grouped product)
 };
 
 struct GemmPlan {
@@ -98,6 +99,9 @@ hipError_t launch_decode_fused(const void* x, const void* b, const float* sb, vo
 bool use_persistent(int64_t tiles, int64_t k, bool grouped, bool measured_tile);
 // Whether fp8_gemm_nt (bf16 output, FP32 scales) runs this plan's tiles as the persistent walk.
 bool plan_persistent(const GemmPlan& plan, int64_t m, int64_t n, int64_t k);
+// The grouped product's tile (kGemmTile128x512 or kGemmTile128x256).
+GemmKind plan_grouped_gemm(int64_t m, int64_t n, int64_t k);
+bool plan_grouped_walk(int64_t m, int64_t n, int64_t k);
 hipError_t launch_grouped_gemm(const void* a, const float* sa, int64_t sa_ld, const int32_t* m_indices,
                                const void* b, const float* sb, int32_t num_groups, void* d, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream);

@@ -479,6 +479,18 @@ const char* fgfp8_last_error(void);
  * prints each call's kernel choice to stderr. */
 int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
 
+/* The kernel m_grouped_fp8_gemm_nt_contiguous runs for an m x n x k call
+ * (m the padded row count, a multiple of 128): "tile128x512_w2x4" (8 waves
+ * of 64x128, one workgroup per 128-row block and 512 columns; its scales
+ * are loaded into registers) or "tile128x256_w2x4" (8 waves of 64x64),
+ * followed by " persistent" when the 128x256 tiles are walked by one
+ * workgroup per compute unit.  The tile with fewer CU-rounds times tile area
+ * over its measured efficiency is taken; FGFP8_GROUPED_TILE, set to one of
+ * the two names, forces it (tuning and tests; same values either way).
+ * Writes a NUL-terminated string of at most len bytes into buf.  Host-only.
+ * FGFP8_EINVAL for a null buffer or a bad shape. */
+int fgfp8_describe_grouped(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);
+
 /* The path fp8_linear_nt takes for an m x n x k call, act_out non-zero when
  * the caller passes q_e4m3/sa: "fused act-quant + decode_splitk_slab16
  * split=S slabs=L form=F" (F = lds4, lds16 or registers, as described at

@@ -33,6 +33,7 @@ def test_library_exports_every_declared_function():
         "m_grouped_fp8_gemm_nt_contiguous",
         "fgfp8_last_error",
         "fgfp8_describe_gemm",
+        "fgfp8_describe_grouped",
         "fgfp8_describe_linear",
         "fp8_linear_nt",
         "m_grouped_fp8_gemm_nt_masked",
@@ -354,6 +355,26 @@ def test_no_device_is_reported_not_crashed():
     assert lib.moe_gather_quantize_tokens(P, 10, 128, 4, P, P, 256, P, P, 256, None) == fg.FGFP8_ENODEV
     assert lib.silu_mul_quantize(P, 256, 128, P, P, P, 256, None) == fg.FGFP8_ENODEV
     assert lib.moe_combine(P, 64, 128, P, P, 8, 4, P, None) == fg.FGFP8_ENODEV
+
+
+def test_describe_grouped_plans(monkeypatch):
+    """The grouped product's tile: 128x512 where it takes fewer rounds of the
+    256 CUs per unit of work (the 32-expert MoE layout: 273 blocks x 8 such
+    tiles against 16 of 128x256), 128x256 for narrow N, the override, and the
+    shape checks."""
+    assert fg.describe_grouped(34944, 4096, 7168) == "tile128x512_w2x4"
+    assert fg.describe_grouped(256, 384, 512).startswith("tile128x256_w2x4")
+    monkeypatch.setenv("FGFP8_GROUPED_TILE", "tile128x256_w2x4")
+    assert fg.describe_grouped(34944, 4096, 7168) == "tile128x256_w2x4"
+    monkeypatch.setenv("FGFP8_PERSISTENT", "1")
+    assert fg.describe_grouped(34944, 4096, 7168) == "tile128x256_w2x4 persistent"
+    monkeypatch.setenv("FGFP8_GROUPED_TILE", "tile128x512_w2x4")
+    assert fg.describe_grouped(256, 384, 512) == "tile128x512_w2x4"  # the wide tile has no walk
+    buf = ctypes.create_string_buffer(64)
+    lib = fg.library()
+    for m, n, k in [(100, 4096, 7168), (0, 4096, 7168), (256, 0, 128), (256, 128, 100)]:
+        assert lib.fgfp8_describe_grouped(m, n, k, buf, 64) == fg.FGFP8_EINVAL, (m, n, k)
+    assert lib.fgfp8_describe_grouped(256, 128, 128, None, 64) == fg.FGFP8_EINVAL
 
 
 def test_describe_gemm_plans():

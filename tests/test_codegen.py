@@ -11,7 +11,8 @@ drains per kernel: one after the loop for the three-stage tiles, and one more
 for the two-stage tiles (256x256, 256x192: their wait at the top of each
 chunk is a full drain by design, since their copies are one chunk ahead) and
 for the fused gate_up kernel (its epilogue waits once for its m_indices
-loads).  The persistent walk of a
+loads), and for the 128x512 tile (before its loop, once for the first
+chunk's scale loads into registers).  The persistent walk of a
 three-stage tile adds one drain, taken once per tile before its stores leave
 the counter.
 """
@@ -64,6 +65,11 @@ def test_gemm_loops_have_no_full_drain(tmp_path):
         # and the others), each copy with its own drains
         waves = int(tile.group(3)) * int(tile.group(4))
         if waves >= 8 and (two_stage or "persistent" in name):
+            allowed += 1
+        # the 128x512 tile keeps its scales in registers: before one copy of
+        # its loop the compiler waits for the first chunk's scale loads, which
+        # the first chunk-top wait of the loop waits for anyway
+        if tile.group(1, 2) == ("128", "512"):
             allowed += 1
         assert n <= allowed, f"{name}: {n} full vmcnt drains"
         loops = mfma_loop_drains(asm, name)

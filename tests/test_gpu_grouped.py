@@ -105,9 +105,10 @@ def test_one_group_equals_dense():
 def test_moe_zipf_32_experts_every_tile():
     """The 32-expert Zipf case (K = 7168, N = 4096): every output column of
     one real row from each 64-row band of the layout (the height of a wave's
-    tile) that holds real rows, so every 128x256 workgroup tile of every
-    expert -- and every 64-row wave tile with real rows -- is compared with
-    the oracle, with each expert's whole weight quantized by the oracle."""
+    tile) that holds real rows, so every workgroup tile of every expert (128
+    rows, 512 or 256 columns as planned) -- and every 64-row wave tile with
+    real rows -- is compared with the oracle, with each expert's whole weight
+    quantized by the oracle."""
     g = workloads.moe_grouped()
     assert g.num_groups == 32 and g.k == 7168 and g.n == 4096
     assert np.all(g.starts % 128 == 0) and g.m % 128 == 0
@@ -155,9 +156,37 @@ def test_persistent_walk_matches_per_block_kernel(sizes, n, k, monkeypatch):
     several tiles per workgroup) gives the same bits as one workgroup per
     block."""
     g = workloads.small_grouped(sizes, n, k, seed=sum(sizes) + 7)
+    monkeypatch.setenv("FGFP8_GROUPED_TILE", "tile128x256_w2x4")  # the walk's tile
     monkeypatch.setenv("FGFP8_PERSISTENT", "0")
     _, _, _, _, d1 = gpu_grouped(g)
     monkeypatch.setenv("FGFP8_PERSISTENT", "1")
+    q, sa, qb, sb, d2 = gpu_grouped(g)
+    real = torch.from_numpy(g.m_indices >= 0).cuda()
+    assert torch.equal(d1[real].view(torch.int16), d2[real].view(torch.int16))
+    check_groups(g, q, sa, qb, sb, d2, rows_per_group=16)
+
+
+@pytest.mark.parametrize(
+    "sizes,n,k",
+    [
+        ([5, 0, 130, 1, 128], 512, 128),
+        ([300, 129, 64, 0, 1], 700, 256),
+        ([700, 1000, 260, 0, 513], 1000, 384),
+        ([5, 0, 2000, 1, 128, 900], 4224, 640),
+        ([1] * 9, 128, 128),
+    ],
+)
+def test_wide_tile_matches_128x256(sizes, n, k, monkeypatch):
+    """The 128x512 grouped tile (its scales loaded into registers, not staged
+    through LDS) gives the same bits as the 128x256 tile on every real row:
+    ragged N inside and across 512-column tiles, a one-chunk K, empty and
+    one-row groups.  It also meets the oracle."""
+    g = workloads.small_grouped(sizes, n, k, seed=sum(sizes) + n + 11)
+    print(f"wide tile {sizes} n={n} k={k}", flush=True)
+    monkeypatch.setenv("FGFP8_PERSISTENT", "0")
+    monkeypatch.setenv("FGFP8_GROUPED_TILE", "tile128x256_w2x4")
+    _, _, _, _, d1 = gpu_grouped(g)
+    monkeypatch.setenv("FGFP8_GROUPED_TILE", "tile128x512_w2x4")
     q, sa, qb, sb, d2 = gpu_grouped(g)
     real = torch.from_numpy(g.m_indices >= 0).cuda()
     assert torch.equal(d1[real].view(torch.int16), d2[real].view(torch.int16))
