@@ -1219,8 +1219,10 @@ def bench_moe_layer(args, fg, torch, workloads):
                 "frac": round(f1 / stage[gu] / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": None,
                 "algorithmic_flops_per_launch": f1, "mean_launch_us": round(stage[gu] * 1e6, 2)}
     else:
-        # both products run the same tile (down, at K <= 4096, in the persistent walk): the per-launch average
-        roof = {"bound": "mfma", "kernel": "grouped_gemm_nt[_persistent]_kernel<tile128x256_w2x4> (gate_up and down launches averaged)",
+        # both products run m_grouped_fp8_gemm_nt_contiguous: the per-launch average
+        plans = sorted({fg.describe_grouped(m, 2 * it, hd), fg.describe_grouped(m, hd, it)})
+        roof = {"bound": "mfma", "kernel": "m_grouped_fp8_gemm_nt_contiguous [" + "; ".join(plans) +
+                "] (gate_up and down launches averaged)",
                 "achieved": round(flops / gemm_s / 1e12, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(flops / gemm_s / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": None,
                 "algorithmic_flops_per_launch": flops / 2, "mean_launch_us": round(gemm_s / 2 * 1e6, 2)}
