@@ -1938,7 +1938,10 @@ hipError_t launch_grouped_gemm_silu(const void* a, const float* sa, int64_t sa_l
 // Tuning and test override: FGFP8_GROUPED_TILE=<tile name>.
 constexpr double kEff128x512 = 0.84;
 GemmKind plan_grouped_gemm(int64_t m, int64_t n, int64_t k) {
-  (void)k;
+  // The wide tile's weight panel (512 rows of K bytes) is addressed with
+  // 32-bit buffer offsets: beyond 2^23 - 128 it would wrap, so such K takes
+  // the 128x256 tile (256 K < 2^32 for every K the calls accept), forced or not.
+  if (512 * k >= (int64_t(1) << 32)) return kGemmTile128x256;
   if (const char* force = getenv("FGFP8_GROUPED_TILE")) {
     if (strcmp(force, gemm_kind_name(kGemmTile128x512)) == 0) return kGemmTile128x512;
     if (strcmp(force, gemm_kind_name(kGemmTile128x256)) == 0) return kGemmTile128x256;

@@ -486,7 +486,9 @@ int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len)
  * followed by " persistent" when the 128x256 tiles are walked by one
  * workgroup per compute unit.  The tile with fewer CU-rounds times tile area
  * over its measured efficiency is taken; FGFP8_GROUPED_TILE, set to one of
- * the two names, forces it (tuning and tests; same values either way).
+ * the two names, forces it (tuning and tests; same values either way).  K of
+ * 2^23 or more always takes 128x256 (the wide tile's 512-row weight panel
+ * would pass 32-bit buffer offsets).
  * Writes a NUL-terminated string of at most len bytes into buf.  Host-only.
  * FGFP8_EINVAL for a null buffer or a bad shape. */
 int fgfp8_describe_grouped(int64_t m, int64_t n, int64_t k, char* buf, int64_t len);

@@ -370,6 +370,11 @@ def test_describe_grouped_plans(monkeypatch):
     assert fg.describe_grouped(34944, 4096, 7168) == "tile128x256_w2x4 persistent"
     monkeypatch.setenv("FGFP8_GROUPED_TILE", "tile128x512_w2x4")
     assert fg.describe_grouped(256, 384, 512) == "tile128x512_w2x4"  # the wide tile has no walk
+    # its 512-row weight panel must stay within 32-bit buffer offsets, forced or not
+    assert fg.describe_grouped(256, 4096, (1 << 23) - 128) == "tile128x512_w2x4"
+    assert fg.describe_grouped(256, 4096, 1 << 23).startswith("tile128x256_w2x4")
+    monkeypatch.delenv("FGFP8_GROUPED_TILE")
+    assert fg.describe_grouped(34944, 4096, (1 << 24) - 128).startswith("tile128x256_w2x4")
     buf = ctypes.create_string_buffer(64)
     lib = fg.library()
     for m, n, k in [(100, 4096, 7168), (0, 4096, 7168), (256, 0, 128), (256, 128, 100)]:
