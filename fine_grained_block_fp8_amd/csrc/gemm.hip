@@ -1934,8 +1934,11 @@ hipError_t launch_grouped_gemm_silu(const void* a, const float* sa, int64_t sa_l
 // weight bytes per FLOP.  Measured (interleaved A/B, one box): the 32-expert
 // product at K = 7168, N = 4096 1107.9-1109.2 us against 1106.2-1108.5 us for
 // 128x256; the MoE layer's down product (K = 2048, N = 7168) 630.1-630.6 us
-// against 645.0-645.5 for 128x256 in the persistent walk, hence 0.84.
-// Tuning and test override: FGFP8_GROUPED_TILE=<tile name>.
+// against 645.0-645.5 for 128x256 in the persistent walk, hence 0.84.  At
+// K <= 1024 the walk, which hides each tile's pipeline fill behind the last
+// one's chunks, is ahead (M_pad = 34944 over 32 experts: N = 14336 758-764 us
+// against 789-795 for 128x512; N = 4096 223 against 224-225), so those shapes
+// keep 128x256 tiles.  Tuning and test override: FGFP8_GROUPED_TILE=<tile name>.
 constexpr double kEff128x512 = 0.84;
 GemmKind plan_grouped_gemm(int64_t m, int64_t n, int64_t k) {
   // The wide tile's weight panel (512 rows of K bytes) is addressed with
@@ -1946,6 +1949,7 @@ GemmKind plan_grouped_gemm(int64_t m, int64_t n, int64_t k) {
     if (strcmp(force, gemm_kind_name(kGemmTile128x512)) == 0) return kGemmTile128x512;
     if (strcmp(force, gemm_kind_name(kGemmTile128x256)) == 0) return kGemmTile128x256;
   }
+  if (k <= 1024) return kGemmTile128x256;
   const int64_t blocks = m / 128;
   auto cost = [&](int64_t bn, double eff) {
     const int64_t tiles = blocks * ((n + bn - 1) / bn);

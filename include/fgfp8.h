@@ -486,7 +486,8 @@ int fgfp8_describe_gemm(int64_t m, int64_t n, int64_t k, char* buf, int64_t len)
  * followed by " persistent" when the 128x256 tiles are walked by one
  * workgroup per compute unit.  The tile with fewer CU-rounds times tile area
  * over its measured efficiency is taken; FGFP8_GROUPED_TILE, set to one of
- * the two names, forces it (tuning and tests; same values either way).  K of
+ * the two names, forces it (tuning and tests; same values either way).
+ * Without it, K <= 1024 takes 128x256 (its walk is ahead there).  K of
  * 2^23 or more always takes 128x256 (the wide tile's 512-row weight panel
  * would pass 32-bit buffer offsets).
  * Writes a NUL-terminated string of at most len bytes into buf.  Host-only.

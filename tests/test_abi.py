@@ -363,6 +363,8 @@ def test_describe_grouped_plans(monkeypatch):
     tiles against 16 of 128x256), 128x256 for narrow N, the override, and the
     shape checks."""
     assert fg.describe_grouped(34944, 4096, 7168) == "tile128x512_w2x4"
+    assert fg.describe_grouped(34944, 7168, 2048) == "tile128x512_w2x4"
+    assert fg.describe_grouped(34944, 14336, 1024) == "tile128x256_w2x4 persistent"  # short K: the walk
     assert fg.describe_grouped(256, 384, 512).startswith("tile128x256_w2x4")
     monkeypatch.setenv("FGFP8_GROUPED_TILE", "tile128x256_w2x4")
     assert fg.describe_grouped(34944, 4096, 7168) == "tile128x256_w2x4"
